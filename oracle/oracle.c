@@ -1,0 +1,418 @@
+/*
+ * Plain, slow CPU oracle for tiled block-32 quantized matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path (the
+ * HIP library and its Python binding) never calls it and shares no code,
+ * header, table or constant with it.
+ *
+ * Source of every definition: the page "Hexagon backend developer details"
+ * (llama.cpp docs/backend/snapdragon/developer.md), section "Tiled Weight
+ * Formats" with its subsections "Tile Dimensions and Grid Layout" and
+ * "Block-32 Quantized Formats" (Q4_0, Q8_0, IQ4_NL), and section "Memory
+ * buffers" (dynamically quantized activations).  Where the page is silent the
+ * reading taken is stated at the function.
+ *
+ * Everything is scalar C, one element at a time, in the order the page states
+ * it.  Floating-point results are fp64 unless the data format fixes the
+ * precision (fp16 scales, fp32 activation quantization).
+ *
+ * Parity pins: every exported function is pinned by the tests under
+ * tests/test_oracle_*.py except or_flat_decode's nibble order (the flat GGML
+ * block layout is not printed on the page), which is "parity unpinned" by the
+ * page and only self-consistent with the input generator.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_IQ4_NL = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
+
+/* ---------------------------------------------------------------------------
+ * IEEE 754 binary16 / bfloat16 conversions, written from the format
+ * definitions (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits;
+ * bfloat16 is the upper half of a binary32).
+ * ------------------------------------------------------------------------- */
+
+/* binary16 bits -> value, exact (every binary16 value is a binary32 value). */
+float or_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);              /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);  /* (1 + f/1024) * 2^(e-15) */
+    return (float)(sign ? -v : v);
+}
+
+/* value -> binary16 bits, round to nearest, ties to even, with subnormals and
+ * overflow to infinity. */
+uint16_t or_f32_to_f16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs((double)x);
+    if (isnan(x))
+        return 0x7e00;
+    if (a >= 65520.0)                 /* halfway to 2^16 and above: infinity */
+        return sign | 0x7c00;
+    if (a == 0.0)
+        return sign;
+    int ex;
+    frexp(a, &ex);                    /* a = m * 2^ex, 0.5 <= m < 1 */
+    int e = ex - 1;                   /* a in [2^e, 2^(e+1)) */
+    if (e < -14)
+        e = -14;                      /* subnormal range shares the quantum of 2^-14 */
+    double quantum = ldexp(1.0, e - 10);
+    double n = a / quantum;           /* exact: a has 24 significant bits */
+    double fl = floor(n);
+    double r = n - fl;
+    if (r > 0.5 || (r == 0.5 && fmod(fl, 2.0) != 0.0))
+        fl += 1.0;
+    long ni = (long)fl;
+    if (ni == 2048) {                 /* rounded up into the next binade */
+        ni = 1024;
+        e += 1;
+    }
+    if (e > 15)
+        return sign | 0x7c00;
+    if (ni < 1024)                    /* subnormal (only possible at e == -14) */
+        return sign | (uint16_t)ni;
+    return sign | (uint16_t)(((e + 15) << 10) | (ni - 1024));
+}
+
+float or_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* ---------------------------------------------------------------------------
+ * Sizes.  Tile sizes from "Block-32 Quantized Formats": Q4_0 576 B, Q8_0
+ * 1088 B, IQ4_NL 576 B.  Flat block sizes follow the GGML block-32 layouts
+ * (2-byte fp16 scale + 16 bytes of nibbles, or + 32 int8 quants).
+ * ------------------------------------------------------------------------- */
+long or_tile_bytes(int type)
+{
+    switch (type) {
+    case OR_Q4_0: return 576;
+    case OR_Q8_0: return 1088;
+    case OR_IQ4_NL: return 576;
+    }
+    return 0;
+}
+
+long or_block_bytes(int type)
+{
+    switch (type) {
+    case OR_Q4_0: return 18;
+    case OR_Q8_0: return 34;
+    case OR_IQ4_NL: return 18;
+    }
+    return 0;
+}
+
+/* "Tile Dimensions and Grid Layout": n_k_tiles = ne0 / 32, n_col_tiles =
+ * (ne1 + 31) / 32, with ne0 = K and ne1 = N. */
+long or_tiled_bytes(int type, long K, long N)
+{
+    return (K / 32) * ((N + 31) / 32) * or_tile_bytes(type);
+}
+
+long or_flat_bytes(int type, long K, long N)
+{
+    return N * (K / 32) * or_block_bytes(type);
+}
+
+/* ---------------------------------------------------------------------------
+ * Flat row-major GGML block-32 layout (the repack source).  The page says only
+ * that weights are repacked "from flat row-major GGML layouts"; the reading
+ * taken is GGML's own block-32 layout: row n holds K/32 consecutive blocks;
+ * a Q4_0 / IQ4_NL block is an fp16 scale followed by 16 bytes whose low
+ * nibbles are elements 0..15 and high nibbles elements 16..31; a Q8_0 block is
+ * an fp16 scale followed by 32 int8 elements.
+ *
+ * codes[n*K + k] receives the raw code of element k of row n: 0..15 for the
+ * 4-bit types, the int8 byte (as uint8) for Q8_0.  scales[n*(K/32) + b]
+ * receives the fp16 bits of block b of row n.
+ * ------------------------------------------------------------------------- */
+void or_flat_decode(int type, const uint8_t *flat, long K, long N,
+                    uint8_t *codes, uint16_t *scales)
+{
+    long nb = K / 32, bb = or_block_bytes(type);
+    for (long n = 0; n < N; n++) {
+        for (long b = 0; b < nb; b++) {
+            const uint8_t *blk = flat + (n * nb + b) * bb;
+            scales[n * nb + b] = (uint16_t)(blk[0] | (blk[1] << 8));
+            for (int j = 0; j < 32; j++) {
+                uint8_t c;
+                if (type == OR_Q8_0)
+                    c = blk[2 + j];
+                else if (j < 16)
+                    c = blk[2 + j] & 0x0f;
+                else
+                    c = blk[2 + (j - 16)] >> 4;
+                codes[n * K + b * 32 + j] = c;
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Repack into tiles ("Tile Dimensions and Grid Layout" and "Block-32
+ * Quantized Formats").  The tile of row-tile ct and column-tile kt sits at
+ * byte (ct * n_k_tiles + kt) * tile_size.  Inside it, quant[row][col] is the
+ * code of output row n = 32*ct + row and K index 32*kt + col.
+ *
+ *   Q4_0, IQ4_NL: 16 column pairs cp; for each, 32 consecutive bytes, one per
+ *     row, holding column 2cp in the low nibble and 2cp+1 in the high nibble.
+ *     Bytes 512..575: the 32 row scales (fp16).
+ *   Q8_0: 16 column pairs; for each, 64 bytes holding, per row, the int8 of
+ *     column 2cp then that of column 2cp+1.  Bytes 1024..1087: row scales.
+ *
+ * Reading for the ragged last row-tile (the page only gives the (ne1+31)/32
+ * rounding): rows n >= N hold zero codes and a +0.0 scale, so they contribute
+ * exactly nothing.
+ * ------------------------------------------------------------------------- */
+static uint8_t code_at(int type, const uint8_t *flat, long K, long n, long k)
+{
+    long nb = K / 32, bb = or_block_bytes(type);
+    const uint8_t *blk = flat + (n * nb + k / 32) * bb;
+    int j = (int)(k % 32);
+    if (type == OR_Q8_0)
+        return blk[2 + j];
+    return j < 16 ? (blk[2 + j] & 0x0f) : (blk[2 + j - 16] >> 4);
+}
+
+static uint16_t scale_at(int type, const uint8_t *flat, long K, long n, long kt)
+{
+    long nb = K / 32, bb = or_block_bytes(type);
+    const uint8_t *blk = flat + (n * nb + kt) * bb;
+    return (uint16_t)(blk[0] | (blk[1] << 8));
+}
+
+void or_repack(int type, const uint8_t *flat, long K, long N, uint8_t *tiles)
+{
+    long n_k_tiles = K / 32;
+    long n_col_tiles = (N + 31) / 32;
+    long ts = or_tile_bytes(type);
+    for (long ct = 0; ct < n_col_tiles; ct++) {
+        for (long kt = 0; kt < n_k_tiles; kt++) {
+            uint8_t *tile = tiles + (ct * n_k_tiles + kt) * ts;
+            for (int row = 0; row < 32; row++) {
+                long n = 32 * ct + row;
+                int valid = n < N;
+                for (int cp = 0; cp < 16; cp++) {
+                    uint8_t c0 = valid ? code_at(type, flat, K, n, 32 * kt + 2 * cp) : 0;
+                    uint8_t c1 = valid ? code_at(type, flat, K, n, 32 * kt + 2 * cp + 1) : 0;
+                    if (type == OR_Q8_0) {
+                        tile[cp * 64 + 2 * row + 0] = c0;
+                        tile[cp * 64 + 2 * row + 1] = c1;
+                    } else {
+                        tile[cp * 32 + row] = (uint8_t)((c1 << 4) | c0);
+                    }
+                }
+                uint16_t s = valid ? scale_at(type, flat, K, n, kt) : 0;
+                long so = (type == OR_Q8_0) ? 1024 : 512;
+                tile[so + 2 * row + 0] = (uint8_t)(s & 0xff);
+                tile[so + 2 * row + 1] = (uint8_t)(s >> 8);
+            }
+        }
+    }
+}
+
+/* Inverse of or_repack for rows n < N: codes[n*K + k], scales[n*(K/32)+kt]. */
+void or_unpack(int type, const uint8_t *tiles, long K, long N,
+               uint8_t *codes, uint16_t *scales)
+{
+    long n_k_tiles = K / 32;
+    long ts = or_tile_bytes(type);
+    for (long n = 0; n < N; n++) {
+        long ct = n / 32;
+        int row = (int)(n % 32);
+        for (long kt = 0; kt < n_k_tiles; kt++) {
+            const uint8_t *tile = tiles + (ct * n_k_tiles + kt) * ts;
+            for (int col = 0; col < 32; col++) {
+                int cp = col / 2;
+                uint8_t c;
+                if (type == OR_Q8_0)
+                    c = tile[cp * 64 + 2 * row + (col & 1)];
+                else
+                    c = (col & 1) ? (tile[cp * 32 + row] >> 4) : (tile[cp * 32 + row] & 0x0f);
+                codes[n * K + kt * 32 + col] = c;
+            }
+            long so = (type == OR_Q8_0) ? 1024 : 512;
+            scales[n * n_k_tiles + kt] =
+                (uint16_t)(tile[so + 2 * row] | (tile[so + 2 * row + 1] << 8));
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Integer weight value of a code.  Q8_0: the int8 itself.  Q4_0: the page
+ * gives only "4-bit quants" and a row scale; the reading taken is GGML's
+ * zero point of 8, value = d * (code - 8), consistent with the page's own
+ * half-range offsets for Q2_0 ("codes 0..3 representing signed values -1..2")
+ * and Q3_K ("low2 - 4").  IQ4_NL: the code indexes a 16-entry non-linear
+ * table (the page names it but does not print it); here the table is an
+ * int8[16] supplied by the caller.
+ * ------------------------------------------------------------------------- */
+static int weight_value(int type, uint8_t code, const int8_t *lut)
+{
+    switch (type) {
+    case OR_Q4_0: return (int)code - 8;
+    case OR_Q8_0: return (int)(int8_t)code;
+    case OR_IQ4_NL: return (int)lut[code & 0x0f];
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Dynamic activation quantization ("Memory buffers": activations are
+ * dynamically quantized; "Q2_0 Format › HVX Vector Dot-Product": the dot runs
+ * against Q8_0 activation tiles).  Reading: Q8_0 per 32-element K block --
+ *   amax = max |x_j|;  d = amax / 127 (fp32);  id = d != 0 ? 1/d : 0 (fp32);
+ *   q_j  = round-half-away-from-zero(x_j * id) (fp32 product);
+ *   the stored scale is d rounded to fp16 (nearest-even).
+ * q is planar row-major q[m*K + k]; d[m*(K/32) + kt].  Inputs are read at row
+ * stride ldx elements, as fp32, bf16 or fp16 (each converted exactly).
+ * Returns 0, or -1 if some |q| > 127 (cannot happen for finite input).
+ * ------------------------------------------------------------------------- */
+static float load_act(int dtype, const void *x, long idx)
+{
+    switch (dtype) {
+    case OR_F32: return ((const float *)x)[idx];
+    case OR_BF16: return or_bf16_to_f32(((const uint16_t *)x)[idx]);
+    case OR_F16: return or_f16_to_f32(((const uint16_t *)x)[idx]);
+    }
+    return 0.0f;
+}
+
+int or_quantize_act(int dtype, const void *x, long M, long K, long ldx,
+                    int8_t *q, uint16_t *d)
+{
+    long nb = K / 32;
+    for (long m = 0; m < M; m++) {
+        for (long kt = 0; kt < nb; kt++) {
+            float amax = 0.0f;
+            for (int j = 0; j < 32; j++) {
+                float v = fabsf(load_act(dtype, x, m * ldx + kt * 32 + j));
+                if (v > amax)
+                    amax = v;
+            }
+            float dv = amax / 127.0f;
+            float id = (dv != 0.0f) ? 1.0f / dv : 0.0f;
+            for (int j = 0; j < 32; j++) {
+                float prod = load_act(dtype, x, m * ldx + kt * 32 + j) * id;
+                float r = roundf(prod);
+                if (r > 127.0f || r < -127.0f)
+                    return -1;
+                q[m * K + kt * 32 + j] = (int8_t)r;
+            }
+            d[m * nb + kt] = or_f32_to_f16(dv);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Per-block integer dot products: isum[(m*N + n)*(K/32) + kt] =
+ *   sum_{j<32} w[n][32kt+j] * q[m][32kt+j], exact in int64, checked to fit
+ * int32 (returns -1 otherwise).  Weights are read back out of the tiles.
+ * ------------------------------------------------------------------------- */
+int or_block_dots(int type, const uint8_t *tiles, long K, long N,
+                  const int8_t *q, long M, const int8_t *lut, int32_t *isum)
+{
+    long nb = K / 32;
+    uint8_t *codes = malloc((size_t)(K > 0 ? K : 1));
+    for (long n = 0; n < N; n++) {
+        /* unpack one row at a time through the tile layout */
+        long ct = n / 32;
+        int row = (int)(n % 32);
+        long ts = or_tile_bytes(type);
+        for (long kt = 0; kt < nb; kt++) {
+            const uint8_t *tile = tiles + (ct * nb + kt) * ts;
+            for (int col = 0; col < 32; col++) {
+                int cp = col / 2;
+                codes[kt * 32 + col] = (type == OR_Q8_0)
+                    ? tile[cp * 64 + 2 * row + (col & 1)]
+                    : ((col & 1) ? (tile[cp * 32 + row] >> 4) : (tile[cp * 32 + row] & 0x0f));
+            }
+        }
+        for (long m = 0; m < M; m++) {
+            for (long kt = 0; kt < nb; kt++) {
+                int64_t s = 0;
+                for (int j = 0; j < 32; j++)
+                    s += (int64_t)weight_value(type, codes[kt * 32 + j], lut) *
+                         (int64_t)q[m * K + kt * 32 + j];
+                if (s > INT32_MAX || s < INT32_MIN) {
+                    free(codes);
+                    return -1;
+                }
+                isum[(m * N + n) * nb + kt] = (int32_t)s;
+            }
+        }
+    }
+    free(codes);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * The product itself, from its plain definition:
+ *   y[m][n] = sum_k W[n][k] * A[m][k],   W[n][k] = dw[n][kt] * w[n][k],
+ *                                        A[m][k] = da[m][kt] * q[m][k],
+ * i.e. GGML's dst = src0^T * src1 with ne0 = K and ne1 = N, each row scale
+ * applied to its 32-element block ("multiplied by the row scale d").
+ * Dequantize-then-dot in fp64, straight from the tiles, for output rows
+ * n0 <= n < n1 and every m; y[m*ldy + n].  acond[m*ldy + n] (if not NULL)
+ * receives sum_k |W*A|, the scale of the rounding error any fp32 summation of
+ * the same terms can make.
+ * ------------------------------------------------------------------------- */
+void or_matmul(int type, const uint8_t *tiles, long K, long N,
+               const int8_t *q, const uint16_t *d, long M, const int8_t *lut,
+               long n0, long n1, double *y, double *acond, long ldy)
+{
+    long nb = K / 32;
+    long ts = or_tile_bytes(type);
+    long so = (type == OR_Q8_0) ? 1024 : 512;
+    if (n1 > N)
+        n1 = N;
+    double *wrow = malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    for (long n = n0; n < n1; n++) {
+        long ct = n / 32;
+        int row = (int)(n % 32);
+        for (long kt = 0; kt < nb; kt++) {
+            const uint8_t *tile = tiles + (ct * nb + kt) * ts;
+            double dw = (double)or_f16_to_f32(
+                (uint16_t)(tile[so + 2 * row] | (tile[so + 2 * row + 1] << 8)));
+            for (int col = 0; col < 32; col++) {
+                int cp = col / 2;
+                uint8_t c = (type == OR_Q8_0)
+                    ? tile[cp * 64 + 2 * row + (col & 1)]
+                    : ((col & 1) ? (tile[cp * 32 + row] >> 4) : (tile[cp * 32 + row] & 0x0f));
+                wrow[kt * 32 + col] = dw * (double)weight_value(type, c, lut);
+            }
+        }
+        for (long m = 0; m < M; m++) {
+            double s = 0.0, a = 0.0;
+            for (long k = 0; k < K; k++) {
+                double act = (double)or_f16_to_f32(d[m * nb + k / 32]) * (double)q[m * K + k];
+                double t = wrow[k] * act;
+                s += t;
+                a += fabs(t);
+            }
+            y[m * ldy + n] = s;
+            if (acond)
+                acond[m * ldy + n] = a;
+        }
+    }
+    free(wrow);
+}

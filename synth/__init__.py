@@ -1,0 +1,154 @@
+"""Seeded synthetic inputs for tiled block-32 quantized matmul.
+
+This module only draws random numbers and lays them out in the flat GGML
+block-32 source format; it holds none of the method's arithmetic (no repack,
+no activation quantization, no dot products).  Both the CPU oracle tests and
+the HIP path's tests and benchmark take their inputs from here.
+
+Generator: numpy.random.default_rng(seed) (PCG64).  Draw order per workload:
+weight codes, then weight scales, then activations.
+
+Flat layout written here (GGML block-32, little-endian): row n holds K/32
+consecutive blocks; a Q4_0 / IQ4_NL block is 2 bytes of fp16 scale followed by
+16 bytes whose low nibbles are elements 0..15 and high nibbles elements
+16..31; a Q8_0 block is 2 bytes of fp16 scale followed by 32 int8 elements.
+"""
+import dataclasses
+
+import numpy as np
+
+Q4_0, Q8_0, IQ4_NL = 0, 1, 2
+TYPE_NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", IQ4_NL: "iq4_nl"}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, IQ4_NL: 18}
+
+# Stand-in for the 16-entry non-linear IQ4_NL table.  The page names the table
+# but does not print its values; any 16 int8 entries keep the integer path
+# exact.  These are round(127 * sign(u) * |u|**1.5) for u = (2i - 15) / 15,
+# a symmetric, denser-near-zero codebook of our own construction.
+IQ4_NL_STANDIN_LUT = np.array(
+    [-127, -102, -80, -59, -40, -24, -11, -2, 2, 11, 24, 40, 59, 80, 102, 127],
+    dtype=np.int8)
+
+
+def _standin_lut_formula():
+    u = (2 * np.arange(16) - 15) / 15.0
+    v = 127.0 * np.sign(u) * np.abs(u) ** 1.5
+    return (np.sign(v) * np.floor(np.abs(v) + 0.5)).astype(np.int8)
+
+
+assert np.array_equal(_standin_lut_formula(), IQ4_NL_STANDIN_LUT)
+
+
+def draw_codes(rng, qtype, N, K):
+    """Weight codes [N, K]: 0..15 (Q4_0, IQ4_NL) or int8 in [-127, 127] (Q8_0)."""
+    if qtype == Q8_0:
+        return rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    return rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+
+
+def draw_scales(rng, dist, N, K):
+    """fp16 scale bits [N, K/32].  dist: 'uniform' -> U[1e-3, 1e-2);
+    'absnormal' -> |N(0,1)| * 0.01.  Drawn in float64, cast to float32, then
+    to fp16 by numpy (round to nearest even)."""
+    shape = (N, K // 32)
+    if dist == "uniform":
+        s = rng.uniform(1e-3, 1e-2, size=shape)
+    elif dist == "absnormal":
+        s = np.abs(rng.standard_normal(size=shape)) * 0.01
+    else:
+        raise ValueError(dist)
+    return s.astype(np.float32).astype(np.float16).view(np.uint16)
+
+
+def pack_flat(qtype, codes, scale_bits):
+    """Write codes [N, K] and fp16 scale bits [N, K/32] as flat GGML blocks."""
+    N, K = codes.shape
+    nb = K // 32
+    bb = BLOCK_BYTES[qtype]
+    out = np.empty((N, nb, bb), np.uint8)
+    sb = np.ascontiguousarray(scale_bits, dtype=np.uint16).reshape(N, nb)
+    out[:, :, 0] = (sb & 0xFF).astype(np.uint8)
+    out[:, :, 1] = (sb >> 8).astype(np.uint8)
+    c = codes.reshape(N, nb, 32)
+    if qtype == Q8_0:
+        out[:, :, 2:] = c.view(np.uint8)
+    else:
+        c = c.astype(np.uint8)
+        out[:, :, 2:] = c[:, :, :16] | (c[:, :, 16:] << 4)
+    return out.reshape(-1)
+
+
+def draw_activations(rng, M, K, dtype="f32"):
+    """Activations N(0,1) [M, K]: float32, or bf16 / fp16 bit patterns (uint16)
+    rounded to nearest even from the float32 draw."""
+    x = rng.standard_normal(size=(M, K), dtype=np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        u = x.view(np.uint32).astype(np.uint64)
+        # round to nearest even on the upper 16 bits (finite inputs only)
+        r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        return r.astype(np.uint16)
+    raise ValueError(dtype)
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    qtype: int
+    K: int
+    N: int
+    M: int
+    scale_dist: str
+    act_dtype: str = "f32"
+    seed: int = 0
+    path: str = "qgemv"     # qgemv (M <= 8) or qgemm
+
+    @property
+    def n_col_tiles(self):
+        return (self.N + 31) // 32
+
+    @property
+    def tile_bytes(self):
+        return {Q4_0: 576, Q8_0: 1088, IQ4_NL: 576}[self.qtype]
+
+    @property
+    def weight_bytes(self):
+        return (self.K // 32) * self.n_col_tiles * self.tile_bytes
+
+
+@dataclasses.dataclass
+class Inputs:
+    codes: np.ndarray
+    scale_bits: np.ndarray
+    flat: np.ndarray
+    x: np.ndarray
+    lut: np.ndarray
+
+
+def make_inputs(w: Workload, M=None):
+    """Draw one workload's inputs: codes, then scales, then activations."""
+    rng = np.random.default_rng(w.seed)
+    codes = draw_codes(rng, w.qtype, w.N, w.K)
+    sb = draw_scales(rng, w.scale_dist, w.N, w.K)
+    flat = pack_flat(w.qtype, codes, sb)
+    x = draw_activations(rng, w.M if M is None else M, w.K, w.act_dtype)
+    return Inputs(codes, sb, flat, x, IQ4_NL_STANDIN_LUT.copy())
+
+
+# The synthetic workloads: shapes and value distributions of the pages'
+# setting (a Q4_0 FFN up-projection 4096 -> 14336, a 128001-entry lm-head).
+WORKLOADS = {
+    "q4_0_gemv_k256_n64_m1": Workload("q4_0_gemv_k256_n64_m1", Q4_0, 256, 64, 1, "uniform"),
+    "q8_0_gemv_k4096_n4096_m1": Workload("q8_0_gemv_k4096_n4096_m1", Q8_0, 4096, 4096, 1, "absnormal"),
+    "q4_0_gemv_k4096_n14336_m1": Workload("q4_0_gemv_k4096_n14336_m1", Q4_0, 4096, 14336, 1, "uniform"),
+    "q4_0_gemv_k4096_n14336_m4": Workload("q4_0_gemv_k4096_n14336_m4", Q4_0, 4096, 14336, 4, "uniform"),
+    "q4_0_gemv_k4096_n14336_m8": Workload("q4_0_gemv_k4096_n14336_m8", Q4_0, 4096, 14336, 8, "uniform"),
+    "iq4_nl_gemm_m512_k4096_n4096": Workload("iq4_nl_gemm_m512_k4096_n4096", IQ4_NL, 4096, 4096, 512,
+                                             "uniform", act_dtype="bf16", path="qgemm"),
+    "q8_0_lmhead_k4096_n128001_m1": Workload("q8_0_lmhead_k4096_n128001_m1", Q8_0, 4096, 128001, 1, "absnormal"),
+    "q8_0_lmhead_k4096_n128001_m128": Workload("q8_0_lmhead_k4096_n128001_m128", Q8_0, 4096, 128001, 128,
+                                               "absnormal", path="qgemm"),
+}
