@@ -1,0 +1,197 @@
+// C ABI of the tiledq library: host-side validation, then one launch on the
+// caller's stream.  Support is decided from static properties only (type,
+// shape, pointer alignment), as the page "Hexagon backend developer details"
+// asks of supports_op in "supports_op Independence from Buffer and Repack
+// State"; launch geometry is computed here on the host ("Host-Side
+// Precomputation via kernel_params").
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace {
+
+constexpr int64_t MAX_K = int64_t(1) << 20;
+constexpr int64_t MAX_N = int64_t(1) << 30;
+constexpr int64_t MAX_M = int64_t(1) << 20;
+constexpr int64_t MAX_PROD = int64_t(1) << 40;
+constexpr int64_t MAX_MK = int64_t(1) << 36;
+
+bool valid_type(int t) { return t == TQ_Q4_0 || t == TQ_Q8_0 || t == TQ_IQ4_NL; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool valid_kn(int64_t K, int64_t N)
+{
+    return K >= 32 && K <= MAX_K && K % 32 == 0 && N >= 0 && N <= MAX_N && K * N < MAX_PROD;
+}
+
+bool valid_mk(int64_t M, int64_t K) { return M >= 0 && M <= MAX_M && M * K < MAX_MK; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_E_LAUNCH; }
+
+tq::Lut pack_lut(const int8_t *lut)
+{
+    tq::Lut t{};
+    if (lut)
+        for (int i = 0; i < 16; i++)
+            t.w[i / 4] |= (uint32_t)(uint8_t)lut[i] << (8 * (i % 4));
+    return t;
+}
+
+int check_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
+                 const uint16_t *d, int64_t M, const int8_t *lut, const void *out, int64_t ldy,
+                 bool need_d)
+{
+    if (!valid_type(type))
+        return TQ_E_TYPE;
+    if (!valid_kn(K, N) || !valid_mk(M, K) || ldy < N)
+        return TQ_E_SHAPE;
+    if (M == 0 || N == 0)
+        return TQ_OK;
+    if (!tiles || !q || (need_d && !d) || !out || (type == TQ_IQ4_NL && !lut))
+        return TQ_E_NULL;
+    if (!aligned(tiles, 16) || !aligned(q, 16) || (need_d && !aligned(d, 2)) ||
+        !aligned(out, 4))
+        return TQ_E_ALIGN;
+    return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq_tile_bytes(int type)
+{
+    switch (type) {
+    case TQ_Q4_0: return tq::Fmt<TQ_Q4_0>::tile;
+    case TQ_Q8_0: return tq::Fmt<TQ_Q8_0>::tile;
+    case TQ_IQ4_NL: return tq::Fmt<TQ_IQ4_NL>::tile;
+    }
+    return 0;
+}
+
+size_t tq_block_bytes(int type)
+{
+    switch (type) {
+    case TQ_Q4_0: return tq::Fmt<TQ_Q4_0>::block;
+    case TQ_Q8_0: return tq::Fmt<TQ_Q8_0>::block;
+    case TQ_IQ4_NL: return tq::Fmt<TQ_IQ4_NL>::block;
+    }
+    return 0;
+}
+
+size_t tq_tiled_bytes(int type, int64_t K, int64_t N)
+{
+    if (!valid_type(type) || !valid_kn(K, N))
+        return 0;
+    return (size_t)(K / 32) * (size_t)((N + 31) / 32) * tq_tile_bytes(type);
+}
+
+size_t tq_flat_bytes(int type, int64_t K, int64_t N)
+{
+    if (!valid_type(type) || !valid_kn(K, N))
+        return 0;
+    return (size_t)N * (size_t)(K / 32) * tq_block_bytes(type);
+}
+
+int tq_supported(int type, int64_t K, int64_t N, int64_t M, int path)
+{
+    if (!valid_type(type) || !valid_kn(K, N) || !valid_mk(M, K))
+        return 0;
+    if (path == TQ_PATH_GEMV)
+        return M <= 8;
+    return path == TQ_PATH_GEMM;
+}
+
+const char *tq_status_string(int status)
+{
+    switch (status) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_E_NULL: return "TQ_E_NULL: required pointer is NULL";
+    case TQ_E_TYPE: return "TQ_E_TYPE: unknown type, dtype or path";
+    case TQ_E_SHAPE: return "TQ_E_SHAPE: shape outside the supported domain";
+    case TQ_E_ALIGN: return "TQ_E_ALIGN: pointer misaligned";
+    case TQ_E_LAUNCH: return "TQ_E_LAUNCH: kernel launch failed";
+    }
+    return "unknown tq_status";
+}
+
+int tq_repack_tiles(int type, const void *flat, int64_t K, int64_t N, void *tiles,
+                    hipStream_t stream)
+{
+    if (!valid_type(type))
+        return TQ_E_TYPE;
+    if (!valid_kn(K, N))
+        return TQ_E_SHAPE;
+    if (N == 0)
+        return TQ_OK;
+    if (!flat || !tiles)
+        return TQ_E_NULL;
+    if (!aligned(flat, 2) || !aligned(tiles, 16))
+        return TQ_E_ALIGN;
+    return launch_status(tq::launch_repack(type, flat, K, N, tiles, stream));
+}
+
+int tq_quantize_act(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx, int8_t *q,
+                    uint16_t *d, hipStream_t stream)
+{
+    if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16)
+        return TQ_E_TYPE;
+    if (K < 32 || K > MAX_K || K % 32 != 0 || !valid_mk(M, K) || ldx < K ||
+        M * ldx >= MAX_PROD)
+        return TQ_E_SHAPE;
+    if (M == 0)
+        return TQ_OK;
+    if (!x || !q || !d)
+        return TQ_E_NULL;
+    if (!aligned(x, dtype == TQ_F32 ? 4 : 2) || !aligned(q, 4) || !aligned(d, 2))
+        return TQ_E_ALIGN;
+    return launch_status(tq::launch_quantize(dtype, x, M, K, ldx, q, d, stream));
+}
+
+int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
+             const uint16_t *d, int64_t M, const int8_t *lut, float *y, int64_t ldy,
+             hipStream_t stream)
+{
+    if (valid_type(type) && M > 8)
+        return TQ_E_SHAPE;
+    int st = check_matmul(type, tiles, K, N, q, d, M, lut, y, ldy, true);
+    if (st != TQ_OK || M == 0 || N == 0)
+        return st;
+    return launch_status(
+        tq::launch_qgemv(type, tiles, K, N, q, d, M, pack_lut(lut), y, ldy, nullptr, stream));
+}
+
+int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
+             const uint16_t *d, int64_t M, const int8_t *lut, float *y, int64_t ldy,
+             hipStream_t stream)
+{
+    int st = check_matmul(type, tiles, K, N, q, d, M, lut, y, ldy, true);
+    if (st != TQ_OK || M == 0 || N == 0)
+        return st;
+    return launch_status(
+        tq::launch_qgemm(type, tiles, K, N, q, d, M, pack_lut(lut), y, ldy, nullptr, stream));
+}
+
+int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
+                  int64_t M, const int8_t *lut, int32_t *isum, int path, hipStream_t stream)
+{
+    if (path != TQ_PATH_GEMV && path != TQ_PATH_GEMM)
+        return TQ_E_TYPE;
+    if (path == TQ_PATH_GEMV && valid_type(type) && M > 8)
+        return TQ_E_SHAPE;
+    int st = check_matmul(type, tiles, K, N, q, nullptr, M, lut, isum, N, false);
+    if (st != TQ_OK || M == 0 || N == 0)
+        return st;
+    if ((int64_t)M * N * (K / 32) >= MAX_PROD)
+        return TQ_E_SHAPE;
+    const tq::Lut t = pack_lut(lut);
+    hipError_t e = (path == TQ_PATH_GEMV)
+                       ? tq::launch_qgemv(type, tiles, K, N, q, nullptr, M, t, nullptr, N,
+                                          isum, stream)
+                       : tq::launch_qgemm(type, tiles, K, N, q, nullptr, M, t, nullptr, N,
+                                          isum, stream);
+    return launch_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+"""Torch-facing binding of the tiledq C ABI.
+
+Argument marshalling only: device pointers, sizes and the current HIP stream
+go to libtiledq.so; every step of the computation runs in its HIP kernels.
+Tensors must live on the GPU; outputs are allocated with torch unless given.
+"""
+import ctypes
+
+import torch
+
+from ._lib import TiledqError, check, lib
+
+Q4_0, Q8_0, IQ4_NL = 0, 1, 2
+F32, BF16, F16 = 0, 1, 2
+PATH_GEMV, PATH_GEMM = 0, 1
+
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise TiledqError("tiledq operates on GPU tensors only")
+        if t is not None and not t.is_contiguous():
+            raise TiledqError("tiledq expects contiguous tensors")
+
+
+def _lut_arg(lut):
+    if lut is None:
+        return None
+    vals = [int(v) for v in (lut.tolist() if hasattr(lut, "tolist") else lut)]
+    if len(vals) != 16 or any(v < -128 or v > 127 for v in vals):
+        raise TiledqError("lut must hold 16 int8 values")
+    return (ctypes.c_int8 * 16)(*vals)
+
+
+def tile_bytes(qtype):
+    return lib().tq_tile_bytes(qtype)
+
+
+def block_bytes(qtype):
+    return lib().tq_block_bytes(qtype)
+
+
+def tiled_bytes(qtype, K, N):
+    return lib().tq_tiled_bytes(qtype, K, N)
+
+
+def flat_bytes(qtype, K, N):
+    return lib().tq_flat_bytes(qtype, K, N)
+
+
+def supported(qtype, K, N, M, path=PATH_GEMV):
+    return bool(lib().tq_supported(qtype, K, N, M, path))
+
+
+def repack_tiles(qtype, flat, K, N, out=None):
+    """Flat GGML blocks (uint8 GPU tensor) -> tiles (uint8 GPU tensor)."""
+    _need_cuda(flat, out)
+    nbytes = tiled_bytes(qtype, K, N)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=flat.device)
+    if flat.numel() * flat.element_size() < flat_bytes(qtype, K, N) or \
+            out.numel() * out.element_size() < nbytes:
+        raise TiledqError("repack_tiles: buffer too small")
+    check(lib().tq_repack_tiles(qtype, _ptr(flat), K, N, _ptr(out), _stream(flat)),
+          "tq_repack_tiles")
+    return out
+
+
+def quantize_act(x, K=None, q=None, d=None):
+    """x [M, >=K] fp32 / bf16 / fp16 -> (q int8 [M, K], d fp16 [M, K/32])."""
+    if x.dim() != 2 or x.dtype not in _DTYPES:
+        raise TiledqError("quantize_act: x must be 2-D fp32, bf16 or fp16")
+    if not x.is_cuda or x.stride(1) != 1:
+        raise TiledqError("quantize_act: x must be a GPU tensor with unit column stride")
+    M, Kx = x.shape
+    K = Kx if K is None else K
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((M, K // 32), dtype=torch.float16, device=x.device)
+    _need_cuda(q, d)
+    check(lib().tq_quantize_act(_DTYPES[x.dtype], _ptr(x), M, K, x.stride(0), _ptr(q), _ptr(d),
+                                _stream(x)), "tq_quantize_act")
+    return q, d
+
+
+def _matmul(fn, name, qtype, tiles, K, N, q, d, lut, out):
+    _need_cuda(tiles, q, d, out)
+    M = q.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=q.device)
+    if out.dim() != 2 or out.shape[0] < M or out.stride(1) != 1 or out.dtype != torch.float32:
+        raise TiledqError(f"{name}: bad output tensor")
+    ldy = out.stride(0)
+    check(fn(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut), _ptr(out), ldy,
+             _stream(q)), name)
+    return out
+
+
+def qgemv(qtype, tiles, K, N, q, d, lut=None, out=None):
+    """Decode product y [M, N] = W (tiles) x A (q, d), M <= 8."""
+    return _matmul(lib().tq_qgemv, "tq_qgemv", qtype, tiles, K, N, q, d, lut, out)
+
+
+def qgemm(qtype, tiles, K, N, q, d, lut=None, out=None):
+    """Prefill product y [M, N] on int8 MFMA, any M."""
+    return _matmul(lib().tq_qgemm, "tq_qgemm", qtype, tiles, K, N, q, d, lut, out)
+
+
+def block_dots(qtype, tiles, K, N, q, lut=None, path=PATH_GEMV, out=None):
+    """Integer block dots int32 [M, N, K/32] as computed inside qgemv / qgemm."""
+    _need_cuda(tiles, q, out)
+    M = q.shape[0]
+    if out is None:
+        out = torch.empty((M, N, K // 32), dtype=torch.int32, device=q.device)
+    check(lib().tq_block_dots(qtype, _ptr(tiles), K, N, _ptr(q), M, _lut_arg(lut), _ptr(out),
+                              path, _stream(q)), "tq_block_dots")
+    return out

@@ -1,0 +1,158 @@
+/*
+ * tiledq -- matrix-vector and matrix-matrix multiply over block-32 quantized
+ * weights repacked into 32x32 tiles, on AMD Instinct MI355X (gfx950).
+ *
+ * Formats follow the page "Hexagon backend developer details" (llama.cpp
+ * docs/backend/snapdragon/developer.md), section "Tiled Weight Formats":
+ *
+ *   Grid ("Tile Dimensions and Grid Layout").  A weight matrix of logical
+ *   shape [ne0, ne1] = [K, N] (N output rows of K elements each) is cut into
+ *   32-row x 32-column tiles: n_k_tiles = K / 32, n_col_tiles = (N + 31) / 32.
+ *   The tile of row-tile ct (output rows 32ct..32ct+31) and column-tile kt
+ *   (K indices 32kt..32kt+31) sits at byte (ct * n_k_tiles + kt) * tile_size,
+ *   so the n_k_tiles tiles of one 32-row stripe are contiguous.
+ *
+ *   Tiles ("Block-32 Quantized Formats"), quant[row][col] for row, col < 32:
+ *     Q4_0   576 B: bytes cp*32 + row (cp = 0..15) hold quant[row][2cp] in the
+ *            low nibble and quant[row][2cp+1] in the high nibble; bytes
+ *            512 + 2*row hold row's fp16 scale d.  Weight = d * (quant - 8).
+ *     Q8_0  1088 B: byte cp*64 + 2*row + h holds int8 quant[row][2cp + h];
+ *            bytes 1024 + 2*row hold the fp16 scale d.  Weight = d * quant.
+ *     IQ4_NL 576 B: the Q4_0 layout, each nibble an index into a 16-entry
+ *            table.  Weight = d * lut[index].
+ *   Rows n >= N of the last row-tile are zero (codes 0, scale +0.0).
+ *
+ *   Flat source ("repacked from flat row-major GGML layouts"): row n holds
+ *   K/32 consecutive GGML blocks: Q4_0 / IQ4_NL = fp16 d + 16 bytes (low
+ *   nibbles elements 0..15, high nibbles 16..31), 18 B; Q8_0 = fp16 d + 32
+ *   int8, 34 B.
+ *
+ *   Activations (section "Memory buffers": dynamically quantized activations,
+ *   used as Q8_0 activation tiles by the vector dot of "Q2_0 Format"): per
+ *   32-element K block, d = amax/127 (fp32), q = round-half-away(x * (1/d)),
+ *   d stored as fp16 (nearest-even).  q is int8 row-major [M][K], d is fp16
+ *   [M][K/32].  Domain: finite x, each block all zero or with amax >= 2^-120.
+ *
+ *   Product: y[m*ldy + n] = sum_k W[n][k] * A[m][k] for m < M, n < N, with
+ *   W the dequantized weights and A[m][k] = d[m][k/32] * q[m][k] (GGML's
+ *   dst = src0^T * src1).  Per 32-element block the integer dot
+ *   isum = sum_j w_int * q is formed exactly in int32, then scaled by the
+ *   fp16 row scale times the fp16 activation scale (exact in fp32) and
+ *   summed in fp32 over blocks.
+ *
+ * Calling convention (all entry points):
+ *   - Data pointers are DEVICE pointers, except `lut`, which is a HOST
+ *     pointer to 16 int8 (copied by value into the launch; may be freed on
+ *     return).  The caller allocates and owns every buffer; the library
+ *     allocates nothing, frees nothing and keeps no pointer after return.
+ *   - Each call validates its arguments on the host, then enqueues its
+ *     kernel(s) on `stream` (NULL = the default stream) and returns without
+ *     synchronizing.  Buffers must stay alive until that work has completed.
+ *     Faults inside a kernel surface at the caller's next synchronization.
+ *   - Validation errors are returned before anything is enqueued and leave
+ *     every output untouched.  M == 0 or N == 0 is TQ_OK with no launch.
+ *   - The library is stateless; calls on different streams may run
+ *     concurrently.  Outputs of concurrent calls must not overlap.
+ *   - Shapes: 32 <= K <= 2^20 with K % 32 == 0; 0 <= N <= 2^30;
+ *     0 <= M <= 2^20; K*N and M*K each below 2^40.
+ */
+#ifndef TILEDQ_H
+#define TILEDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TQ_Q4_0 = 0, TQ_Q8_0 = 1, TQ_IQ4_NL = 2 } tq_type;
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+typedef enum {
+    TQ_OK = 0,
+    TQ_E_NULL = 1,    /* a required pointer is NULL                           */
+    TQ_E_TYPE = 2,    /* unknown tq_type / tq_dtype / path                    */
+    TQ_E_SHAPE = 3,   /* K, N, M, ldx or ldy outside the documented domain     */
+    TQ_E_ALIGN = 4,   /* a pointer lacks the documented alignment             */
+    TQ_E_LAUNCH = 5   /* the HIP runtime rejected a launch                    */
+} tq_status;
+
+/* Which kernel family tq_block_dots runs. */
+typedef enum { TQ_PATH_GEMV = 0, TQ_PATH_GEMM = 1 } tq_path;
+
+/* Bytes of one tile ("Block-32 Quantized Formats"): 576, 1088, 576; 0 for an
+ * unknown type. */
+size_t tq_tile_bytes(int type);
+
+/* Bytes of one flat GGML block: 18, 34, 18; 0 for an unknown type. */
+size_t tq_block_bytes(int type);
+
+/* (K/32) * ((N+31)/32) * tq_tile_bytes(type) ("Tile Dimensions and Grid
+ * Layout"); 0 if the shape or type is invalid. */
+size_t tq_tiled_bytes(int type, int64_t K, int64_t N);
+
+/* N * (K/32) * tq_block_bytes(type); 0 if the shape or type is invalid. */
+size_t tq_flat_bytes(int type, int64_t K, int64_t N);
+
+/* 1 if (type, K, N, M) is supported by `path` (TQ_PATH_GEMV needs
+ * M <= 8), judged from these static properties alone; 0 otherwise. */
+int tq_supported(int type, int64_t K, int64_t N, int64_t M, int path);
+
+/* Static, NUL-terminated name of a status code. */
+const char *tq_status_string(int status);
+
+/* Repack flat GGML blocks into tiles ("Tiled Weight Formats": repacking at
+ * model load or at run time).
+ *   flat  : device, tq_flat_bytes(type, K, N) bytes, 2-byte aligned.
+ *   tiles : device, tq_tiled_bytes(type, K, N) bytes, 16-byte aligned; fully
+ *           written, padding rows included.  Must not overlap `flat`.
+ * Bit-exact byte permutation; deterministic. */
+int tq_repack_tiles(int type, const void *flat, int64_t K, int64_t N,
+                    void *tiles, hipStream_t stream);
+
+/* Dynamic activation quantization ("Memory buffers"), per 32-element block.
+ *   x   : device, M rows of K elements at row stride ldx (>= K) elements;
+ *         fp32 (4-byte aligned) or bf16 / fp16 (2-byte aligned), per dtype.
+ *   q   : device, int8 [M][K] row-major, 4-byte aligned.
+ *   d   : device, fp16 bits [M][K/32] row-major, 2-byte aligned.
+ * Bit-exact (IEEE fp32 divide, round half away from zero, fp16 nearest-even). */
+int tq_quantize_act(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
+                    int8_t *q, uint16_t *d, hipStream_t stream);
+
+/* Decode matrix-vector product over tiles (M <= 8 activation rows), reading
+ * every weight tile exactly once.
+ *   tiles : device, tq_tiled_bytes(type, K, N) bytes, 16-byte aligned.
+ *   q, d  : device, from tq_quantize_act with the same M and K; q 16-byte
+ *           aligned, d 2-byte aligned.
+ *   M     : 1..8 (else TQ_E_SHAPE).
+ *   lut   : host, 16 int8 table entries for TQ_IQ4_NL (required), ignored
+ *           (may be NULL) for the other types.
+ *   y     : device fp32, y[m*ldy + n] written for m < M, n < N only;
+ *           ldy >= N; 4-byte aligned.
+ * Deterministic: repeated calls give identical bytes. */
+int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N,
+             const int8_t *q, const uint16_t *d, int64_t M,
+             const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
+
+/* Prefill matrix-matrix product over tiles with int8 matrix-core (MFMA)
+ * instructions, any M >= 1.  Arguments as tq_qgemv.  Same integer block dots
+ * as tq_qgemv; deterministic. */
+int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N,
+             const int8_t *q, const uint16_t *d, int64_t M,
+             const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
+
+/* Test instrument: run the tq_qgemv (path TQ_PATH_GEMV, M <= 8) or tq_qgemm
+ * (TQ_PATH_GEMM) kernel with the integer block dots as output instead of y:
+ * isum[(m*N + n)*(K/32) + kt] (int32, device, 4-byte aligned) =
+ * sum_{j<32} w_int[n][32kt+j] * q[m][32kt+j], for m < M, n < N. */
+int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N,
+                  const int8_t *q, int64_t M, const int8_t *lut,
+                  int32_t *isum, int path, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEDQ_H */

@@ -1,0 +1,141 @@
+"""The C-ABI library loads on a machine without a GPU, exports every entry
+point include/tiledq.h declares, and rejects bad arguments on the host before
+any HIP call (no compute is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "tiledq.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(tq_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from block_quantized_matmul_repack_amd import _lib
+    return _lib.lib()
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("tq_repack_tiles", "tq_quantize_act", "tq_qgemv", "tq_qgemm", "tq_block_dots"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(L):
+    from block_quantized_matmul_repack_amd import _lib
+    syms = declared_symbols()
+    assert syms
+    for name in syms:
+        assert hasattr(L, name), name
+        assert name in _lib.SIGNATURES, name
+
+
+def test_sizes_match_oracle(L, orc):
+    for t in (0, 1, 2):
+        assert L.tq_tile_bytes(t) == orc.tile_bytes(t)
+        assert L.tq_block_bytes(t) == orc.block_bytes(t)
+        for K, N in ((32, 1), (4096, 4096), (4096, 14336), (4096, 128001), (96, 70)):
+            assert L.tq_tiled_bytes(t, K, N) == orc.tiled_bytes(t, K, N)
+            assert L.tq_flat_bytes(t, K, N) == orc.flat_bytes(t, K, N)
+    assert L.tq_tile_bytes(7) == 0
+    assert L.tq_tiled_bytes(0, 33, 4) == 0 and L.tq_flat_bytes(0, 16, 4) == 0
+
+
+def test_supported_static_properties(L):
+    assert L.tq_supported(0, 4096, 4096, 8, 0) == 1
+    assert L.tq_supported(0, 4096, 4096, 9, 0) == 0
+    assert L.tq_supported(2, 4096, 4096, 512, 1) == 1
+    assert L.tq_supported(3, 4096, 4096, 1, 0) == 0
+    assert L.tq_supported(0, 4001, 4096, 1, 0) == 0
+    assert L.tq_supported(0, 4096, 4096, 1, 5) == 0
+
+
+# Fake, never-dereferenced device addresses: validation fails before any use.
+A16 = ctypes.c_void_p(0x10000)
+A2 = ctypes.c_void_p(0x10002)
+NUL = None
+LUT = (ctypes.c_int8 * 16)(*range(-8, 8))
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert L.tq_status_string(s).startswith(b"TQ_")
+
+
+def test_repack_validation(L):
+    assert L.tq_repack_tiles(9, A16, 64, 32, A16, NUL) == 2
+    assert L.tq_repack_tiles(0, A16, 48, 32, A16, NUL) == 3
+    assert L.tq_repack_tiles(0, A16, 0, 32, A16, NUL) == 3
+    assert L.tq_repack_tiles(0, A16, 64, -1, A16, NUL) == 3
+    assert L.tq_repack_tiles(0, NUL, 64, 32, A16, NUL) == 1
+    assert L.tq_repack_tiles(0, A16, 64, 32, A2, NUL) == 4
+    assert L.tq_repack_tiles(0, ctypes.c_void_p(0x10001), 64, 32, A16, NUL) == 4
+    assert L.tq_repack_tiles(0, NUL, 64, 0, NUL, NUL) == 0       # empty: OK, no launch
+
+
+def test_quantize_validation(L):
+    assert L.tq_quantize_act(5, A16, 1, 64, 64, A16, A16, NUL) == 2
+    assert L.tq_quantize_act(0, A16, 1, 60, 64, A16, A16, NUL) == 3
+    assert L.tq_quantize_act(0, A16, 1, 64, 32, A16, A16, NUL) == 3   # ldx < K
+    assert L.tq_quantize_act(0, A16, -1, 64, 64, A16, A16, NUL) == 3
+    assert L.tq_quantize_act(0, NUL, 1, 64, 64, A16, A16, NUL) == 1
+    assert L.tq_quantize_act(0, A2, 1, 64, 64, A16, A16, NUL) == 4    # fp32 needs 4 B
+    assert L.tq_quantize_act(1, A2, 1, 64, 64, A16, A16, NUL) != 4    # bf16 needs 2 B
+    assert L.tq_quantize_act(0, NUL, 0, 64, 64, NUL, NUL, NUL) == 0
+
+
+@pytest.mark.parametrize("fn", ["tq_qgemv", "tq_qgemm"])
+def test_matmul_validation(L, fn):
+    f = getattr(L, fn)
+    assert f(9, A16, 64, 32, A16, A16, 1, NUL, A16, 32, NUL) == 2
+    assert f(0, A16, 48, 32, A16, A16, 1, NUL, A16, 32, NUL) == 3
+    assert f(0, A16, 64, 32, A16, A16, 1, NUL, A16, 31, NUL) == 3     # ldy < N
+    assert f(0, NUL, 64, 32, A16, A16, 1, NUL, A16, 32, NUL) == 1
+    assert f(0, A16, 64, 32, NUL, A16, 1, NUL, A16, 32, NUL) == 1
+    assert f(0, A16, 64, 32, A16, NUL, 1, NUL, A16, 32, NUL) == 1
+    assert f(0, A16, 64, 32, A16, A16, 1, NUL, NUL, 32, NUL) == 1
+    assert f(2, A16, 64, 32, A16, A16, 1, NUL, A16, 32, NUL) == 1     # IQ4_NL needs the table
+    assert f(0, A2, 64, 32, A16, A16, 1, NUL, A16, 32, NUL) == 4
+    assert f(0, A16, 64, 32, A2, A16, 1, NUL, A16, 32, NUL) == 4
+    assert f(0, A16, 64, 32, A16, A16, 1, NUL, A2, 32, NUL) == 4
+    assert f(0, NUL, 64, 32, NUL, NUL, 0, NUL, NUL, 32, NUL) == 0     # M == 0
+    assert f(0, NUL, 64, 0, NUL, NUL, 4, NUL, NUL, 0, NUL) == 0       # N == 0
+    assert f(2, NUL, 64, 0, NUL, NUL, 4, LUT, NUL, 0, NUL) == 0
+
+
+def test_gemv_m_limit(L):
+    assert L.tq_qgemv(0, A16, 64, 32, A16, A16, 9, NUL, A16, 32, NUL) == 3
+    assert L.tq_block_dots(0, A16, 64, 32, A16, 9, NUL, A16, 0, NUL) == 3
+    assert L.tq_block_dots(0, A16, 64, 32, A16, 9, NUL, A16, 7, NUL) == 2
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import block_quantized_matmul_repack_amd as tq
+    x = torch.zeros(2, 64)
+    with pytest.raises(tq.TiledqError):
+        tq.quantize_act(x)
+    with pytest.raises(tq.TiledqError):
+        tq.repack_tiles(0, torch.zeros(36, dtype=torch.uint8), 64, 1)
+
+
+def test_product_code_never_touches_oracle():
+    """The HIP path and its binding neither import nor load the oracle."""
+    pkg = os.path.join(ROOT, "block_quantized_matmul_repack_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in src.lower(), fn
+                assert "synth" not in src, fn

@@ -1,0 +1,177 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: repack bytes, quantized activations and scales, per-block integer
+dots of both the GEMV and the GEMM kernel.  fp32 outputs: within the
+tolerance stated in gpu_helpers (1e-3 relative with a cancellation floor).
+Shapes span several tiles and ragged tails; all inputs are seeded.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import check_y, make, tiles_slice, to_dev_act
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+Q4_0, Q8_0, IQ4_NL = synth.Q4_0, synth.Q8_0, synth.IQ4_NL
+TYPES = [Q4_0, Q8_0, IQ4_NL]
+LUT = synth.IQ4_NL_STANDIN_LUT
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_quantized_matmul_repack_amd as tq
+    tq.lib()
+    return tq
+
+
+SHAPES = [(32, 1), (64, 31), (96, 33), (256, 64), (512, 65), (1024, 100), (4096, 97)]
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("K,N", SHAPES)
+def test_repack_bitexact(tq, qtype, K, N):
+    inp = make(qtype, K, N, 1, seed=K * 7 + N)
+    ref = oracle.repack(qtype, inp.flat, K, N)
+    flat = torch.from_numpy(inp.flat).cuda()
+    out = torch.full((ref.size + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    tq.repack_tiles(qtype, flat, K, N, out=out[:ref.size])
+    got = out.cpu().numpy()
+    assert np.array_equal(got[:ref.size], ref)
+    assert (got[ref.size:] == 0xA5).all()          # guard band untouched
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 256), (8, 4096), (37, 1024)])
+def test_quantize_bitexact(tq, act, M, K):
+    inp = make(Q8_0, K, 1, M, seed=M * 1000 + K, act=act)
+    x = inp.x.copy()
+    if act == "f32":
+        x[0, :32] = 0.0
+        if K >= 64:
+            x[0, 32:64] = 0.25
+            x[0, 32] = 127.0
+            x[0, 33:40] = [2.5, -2.5, 0.5, -0.5, 1.5, 126.5, -126.5]
+    dt = {"f32": oracle.F32, "bf16": oracle.BF16, "f16": oracle.F16}[act]
+    qr, dr = oracle.quantize_act(x, dt)
+    q, d = tq.quantize_act(to_dev_act(x, act))
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(d.cpu().view(torch.int16).numpy().view(np.uint16), dr)
+
+
+def test_quantize_row_stride(tq):
+    inp = make(Q8_0, 256, 1, 5, seed=3)
+    wide = np.concatenate([inp.x, np.full((5, 64), 9e5, np.float32)], axis=1)
+    qr, dr = oracle.quantize_act(wide, oracle.F32, K=256)
+    q, d = tq.quantize_act(torch.from_numpy(wide).cuda(), K=256)
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(d.cpu().view(torch.int16).numpy().view(np.uint16), dr)
+
+
+def _dev(inp, qtype, K, N):
+    tiles = oracle.repack(qtype, inp.flat, K, N)
+    return tiles, torch.from_numpy(tiles).cuda()
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("K,N", [(64, 33), (512, 100), (4096, 64)])
+def test_block_dots_gemv(tq, qtype, M, K, N):
+    inp = make(qtype, K, N, M, seed=M + 10 * K + N)
+    tiles, tdev = _dev(inp, qtype, K, N)
+    q, _ = oracle.quantize_act(inp.x)
+    ref = oracle.block_dots(qtype, tiles, K, N, q, LUT)
+    got = tq.block_dots(qtype, tdev, K, N, torch.from_numpy(q).cuda(), lut=LUT,
+                        path=tq.PATH_GEMV).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M", [1, 8, 33, 130])
+@pytest.mark.parametrize("K,N", [(64, 33), (512, 100), (1024, 129)])
+def test_block_dots_gemm(tq, qtype, M, K, N):
+    inp = make(qtype, K, N, M, seed=M + 10 * K + N + 1)
+    tiles, tdev = _dev(inp, qtype, K, N)
+    q, _ = oracle.quantize_act(inp.x)
+    ref = oracle.block_dots(qtype, tiles, K, N, q, LUT)
+    got = tq.block_dots(qtype, tdev, K, N, torch.from_numpy(q).cuda(), lut=LUT,
+                        path=tq.PATH_GEMM).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+def _y_case(tq, fn, qtype, M, K, N, seed):
+    inp = make(qtype, K, N, M, seed=seed)
+    tiles, tdev = _dev(inp, qtype, K, N)
+    q, d = oracle.quantize_act(inp.x)
+    y_ref, acond = oracle.matmul(qtype, tiles, K, N, q, d, LUT)
+    qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+    out = torch.full((M, N + 16), 7.0, dtype=torch.float32, device="cuda")
+    fn(qtype, tdev, K, N, qd, dd, lut=LUT, out=out)
+    got = out.cpu().numpy()
+    assert (got[:, N:] == 7.0).all()               # columns beyond N untouched
+    return check_y(got[:, :N], y_ref, acond, (qtype, M, K, N))
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("K,N", [(256, 64), (1024, 97), (4096, 300)])
+def test_qgemv_y(tq, qtype, M, K, N):
+    _y_case(tq, tq.qgemv, qtype, M, K, N, seed=M * 3 + K + N)
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M", [1, 9, 128, 200])
+@pytest.mark.parametrize("K,N", [(256, 64), (1024, 97), (2048, 300)])
+def test_qgemm_y(tq, qtype, M, K, N):
+    _y_case(tq, tq.qgemm, qtype, M, K, N, seed=M * 5 + K + N)
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+def test_gemv_gemm_agree(tq, qtype):
+    K, N, M = 1024, 130, 8
+    inp = make(qtype, K, N, M, seed=99)
+    _, tdev = _dev(inp, qtype, K, N)
+    qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+    b1 = tq.block_dots(qtype, tdev, K, N, qd, lut=LUT, path=tq.PATH_GEMV)
+    b2 = tq.block_dots(qtype, tdev, K, N, qd, lut=LUT, path=tq.PATH_GEMM)
+    assert torch.equal(b1, b2)
+    y1 = tq.qgemv(qtype, tdev, K, N, qd, dd, lut=LUT)
+    y2 = tq.qgemm(qtype, tdev, K, N, qd, dd, lut=LUT)
+    assert torch.allclose(y1, y2, rtol=1e-5, atol=1e-6 * float(y1.abs().max()))
+
+
+@pytest.mark.parametrize("fn", ["qgemv", "qgemm"])
+def test_deterministic(tq, fn):
+    K, N, M = 2048, 200, 4
+    inp = make(Q4_0, K, N, M, seed=5)
+    _, tdev = _dev(inp, Q4_0, K, N)
+    qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+    f = getattr(tq, fn)
+    y1 = f(Q4_0, tdev, K, N, qd, dd)
+    y2 = f(Q4_0, tdev, K, N, qd, dd)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_iq4_identity_table_equals_q4_0(tq):
+    K, N, M = 512, 70, 3
+    inp = make(Q4_0, K, N, M, seed=8)
+    _, tdev = _dev(inp, Q4_0, K, N)
+    qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+    ident = np.arange(16, dtype=np.int8) - 8
+    for f in (tq.qgemv, tq.qgemm):
+        assert torch.equal(f(Q4_0, tdev, K, N, qd, dd), f(IQ4_NL, tdev, K, N, qd, dd, lut=ident))
+
+
+def test_empty_shapes_are_noops(tq):
+    q = torch.zeros((1, 64), dtype=torch.int8, device="cuda")
+    d = torch.zeros((1, 2), dtype=torch.float16, device="cuda")
+    t = torch.zeros(0, dtype=torch.uint8, device="cuda")
+    y = tq.qgemv(Q4_0, t, 64, 0, q, d)
+    assert y.shape == (1, 0)
+    y = tq.qgemm(Q4_0, t, 64, 0, q, d)
+    assert y.shape == (1, 0)
+    torch.cuda.synchronize()
