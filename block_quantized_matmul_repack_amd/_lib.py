@@ -24,7 +24,8 @@ SIGNATURES = {
     "tq_status_string": (ctypes.c_char_p, [INT]),
     "tq_repack_tiles": (INT, [INT, P, I64, I64, P, P]),
     "tq_quantize_act": (INT, [INT, P, I64, I64, I64, P, P, P]),
-    "tq_qgemv": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
+    "tq_qgemv_workspace_bytes": (SZ, [INT, I64, I64, I64]),
+    "tq_qgemv": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P, SZ, P]),
     "tq_qgemm": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_block_dots": (INT, [INT, P, I64, I64, P, I64, P, P, INT, P]),
 }

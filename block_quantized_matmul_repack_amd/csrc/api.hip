@@ -149,17 +149,26 @@ int tq_quantize_act(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
     return launch_status(tq::launch_quantize(dtype, x, M, K, ldx, q, d, stream));
 }
 
+size_t tq_qgemv_workspace_bytes(int type, int64_t K, int64_t N, int64_t M)
+{
+    if (!valid_type(type) || !valid_kn(K, N) || N == 0 || M < 1 || M > 8)
+        return 0;
+    return tq::gemv_workspace_bytes(K, N, M);
+}
+
 int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
              const uint16_t *d, int64_t M, const int8_t *lut, float *y, int64_t ldy,
-             hipStream_t stream)
+             void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (valid_type(type) && M > 8)
         return TQ_E_SHAPE;
     int st = check_matmul(type, tiles, K, N, q, d, M, lut, y, ldy, true);
     if (st != TQ_OK || M == 0 || N == 0)
         return st;
-    return launch_status(
-        tq::launch_qgemv(type, tiles, K, N, q, d, M, pack_lut(lut), y, ldy, nullptr, stream));
+    if (workspace && !aligned(workspace, 256))
+        return TQ_E_ALIGN;
+    return launch_status(tq::launch_qgemv(type, tiles, K, N, q, d, M, pack_lut(lut), y, ldy,
+                                          nullptr, workspace, workspace_bytes, stream));
 }
 
 int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
@@ -188,7 +197,7 @@ int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N, const int8_
     const tq::Lut t = pack_lut(lut);
     hipError_t e = (path == TQ_PATH_GEMV)
                        ? tq::launch_qgemv(type, tiles, K, N, q, nullptr, M, t, nullptr, N,
-                                          isum, stream)
+                                          isum, nullptr, 0, stream)
                        : tq::launch_qgemm(type, tiles, K, N, q, nullptr, M, t, nullptr, N,
                                           isum, stream);
     return launch_status(e);

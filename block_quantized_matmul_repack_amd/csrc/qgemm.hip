@@ -1,16 +1,27 @@
 // Prefill matrix-matrix product over 32x32 tiles with int8 MFMA.
 //
-// A workgroup of 8 waves owns a BM x BN = 128 x 64 output block (M rows of
-// activations x N output features).  Per 32-element K block kt it stages in
-// LDS: the activation block (128 rows x 32 int8, natural K order) with its
-// fp16 scales, and the two weight tiles of its two stripes decoded to int8
-// in [row][K] order (the tile's [column pair][row] byte order is transposed
-// on the way in: "Block-32 Quantized Formats") with their fp16 row scales.
-// Each wave then runs one v_mfma_i32_32x32x32_i8 on its 32 x 32 sub-block;
-// the instruction's K depth equals the block size, so its int32 output is
-// exactly the per-block integer dot, which is scaled by (row scale x
-// activation scale, exact in fp32) and accumulated in fp32.  The next
-// block's global loads are issued before the current block's MFMA.
+// A workgroup of 8 waves owns a BM x BN = 128 x 64 output block (128
+// activation rows x two 32-row weight stripes); wave (wm, wn) owns one
+// 32 x 32 sub-block.  The K loop advances KB = 4 k-blocks per step:
+//   - activations: 64 rows x 4 x 32 int8, natural K order, and their fp16
+//     block scales go to LDS as loaded;
+//   - weights: each of the 8 waves takes one of the step's 8 tiles (2
+//     stripes x 4 blocks) and reads it as dwords of 4 rows / 2 rows of a
+//     column pair ("Block-32 Quantized Formats"), transposes bytes in
+//     registers with v_perm_b32, decodes them to int8 (code - 8, table
+//     lookup, or the int8 itself) and writes them to LDS in [row][K] order,
+//     with the fp16 row scales.
+// LDS is double-buffered and the global loads run two steps ahead of the
+// MFMAs (two register stages), with one barrier per step.  Q4_0 weights are
+// staged as 16 * (code - 8) (two bit operations per 4 weights); the 16 is
+// taken out of the fp32 result at the end, exactly.
+//
+// Per k-block each wave runs one v_mfma_i32_32x32x32_i8, whose K depth equals
+// the block size, so its int32 result is exactly the per-block integer dot.
+// The scale products dw[n] * da[m] (fp16 x fp16, exact in fp32) for the whole
+// 32 x 32 sub-block come from one rank-1 v_mfma_f32_32x32x8_f16, so the
+// vector ALU only converts each dot and adds it into the fp32 accumulator
+// (2 operations per output per block).
 #include "tq_internal.h"
 
 namespace tq {
@@ -18,161 +29,237 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 64, THREADS = 512;
-constexpr int LDS_ROW = 48;    // bytes per staged 32-byte row (padding spreads LDS banks)
+constexpr int BM = 128, BN = 64, KB = 4, THREADS = 512;
+#ifndef TQ_GEMM_MIN_BLOCKS
+#define TQ_GEMM_MIN_BLOCKS 1      // workgroups per CU the register budget is sized for
+#endif
+#ifndef TQ_GEMM_KB_UNROLL
+#define TQ_GEMM_KB_UNROLL 4
+#endif
+constexpr int LDS_ROW = 48;   // bytes per staged 32-byte row: 16 lanes of a b128 read hit all banks
 
 template <int QT>
-struct Stage {
-    uint4 a;          // 16 bytes of activations (threads 0..255)
-    uint16_t da;      // activation scale (threads 256..383)
-    uint32_t w[2];    // weight quant dwords
-    uint16_t dw;      // weight row scale (threads 448..511)
+struct StageRegs;
+template <>
+struct StageRegs<TQ_Q4_0> {
+    uint4 a[2];               // activations: 2 x 16 bytes
+    uint16_t da;              // one activation block scale
+    uint32_t w[2];            // weight dwords: rows 4g..4g+3 at column pairs 4c+2hh, 4c+2hh+1
+    uint16_t dw;              // weight row scale
+};
+template <>
+struct StageRegs<TQ_IQ4_NL> : StageRegs<TQ_Q4_0> {};
+template <>
+struct StageRegs<TQ_Q8_0> {
+    uint4 a[2];
+    uint16_t da;
+    uint32_t w[4];            // weight dwords: rows 2p, 2p+1 at column pairs 8h+4hh .. 8h+4hh+3
+    uint16_t dw;
 };
 
+struct Lds {
+    uint8_t A[2][KB][BM * LDS_ROW];
+    uint8_t B[2][KB][BN * LDS_ROW];
+    uint16_t da[2][KB][BM];
+    uint16_t dw[2][KB][BN];
+};
+
+// Buffer ranges of one workgroup: its activation rows, their scales, and its
+// two weight stripes.  Loads past them return zero.
+struct Ranges {
+    __amdgpu_buffer_rsrc_t q, d, w;
+};
+
+// Thread roles per step.  Every load is a raw buffer load issued by every
+// thread; out-of-range operands (rows >= M, blocks >= K/32, stripes past N)
+// read as zero, so there are no branches around loads and the compiler can
+// wait for exactly the older stage.  Activations: 128 rows x 4 blocks x 2
+// halves = 1024 chunks of 16 bytes (chunk ch: row ch/8, block (ch/2)%4, half
+// ch%2), two per thread, plus one block scale per thread (row t/4, block
+// t%4).  Weights: wave w takes the tile of stripe w/4, block w%4; lane
+// 32*hh + l reads, for tile lane l, half hh of that lane's column pairs.
 template <int QT, bool DOTS>
-__device__ __forceinline__ void load_stage(Stage<QT> &s, const uint8_t *tiles, int64_t nkt,
-                                           int64_t nct, int64_t ct0, const int8_t *q,
-                                           const uint16_t *d, int64_t M, int64_t K, int64_t m0,
-                                           int64_t kt, int tid)
+__device__ __forceinline__ void load_step(StageRegs<QT> &s, const Ranges &rg, int nkt, int K,
+                                          int kt0, int tid)
 {
     constexpr int TS = Fmt<QT>::tile;
-    if (tid < 256) {
-        const int64_t m = m0 + (tid >> 1);
-        if (m < M)
-            s.a = *(const uint4 *)(q + m * K + kt * 32 + 16 * (tid & 1));
-        else
-            s.a = make_uint4(0, 0, 0, 0);
-    } else if (tid < 384) {
-        const int64_t m = m0 + (tid - 256);
-        s.da = (!DOTS && m < M) ? d[m * nkt + kt] : (uint16_t)0;   // no scales in block-dot mode
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int ch = tid + THREADS * i;
+        const int row = ch >> 3, kb = (ch >> 1) & 3, h = ch & 1;
+        const int kt = kt0 + kb;
+        const int off = kt < nkt ? row * K + kt * 32 + 16 * h : BUF_OOB;
+        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rg.q, off, 0, 0);
+        s.a[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
-    // weight quants: Q8_0 512 dwords over 2 tiles (1 per thread);
-    // 4-bit 256 dwords (threads 256..511, 1 each)
+    if constexpr (DOTS) {
+        s.da = 0;
+    } else {
+        const int row = tid >> 2, kt = kt0 + (tid & 3);
+        const int off = kt < nkt ? (row * nkt + kt) * 2 : BUF_OOB;
+        s.da = __builtin_amdgcn_raw_buffer_load_b16(rg.d, off, 0, 0);
+    }
+    const int wave = tid >> 6, lane = tid & 63;
+    const int tt = wave >> 2, kt = kt0 + (wave & 3), l = lane & 31, hh = lane >> 5;
+    const int tile = kt < nkt ? (tt * nkt + kt) * TS : BUF_OOB;
     if constexpr (QT == TQ_Q8_0) {
-        const int tt = tid >> 8, w = tid & 255;
-        const int64_t ct = ct0 + tt;
-        s.w[0] = (ct < nct) ? __builtin_nontemporal_load(
-                                  (const uint32_t *)(tiles + (ct * nkt + kt) * TS) + w)
-                            : 0u;
-    } else if (tid >= 256) {
-        const int i = tid - 256, tt = i >> 7, w = i & 127;
-        const int64_t ct = ct0 + tt;
-        s.w[0] = (ct < nct) ? __builtin_nontemporal_load(
-                                  (const uint32_t *)(tiles + (ct * nkt + kt) * TS) + w)
-                            : 0u;
+        const int p = l >> 1, h = l & 1;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            s.w[i] = __builtin_amdgcn_raw_buffer_load_b32(
+                rg.w, tile + ((8 * h + 4 * hh + i) * 16 + p) * 4, 0, BUF_NT);
+    } else {
+        const int g = l >> 2, c = l & 3;
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+            s.w[i] = __builtin_amdgcn_raw_buffer_load_b32(
+                rg.w, tile + ((4 * c + 2 * hh + i) * 8 + g) * 4, 0, BUF_NT);
     }
-    if (tid >= 448) {
-        const int i = tid - 448, tt = i >> 5, r = i & 31;
-        const int64_t ct = ct0 + tt;
-        s.dw = (ct < nct) ? ((const uint16_t *)(tiles + (ct * nkt + kt) * TS +
-                                                Fmt<QT>::scale_off))[r]
-                          : (uint16_t)0;
-    }
+    s.dw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, tile + Fmt<QT>::scale_off + 2 * l, 0, 0);
 }
 
 template <int QT>
-__device__ __forceinline__ void store_stage(const Stage<QT> &s, uint8_t *As, uint8_t *Bs,
-                                            float *das, float *dws, const Lut &lut, int tid)
+__device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds &L, int buf,
+                                           const Lut &lut, int tid)
 {
-    if (tid < 256)
-        *(uint4 *)(As + (tid >> 1) * LDS_ROW + 16 * (tid & 1)) = s.a;
-    else if (tid < 384)
-        das[tid - 256] = f16_bits_to_f32(s.da);
-    if constexpr (QT == TQ_Q8_0) {
-        // dword w = cp*16 + p: [row 2p: col 2cp, 2cp+1][row 2p+1: col 2cp, 2cp+1]
-        const int tt = tid >> 8, w = tid & 255, cp = w >> 4, p = w & 15;
-        uint8_t *b = Bs + (32 * tt + 2 * p) * LDS_ROW + 2 * cp;
-        *(uint16_t *)b = (uint16_t)(s.w[0] & 0xFFFFu);
-        *(uint16_t *)(b + LDS_ROW) = (uint16_t)(s.w[0] >> 16);
-    } else if (tid >= 256) {
-        // dword w = cp*8 + g: byte j = row 4g+j, low nibble col 2cp, high col 2cp+1
-        const int i = tid - 256, tt = i >> 7, w = i & 127, cp = w >> 3, g = w & 7;
-        const uint32_t v = s.w[0];
-        uint32_t lo, hi;
-        if constexpr (QT == TQ_Q4_0) {
-            // code - 8 for 4-bit codes, bytewise: (c ^ 8) is c - 8 in 4-bit two's
-            // complement; sign-extend it to 8 bits
-            const uint32_t tl = (v & 0x0F0F0F0Fu) ^ 0x08080808u;
-            const uint32_t th = ((v >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
-            lo = tl | (((tl >> 3) & 0x01010101u) * 0xF0u);
-            hi = th | (((th >> 3) & 0x01010101u) * 0xF0u);
-        } else {
-            lo = lut16(v & 0x0F0F0F0Fu, lut);
-            hi = lut16((v >> 4) & 0x0F0F0F0Fu, lut);
-        }
-        // interleave: row j gets (lo byte j, hi byte j)
-        const uint32_t p01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // [lo0, hi0, lo1, hi1]
-        const uint32_t p23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // [lo2, hi2, lo3, hi3]
-        uint8_t *b = Bs + (32 * tt + 4 * g) * LDS_ROW + 2 * cp;
-        *(uint16_t *)b = (uint16_t)(p01 & 0xFFFFu);
-        *(uint16_t *)(b + LDS_ROW) = (uint16_t)(p01 >> 16);
-        *(uint16_t *)(b + 2 * LDS_ROW) = (uint16_t)(p23 & 0xFFFFu);
-        *(uint16_t *)(b + 3 * LDS_ROW) = (uint16_t)(p23 >> 16);
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int ch = tid + THREADS * i;
+        const int row = ch >> 3, kb = (ch >> 1) & 3, h = ch & 1;
+        *(uint4 *)(L.A[buf][kb] + row * LDS_ROW + 16 * h) = s.a[i];
     }
-    if (tid >= 448)
-        dws[tid - 448] = f16_bits_to_f32(s.dw);
+    L.da[buf][tid & 3][tid >> 2] = s.da;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int tt = wave >> 2, kb = wave & 3, l = lane & 31, hh = lane >> 5;
+    uint8_t *B = L.B[buf][kb] + (32 * tt) * LDS_ROW;
+    if constexpr (QT == TQ_Q8_0) {
+        // rows 2p (low halfwords) and 2p+1 (high halfwords), K 16h+8hh .. +7
+        const int p = l >> 1, h = l & 1;
+        const uint32_t a0 = __builtin_amdgcn_perm(s.w[1], s.w[0], 0x05040100u);
+        const uint32_t a1 = __builtin_amdgcn_perm(s.w[3], s.w[2], 0x05040100u);
+        const uint32_t b0 = __builtin_amdgcn_perm(s.w[1], s.w[0], 0x07060302u);
+        const uint32_t b1 = __builtin_amdgcn_perm(s.w[3], s.w[2], 0x07060302u);
+        *(uint2 *)(B + (2 * p) * LDS_ROW + 16 * h + 8 * hh) = make_uint2(a0, a1);
+        *(uint2 *)(B + (2 * p + 1) * LDS_ROW + 16 * h + 8 * hh) = make_uint2(b0, b1);
+    } else {
+        // rows 4g+j: byte j of the two column-pair dwords holds K = 2cp (low
+        // nibble) and 2cp+1 (high nibble) for cp = 4c+2hh, 4c+2hh+1, i.e. the
+        // 4 consecutive K = 8c+4hh .. 8c+4hh+3
+        const int g = l >> 2, c = l & 3;
+        const uint32_t p01 = __builtin_amdgcn_perm(s.w[1], s.w[0], 0x05010400u);  // rows 0, 1
+        const uint32_t p23 = __builtin_amdgcn_perm(s.w[1], s.w[0], 0x07030602u);  // rows 2, 3
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+            const uint32_t pr = r ? p23 : p01;
+            uint32_t lo, hi;          // per byte: even-K / odd-K weight
+            if constexpr (QT == TQ_Q4_0) {
+                const uint32_t t = pr ^ 0x88888888u;      // nibble c -> c - 8 (4-bit two's complement)
+                lo = (t << 4) & 0xF0F0F0F0u;              // 16 * (even-column code - 8)
+                hi = t & 0xF0F0F0F0u;                     // 16 * (odd-column code - 8)
+            } else {
+                lo = lut16(pr & 0x0F0F0F0Fu, lut);
+                hi = lut16((pr >> 4) & 0x0F0F0F0Fu, lut);
+            }
+            const uint32_t r0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // row 2r:   K +0..+3
+            const uint32_t r1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // row 2r+1: K +0..+3
+            *(uint32_t *)(B + (4 * g + 2 * r) * LDS_ROW + 8 * c + 4 * hh) = r0;
+            *(uint32_t *)(B + (4 * g + 2 * r + 1) * LDS_ROW + 8 * c + 4 * hh) = r1;
+        }
+    }
+    if (hh == 0)
+        L.dw[buf][kb][32 * tt + l] = s.dw;
 }
 
 template <int QT, bool DOTS>
-__global__ __launch_bounds__(THREADS) void k_qgemm(const uint8_t *__restrict__ tiles,
+__global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uint8_t *__restrict__ tiles,
                                                    int64_t nkt, int64_t N,
                                                    const int8_t *__restrict__ q,
                                                    const uint16_t *__restrict__ d, int64_t M,
                                                    int64_t K, Lut lut, float *__restrict__ y,
                                                    int64_t ldy, int32_t *__restrict__ isum)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t As[BM * LDS_ROW];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[BN * LDS_ROW];
-    __shared__ __attribute__((aligned(16))) float das[BM];
-    __shared__ float dws[BN];
+    __shared__ __attribute__((aligned(16))) Lds L;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 3, wn = wave >> 2;
+    const int li = lane & 31, lk = lane >> 5;
     const int64_t nct = (N + 31) / 32;
     const int64_t ct0 = (int64_t)blockIdx.x * (BN / 32);
     const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int64_t nsteps = (nkt + KB - 1) / KB;
+    constexpr int TS = Fmt<QT>::tile;
+    Ranges rg;
+    rg.q = make_rsrc(q + m0 * K, min<int64_t>(M - m0, BM) * K);
+    rg.d = make_rsrc(DOTS ? (const void *)q : (const void *)(d + m0 * nkt),
+                     DOTS ? 0 : min<int64_t>(M - m0, BM) * nkt * 2);
+    rg.w = make_rsrc(tiles + ct0 * nkt * TS, min<int64_t>(nct - ct0, BN / 32) * nkt * TS);
 
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; r++)
         acc[r] = 0.0f;
 
-    const int li = lane & 31, lk = lane >> 5;
-    Stage<QT> st;
-    load_stage<QT, DOTS>(st, tiles, nkt, nct, ct0, q, d, M, K, m0, 0, tid);
-    for (int64_t kt = 0; kt < nkt; kt++) {
-        __syncthreads();                 // previous block's LDS reads are done
-        store_stage<QT>(st, As, Bs, das, dws, lut, tid);
-        __syncthreads();
-        if (kt + 1 < nkt)
-            load_stage<QT, DOTS>(st, tiles, nkt, nct, ct0, q, d, M, K, m0, kt + 1, tid);
-
-        const v4i a = *(const v4i *)(As + (32 * wm + li) * LDS_ROW + 16 * lk);
-        const v4i b = *(const v4i *)(Bs + (32 * wn + li) * LDS_ROW + 16 * lk);
-        v16i z = {};
-        const v16i dot = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
-        // output layout: lane holds column li, rows 8*(r/4) + 4*lk + (r%4)
-        if constexpr (DOTS) {
-            const int64_t n = 32 * (ct0 + wn) + li;
+    auto compute = [&](int buf, int64_t step) {
+#pragma unroll TQ_GEMM_KB_UNROLL
+        for (int kb = 0; kb < KB; kb++) {
+            const v4i a = *(const v4i *)(L.A[buf][kb] + (32 * wm + li) * LDS_ROW + 16 * lk);
+            const v4i b = *(const v4i *)(L.B[buf][kb] + (32 * wn + li) * LDS_ROW + 16 * lk);
+            const v16i z = {};
+            const v16i dot = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
+            // output layout: lane holds column li, rows 8*(r/4) + 4*lk + (r%4)
+            if constexpr (DOTS) {
+                const int64_t kt = step * KB + kb;
+                const int64_t n = 32 * (ct0 + wn) + li;
+                if (kt < nkt && n < N) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int64_t m = m0 + 32 * wm + 8 * (r >> 2) + 4 * lk + (r & 3);
-                if (m < M && n < N)
-                    isum[(m * N + n) * nkt + kt] = dot[r];
-            }
-        } else {
-            const float dw = dws[32 * wn + li];
+                    for (int r = 0; r < 16; r++) {
+                        const int64_t m = m0 + 32 * wm + 8 * (r >> 2) + 4 * lk + (r & 3);
+                        if (m < M)
+                            isum[(m * N + n) * nkt + kt] = (QT == TQ_Q4_0) ? (dot[r] >> 4) : dot[r];
+                    }
+                }
+            } else {
+                // rank-1 fp16 MFMA: sc[m][n] = da[m] * dw[n], exact in fp32
+                const uint16_t dab = L.da[buf][kb][32 * wm + li];
+                const uint16_t dwb = L.dw[buf][kb][32 * wn + li];
+                v4h ua = {}, ub = {};
+                ua[0] = __builtin_bit_cast(_Float16, lk == 0 ? dab : (uint16_t)0);
+                ub[0] = __builtin_bit_cast(_Float16, lk == 0 ? dwb : (uint16_t)0);
+                const v16f zf = {};
+                const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(ua, ub, zf, 0, 0, 0);
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const float4 da = *(const float4 *)(das + 32 * wm + 8 * g + 4 * lk);
-                acc[4 * g + 0] = fmaf((float)dot[4 * g + 0], da.x * dw, acc[4 * g + 0]);
-                acc[4 * g + 1] = fmaf((float)dot[4 * g + 1], da.y * dw, acc[4 * g + 1]);
-                acc[4 * g + 2] = fmaf((float)dot[4 * g + 2], da.z * dw, acc[4 * g + 2]);
-                acc[4 * g + 3] = fmaf((float)dot[4 * g + 3], da.w * dw, acc[4 * g + 3]);
+                for (int r = 0; r < 16; r++)
+                    acc[r] = fmaf((float)dot[r], sc[r], acc[r]);
             }
         }
+    };
+
+    // Two register stages: step s+1's data is in flight while step s+2 is
+    // issued.  Prefetches past the last step re-read the last step, so every
+    // iteration issues the same loads.
+    StageRegs<QT> r0, r1;
+    const int64_t last = nsteps - 1;
+    load_step<QT, DOTS>(r0, rg, (int)nkt, (int)K, 0, tid);
+    load_step<QT, DOTS>(r1, rg, (int)nkt, (int)K, (int)min<int64_t>(1, last) * KB, tid);
+    store_step<QT>(r0, L, 0, lut, tid);
+    __syncthreads();
+    for (int64_t step = 0; step < nsteps; step += 2) {
+        // even step: buffer 0 is computed, r1 holds step+1, r0 is free
+        load_step<QT, DOTS>(r0, rg, (int)nkt, (int)K, (int)min<int64_t>(step + 2, last) * KB, tid);
+        compute(0, step);
+        store_step<QT>(r1, L, 1, lut, tid);
+        __syncthreads();
+        if (step + 1 >= nsteps)
+            break;
+        // odd step: buffer 1 is computed, r0 holds step+2, r1 is free
+        load_step<QT, DOTS>(r1, rg, (int)nkt, (int)K, (int)min<int64_t>(step + 3, last) * KB, tid);
+        compute(1, step + 1);
+        store_step<QT>(r0, L, 0, lut, tid);
+        __syncthreads();
     }
     if constexpr (DOTS)
         return;
@@ -182,7 +269,7 @@ __global__ __launch_bounds__(THREADS) void k_qgemm(const uint8_t *__restrict__ t
         for (int r = 0; r < 16; r++) {
             const int64_t m = m0 + 32 * wm + 8 * (r >> 2) + 4 * lk + (r & 3);
             if (m < M)
-                y[m * ldy + n] = acc[r];
+                y[m * ldy + n] = (QT == TQ_Q4_0) ? acc[r] * 0.0625f : acc[r];
         }
     }
 }
@@ -194,6 +281,10 @@ hipError_t launch_t(const void *tiles, int64_t K, int64_t N, const int8_t *q, co
 {
     const int64_t nkt = K / 32;
     const int64_t nct = (N + 31) / 32;
+    // x = weight blocks, y = activation blocks.  The dispatcher deals
+    // consecutive workgroup ids round-robin to the 8 XCDs, so when the x
+    // extent is a multiple of 8 all activation blocks of one weight block run
+    // on one XCD and each weight tile is fetched into a single L2.
     dim3 grid((unsigned)((nct + BN / 32 - 1) / (BN / 32)), (unsigned)((M + BM - 1) / BM));
     if (isum)
         k_qgemm<QT, true><<<grid, THREADS, 0, s>>>((const uint8_t *)tiles, nkt, N, q, d, M, K,

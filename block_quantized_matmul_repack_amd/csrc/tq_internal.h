@@ -21,6 +21,28 @@ template <> struct Fmt<TQ_Q8_0> {
     static constexpr int tile = 1088, scale_off = 1024, block = 34;
 };
 
+// Raw buffer loads (CDNA buffer resource descriptor, stride 0): a load whose
+// byte offset lies outside [0, bytes) returns zero, so out-of-range operands
+// are zeroed without branches and every path issues the same loads.  Ranges
+// stay below 2^31 bytes; BUF_OOB is an offset past all of them.
+constexpr int64_t BUF_MAX_BYTES = 0x7E000000;
+constexpr int BUF_OOB = 0x7F000000;  // + any in-tile offset stays positive
+constexpr int BUF_NT = 2;                 // aux bits: nontemporal (stream past the caches)
+
+// `base` and `bytes` must be the same in every lane of the wave (they are
+// read from the first active lane so the descriptor lives in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const int64_t n = bytes < 0 ? 0 : (bytes < BUF_MAX_BYTES ? bytes : BUF_MAX_BYTES);
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int nr = __builtin_amdgcn_readfirstlane((int)n);
+    // descriptor word 3: 32-bit data format, required by gfx9-family raw buffers
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, nr,
+                                             0x00020000);
+}
+
 // IQ4_NL table as four little-endian dwords (entries 4i..4i+3 in dword i).
 struct Lut {
     uint32_t w[4];
@@ -49,13 +71,23 @@ __device__ __forceinline__ uint32_t lut16(uint32_t idx, const Lut &t)
     return (hi & m) | (lo & ~m);
 }
 
+// K-split of the decode GEMV: S workgroups per stripe, `chunk` k-tiles each;
+// part / cnt point into the caller's workspace when S > 1.
+struct Split {
+    int S, chunk;
+    float *part;
+    uint32_t *cnt;
+};
+Split gemv_split(int64_t K, int64_t N);
+size_t gemv_workspace_bytes(int64_t K, int64_t N, int64_t M);
+
 hipError_t launch_repack(int type, const void *flat, int64_t K, int64_t N, void *tiles,
                          hipStream_t s);
 hipError_t launch_quantize(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
                            int8_t *q, uint16_t *d, hipStream_t s);
 hipError_t launch_qgemv(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
                         const uint16_t *d, int64_t M, const Lut &lut, float *y, int64_t ldy,
-                        int32_t *isum, hipStream_t s);
+                        int32_t *isum, void *ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
                         const uint16_t *d, int64_t M, const Lut &lut, float *y, int64_t ldy,
                         int32_t *isum, hipStream_t s);

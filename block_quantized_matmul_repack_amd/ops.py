@@ -94,27 +94,51 @@ def quantize_act(x, K=None, q=None, d=None):
     return q, d
 
 
-def _matmul(fn, name, qtype, tiles, K, N, q, d, lut, out):
-    _need_cuda(tiles, q, d, out)
+def _out(name, q, N, out):
     M = q.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=q.device)
     if out.dim() != 2 or out.shape[0] < M or out.stride(1) != 1 or out.dtype != torch.float32:
         raise TiledqError(f"{name}: bad output tensor")
-    ldy = out.stride(0)
-    check(fn(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut), _ptr(out), ldy,
-             _stream(q)), name)
     return out
 
 
-def qgemv(qtype, tiles, K, N, q, d, lut=None, out=None):
-    """Decode product y [M, N] = W (tiles) x A (q, d), M <= 8."""
-    return _matmul(lib().tq_qgemv, "tq_qgemv", qtype, tiles, K, N, q, d, lut, out)
+# Zero-filled qgemv workspaces, one per (device, stream): every call leaves
+# its workspace zero-filled, so it is reused by later calls on the same stream
+# without clearing (calls on one stream never overlap).
+_workspaces = {}
+
+
+def workspace(device, stream_handle, nbytes):
+    key = (device, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def qgemv(qtype, tiles, K, N, q, d, lut=None, out=None, split=True):
+    """Decode product y [M, N] = W (tiles) x A (q, d), M <= 8.  split=False
+    runs one workgroup per stripe (no workspace)."""
+    _need_cuda(tiles, q, d, out)
+    out = _out("tq_qgemv", q, N, out)
+    M = q.shape[0]
+    st = _stream(q)
+    need = lib().tq_qgemv_workspace_bytes(qtype, K, N, M) if split else 0
+    ws = workspace(q.device, st.value, need) if need else None
+    check(lib().tq_qgemv(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut),
+                         _ptr(out), out.stride(0), _ptr(ws), need, st), "tq_qgemv")
+    return out
 
 
 def qgemm(qtype, tiles, K, N, q, d, lut=None, out=None):
     """Prefill product y [M, N] on int8 MFMA, any M."""
-    return _matmul(lib().tq_qgemm, "tq_qgemm", qtype, tiles, K, N, q, d, lut, out)
+    _need_cuda(tiles, q, d, out)
+    out = _out("tq_qgemm", q, N, out)
+    check(lib().tq_qgemm(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), q.shape[0], _lut_arg(lut),
+                         _ptr(out), out.stride(0), _stream(q)), "tq_qgemm")
+    return out
 
 
 def block_dots(qtype, tiles, K, N, q, lut=None, path=PATH_GEMV, out=None):

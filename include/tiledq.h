@@ -121,6 +121,11 @@ int tq_repack_tiles(int type, const void *flat, int64_t K, int64_t N,
 int tq_quantize_act(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
                     int8_t *q, uint16_t *d, hipStream_t stream);
 
+/* Bytes of workspace tq_qgemv can use for (type, K, N, M) to split K across
+ * workgroups when N alone gives too few of them (0: no split is useful, or
+ * the arguments are invalid). */
+size_t tq_qgemv_workspace_bytes(int type, int64_t K, int64_t N, int64_t M);
+
 /* Decode matrix-vector product over tiles (M <= 8 activation rows), reading
  * every weight tile exactly once.
  *   tiles : device, tq_tiled_bytes(type, K, N) bytes, 16-byte aligned.
@@ -131,14 +136,23 @@ int tq_quantize_act(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
  *           (may be NULL) for the other types.
  *   y     : device fp32, y[m*ldy + n] written for m < M, n < N only;
  *           ldy >= N; 4-byte aligned.
- * Deterministic: repeated calls give identical bytes. */
+ *   workspace, workspace_bytes : optional device scratch, 256-byte aligned,
+ *           owned by the caller.  It must be zero-filled before its first
+ *           use; every call leaves it zero-filled again, so it can be reused
+ *           by later calls of any shape without clearing.  Calls that share
+ *           a workspace must not run concurrently.  With NULL or fewer than
+ *           tq_qgemv_workspace_bytes() bytes the K dimension is not split
+ *           (same result, fewer workgroups).
+ * Deterministic: repeated calls give identical bytes, with or without the
+ * workspace (partial sums are added in a fixed order). */
 int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N,
              const int8_t *q, const uint16_t *d, int64_t M,
-             const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
+             const int8_t *lut, float *y, int64_t ldy,
+             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Prefill matrix-matrix product over tiles with int8 matrix-core (MFMA)
- * instructions, any M >= 1.  Arguments as tq_qgemv.  Same integer block dots
- * as tq_qgemv; deterministic. */
+ * instructions, any M >= 1.  Arguments as tq_qgemv without the workspace.
+ * Same integer block dots as tq_qgemv; deterministic. */
 int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N,
              const int8_t *q, const uint16_t *d, int64_t M,
              const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);

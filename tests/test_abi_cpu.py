@@ -68,6 +68,18 @@ NUL = None
 LUT = (ctypes.c_int8 * 16)(*range(-8, 8))
 
 
+def test_workspace_bytes(L):
+    # K=N=4096, M=1: 128 stripes, each split S ways -> 512 B of counters (one
+    # uint32 per stripe, padded to 256 B) + S * 32 fp32 partials per stripe
+    ws = L.tq_qgemv_workspace_bytes(1, 4096, 4096, 1)
+    assert (ws - 512) % (128 * 32 * 4) == 0 and 2 <= (ws - 512) // (128 * 32 * 4) <= 8
+    assert L.tq_qgemv_workspace_bytes(1, 4096, 128001, 1) == 0      # enough stripes
+    assert L.tq_qgemv_workspace_bytes(1, 4096, 4096, 9) == 0
+    assert L.tq_qgemv_workspace_bytes(1, 4000 + 1, 4096, 1) == 0
+    assert L.tq_qgemv_workspace_bytes(1, 4096, 0, 1) == 0           # empty: no division by 0
+    assert L.tq_qgemv_workspace_bytes(1, 4096, 4096, 0) == 0
+
+
 def test_status_strings(L):
     for s in range(6):
         assert L.tq_status_string(s).startswith(b"TQ_")
@@ -97,7 +109,11 @@ def test_quantize_validation(L):
 
 @pytest.mark.parametrize("fn", ["tq_qgemv", "tq_qgemm"])
 def test_matmul_validation(L, fn):
-    f = getattr(L, fn)
+    if fn == "tq_qgemv":
+        def f(*a):
+            return L.tq_qgemv(*a[:10], None, 0, a[10])
+    else:
+        f = L.tq_qgemm
     assert f(9, A16, 64, 32, A16, A16, 1, NUL, A16, 32, NUL) == 2
     assert f(0, A16, 48, 32, A16, A16, 1, NUL, A16, 32, NUL) == 3
     assert f(0, A16, 64, 32, A16, A16, 1, NUL, A16, 31, NUL) == 3     # ldy < N
@@ -115,7 +131,8 @@ def test_matmul_validation(L, fn):
 
 
 def test_gemv_m_limit(L):
-    assert L.tq_qgemv(0, A16, 64, 32, A16, A16, 9, NUL, A16, 32, NUL) == 3
+    assert L.tq_qgemv(0, A16, 64, 32, A16, A16, 9, NUL, A16, 32, NUL, 0, NUL) == 3
+    assert L.tq_qgemv(0, A16, 64, 32, A16, A16, 1, NUL, A16, 32, A16 if False else ctypes.c_void_p(0x10010), 4096, NUL) == 4
     assert L.tq_block_dots(0, A16, 64, 32, A16, 9, NUL, A16, 0, NUL) == 3
     assert L.tq_block_dots(0, A16, 64, 32, A16, 9, NUL, A16, 7, NUL) == 2
 

@@ -175,3 +175,47 @@ def test_empty_shapes_are_noops(tq):
     y = tq.qgemm(Q4_0, t, 64, 0, q, d)
     assert y.shape == (1, 0)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("K,N", [(96, 40), (160, 300), (4064, 33), (2048, 1), (4096, 4096)])
+def test_qgemv_split_and_unsplit(tq, qtype, M, K, N):
+    """K split across workgroups (workspace) and one workgroup per stripe both
+    meet the tolerance and are each bitwise repeatable."""
+    inp = make(qtype, K, N, M, seed=M * 7 + K + N)
+    tiles, tdev = _dev(inp, qtype, K, N)
+    q, d = oracle.quantize_act(inp.x)
+    y_ref, acond = oracle.matmul(qtype, tiles, K, N, q, d, LUT)
+    qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+    for split in (True, False):
+        y1 = tq.qgemv(qtype, tdev, K, N, qd, dd, lut=LUT, split=split)
+        y2 = tq.qgemv(qtype, tdev, K, N, qd, dd, lut=LUT, split=split)
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+        check_y(y1.cpu().numpy(), y_ref, acond, (qtype, M, K, N, split))
+    ref = oracle.block_dots(qtype, tiles, K, N, q, LUT)
+    got = tq.block_dots(qtype, tdev, K, N, qd, lut=LUT, path=tq.PATH_GEMV).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_qgemv_workspace_reused_across_shapes(tq):
+    """One workspace serves calls of different shapes in a row (its counter
+    and partial offsets depend on the shape): every call must leave it zero."""
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    L = tq.lib()
+    import ctypes
+    for (K, N) in [(4096, 2048), (2048, 4096), (4096, 4096), (1024, 100), (4096, 4096)]:
+        inp = make(Q4_0, K, N, 1, seed=K + N)
+        tiles, tdev = _dev(inp, Q4_0, K, N)
+        q, d = oracle.quantize_act(inp.x)
+        y_ref, acond = oracle.matmul(Q4_0, tiles, K, N, q, d)
+        qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+        y = torch.full((1, N), float("nan"), device="cuda")
+        need = L.tq_qgemv_workspace_bytes(Q4_0, K, N, 1)
+        assert 0 < need <= ws.numel()
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert L.tq_qgemv(Q4_0, ctypes.c_void_p(tdev.data_ptr()), K, N, ctypes.c_void_p(qd.data_ptr()),
+                          ctypes.c_void_p(dd.data_ptr()), 1, None, ctypes.c_void_p(y.data_ptr()), N,
+                          ctypes.c_void_p(ws.data_ptr()), ws.numel(), st) == 0
+        check_y(y.cpu().numpy(), y_ref, acond, (K, N))
+        assert int(ws.count_nonzero()) == 0
