@@ -1,0 +1,137 @@
+"""GPU parity at the workloads' full sizes, through the same binding calls
+(and so the same launch geometry, K split included) that bench.py times.
+
+Repack and quantization are compared in full, bit for bit.  y is compared in
+full where the oracle finishes in seconds, else on sampled 32-row stripes
+(first, middle and the ragged last one).  Integer block dots are compared on
+the same stripes, running the GEMV / GEMM kernel on that stripe's slice of
+the tile buffer.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import check_y, to_dev_act
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+LUT = synth.IQ4_NL_STANDIN_LUT
+_DT = {"f32": oracle.F32, "bf16": oracle.BF16, "f16": oracle.F16}
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_quantized_matmul_repack_amd as tq
+    tq.lib()
+    return tq
+
+
+class Case:
+    """One workload: inputs, oracle repack and quantization, device copies."""
+
+    def __init__(self, tq, name, M=None):
+        w = synth.WORKLOADS[name]
+        self.w = w
+        self.M = w.M if M is None else M
+        print(f"[full] {name} M={self.M}: generating", flush=True)
+        self.inp = synth.make_inputs(w, M=self.M)
+        self.tiles_ref = oracle.repack(w.qtype, self.inp.flat, w.K, w.N)
+        self.q_ref, self.d_ref = oracle.quantize_act(self.inp.x, _DT[w.act_dtype])
+        print(f"[full] {name}: device repack + quantize", flush=True)
+        flat = torch.from_numpy(self.inp.flat).cuda()
+        self.tiles = tq.repack_tiles(w.qtype, flat, w.K, w.N)
+        del flat
+        self.q, self.d = tq.quantize_act(to_dev_act(self.inp.x, w.act_dtype))
+        torch.cuda.synchronize()
+
+
+def _stripes(w):
+    nct = w.n_col_tiles
+    return sorted({0, nct // 2, nct - 1})
+
+
+def _check_case(tq, c, fn, full_y):
+    w = c.w
+    assert np.array_equal(c.tiles.cpu().numpy(), c.tiles_ref), "repack differs"
+    assert np.array_equal(c.q.cpu().numpy(), c.q_ref), "quantized activations differ"
+    assert np.array_equal(c.d.cpu().view(torch.int16).numpy().view(np.uint16), c.d_ref)
+    print(f"[full] {w.name}: {fn.__name__}", flush=True)
+    y = fn(w.qtype, c.tiles, w.K, w.N, c.q, c.d, lut=c.inp.lut).cpu().numpy()
+    if full_y:
+        y_ref, acond = oracle.matmul(w.qtype, c.tiles_ref, w.K, w.N, c.q_ref, c.d_ref, c.inp.lut)
+        check_y(y, y_ref, acond, w.name)
+    else:
+        for s in _stripes(w):
+            n0, n1 = 32 * s, min(32 * s + 32, w.N)
+            y_ref, acond = oracle.matmul(w.qtype, c.tiles_ref, w.K, w.N, c.q_ref, c.d_ref,
+                                         c.inp.lut, n0=n0, n1=n1)
+            check_y(y[:, n0:n1], y_ref[:, n0:n1], acond[:, n0:n1], (w.name, s))
+
+
+def _check_dots(tq, c, path):
+    """Block dots of sampled stripes, from the kernel run on the stripe's slice."""
+    w = c.w
+    ts = oracle.tile_bytes(w.qtype)
+    nkt = w.K // 32
+    for s in _stripes(w):
+        n = min(32, w.N - 32 * s)
+        sl = c.tiles[s * nkt * ts:(s + 1) * nkt * ts]
+        sl_ref = c.tiles_ref[s * nkt * ts:(s + 1) * nkt * ts]
+        got = tq.block_dots(w.qtype, sl, w.K, n, c.q, lut=c.inp.lut, path=path).cpu().numpy()
+        ref = oracle.block_dots(w.qtype, sl_ref, w.K, n, c.q_ref, c.inp.lut)
+        assert np.array_equal(got, ref), (w.name, s)
+
+
+def test_q4_0_k256_n64_m1(tq):
+    c = Case(tq, "q4_0_gemv_k256_n64_m1")
+    _check_case(tq, c, tq.qgemv, full_y=True)
+    _check_dots(tq, c, tq.PATH_GEMV)
+
+
+def test_q8_0_k4096_n4096_m1(tq):
+    c = Case(tq, "q8_0_gemv_k4096_n4096_m1")
+    _check_case(tq, c, tq.qgemv, full_y=True)
+    _check_dots(tq, c, tq.PATH_GEMV)
+    got = tq.block_dots(c.w.qtype, c.tiles, c.w.K, c.w.N, c.q, path=tq.PATH_GEMV).cpu().numpy()
+    ref = oracle.block_dots(c.w.qtype, c.tiles_ref, c.w.K, c.w.N, c.q_ref)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_q4_0_k4096_n14336(tq, M):
+    c = Case(tq, "q4_0_gemv_k4096_n14336_m1", M=M)
+    _check_case(tq, c, tq.qgemv, full_y=True)
+    _check_dots(tq, c, tq.PATH_GEMV)
+
+
+def test_iq4_nl_m512_k4096_n4096(tq):
+    c = Case(tq, "iq4_nl_gemm_m512_k4096_n4096")
+    _check_case(tq, c, tq.qgemm, full_y=False)
+    _check_dots(tq, c, tq.PATH_GEMM)
+
+
+@pytest.fixture(scope="module")
+def lmhead(tq):
+    return Case(tq, "q8_0_lmhead_k4096_n128001_m128")
+
+
+def test_q8_0_lmhead_n128001_m1(tq, lmhead):
+    """Decode over the 128001-row lm-head (ragged last tile, 1 valid row)."""
+    w = lmhead.w
+    assert w.n_col_tiles == 4001 and w.N - 32 * (w.n_col_tiles - 1) == 1
+    assert np.array_equal(lmhead.tiles.cpu().numpy(), lmhead.tiles_ref), "repack differs"
+    q1, d1 = lmhead.q[:1].contiguous(), lmhead.d[:1].contiguous()
+    y = tq.qgemv(w.qtype, lmhead.tiles, w.K, w.N, q1, d1).cpu().numpy()
+    y_ref, acond = oracle.matmul(w.qtype, lmhead.tiles_ref, w.K, w.N, lmhead.q_ref[:1],
+                                 lmhead.d_ref[:1])
+    check_y(y, y_ref, acond, "lmhead m1")
+
+
+def test_q8_0_lmhead_n128001_m128(tq, lmhead):
+    """Prefill over the lm-head: sampled stripes, ragged last one included."""
+    _check_case(tq, lmhead, tq.qgemm, full_y=False)
+    _check_dots(tq, lmhead, tq.PATH_GEMM)
