@@ -2,7 +2,8 @@
 """Benchmark of the tiled block-32 quantized matmul hot path on one MI355X.
 
 Step (the decode hot path, one token): dynamic int8 quantization of the
-activation row, then the tiled GEMV over the repacked weights -- on the
+activation row and the tiled GEMV over the repacked weights, fused in one
+launch (tq_qgemv_x; the two-launch form is timed as well) -- on the
 Q8_0 K=4096 N=4096 M=1 workload (fp16 scales |N(0,1)|*0.01, int8 codes
 uniform in [-127, 127], fp32 activations N(0,1), seed 0).  The weights are
 repacked on the GPU once, at load (as the pages place repacking), into R
@@ -12,8 +13,8 @@ Infinity Cache.  All inputs are resident in HBM before the timed region;
 the K timed steps are replayed from a HIP graph.
 
 Printed: one JSON line.  value = weight-tile bytes per step / step time
-(GB/s).  roofline = the GEMV kernel alone: algorithmic bytes (weight tiles
-+ int8 activations + fp16 activation scales + fp32 outputs) per launch over
+(GB/s).  roofline = the fused decode kernel: algorithmic bytes (weight tiles
++ fp32 activations + fp32 outputs) per launch over
 its average duration: launches replayed back to back from a HIP graph on the
 current stream, bracketed by HIP events recorded on that stream.
 Also reported: the int8-MFMA GEMM on the IQ4_NL M=512 K=N=4096 workload
@@ -33,6 +34,49 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 ROTATE_BYTES = 1 << 30         # defeat the 256 MB Infinity Cache
 
+# HBM traffic of the kernels, from rocprofv3 --pmc passes (FETCH_SIZE, then
+# WRITE_SIZE, each in its own run) of `bench.py --launch-only <kernel>`: KiB
+# per dispatch as the counters read them, averaged over the dispatches.  The
+# same counters read for a plain 256 MiB device copy (`--launch-only copy`)
+# give FETCH_SIZE 131083.55 KiB and WRITE_SIZE 262144 KiB for 262144 KiB moved
+# each way, so FETCH_SIZE is scaled by 262144 / 131084.5 and WRITE_SIZE by 1.
+# "src" is the SHA-256 of the kernel's sources when the counters were taken;
+# once they differ, traffic is reported as null.
+FETCH_SCALE = 262144.0 / 131083.55
+WRITE_SCALE = 1.0
+TRAFFIC = {
+    "decode": {"fetch_kib": 8800.01, "write_kib": 112.0,
+               "src": "5d3d160ec6b7c826abeb384a368f5408e462aecf08881cfe559e7961da1f2b73"},
+    "gemm": {"fetch_kib": 13372.03, "write_kib": 8192.0,
+             "src": "a40974dde259adcd55e77d23c28bbade68e77fb96952905afc3e11677c5f914e"},
+    "repack": {"fetch_kib": 16147.18, "write_kib": 32256.0,
+               "src": "13f67fc23bdb53a872fa4d68cba950443435a92c9b34cc58fa3a145511c45c34"},
+}
+KERNEL_SOURCES = {
+    "decode": ("qgemv.hip", "tq_internal.h"),
+    "gemm": ("qgemm.hip", "tq_internal.h"),
+    "repack": ("repack.hip", "tq_internal.h"),
+}
+LAUNCH_ONLY = ("decode", "gemm", "repack", "copy")
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "block_quantized_matmul_repack_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(kernel):
+    """Counter-measured HBM bytes per launch, or None if the kernel's sources
+    changed since the counters were taken (or none were taken)."""
+    t = TRAFFIC.get(kernel)
+    if t is None or t["src"] != source_hash(kernel):
+        return None
+    return int(round(1024 * (t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE)))
+
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -45,13 +89,15 @@ def parse():
     p.add_argument("--no-extra", action="store_true",
                    help="skip the GEMM and repack measurements")
     p.add_argument("--eager", action="store_true", help="time eager launches, not a graph")
+    p.add_argument("--launch-only", choices=sorted(LAUNCH_ONLY), default=None,
+                   help="no timing: launch one kernel --steps times on the bench's inputs "
+                        "(for rocprofv3 --pmc counter passes) and exit")
     return p.parse_args()
 
 
-def gemv_bytes(w):
-    """Algorithmic bytes of one qgemv launch: tiles + q + d + y."""
-    nkt = w.K // 32
-    return w.weight_bytes + w.M * w.K + w.M * nkt * 2 + w.M * w.N * 4
+def gemv_x_bytes(w):
+    """Algorithmic bytes of one fused decode launch: tiles + fp32 x + fp32 y."""
+    return w.weight_bytes + 4 * w.M * w.K + 4 * w.M * w.N
 
 
 def capture(torch, fn, n):
@@ -84,7 +130,8 @@ def kernel_us(torch, fn, n=200):
     return a.elapsed_time(b) / n * 1e3
 
 
-def measure_gemv(torch, tq, synth, args):
+def setup_decode(torch, tq, synth):
+    """Decode-step inputs in HBM; returns (workload, copies, step, step2, parts)."""
     import numpy as np
     w = synth.WORKLOADS["q8_0_gemv_k4096_n4096_m1"]
     inp = synth.make_inputs(w)
@@ -100,12 +147,25 @@ def measure_gemv(torch, tq, synth, args):
     d = torch.empty((w.M, w.K // 32), dtype=torch.float16, device="cuda")
     y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
 
-    def step(i):
+    def step(i):                 # one decode token: quantize + GEMV in one launch
+        tq.qgemv_x(w.qtype, tiles[i % R], w.K, w.N, xs[i % X: i % X + 1], out=y)
+
+    def step2(i):                # the same with the quantization as its own launch
         tq.quantize_act(xs[i % X: i % X + 1], q=q, d=d)
         tq.qgemv(w.qtype, tiles[i % R], w.K, w.N, q, d, out=y)
 
+    parts = {
+        "qgemv": lambda i: tq.qgemv(w.qtype, tiles[i % R], w.K, w.N, q, d, out=y),
+        "quantize_act": lambda i: tq.quantize_act(xs[i % X: i % X + 1], q=q, d=d),
+    }
+    return w, R, step, step2, parts
+
+
+def measure_gemv(torch, tq, synth, args):
+    w, R, step, step2, parts = setup_decode(torch, tq, synth)
     for i in range(args.warmup):
         step(i)
+        step2(i)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -113,19 +173,28 @@ def measure_gemv(torch, tq, synth, args):
         run = lambda: [step(i) for i in range(K)]
     else:
         run = capture(torch, step, K).replay
-
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
-    gemv_us = kernel_us(torch, lambda i: tq.qgemv(w.qtype, tiles[i % R], w.K, w.N, q, d, out=y))
-    quant_us = kernel_us(torch, lambda i: tq.quantize_act(xs[i % X: i % X + 1], q=q, d=d))
-    return w, R, dt, gemv_us, quant_us
+    two = capture(torch, step2, 500)
+    t1 = time.perf_counter()
+    two.replay()
+    torch.cuda.synchronize()
+    two_us = (time.perf_counter() - t1) / 500 * 1e6
+
+    detail = {
+        "qgemv_x_us": kernel_us(torch, step),
+        "qgemv_us": kernel_us(torch, parts["qgemv"]),
+        "quantize_act_us": kernel_us(torch, parts["quantize_act"]),
+        "two_launch_step_us": two_us,
+    }
+    return w, R, dt, detail
 
 
-def measure_gemm(torch, tq, synth, n=200):
+def setup_gemm(torch, tq, synth):
     import numpy as np
     w = synth.WORKLOADS["iq4_nl_gemm_m512_k4096_n4096"]
     inp = synth.make_inputs(w)
@@ -136,19 +205,32 @@ def measure_gemm(torch, tq, synth, n=200):
     q, d = tq.quantize_act(x)
     y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
     f = lambda i: tq.qgemm(w.qtype, tiles[i % R], w.K, w.N, q, d, lut=inp.lut, out=y)
+    quant = lambda i: tq.quantize_act(x, q=q, d=d)
+    return w, f, quant
+
+
+def gemm_bytes(w):
+    """Algorithmic bytes of one GEMM launch: tiles + int8 q + fp16 d + fp32 y."""
+    return w.weight_bytes + w.M * w.K + 2 * w.M * (w.K // 32) + 4 * w.M * w.N
+
+
+def measure_gemm(torch, tq, synth, n=200):
+    w, f, quant = setup_gemm(torch, tq, synth)
     for i in range(20):
         f(i)
     us = kernel_us(torch, f, n)
-    quant_us = kernel_us(torch, lambda i: tq.quantize_act(x, q=q, d=d), 50)
+    quant_us = kernel_us(torch, quant, 50)
     tops = 2.0 * w.M * w.N * w.K / us / 1e6
+    tb = traffic_bytes("gemm")
     return {"workload": w.name, "metric": "qgemm int8 TOPS", "value": round(tops, 2),
             "unit": "TOPS", "kernel_us": round(us, 3), "quantize_act_us": round(quant_us, 3),
+            "hbm_GB_s": round(gemm_bytes(w) / us / 1e3, 1),
             "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4),
-                         "traffic": None}}
+                         "traffic": tb, "bytes_per_launch": gemm_bytes(w)}}
 
 
-def measure_repack(torch, tq, synth, n=50):
+def setup_repack(torch, tq, synth):
     w = synth.WORKLOADS["q4_0_gemv_k4096_n14336_m1"]
     inp = synth.make_inputs(w)
     fb = inp.flat.size
@@ -156,6 +238,11 @@ def measure_repack(torch, tq, synth, n=50):
     flats = [torch.from_numpy(inp.flat).cuda() for _ in range(min(R, 32))]
     out = torch.empty(w.weight_bytes, dtype=torch.uint8, device="cuda")
     f = lambda i: tq.repack_tiles(w.qtype, flats[i % len(flats)], w.K, w.N, out=out)
+    return w, f, fb
+
+
+def measure_repack(torch, tq, synth, n=50):
+    w, f, fb = setup_repack(torch, tq, synth)
     for i in range(5):
         f(i)
     us = kernel_us(torch, f, n)
@@ -163,7 +250,26 @@ def measure_repack(torch, tq, synth, n=50):
     return {"workload": "repack " + w.name, "kernel_us": round(us, 3), "GB_s": round(gbs, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None}}
+                         "traffic": traffic_bytes("repack"),
+                         "bytes_per_launch": fb + w.weight_bytes}}
+
+
+def launch_only(torch, tq, synth, kernel, n):
+    """Launch one kernel n times, eagerly, untimed (counter collection)."""
+    if kernel == "decode":
+        f = setup_decode(torch, tq, synth)[2]
+    elif kernel == "gemm":
+        f = setup_gemm(torch, tq, synth)[1]
+    elif kernel == "repack":
+        f = setup_repack(torch, tq, synth)[1]
+    else:                                   # calibration: a plain 256 MiB copy
+        a = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        f = lambda i: b.copy_(a)
+    for i in range(n):
+        f(i)
+    torch.cuda.synchronize()
+    print(f"launched {kernel} x{n}", flush=True)
 
 
 def cpu_baseline(synth, w, seconds):
@@ -199,27 +305,31 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     tq.lib()
+    if args.launch_only:
+        launch_only(torch, tq, synth, args.launch_only, args.steps)
+        return
 
-    w, R, dt, gemv_us, quant_us = measure_gemv(torch, tq, synth, args)
+    w, R, dt, det = measure_gemv(torch, tq, synth, args)
     K = args.steps
     ms = dt / K * 1e3
     value = w.weight_bytes / (dt / K) / 1e9
-    achieved = gemv_bytes(w) / gemv_us / 1e3
+    achieved = gemv_x_bytes(w) / det["qgemv_x_us"] / 1e3
     line = {
         "metric": "qgemv weight-stream GB/s (% of HBM peak); qgemm int8 TOPS (% MFMA peak)",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": w.name, "qtype": "q8_0", "K": w.K, "N": w.N, "M": w.M,
-                   "step": "quantize_act + qgemv", "weight_copies": R,
+                   "step": "quantize_act + qgemv fused (tq_qgemv_x)", "weight_copies": R,
                    "launch": "eager" if args.eager else "hip graph",
                    "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "kernel": "qgemv", "kernel_us": round(gemv_us, 3),
-                     "bytes_per_launch": gemv_bytes(w)},
-        "quantize_act_us": round(quant_us, 3),
+                     "traffic": traffic_bytes("decode"),
+                     "kernel": "k_qgemv (fused quantize, Q8_0, M=1)",
+                     "kernel_us": round(det["qgemv_x_us"], 3),
+                     "bytes_per_launch": gemv_x_bytes(w)},
+        "decode_detail_us": {k: round(v, 3) for k, v in det.items()},
     }
     if not args.no_extra:
         line["qgemm"] = measure_gemm(torch, tq, synth)

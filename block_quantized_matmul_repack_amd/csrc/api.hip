@@ -167,7 +167,32 @@ int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
         return st;
     if (workspace && !aligned(workspace, 256))
         return TQ_E_ALIGN;
-    return launch_status(tq::launch_qgemv(type, tiles, K, N, q, d, M, pack_lut(lut), y, ldy,
+    const tq::Act act{q, d, nullptr, -1, 0};
+    return launch_status(tq::launch_qgemv(type, tiles, K, N, act, M, pack_lut(lut), y, ldy,
+                                          nullptr, workspace, workspace_bytes, stream));
+}
+
+int tq_qgemv_x(int type, const void *tiles, int64_t K, int64_t N, int dtype, const void *x,
+               int64_t ldx, int64_t M, const int8_t *lut, float *y, int64_t ldy,
+               void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16)
+        return TQ_E_TYPE;
+    if (valid_type(type) && M > 8)
+        return TQ_E_SHAPE;
+    if (ldx < K || M * ldx >= MAX_PROD)
+        return TQ_E_SHAPE;
+    // x stands in for q in the common checks; its own alignment is checked below
+    int st = check_matmul(type, tiles, K, N, (const int8_t *)tiles, nullptr, M, lut, y, ldy,
+                          false);
+    if (st != TQ_OK || M == 0 || N == 0)
+        return st;
+    if (!x)
+        return TQ_E_NULL;
+    if (!aligned(x, dtype == TQ_F32 ? 4 : 2) || (workspace && !aligned(workspace, 256)))
+        return TQ_E_ALIGN;
+    const tq::Act act{nullptr, nullptr, x, dtype, ldx};
+    return launch_status(tq::launch_qgemv(type, tiles, K, N, act, M, pack_lut(lut), y, ldy,
                                           nullptr, workspace, workspace_bytes, stream));
 }
 
@@ -195,9 +220,10 @@ int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N, const int8_
     if ((int64_t)M * N * (K / 32) >= MAX_PROD)
         return TQ_E_SHAPE;
     const tq::Lut t = pack_lut(lut);
+    const tq::Act act{q, nullptr, nullptr, -1, 0};
     hipError_t e = (path == TQ_PATH_GEMV)
-                       ? tq::launch_qgemv(type, tiles, K, N, q, nullptr, M, t, nullptr, N,
-                                          isum, nullptr, 0, stream)
+                       ? tq::launch_qgemv(type, tiles, K, N, act, M, t, nullptr, N, isum,
+                                          nullptr, 0, stream)
                        : tq::launch_qgemm(type, tiles, K, N, q, nullptr, M, t, nullptr, N,
                                           isum, stream);
     return launch_status(e);

@@ -203,39 +203,58 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
     for (int r = 0; r < 16; r++)
         acc[r] = 0.0f;
 
-    auto compute = [&](int buf, int64_t step) {
-#pragma unroll TQ_GEMM_KB_UNROLL
-        for (int kb = 0; kb < KB; kb++) {
-            const v4i a = *(const v4i *)(L.A[buf][kb] + (32 * wm + li) * LDS_ROW + 16 * lk);
-            const v4i b = *(const v4i *)(L.B[buf][kb] + (32 * wn + li) * LDS_ROW + 16 * lk);
-            const v16i z = {};
-            const v16i dot = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
-            // output layout: lane holds column li, rows 8*(r/4) + 4*lk + (r%4)
-            if constexpr (DOTS) {
-                const int64_t kt = step * KB + kb;
-                const int64_t n = 32 * (ct0 + wn) + li;
-                if (kt < nkt && n < N) {
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int64_t m = m0 + 32 * wm + 8 * (r >> 2) + 4 * lk + (r & 3);
-                        if (m < M)
-                            isum[(m * N + n) * nkt + kt] = (QT == TQ_Q4_0) ? (dot[r] >> 4) : dot[r];
-                    }
-                }
-            } else {
-                // rank-1 fp16 MFMA: sc[m][n] = da[m] * dw[n], exact in fp32
-                const uint16_t dab = L.da[buf][kb][32 * wm + li];
-                const uint16_t dwb = L.dw[buf][kb][32 * wn + li];
-                v4h ua = {}, ub = {};
-                ua[0] = __builtin_bit_cast(_Float16, lk == 0 ? dab : (uint16_t)0);
-                ub[0] = __builtin_bit_cast(_Float16, lk == 0 ? dwb : (uint16_t)0);
-                const v16f zf = {};
-                const v16f sc = __builtin_amdgcn_mfma_f32_32x32x8f16(ua, ub, zf, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-                    acc[r] = fmaf((float)dot[r], sc[r], acc[r]);
-            }
+    // One k-block: the int8 MFMA (exact block dots) and, for y, the rank-1
+    // fp16 MFMA giving sc[m][n] = da[m] * dw[n] (exact in fp32).
+    auto mfmas = [&](int buf, int kb, v16i &dot, v16f &sc) {
+        const v4i a = *(const v4i *)(L.A[buf][kb] + (32 * wm + li) * LDS_ROW + 16 * lk);
+        const v4i b = *(const v4i *)(L.B[buf][kb] + (32 * wn + li) * LDS_ROW + 16 * lk);
+        const v16i z = {};
+        dot = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
+        if constexpr (!DOTS) {
+            const uint16_t dab = L.da[buf][kb][32 * wm + li];
+            const uint16_t dwb = L.dw[buf][kb][32 * wn + li];
+            v4h ua = {}, ub = {};
+            ua[0] = __builtin_bit_cast(_Float16, lk == 0 ? dab : (uint16_t)0);
+            ub[0] = __builtin_bit_cast(_Float16, lk == 0 ? dwb : (uint16_t)0);
+            const v16f zf = {};
+            sc = __builtin_amdgcn_mfma_f32_32x32x8f16(ua, ub, zf, 0, 0, 0);
         }
+    };
+    // Output layout of both MFMAs: lane holds column li, rows
+    // 8*(r/4) + 4*lk + (r%4).
+    auto epilogue = [&](int64_t kt, const v16i &dot, const v16f &sc) {
+        if constexpr (DOTS) {
+            const int64_t n = 32 * (ct0 + wn) + li;
+            if (kt < nkt && n < N) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int64_t m = m0 + 32 * wm + 8 * (r >> 2) + 4 * lk + (r & 3);
+                    if (m < M)
+                        isum[(m * N + n) * nkt + kt] = (QT == TQ_Q4_0) ? (dot[r] >> 4) : dot[r];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                acc[r] = fmaf((float)dot[r], sc[r], acc[r]);
+        }
+    };
+    // Software pipeline over the step's k-blocks: the MFMAs of block kb+1 are
+    // issued before the vector epilogue of block kb, so the matrix cores and
+    // the vector ALU work at the same time (the scheduling barriers keep the
+    // compiler from regrouping them).
+    auto compute = [&](int buf, int64_t step) {
+        v16i dot[2];
+        v16f sc[2];
+        mfmas(buf, 0, dot[0], sc[0]);
+#pragma unroll
+        for (int kb = 1; kb < KB; kb++) {
+            mfmas(buf, kb, dot[kb & 1], sc[kb & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            epilogue(step * KB + kb - 1, dot[(kb - 1) & 1], sc[(kb - 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        epilogue(step * KB + KB - 1, dot[(KB - 1) & 1], sc[(KB - 1) & 1]);
     };
 
     // Two register stages: step s+1's data is in flight while step s+2 is

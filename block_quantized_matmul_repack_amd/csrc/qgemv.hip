@@ -26,10 +26,9 @@
 //
 // Work split.  Workgroup (ct, ks) takes k-tiles [ks*C, (ks+1)*C) of stripe
 // ct.  Its waves' partial sums are added in a fixed order through LDS.  With
-// S > 1 workgroups per stripe the partials go to a workspace and the last
-// workgroup to finish (atomic counter) adds the S partials in ks order, so
-// results are deterministic for every S; it then zeroes the partials and the
-// counter, so the workspace is all-zero again after every call.
+// S > 1 workgroups per stripe the S partials are added in a fixed pairwise
+// tree through a workspace (see the end of k_qgemv), so results are
+// deterministic for every S and the workspace is all-zero after every call.
 #include <algorithm>
 
 #include "tq_internal.h"
@@ -51,9 +50,6 @@ __device__ __forceinline__ int dpp_xor2(int v)
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-// Largest S * M * 32 of a split: the last workgroup gathers that many partials
-// into LDS.
-constexpr int MAX_SPLIT_OUT = 2048;
 // LDS for one pass of staged activations (int8 q and fp16 scales, all M rows).
 constexpr int ACT_LDS_BYTES = 32768;
 
@@ -234,14 +230,15 @@ __device__ __forceinline__ void store_unit(const Unit<QT> &u, uint8_t *dst, int 
     }
 }
 
-template <int QT, int MM, int NW, bool DOTS>
+// XT < 0: activations arrive quantized (act.q, act.d).  XT = a tq_dtype: raw
+// activations act.x are quantized here, per pass, straight into LDS with the
+// same quant32() as tq_quantize_act, so q and d are bit-identical.
+template <int QT, int MM, int NW, int XT, bool DOTS>
 __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ tiles, int nkt,
-                                                   int64_t N, const int8_t *__restrict__ q,
-                                                   const uint16_t *__restrict__ d, int64_t K,
-                                                   Lut lut, float *__restrict__ y, int64_t ldy,
+                                                   int64_t N, Act act, int64_t K, Lut lut,
+                                                   float *__restrict__ y, int64_t ldy,
                                                    int32_t *__restrict__ isum, int chunk, int S,
-                                                   float *__restrict__ ws_part,
-                                                   uint32_t *__restrict__ ws_cnt)
+                                                   uint64_t *__restrict__ ws_slots)
 {
     constexpr int TS = Fmt<QT>::tile;
     constexpr int UB = Unit<QT>::BYTES;
@@ -249,15 +246,15 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     __shared__ __attribute__((aligned(16))) uint8_t stage[NW][UB];
     __shared__ __attribute__((aligned(16))) uint8_t act_lds[ACT_LDS_BYTES];
     __shared__ float red[2 * NW][MM][32];
-    __shared__ float gath[MAX_SPLIT_OUT];
-    __shared__ int last_flag;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, l = lane & 31;
+    const int hs = 2 * wave + half;                       // half-wave slot in the workgroup
     const int64_t ct = blockIdx.x / S;
     const int ks = blockIdx.x - (int)(ct * S);
     const int kt0 = ks * chunk;
-    const int nt = min(chunk, nkt - kt0);                 // tiles of this workgroup
+    const int nt = max(0, min(chunk, nkt - kt0));         // tiles of this workgroup
+    const int64_t nct = (N + 31) / 32;
     const uint8_t *cbase = tiles + (ct * (int64_t)nkt + kt0) * TS;
     const int64_t nb = nkt;
 
@@ -288,15 +285,55 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     uint16_t *ds = (uint16_t *)(act_lds + MM * P * 32);
     for (int pb = 0; pb < nt; pb += P) {
         const int pn = min(P, nt - pb);                   // tiles in this pass
+        const int nunits = (pn + 1) >> 1;
+        const uint8_t *pbase = cbase + (int64_t)pb * TS;
+        auto load_stage = [&](Unit<QT> &u, int j) {
+            load_unit<QT>(u, pbase + (int64_t)j * UB, min(2, pn - 2 * j) * (TS / 16), lane);
+        };
+        const int count = wave < nunits ? (nunits - 1 - wave) / NW + 1 : 0;   // units of this wave
         __syncthreads();                                  // previous pass done with qs / ds
-        for (int c = threadIdx.x; c < MM * pn * 2; c += NW * 64) {
-            const int m = c / (pn * 2), o = c - m * pn * 2;   // 16-byte chunk o of row m
-            *(uint4 *)(qs + m * P * 32 + o * 16) =
-                *(const uint4 *)(q + m * K + (int64_t)(kt0 + pb) * 32 + o * 16);
-        }
-        for (int c = threadIdx.x; c < MM * pn; c += NW * 64) {
-            const int m = c / pn, o = c - m * pn;
-            ds[m * P + o] = DOTS ? (uint16_t)0 : d[m * nb + kt0 + pb + o];
+        // the pass's first weight unit is in flight while the activations
+        // are staged
+        Unit<QT> ua, ub;
+        if (count > 0)
+            load_stage(ua, wave);
+        if constexpr (XT < 0) {
+            for (int c = threadIdx.x; c < MM * pn * 2; c += NW * 64) {
+                const int m = c / (pn * 2), o = c - m * pn * 2;   // 16-byte chunk o of row m
+                *(uint4 *)(qs + m * P * 32 + o * 16) =
+                    *(const uint4 *)(act.q + m * K + (int64_t)(kt0 + pb) * 32 + o * 16);
+            }
+            for (int c = threadIdx.x; c < MM * pn; c += NW * 64) {
+                const int m = c / pn, o = c - m * pn;
+                ds[m * P + o] = DOTS ? (uint16_t)0 : act.d[m * nb + kt0 + pb + o];
+            }
+        } else {
+            // one 32-element block per half-wave, one element per lane; the
+            // loads of XB blocks are issued together
+            constexpr int XB = 4;
+            const int nblk = MM * pn;
+            for (int b0 = hs; b0 < nblk; b0 += 2 * NW * XB) {
+                float v[XB];
+#pragma unroll
+                for (int u = 0; u < XB; u++) {
+                    const int b = min(b0 + u * 2 * NW, nblk - 1);
+                    const int m = b / pn, tp = b - m * pn;
+                    v[u] = load_x<XT>(act.x, m * act.ldx + (int64_t)(kt0 + pb + tp) * 32 + l);
+                }
+#pragma unroll
+                for (int u = 0; u < XB; u++) {
+                    const int b = b0 + u * 2 * NW;
+                    if (b < nblk) {
+                        const int m = b / pn, tp = b - m * pn;
+                        int8_t qv;
+                        uint16_t db;
+                        quant32(v[u], qv, db);
+                        qs[m * P * 32 + tp * 32 + l] = qv;
+                        if (l == 0)
+                            ds[m * P + tp] = db;
+                    }
+                }
+            }
         }
         __syncthreads();
 
@@ -304,11 +341,6 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
         // (indices clamped into range), the next stage is always issued before
         // the current one is used and the last is peeled, so one stage's
         // loads overlap the previous stage's compute.
-        const int nunits = (pn + 1) >> 1;
-        const uint8_t *pbase = cbase + (int64_t)pb * TS;
-        auto load_stage = [&](Unit<QT> &u, int j) {
-            load_unit<QT>(u, pbase + (int64_t)j * UB, min(2, pn - 2 * j) * (TS / 16), lane);
-        };
         auto process = [&](const Unit<QT> &u, int j) {
             store_unit<QT>(u, my, min(2, pn - 2 * j) * (TS / 16), lane);
             const int tp = min(2 * j + half, pn - 1);         // this half's tile, pass-local
@@ -337,12 +369,9 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                     acc[m] = fmaf((float)s[m], dw * f16_bits_to_f32(x.d[m]), acc[m]);
             }
         };
-        const int count = wave < nunits ? (nunits - 1 - wave) / NW + 1 : 0;   // units of this wave
         if (count > 0) {
             // two unit buffers used in turn (no register copies, which would
             // wait for the prefetch); every loop iteration prefetches
-            Unit<QT> ua, ub;
-            load_stage(ua, wave);
             int it = 0;
             for (; it + 2 < count; it += 2) {
                 load_stage(ub, wave + (it + 1) * NW);
@@ -364,7 +393,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
 
 #pragma unroll
     for (int m = 0; m < MM; m++)
-        red[2 * wave + half][m][l] = acc[m];
+        red[hs][m][l] = acc[m];
     __syncthreads();
     const int i = threadIdx.x;
     const int m = i >> 5, r = i & 31;
@@ -380,40 +409,33 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
             y[m * ldy + n] = part;
         return;
     }
-    // Cross-workgroup reduction.  Partials are published and collected with
-    // relaxed agent-scope atomic exchanges, which are coherent across the
-    // XCDs' L2 caches without a cache write-back.  Each publishing lane waits
-    // for its exchange to return (the asm consumes the value) before the
-    // workgroup increments the stripe's counter, so the last workgroup to
-    // arrive finds every partial in place.  It adds them in ks order and
-    // exchanges zeros back, leaving the workspace zero for the next call of
-    // any shape (counter and partial offsets depend on the shape).
-    if (i < MM * 32) {
-        const float old = __hip_atomic_exchange(&ws_part[((ct * S + ks) * MM + m) * 32 + r], part,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("" ::"v"(old));
-    }
-    __syncthreads();
-    if (i == 0)
-        last_flag = (atomicAdd(&ws_cnt[ct], 1u) == (uint32_t)(S - 1));
-    __syncthreads();
-    if (!last_flag)
+    // Cross-workgroup reduction over the S = 2^L workgroups of the stripe, as
+    // a pairwise tree: at level lv, workgroups ks and ks ^ 2^lv pair up.  Each
+    // output exchanges (marker | value bits) into its pair's 64-bit slot with
+    // a relaxed agent-scope atomic (coherent across the XCD L2s without a
+    // cache write-back).  The first to arrive leaves its value there; the
+    // second finds it, adds (fp32 addition is commutative, so the sum has the
+    // same bits whoever arrives second), clears the slot and goes on to the
+    // next level.  The result is ((p0 + p1) + (p2 + p3)) + ... in every run,
+    // and the workspace is zero again when the call ends.
+    if (i >= MM * 32)
         return;
-    // gather all S * MM * 32 partials at once (one round trip), then add them
-    // in ks order
-    for (int g = i; g < S * MM * 32; g += NW * 64)
-        gath[g] = __hip_atomic_exchange(&ws_part[(ct * S) * MM * 32 + g], 0.0f, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (i < MM * 32) {
-        float sum = 0.0f;
-        for (int k = 0; k < S; k++)
-            sum += gath[(k * MM + m) * 32 + r];
-        if (n < N)
-            y[m * ldy + n] = sum;
+    float v = part;
+    uint64_t *slots = ws_slots;
+    for (int lv = 0; (1 << lv) < S; lv++) {
+        const int pairs = S >> (lv + 1);
+        uint64_t *slot = slots + ((ct * pairs + (ks >> (lv + 1))) * MM + m) * 32 + r;
+        const uint64_t mine = (uint64_t(1) << 32) | __float_as_uint(v);
+        const uint64_t old =
+            __hip_atomic_exchange(slot, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == 0)
+            return;                               // first of the pair: done
+        v = v + __uint_as_float((uint32_t)old);
+        __hip_atomic_store(slot, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        slots += (size_t)nct * pairs * MM * 32;
     }
-    if (i == 0)
-        __hip_atomic_store(&ws_cnt[ct], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n < N)
+        y[m * ldy + n] = v;
 }
 
 #ifndef TQ_GEMV_NW
@@ -425,82 +447,83 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
 constexpr int NW = TQ_GEMV_NW;                   // waves per workgroup
 constexpr int64_t TARGET_WG = TQ_GEMV_TARGET_WG; // workgroups wanted for a full chip
 
-template <int QT, int MM>
-hipError_t launch_m(const void *tiles, int64_t K, int64_t N, const int8_t *q, const uint16_t *d,
-                    const Lut &lut, float *y, int64_t ldy, int32_t *isum, const Split &sp,
-                    hipStream_t s)
+template <int QT, int MM, int XT, bool DOTS>
+hipError_t launch_k(const void *tiles, int64_t K, int64_t N, const Act &act, const Lut &lut,
+                    float *y, int64_t ldy, int32_t *isum, const Split &sp, hipStream_t s)
 {
     const int nkt = (int)(K / 32);
     const int64_t nct = (N + 31) / 32;
     dim3 grid((unsigned)(nct * sp.S));
-    if (isum)
-        k_qgemv<QT, MM, NW, true><<<grid, NW * 64, 0, s>>>((const uint8_t *)tiles, nkt, N, q, d,
-                                                           K, lut, y, ldy, isum, sp.chunk, sp.S,
-                                                           sp.part, sp.cnt);
-    else
-        k_qgemv<QT, MM, NW, false><<<grid, NW * 64, 0, s>>>((const uint8_t *)tiles, nkt, N, q, d,
-                                                            K, lut, y, ldy, isum, sp.chunk, sp.S,
-                                                            sp.part, sp.cnt);
+    k_qgemv<QT, MM, NW, XT, DOTS><<<grid, NW * 64, 0, s>>>((const uint8_t *)tiles, nkt, N, act, K,
+                                                           lut, y, ldy, isum, sp.chunk, sp.S,
+                                                           sp.slots);
     return hipGetLastError();
 }
 
+template <int QT, int MM>
+hipError_t launch_m(const void *tiles, int64_t K, int64_t N, const Act &act, const Lut &lut,
+                    float *y, int64_t ldy, int32_t *isum, const Split &sp, hipStream_t s)
+{
+    if (isum)
+        return launch_k<QT, MM, -1, true>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    switch (act.xt) {
+    case -1: return launch_k<QT, MM, -1, false>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    case TQ_F32: return launch_k<QT, MM, TQ_F32, false>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    case TQ_BF16: return launch_k<QT, MM, TQ_BF16, false>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    case TQ_F16: return launch_k<QT, MM, TQ_F16, false>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int QT>
-hipError_t launch_t(const void *tiles, int64_t K, int64_t N, const int8_t *q, const uint16_t *d,
-                    int64_t M, const Lut &lut, float *y, int64_t ldy, int32_t *isum,
-                    const Split &sp, hipStream_t s)
+hipError_t launch_t(const void *tiles, int64_t K, int64_t N, const Act &act, int64_t M,
+                    const Lut &lut, float *y, int64_t ldy, int32_t *isum, const Split &sp,
+                    hipStream_t s)
 {
     switch (M) {
-    case 1: return launch_m<QT, 1>(tiles, K, N, q, d, lut, y, ldy, isum, sp, s);
-    case 2: return launch_m<QT, 2>(tiles, K, N, q, d, lut, y, ldy, isum, sp, s);
-    case 3: return launch_m<QT, 3>(tiles, K, N, q, d, lut, y, ldy, isum, sp, s);
-    case 4: return launch_m<QT, 4>(tiles, K, N, q, d, lut, y, ldy, isum, sp, s);
-    case 5: return launch_m<QT, 5>(tiles, K, N, q, d, lut, y, ldy, isum, sp, s);
-    case 6: return launch_m<QT, 6>(tiles, K, N, q, d, lut, y, ldy, isum, sp, s);
-    case 7: return launch_m<QT, 7>(tiles, K, N, q, d, lut, y, ldy, isum, sp, s);
-    case 8: return launch_m<QT, 8>(tiles, K, N, q, d, lut, y, ldy, isum, sp, s);
+    case 1: return launch_m<QT, 1>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    case 2: return launch_m<QT, 2>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    case 3: return launch_m<QT, 3>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    case 4: return launch_m<QT, 4>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    case 5: return launch_m<QT, 5>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    case 6: return launch_m<QT, 6>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    case 7: return launch_m<QT, 7>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
+    case 8: return launch_m<QT, 8>(tiles, K, N, act, lut, y, ldy, isum, sp, s);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// K-split geometry: enough workgroups to fill the chip (TARGET_WG), chunks of
-// an even number of k-tiles (whole units), never more splits than units.
+// K-split geometry: S = 1, 2, 4 or 8 workgroups per stripe, enough for about
+// TARGET_WG workgroups in all, chunks of an even number of k-tiles (whole
+// units).  Workgroups whose chunk starts past K contribute zero.
 Split gemv_split(int64_t K, int64_t N)
 {
     Split sp{};
     const int64_t nkt = K / 32, nct = (N + 31) / 32;
-    if (nkt < 1 || nct < 1) {
-        sp.S = 1;
-        sp.chunk = (int)std::max<int64_t>(nkt, 1);
-        return sp;
-    }
-    int64_t S = (TARGET_WG + nct - 1) / nct;
-    S = std::min<int64_t>(S, MAX_SPLIT_OUT / (32 * 8));
-    S = std::max<int64_t>(1, std::min<int64_t>(S, (nkt + 1) / 2));
-    int64_t chunk = (nkt + S - 1) / S;
+    sp.S = 1;
+    if (nkt >= 1 && nct >= 1)
+        while (sp.S < 8 && nct * sp.S < TARGET_WG && 2 * sp.S <= (nkt + 1) / 2)
+            sp.S *= 2;
+    int64_t chunk = (nkt + sp.S - 1) / sp.S;
     chunk += chunk & 1;
-    S = (nkt + chunk - 1) / chunk;
-    sp.S = (int)S;
-    sp.chunk = (int)chunk;
+    sp.chunk = (int)std::max<int64_t>(chunk, 1);
     return sp;
 }
 
-// Workspace: one uint32 counter per stripe (padded to 256 bytes), then
-// S * M * 32 fp32 partial sums per stripe.
+// Workspace: the tree's 64-bit slots, (S - 1) * M * 32 per stripe.
 size_t gemv_workspace_bytes(int64_t K, int64_t N, int64_t M)
 {
     const Split sp = gemv_split(K, N);
     if (sp.S <= 1)
         return 0;
-    const int64_t nct = (N + 31) / 32;
-    const size_t cnt = ((size_t)nct * 4 + 255) & ~(size_t)255;
-    return cnt + (size_t)nct * sp.S * M * 32 * 4;
+    return (size_t)((N + 31) / 32) * (sp.S - 1) * M * 32 * 8;
 }
 
-hipError_t launch_qgemv(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
-                        const uint16_t *d, int64_t M, const Lut &lut, float *y, int64_t ldy,
-                        int32_t *isum, void *ws, size_t ws_bytes, hipStream_t s)
+hipError_t launch_qgemv(int type, const void *tiles, int64_t K, int64_t N, const Act &act,
+                        int64_t M, const Lut &lut, float *y, int64_t ldy, int32_t *isum,
+                        void *ws, size_t ws_bytes, hipStream_t s)
 {
     Split sp = gemv_split(K, N);
     if (!isum && sp.S > 1) {
@@ -509,16 +532,13 @@ hipError_t launch_qgemv(int type, const void *tiles, int64_t K, int64_t N, const
             sp.S = 1;
             sp.chunk = (int)(K / 32);
         } else {
-            const int64_t nct = (N + 31) / 32;
-            const size_t cnt = ((size_t)nct * 4 + 255) & ~(size_t)255;
-            sp.cnt = (uint32_t *)ws;
-            sp.part = (float *)((uint8_t *)ws + cnt);
+            sp.slots = (uint64_t *)ws;
         }
     }
     switch (type) {
-    case TQ_Q4_0: return launch_t<TQ_Q4_0>(tiles, K, N, q, d, M, lut, y, ldy, isum, sp, s);
-    case TQ_Q8_0: return launch_t<TQ_Q8_0>(tiles, K, N, q, d, M, lut, y, ldy, isum, sp, s);
-    case TQ_IQ4_NL: return launch_t<TQ_IQ4_NL>(tiles, K, N, q, d, M, lut, y, ldy, isum, sp, s);
+    case TQ_Q4_0: return launch_t<TQ_Q4_0>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
+    case TQ_Q8_0: return launch_t<TQ_Q8_0>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
+    case TQ_IQ4_NL: return launch_t<TQ_IQ4_NL>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
     }
     return hipErrorInvalidValue;
 }

@@ -2,24 +2,13 @@
 // quantized on the fly; the vector dot of "Q2_0 Format" runs against Q8_0
 // activation tiles).  Per 32-element K block: d = amax/127 (IEEE fp32
 // divide), q = round-half-away-from-zero(x * (1/d)), d stored as fp16
-// (nearest-even).  One block per 32 lanes; amax by a 5-step butterfly.
+// (nearest-even) -- quant32() in tq_internal.h.  One block per 32 lanes.
 #include "tq_internal.h"
 
 namespace tq {
 namespace {
 
 constexpr int THREADS = 256;
-
-template <int DT>
-__device__ __forceinline__ float load_x(const void *x, int64_t i)
-{
-    if (DT == TQ_F32)
-        return ((const float *)x)[i];
-    const uint16_t b = ((const uint16_t *)x)[i];
-    if (DT == TQ_BF16)
-        return __builtin_bit_cast(float, (uint32_t)b << 16);
-    return f16_bits_to_f32(b);
-}
 
 template <int DT>
 __global__ __launch_bounds__(THREADS) void k_quantize(const void *__restrict__ x, int64_t M,
@@ -32,17 +21,12 @@ __global__ __launch_bounds__(THREADS) void k_quantize(const void *__restrict__ x
     if (blk >= M * nb)
         return;                      // uniform across the 32 lanes of a block
     const int64_t m = blk / nb, kt = blk - m * nb;
-    const float v = load_x<DT>(x, m * ldx + kt * 32 + j);
-    float amax = fabsf(v);
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, o, 32));
-    const float dd = amax / 127.0f;
-    const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
-    const float p = v * id;
-    q[m * nb * 32 + kt * 32 + j] = (int8_t)(int)roundf(p);
+    int8_t qv;
+    uint16_t db;
+    quant32(load_x<DT>(x, m * ldx + kt * 32 + j), qv, db);
+    q[m * nb * 32 + kt * 32 + j] = qv;
     if (j == 0)
-        d[m * nb + kt] = f32_to_f16_bits(dd);
+        d[m * nb + kt] = db;
 }
 
 }  // namespace

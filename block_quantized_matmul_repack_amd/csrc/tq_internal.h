@@ -58,6 +58,36 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// One activation element of dtype DT at index i, converted exactly to fp32.
+template <int DT>
+__device__ __forceinline__ float load_x(const void *x, int64_t i)
+{
+    if constexpr (DT == TQ_F32)
+        return ((const float *)x)[i];
+    const uint16_t b = ((const uint16_t *)x)[i];
+    if constexpr (DT == TQ_BF16)
+        return __builtin_bit_cast(float, (uint32_t)b << 16);
+    return f16_bits_to_f32(b);
+}
+
+// Dynamic activation quantization of one 32-element K block held one element
+// per lane of a 32-lane group ("Memory buffers": dynamically quantized
+// activations; used as Q8_0 activation tiles): d = amax / 127 (IEEE fp32
+// divide), q = round-half-away-from-zero(v * (1 / d)), the scale stored as
+// fp16 nearest-even.  Every kernel that quantizes activations calls this, so
+// they all produce the same bits.
+__device__ __forceinline__ void quant32(float v, int8_t &q, uint16_t &dbits)
+{
+    float amax = fabsf(v);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+    const float dd = amax / 127.0f;
+    const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
+    q = (int8_t)(int)roundf(v * id);
+    dbits = f32_to_f16_bits(dd);
+}
+
 // 4 table lookups at once: idx holds four byte indices 0..15; returns the four
 // int8 table entries in the same byte positions.  v_perm_b32 selects any byte
 // of an 8-byte pair, so the two table halves are looked up separately and
@@ -71,12 +101,11 @@ __device__ __forceinline__ uint32_t lut16(uint32_t idx, const Lut &t)
     return (hi & m) | (lo & ~m);
 }
 
-// K-split of the decode GEMV: S workgroups per stripe, `chunk` k-tiles each;
-// part / cnt point into the caller's workspace when S > 1.
+// K-split of the decode GEMV: S workgroups per stripe (a power of two),
+// `chunk` k-tiles each; slots points into the caller's workspace when S > 1.
 struct Split {
     int S, chunk;
-    float *part;
-    uint32_t *cnt;
+    uint64_t *slots;
 };
 Split gemv_split(int64_t K, int64_t N);
 size_t gemv_workspace_bytes(int64_t K, int64_t N, int64_t M);
@@ -85,9 +114,19 @@ hipError_t launch_repack(int type, const void *flat, int64_t K, int64_t N, void 
                          hipStream_t s);
 hipError_t launch_quantize(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
                            int8_t *q, uint16_t *d, hipStream_t s);
-hipError_t launch_qgemv(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
-                        const uint16_t *d, int64_t M, const Lut &lut, float *y, int64_t ldy,
-                        int32_t *isum, void *ws, size_t ws_bytes, hipStream_t s);
+// Activations of the decode GEMV: either quantized already (q, d) or raw
+// (x of dtype xt, row stride ldx, quantized inside the GEMV kernel).
+struct Act {
+    const int8_t *q;
+    const uint16_t *d;
+    const void *x;
+    int xt;          // -1: use q, d
+    int64_t ldx;
+};
+
+hipError_t launch_qgemv(int type, const void *tiles, int64_t K, int64_t N, const Act &act,
+                        int64_t M, const Lut &lut, float *y, int64_t ldy, int32_t *isum,
+                        void *ws, size_t ws_bytes, hipStream_t s);
 hipError_t launch_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
                         const uint16_t *d, int64_t M, const Lut &lut, float *y, int64_t ldy,
                         int32_t *isum, hipStream_t s);

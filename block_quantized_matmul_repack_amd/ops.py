@@ -132,6 +132,25 @@ def qgemv(qtype, tiles, K, N, q, d, lut=None, out=None, split=True):
     return out
 
 
+def qgemv_x(qtype, tiles, K, N, x, lut=None, out=None, split=True):
+    """Decode in one launch: quantize x [M, >=K] (fp32 / bf16 / fp16) and
+    multiply, y [M, N]; bit-identical to quantize_act followed by qgemv."""
+    if x.dim() != 2 or x.dtype not in _DTYPES or x.stride(1) != 1:
+        raise TiledqError("qgemv_x: x must be 2-D fp32, bf16 or fp16 with unit column stride")
+    _need_cuda(tiles, out)
+    if not x.is_cuda:
+        raise TiledqError("tiledq operates on GPU tensors only")
+    M = x.shape[0]
+    out = _out("tq_qgemv_x", x, N, out)
+    st = _stream(x)
+    need = lib().tq_qgemv_workspace_bytes(qtype, K, N, M) if split else 0
+    ws = workspace(x.device, st.value, need) if need else None
+    check(lib().tq_qgemv_x(qtype, _ptr(tiles), K, N, _DTYPES[x.dtype], _ptr(x), x.stride(0), M,
+                           _lut_arg(lut), _ptr(out), out.stride(0), _ptr(ws), need, st),
+          "tq_qgemv_x")
+    return out
+
+
 def qgemm(qtype, tiles, K, N, q, d, lut=None, out=None):
     """Prefill product y [M, N] on int8 MFMA, any M."""
     _need_cuda(tiles, q, d, out)

@@ -150,6 +150,17 @@ int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N,
              const int8_t *lut, float *y, int64_t ldy,
              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Decode in one launch: tq_quantize_act fused into tq_qgemv.  Each
+ * workgroup quantizes the activation blocks it needs into on-chip memory
+ * with the same arithmetic as tq_quantize_act, so y is bit-identical to
+ * tq_quantize_act followed by tq_qgemv with the same workspace.
+ *   dtype, x, ldx : as tq_quantize_act (device x, row stride ldx >= K).
+ *   other arguments as tq_qgemv. */
+int tq_qgemv_x(int type, const void *tiles, int64_t K, int64_t N,
+               int dtype, const void *x, int64_t ldx, int64_t M,
+               const int8_t *lut, float *y, int64_t ldy,
+               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Prefill matrix-matrix product over tiles with int8 matrix-core (MFMA)
  * instructions, any M >= 1.  Arguments as tq_qgemv without the workspace.
  * Same integer block dots as tq_qgemv; deterministic. */

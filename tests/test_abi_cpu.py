@@ -69,10 +69,10 @@ LUT = (ctypes.c_int8 * 16)(*range(-8, 8))
 
 
 def test_workspace_bytes(L):
-    # K=N=4096, M=1: 128 stripes, each split S ways -> 512 B of counters (one
-    # uint32 per stripe, padded to 256 B) + S * 32 fp32 partials per stripe
+    # K=N=4096, M=1: 128 stripes, each split S ways (S a power of two): the
+    # pairwise tree needs (S - 1) * 32 slots of 8 bytes per stripe
     ws = L.tq_qgemv_workspace_bytes(1, 4096, 4096, 1)
-    assert (ws - 512) % (128 * 32 * 4) == 0 and 2 <= (ws - 512) // (128 * 32 * 4) <= 8
+    assert ws % (128 * 32 * 8) == 0 and ws // (128 * 32 * 8) + 1 in (2, 4, 8)
     assert L.tq_qgemv_workspace_bytes(1, 4096, 128001, 1) == 0      # enough stripes
     assert L.tq_qgemv_workspace_bytes(1, 4096, 4096, 9) == 0
     assert L.tq_qgemv_workspace_bytes(1, 4000 + 1, 4096, 1) == 0
@@ -128,6 +128,19 @@ def test_matmul_validation(L, fn):
     assert f(0, NUL, 64, 32, NUL, NUL, 0, NUL, NUL, 32, NUL) == 0     # M == 0
     assert f(0, NUL, 64, 0, NUL, NUL, 4, NUL, NUL, 0, NUL) == 0       # N == 0
     assert f(2, NUL, 64, 0, NUL, NUL, 4, LUT, NUL, 0, NUL) == 0
+
+
+def test_qgemv_x_validation(L):
+    f = L.tq_qgemv_x
+    # (type, tiles, K, N, dtype, x, ldx, M, lut, y, ldy, ws, ws_bytes, stream)
+    assert f(0, A16, 64, 32, 7, A16, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 2      # bad dtype
+    assert f(9, A16, 64, 32, 0, A16, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 2      # bad type
+    assert f(0, A16, 64, 32, 0, A16, 64, 9, NUL, A16, 32, NUL, 0, NUL) == 3      # M > 8
+    assert f(0, A16, 64, 32, 0, A16, 32, 1, NUL, A16, 32, NUL, 0, NUL) == 3      # ldx < K
+    assert f(0, A16, 64, 32, 0, NUL, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 1      # x NULL
+    assert f(0, A16, 64, 32, 0, A2, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 4       # fp32 x at 2 B
+    assert f(2, A16, 64, 32, 1, A16, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 1      # IQ4_NL, no table
+    assert f(0, NUL, 64, 0, 0, NUL, 64, 1, NUL, NUL, 0, NUL, 0, NUL) == 0        # N == 0
 
 
 def test_gemv_m_limit(L):

@@ -219,3 +219,34 @@ def test_qgemv_workspace_reused_across_shapes(tq):
                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), st) == 0
         check_y(y.cpu().numpy(), y_ref, acond, (K, N))
         assert int(ws.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (3, 96, 40), (8, 1024, 300), (5, 4064, 33)])
+def test_qgemv_x_equals_two_launches(tq, qtype, act, M, K, N):
+    """Quantize fused into the GEMV gives bit-identical y (same arithmetic),
+    with and without the K split, and meets the oracle's tolerance."""
+    inp = make(qtype, K, N, M, seed=M + K + N + len(act), act=act)
+    tiles, tdev = _dev(inp, qtype, K, N)
+    x = to_dev_act(inp.x, act)
+    for split in (True, False):
+        qd, dd = tq.quantize_act(x)
+        y2 = tq.qgemv(qtype, tdev, K, N, qd, dd, lut=LUT, split=split)
+        y1 = tq.qgemv_x(qtype, tdev, K, N, x, lut=LUT, split=split)
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32)), (split,)
+    dt = {"f32": oracle.F32, "bf16": oracle.BF16, "f16": oracle.F16}[act]
+    q, d = oracle.quantize_act(inp.x, dt)
+    y_ref, acond = oracle.matmul(qtype, tiles, K, N, q, d, LUT)
+    check_y(y1.cpu().numpy(), y_ref, acond, (qtype, act, M, K, N))
+
+
+def test_qgemv_x_row_stride(tq):
+    K, N, M = 512, 64, 2
+    inp = make(Q8_0, K, N, M, seed=77)
+    _, tdev = _dev(inp, Q8_0, K, N)
+    wide = torch.from_numpy(np.concatenate([inp.x, np.full((M, 64), 9e5, np.float32)], 1)).cuda()
+    y1 = tq.qgemv_x(Q8_0, tdev, K, N, wide[:, :K])
+    qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+    y2 = tq.qgemv(Q8_0, tdev, K, N, qd, dd)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
