@@ -53,6 +53,19 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 // LDS for one pass of staged activations (int8 q and fp16 scales, all M rows).
 constexpr int ACT_LDS_BYTES = 32768;
 
+// Weight units each wave keeps in flight (ring depth), per tile type.
+#ifndef TQ_GEMV_DEPTH_Q8
+#define TQ_GEMV_DEPTH_Q8 2
+#endif
+#ifndef TQ_GEMV_DEPTH_Q4
+#define TQ_GEMV_DEPTH_Q4 2
+#endif
+template <int QT>
+constexpr int ring_depth()
+{
+    return QT == TQ_Q8_0 ? TQ_GEMV_DEPTH_Q8 : TQ_GEMV_DEPTH_Q4;
+}
+
 template <int QT>
 struct TileRegs;
 
@@ -204,20 +217,6 @@ struct Unit {
     v4u c[SLOTS];
 };
 
-// Branch-free: lanes past the unit's valid bytes re-read its last chunk (and
-// do not store it), so every path issues the same loads and the compiler can
-// wait for exactly the loads it needs.
-template <int QT>
-__device__ __forceinline__ void load_unit(Unit<QT> &u, const uint8_t *src, int valid_chunks,
-                                          int lane)
-{
-#pragma unroll
-    for (int i = 0; i < Unit<QT>::SLOTS; i++) {
-        const int ch = min(i * 64 + lane, valid_chunks - 1);
-        u.c[i] = __builtin_nontemporal_load((const v4u *)src + ch);
-    }
-}
-
 template <int QT>
 __device__ __forceinline__ void store_unit(const Unit<QT> &u, uint8_t *dst, int valid_chunks,
                                            int lane)
@@ -232,7 +231,7 @@ __device__ __forceinline__ void store_unit(const Unit<QT> &u, uint8_t *dst, int 
 
 // XT < 0: activations arrive quantized (act.q, act.d).  XT = a tq_dtype: raw
 // activations act.x are quantized here, per pass, straight into LDS with the
-// same quant32() as tq_quantize_act, so q and d are bit-identical.
+// same quant_quad() as tq_quantize_act, so q and d are bit-identical.
 template <int QT, int MM, int NW, int XT, bool DOTS>
 __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ tiles, int nkt,
                                                    int64_t N, Act act, int64_t K, Lut lut,
@@ -242,6 +241,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
 {
     constexpr int TS = Fmt<QT>::tile;
     constexpr int UB = Unit<QT>::BYTES;
+    constexpr int D = ring_depth<QT>();
     static_assert(NW * 64 >= MM * 32, "one thread per output of the stripe");
     __shared__ __attribute__((aligned(16))) uint8_t stage[NW][UB];
     __shared__ __attribute__((aligned(16))) uint8_t act_lds[ACT_LDS_BYTES];
@@ -277,6 +277,10 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
         acc[m] = 0.0f;
 
     uint8_t *my = stage[wave];
+    // Weight loads are raw buffer loads over this workgroup's tiles: a unit
+    // or chunk past the range gets offset BUF_OOB, which returns zeros and
+    // moves no data, so every load is issued unconditionally.
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(cbase, (int64_t)nt * TS);
     // The chunk is processed in passes of up to P tiles.  Each pass first
     // copies the pass's int8 activations and fp16 scales into LDS (all M
     // rows), so the unit loop below has only weight loads in flight.
@@ -286,63 +290,112 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     for (int pb = 0; pb < nt; pb += P) {
         const int pn = min(P, nt - pb);                   // tiles in this pass
         const int nunits = (pn + 1) >> 1;
-        const uint8_t *pbase = cbase + (int64_t)pb * TS;
-        auto load_stage = [&](Unit<QT> &u, int j) {
-            load_unit<QT>(u, pbase + (int64_t)j * UB, min(2, pn - 2 * j) * (TS / 16), lane);
-        };
         const int count = wave < nunits ? (nunits - 1 - wave) / NW + 1 : 0;   // units of this wave
+        // the wave's i-th unit of the pass (i >= count: nothing)
+        auto load_stage = [&](Unit<QT> &u, int i) {
+            const int j = wave + i * NW;                  // pass-local unit index
+            const bool ok = i < count;
+            const int vc = ok ? min(2, pn - 2 * j) * (TS / 16) : 0;
+            const int base = ok ? (pb + 2 * j) * TS : BUF_OOB;
+#pragma unroll
+            for (int s = 0; s < Unit<QT>::SLOTS; s++) {
+                const int ch = s * 64 + lane;
+                const int off = ch < vc ? base + 16 * ch : BUF_OOB;
+                u.c[s] = __builtin_bit_cast(
+                    v4u, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, BUF_NT));
+            }
+        };
         __syncthreads();                                  // previous pass done with qs / ds
-        // the pass's first weight unit is in flight while the activations
-        // are staged
-        Unit<QT> ua, ub;
-        if (count > 0)
-            load_stage(ua, wave);
+
+        // Activations: the first batch is loaded before the weight units, so
+        // waiting for it does not wait for the weights; the D units of the
+        // wave are then all in flight while the activations are staged.
+        Unit<QT> u[D];
         if constexpr (XT < 0) {
-            for (int c = threadIdx.x; c < MM * pn * 2; c += NW * 64) {
-                const int m = c / (pn * 2), o = c - m * pn * 2;   // 16-byte chunk o of row m
-                *(uint4 *)(qs + m * P * 32 + o * 16) =
-                    *(const uint4 *)(act.q + m * K + (int64_t)(kt0 + pb) * 32 + o * 16);
-            }
-            for (int c = threadIdx.x; c < MM * pn; c += NW * 64) {
+            constexpr int XB = 4;                         // 16-byte q chunks per thread and batch
+            const int nq = MM * pn * 2, nd = MM * pn;
+            uint4 qv[XB];
+            uint16_t dv[2];
+            auto qchunk = [&](int c) {                    // 16-byte chunk c (clamped) of the pass
+                c = min(c, nq - 1);
+                const int m = c / (pn * 2), o = c - m * pn * 2;
+                return *(const uint4 *)(act.q + m * K + (int64_t)(kt0 + pb) * 32 + o * 16);
+            };
+            auto dval = [&](int c) -> uint16_t {
+                c = min(c, nd - 1);
                 const int m = c / pn, o = c - m * pn;
-                ds[m * P + o] = DOTS ? (uint16_t)0 : act.d[m * nb + kt0 + pb + o];
-            }
+                return DOTS ? (uint16_t)0 : act.d[m * nb + kt0 + pb + o];
+            };
+            auto qput = [&](int c, const uint4 &v) {
+                if (c < nq) {
+                    const int m = c / (pn * 2), o = c - m * pn * 2;
+                    *(uint4 *)(qs + m * P * 32 + o * 16) = v;
+                }
+            };
+            auto dput = [&](int c, uint16_t v) {
+                if (c < nd) {
+                    const int m = c / pn, o = c - m * pn;
+                    ds[m * P + o] = v;
+                }
+            };
+#pragma unroll
+            for (int i = 0; i < XB; i++)
+                qv[i] = qchunk(threadIdx.x + i * NW * 64);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+                dv[i] = dval(threadIdx.x + i * NW * 64);
+#pragma unroll
+            for (int r = 0; r < D; r++)
+                load_stage(u[r], r);
+#pragma unroll
+            for (int i = 0; i < XB; i++)
+                qput(threadIdx.x + i * NW * 64, qv[i]);
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+                dput(threadIdx.x + i * NW * 64, dv[i]);
+            for (int c = threadIdx.x + XB * NW * 64; c < nq; c += NW * 64)
+                qput(c, qchunk(c));
+            for (int c = threadIdx.x + 2 * NW * 64; c < nd; c += NW * 64)
+                dput(c, dval(c));
         } else {
-            // one 32-element block per half-wave, one element per lane; the
-            // loads of XB blocks are issued together
-            constexpr int XB = 4;
+            // one 32-element block per quad of lanes, 8 elements per lane
+            // (quant_quad); QB blocks per batch
+            constexpr int QB = NW * 16;
             const int nblk = MM * pn;
-            for (int b0 = hs; b0 < nblk; b0 += 2 * NW * XB) {
-                float v[XB];
-#pragma unroll
-                for (int u = 0; u < XB; u++) {
-                    const int b = min(b0 + u * 2 * NW, nblk - 1);
+            const int c = lane & 3, bq = threadIdx.x >> 2;
+            auto xload = [&](float (&v)[8], int b) {
+                b = min(b, nblk - 1);
+                const int m = b / pn, tp = b - m * pn;
+                load_x8<XT>(v, act.x, m * act.ldx + (int64_t)(kt0 + pb + tp) * 32 + 8 * c);
+            };
+            // quantized unconditionally (a branch here would let the compiler
+            // sink the load below the weight loads); stored if in range
+            auto xquant = [&](const float (&v)[8], int b) {
+                uint2 qv;
+                uint16_t db;
+                quant_quad(v, qv, db);
+                if (b < nblk) {
                     const int m = b / pn, tp = b - m * pn;
-                    v[u] = load_x<XT>(act.x, m * act.ldx + (int64_t)(kt0 + pb + tp) * 32 + l);
+                    *(uint2 *)(qs + m * P * 32 + tp * 32 + 8 * c) = qv;
+                    if (c == 0)
+                        ds[m * P + tp] = db;
                 }
+            };
+            float v[8];
+            xload(v, bq);
 #pragma unroll
-                for (int u = 0; u < XB; u++) {
-                    const int b = b0 + u * 2 * NW;
-                    if (b < nblk) {
-                        const int m = b / pn, tp = b - m * pn;
-                        int8_t qv;
-                        uint16_t db;
-                        quant32(v[u], qv, db);
-                        qs[m * P * 32 + tp * 32 + l] = qv;
-                        if (l == 0)
-                            ds[m * P + tp] = db;
-                    }
-                }
+            for (int r = 0; r < D; r++)
+                load_stage(u[r], r);
+            xquant(v, bq);
+            for (int b = bq + QB; b < nblk; b += QB) {
+                xload(v, b);
+                xquant(v, b);
             }
         }
         __syncthreads();
 
-        // A stage is one unit of two weight tiles; all loads are unconditional
-        // (indices clamped into range), the next stage is always issued before
-        // the current one is used and the last is peeled, so one stage's
-        // loads overlap the previous stage's compute.
-        auto process = [&](const Unit<QT> &u, int j) {
-            store_unit<QT>(u, my, min(2, pn - 2 * j) * (TS / 16), lane);
+        auto process = [&](const Unit<QT> &un, int j) {
+            store_unit<QT>(un, my, min(2, pn - 2 * j) * (TS / 16), lane);
             const int tp = min(2 * j + half, pn - 1);         // this half's tile, pass-local
             const bool valid = 2 * j + half < pn;
             TileRegs<QT> w;
@@ -369,22 +422,17 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                     acc[m] = fmaf((float)s[m], dw * f16_bits_to_f32(x.d[m]), acc[m]);
             }
         };
-        if (count > 0) {
-            // two unit buffers used in turn (no register copies, which would
-            // wait for the prefetch); every loop iteration prefetches
-            int it = 0;
-            for (; it + 2 < count; it += 2) {
-                load_stage(ub, wave + (it + 1) * NW);
-                process(ua, wave + it * NW);
-                load_stage(ua, wave + (it + 2) * NW);
-                process(ub, wave + (it + 1) * NW);
-            }
-            if (it + 2 == count) {
-                load_stage(ub, wave + (it + 1) * NW);
-                process(ua, wave + it * NW);
-                process(ub, wave + (it + 1) * NW);
-            } else {
-                process(ua, wave + it * NW);
+        // A ring of D unit buffers: buffer r holds the wave's units r, r + D,
+        // ...; after a buffer is used it is refilled with the unit D further
+        // on, so D units stay in flight.  Loads are never under a branch
+        // (past-the-end units are zero-size), which lets the compiler wait
+        // for exactly the oldest buffer.
+        for (int it = 0; it < count; it += D) {
+#pragma unroll
+            for (int r = 0; r < D; r++) {
+                if (it + r < count)
+                    process(u[r], wave + (it + r) * NW);
+                load_stage(u[r], it + r + D);
             }
         }
     }

@@ -58,35 +58,66 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// One activation element of dtype DT at index i, converted exactly to fp32.
+// Eight consecutive activation elements of dtype DT from index i, converted
+// exactly to fp32.  x needs only element alignment: the wide loads are
+// unaligned-capable on this target.
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint16_t u16x8u __attribute__((ext_vector_type(8), aligned(2)));
 template <int DT>
-__device__ __forceinline__ float load_x(const void *x, int64_t i)
+__device__ __forceinline__ void load_x8(float (&v)[8], const void *x, int64_t i)
 {
-    if constexpr (DT == TQ_F32)
-        return ((const float *)x)[i];
-    const uint16_t b = ((const uint16_t *)x)[i];
-    if constexpr (DT == TQ_BF16)
-        return __builtin_bit_cast(float, (uint32_t)b << 16);
-    return f16_bits_to_f32(b);
+    if constexpr (DT == TQ_F32) {
+        const f32x4u a = *(const f32x4u *)((const float *)x + i);
+        const f32x4u b = *(const f32x4u *)((const float *)x + i + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const u16x8u h = *(const u16x8u *)((const uint16_t *)x + i);
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            if constexpr (DT == TQ_BF16)
+                v[e] = __builtin_bit_cast(float, (uint32_t)h[e] << 16);
+            else
+                v[e] = f16_bits_to_f32(h[e]);
+        }
+    }
 }
 
-// Dynamic activation quantization of one 32-element K block held one element
-// per lane of a 32-lane group ("Memory buffers": dynamically quantized
-// activations; used as Q8_0 activation tiles): d = amax / 127 (IEEE fp32
-// divide), q = round-half-away-from-zero(v * (1 / d)), the scale stored as
-// fp16 nearest-even.  Every kernel that quantizes activations calls this, so
-// they all produce the same bits.
-__device__ __forceinline__ void quant32(float v, int8_t &q, uint16_t &dbits)
+// Max over the 4 lanes of a quad (DPP quad permutations, no LDS).
+__device__ __forceinline__ float quad_max(float v)
 {
-    float amax = fabsf(v);
+    const int b = __builtin_bit_cast(int, v);
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, true)));
+    const int c = __builtin_bit_cast(int, v);
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, c, 0x4E, 0xF, 0xF, true)));
+}
+
+// Dynamic activation quantization of one 32-element K block ("Memory
+// buffers": dynamically quantized activations; used as Q8_0 activation
+// tiles): d = amax / 127 (IEEE fp32 divide), q = round-half-away-from-zero(
+// v * (1 / d)), the scale stored as fp16 nearest-even.  The block is held by
+// a quad of lanes, lane c holding elements 8c..8c+7; every lane of the quad
+// must be active.  Returns this lane's 8 int8 codes (element 8c + e in byte
+// e) and, in every lane, the fp16 scale bits.  Every kernel that quantizes
+// activations calls this, so they all produce the same bits.
+__device__ __forceinline__ void quant_quad(const float (&v)[8], uint2 &q, uint16_t &dbits)
+{
+    float amax = fabsf(v[0]);
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1)
-        amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+    for (int e = 1; e < 8; e++)
+        amax = fmaxf(amax, fabsf(v[e]));
+    amax = quad_max(amax);
     const float dd = amax / 127.0f;
     const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
-    q = (int8_t)(int)roundf(v * id);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        w[e >> 2] |= ((uint32_t)(int)roundf(v[e] * id) & 0xFFu) << (8 * (e & 3));
+    q = make_uint2(w[0], w[1]);
     dbits = f32_to_f16_bits(dd);
 }
+
+typedef uint32_t u32x2u __attribute__((ext_vector_type(2), aligned(4)));
 
 // 4 table lookups at once: idx holds four byte indices 0..15; returns the four
 // int8 table entries in the same byte positions.  v_perm_b32 selects any byte
