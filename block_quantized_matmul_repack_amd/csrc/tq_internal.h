@@ -125,10 +125,14 @@ typedef uint32_t u32x2u __attribute__((ext_vector_type(2), aligned(4)));
 // merged on bit 3 of each index.
 __device__ __forceinline__ uint32_t lut16(uint32_t idx, const Lut &t)
 {
-    uint32_t sel = idx & 0x07070707u;
-    uint32_t lo = __builtin_amdgcn_perm(t.w[1], t.w[0], sel);
-    uint32_t hi = __builtin_amdgcn_perm(t.w[3], t.w[2], sel);
-    uint32_t m = ((idx >> 3) & 0x01010101u) * 0xFFu;
+    const uint32_t sel = idx & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(t.w[1], t.w[0], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(t.w[3], t.w[2], sel);
+    // m = 0xFF in the bytes whose index has bit 3 set: shifted to each byte's
+    // sign bit, then replicated by v_perm's sign selectors (8, 9: signs of
+    // bytes 1, 3 of the second operand; 10, 11: of bytes 1, 3 of the first)
+    const uint32_t sb = idx << 4;
+    const uint32_t m = __builtin_amdgcn_perm(sb, sb << 8, 0x0B090A08u);
     return (hi & m) | (lo & ~m);
 }
 
