@@ -1,77 +1,112 @@
 // Repack flat GGML block-32 rows into 32x32 tiles ("Tiled Weight Formats",
 // subsections "Tile Dimensions and Grid Layout" and "Block-32 Quantized
 // Formats").  One workgroup takes one 32-row stripe (ct) and KT consecutive
-// k-tiles: it stages the 32 rows' flat blocks in LDS with coalesced loads
-// (each row's blocks for consecutive kt are contiguous), then writes the KT
-// tiles, which are contiguous in the output, one dword per thread per step.
+// k-tiles, which are contiguous in the output.
+//
+// Load: one flat block (row r, k-tile t) per work item, its quant bytes read
+// as 16-byte vectors; the quants go to LDS transposed, as halfword columns
+// qs[t][32 h + r] (halfword h = quant bytes 2h, 2h+1 of row r), the scales
+// to sc[t][r].  In that layout the 32 rows of one halfword are contiguous, which
+// is what both tile formats need:
+//   Q8_0: tile dword (cp, rp) = halfword cp of rows 2rp and 2rp+1, so a
+//         16-byte tile chunk is a 16-byte LDS read, stored as is;
+//   Q4_0 / IQ4_NL: tile byte (cp, r) = one nibble of each of quant bytes
+//         2h, 2h+1 of row r (h = cp mod 8; low nibbles for cp < 8, high for
+//         cp >= 8), built two rows at a time with shifts and masks.
+// Store: every thread writes whole 16-byte chunks of the tiles.
 #include "tq_internal.h"
 
 namespace tq {
 namespace {
 
-constexpr int KT = 8;          // k-tiles per workgroup
+constexpr int KT = 16;         // k-tiles per workgroup
 constexpr int THREADS = 256;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int QT>
-__global__ __launch_bounds__(THREADS) void k_repack(const uint16_t *__restrict__ flat,
+__global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ flat,
                                                     int64_t nb, int64_t N,
-                                                    uint32_t *__restrict__ tiles)
+                                                    uint8_t *__restrict__ tiles)
 {
-    constexpr int BH = Fmt<QT>::block / 2;      // halfwords per flat block
-    constexpr int TD = Fmt<QT>::tile / 4;       // dwords per tile
-    constexpr int RL = KT * BH;                 // halfwords per staged row
-    __shared__ uint16_t lds[32][RL];
+    constexpr int BB = Fmt<QT>::block;          // flat block bytes (fp16 d + quants)
+    constexpr int QH = (BB - 2) / 2;            // quant halfwords per block: 8 or 16
+    constexpr int TS = Fmt<QT>::tile;
+    constexpr int CH = TS / 16;                 // 16-byte chunks per tile: 36 or 68
+    constexpr int QCH = CH - 4;                 // chunks of quants (the last 4 hold scales)
+    // each tile's halfword columns padded by 16 bytes: the lanes of a store
+    // differ in t, and a tile stride of 16 mod 256 bytes spreads them over
+    // the LDS banks
+    constexpr int TP = QH * 32 + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t qs[KT][TP];
+    __shared__ __attribute__((aligned(16))) uint16_t sc[KT][32];
 
     const int64_t ct = blockIdx.x;
     const int64_t kt0 = (int64_t)blockIdx.y * KT;
     const int te = (int)min<int64_t>(KT, nb - kt0);
-    const int rl = te * BH;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-    for (int r = wave; r < 32; r += THREADS / 64) {
+    // Load: item i = (row r = i / te, tile t = i % te), so a wave reads a few
+    // contiguous runs of blocks; rows past N are zero.
+    for (int i = threadIdx.x; i < te * 32; i += THREADS) {
+        const int r = i / te, t = i - r * te;
         const int64_t n = 32 * ct + r;
-        const uint16_t *src = flat + (n * nb + kt0) * BH;
-        for (int j = lane; j < rl; j += 64)
-            lds[r][j] = (n < N) ? src[j] : (uint16_t)0;
+        uint16_t q[QH];
+        uint16_t d = 0;
+        if (n < N) {
+            const uint8_t *blk = flat + (n * nb + kt0 + t) * BB;
+            d = *(const uint16_t *)blk;
+#pragma unroll
+            for (int v = 0; v < QH / 8; v++) {
+                const u16x8u w = *(const u16x8u *)(blk + 2 + 16 * v);
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    q[8 * v + e] = w[e];
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < QH; h++)
+                q[h] = 0;
+        }
+#pragma unroll
+        for (int h = 0; h < QH; h++)
+            qs[t][32 * h + r] = q[h];
+        sc[t][r] = d;
     }
     __syncthreads();
 
-    uint32_t *dst = tiles + (ct * nb + kt0) * TD;
-    for (int i = threadIdx.x; i < te * TD; i += THREADS) {
-        const int t = i / TD, w = i - t * TD;
-        const uint16_t *blk0 = &lds[0][t * BH];
-        uint32_t out;
-        if constexpr (QT == TQ_Q8_0) {
-            if (w < 256) {
-                // dword (cp, rp): rows 2rp and 2rp+1, columns 2cp and 2cp+1;
-                // the flat halfword qs[2cp..2cp+1] is exactly that byte pair.
-                const int cp = w >> 4, rp = w & 15;
-                out = (uint32_t)blk0[(2 * rp) * RL + 1 + cp] |
-                      ((uint32_t)blk0[(2 * rp + 1) * RL + 1 + cp] << 16);
-            } else {
-                const int s = w - 256;
-                out = (uint32_t)blk0[(2 * s) * RL] | ((uint32_t)blk0[(2 * s + 1) * RL] << 16);
-            }
+    uint8_t *dst = tiles + (ct * nb + kt0) * TS;
+    for (int i = threadIdx.x; i < te * CH; i += THREADS) {
+        const int t = i / CH, c = i - t * CH;
+        u32x4 out;
+        if (c >= QCH) {
+            // scale chunk: dwords of rows 8j .. 8j + 7
+            out = *(const u32x4 *)&sc[t][8 * (c - QCH)];
+        } else if constexpr (QT == TQ_Q8_0) {
+            // dwords (cp, rp .. rp + 3): halfword cp of rows 8j .. 8j + 7
+            out = *(const u32x4 *)&qs[t][32 * (c >> 2) + 8 * (c & 3)];
         } else {
-            if (w < 128) {
-                // dword (cp, g): rows 4g..4g+3 of column pair cp.  Columns
-                // 2cp, 2cp+1 live in the flat halfword qs[2h..2h+1], h = cp mod
-                // 8: low nibbles for cp < 8, high nibbles for cp >= 8.
-                const int cp = w >> 3, g = w & 7, h = cp & 7;
-                out = 0;
+            // dwords (cp, g .. g + 3), g = 4 (c & 1): rows 16 (c & 1) .. + 15
+            const int cp = c >> 1, h = cp & 7;
+            const u32x4 *src = (const u32x4 *)&qs[t][32 * h + 16 * (c & 1)];
+            const u32x4 a = src[0], b = src[1];     // rows +0..+7, +8..+15
+            const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint32_t o[4];
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const uint32_t v = blk0[(4 * g + j) * RL + 1 + h];
-                    const uint32_t b = (cp < 8) ? ((v & 0x0Fu) | ((v >> 4) & 0xF0u))
-                                                : (((v >> 4) & 0x0Fu) | ((v >> 8) & 0xF0u));
-                    out |= b << (8 * j);
+            for (int j = 0; j < 4; j++) {
+                // v holds two rows (low / high halfword); per row the tile
+                // byte takes one nibble of each quant byte of the halfword
+                uint32_t p[2];
+#pragma unroll
+                for (int k = 0; k < 2; k++) {
+                    const uint32_t x = v[2 * j + k];
+                    p[k] = cp < 8 ? ((x & 0x000F000Fu) | ((x >> 4) & 0x00F000F0u))
+                                  : (((x >> 4) & 0x000F000Fu) | ((x >> 8) & 0x00F000F0u));
                 }
-            } else {
-                const int s = w - 128;
-                out = (uint32_t)blk0[(2 * s) * RL] | ((uint32_t)blk0[(2 * s + 1) * RL] << 16);
+                o[j] = __builtin_amdgcn_perm(p[1], p[0], 0x06040200u);
             }
+            out = u32x4{o[0], o[1], o[2], o[3]};
         }
-        dst[i] = out;
+        *(u32x4 *)(dst + (int64_t)t * TS + 16 * c) = out;
     }
 }
 
@@ -82,8 +117,8 @@ hipError_t launch_repack(int type, const void *flat, int64_t K, int64_t N, void 
 {
     const int64_t nb = K / 32;
     dim3 grid((unsigned)((N + 31) / 32), (unsigned)((nb + KT - 1) / KT));
-    const uint16_t *f = (const uint16_t *)flat;
-    uint32_t *t = (uint32_t *)tiles;
+    const uint8_t *f = (const uint8_t *)flat;
+    uint8_t *t = (uint8_t *)tiles;
     switch (type) {
     case TQ_Q4_0: k_repack<TQ_Q4_0><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
     case TQ_IQ4_NL: k_repack<TQ_IQ4_NL><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
