@@ -50,8 +50,14 @@ __device__ __forceinline__ int dpp_xor2(int v)
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-// LDS for one pass of staged activations (int8 q and fp16 scales, all M rows).
-constexpr int ACT_LDS_BYTES = 32768;
+// LDS for one pass of staged activations (int8 q and fp32 scales, all M rows).
+// Up to 4 rows: 32 KB (three workgroups fit a CU's LDS); 5..8 rows: 40 KB,
+// enough for one pass over K = 4096 at M = 8.
+template <int MM>
+constexpr int act_lds_bytes()
+{
+    return MM <= 4 ? 32768 : 40960;
+}
 
 // Weight units each wave keeps in flight (ring depth), per tile type.
 #ifndef TQ_GEMV_DEPTH_Q8
@@ -107,26 +113,28 @@ template <int QT, int MM>
 struct ActRegs;
 template <int MM>
 struct ActRegs<TQ_Q4_0, MM> {
-    uint2 v[MM];             // this lane's 8 consecutive K (split into even / odd K at use)
-    uint16_t d[MM];
+    uint2 v[MM];             // this lane's 8 K: x = the even K, y = the odd K
+    float d[MM];
 };
 template <int MM>
 struct ActRegs<TQ_IQ4_NL, MM> : ActRegs<TQ_Q4_0, MM> {};
 template <int MM>
 struct ActRegs<TQ_Q8_0, MM> {
     uint32_t v[MM][4];       // 16 consecutive K
-    uint16_t d[MM];
+    float d[MM];
 };
 
-// Activations of tile tp (pass-local) from the workgroup's LDS copy:
-// qs[m][tp*32 + K], ds[m][tp].
+// Staged activations of one pass: tile tp's 32 int8 of row m at
+// qs[(tp * MM + m) * 32] -- for 4-bit weights as the 16 even K then the 16
+// odd K, so that a lane's even and odd words come out of LDS ready for the
+// nibble dot products -- and its scale, as fp32, at ds[tp * MM + m].
 template <int QT, int MM>
-__device__ __forceinline__ void lds_act(ActRegs<QT, MM> &r, const int8_t *qs, const uint16_t *ds,
-                                        int pstride, int tp, int l)
+__device__ __forceinline__ void lds_act(ActRegs<QT, MM> &r, const int8_t *qs, const float *ds,
+                                        int tp, int l)
 {
 #pragma unroll
     for (int m = 0; m < MM; m++) {
-        const int8_t *qb = qs + m * pstride * 32 + tp * 32;
+        const int8_t *qb = qs + (tp * MM + m) * 32;
         if constexpr (QT == TQ_Q8_0) {
             const uint4 v = *(const uint4 *)(qb + 16 * (l & 1));
             r.v[m][0] = v.x;
@@ -134,10 +142,19 @@ __device__ __forceinline__ void lds_act(ActRegs<QT, MM> &r, const int8_t *qs, co
             r.v[m][2] = v.z;
             r.v[m][3] = v.w;
         } else {
-            r.v[m] = *(const uint2 *)(qb + 8 * (l & 3));
+            r.v[m].x = *(const uint32_t *)(qb + 4 * (l & 3));
+            r.v[m].y = *(const uint32_t *)(qb + 16 + 4 * (l & 3));
         }
-        r.d[m] = ds[m * pstride + tp];
+        r.d[m] = ds[tp * MM + m];
     }
+}
+
+// Even-K / odd-K split of 8 consecutive int8 (K 8c .. 8c + 7) into the two
+// words the 4-bit layout of the staged activations keeps.
+__device__ __forceinline__ uint2 split_even_odd(uint2 v)
+{
+    return make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),
+                      __builtin_amdgcn_perm(v.y, v.x, 0x07050301u));
 }
 
 // Exact block dots of this lane's row for every m.  For Q4_0 the result is
@@ -192,8 +209,8 @@ __device__ __forceinline__ void block_dots(int (&s)[MM], const TileRegs<QT> &w,
         }
 #pragma unroll
         for (int m = 0; m < MM; m++) {
-            const uint32_t xe = __builtin_amdgcn_perm(x.v[m].y, x.v[m].x, 0x06040200u);  // even K
-            const uint32_t xo = __builtin_amdgcn_perm(x.v[m].y, x.v[m].x, 0x07050301u);  // odd K
+            const uint32_t xe = x.v[m].x;                 // even K
+            const uint32_t xo = x.v[m].y;                 // odd K
             int p[4];
 #pragma unroll
             for (int j = 0; j < 4; j++)
@@ -244,7 +261,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     constexpr int D = ring_depth<QT>();
     static_assert(NW * 64 >= MM * 32, "one thread per output of the stripe");
     __shared__ __attribute__((aligned(16))) uint8_t stage[NW][UB];
-    __shared__ __attribute__((aligned(16))) uint8_t act_lds[ACT_LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t act_lds[act_lds_bytes<MM>()];
     __shared__ float red[2 * NW][MM][32];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -282,11 +299,23 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     // moves no data, so every load is issued unconditionally.
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(cbase, (int64_t)nt * TS);
     // The chunk is processed in passes of up to P tiles.  Each pass first
-    // copies the pass's int8 activations and fp16 scales into LDS (all M
-    // rows), so the unit loop below has only weight loads in flight.
-    constexpr int P = ACT_LDS_BYTES / (MM * 34) & ~1;
+    // stages the pass's int8 activations and scales of all M rows in LDS
+    // (layout at lds_act), so the unit loop has only weight loads in flight.
+    constexpr int P = act_lds_bytes<MM>() / (MM * 36) & ~1;
     int8_t *qs = (int8_t *)act_lds;
-    uint16_t *ds = (uint16_t *)(act_lds + MM * P * 32);
+    float *ds = (float *)(act_lds + MM * P * 32);
+    // one 16-byte chunk (K 16 h .. 16 h + 15 of a tile) of row m into qs
+    auto put_chunk = [&](int tp, int m, int h, uint4 v) {
+        int8_t *qb = qs + (tp * MM + m) * 32;
+        if constexpr (QT == TQ_Q8_0) {
+            *(uint4 *)(qb + 16 * h) = v;
+        } else {
+            const uint2 a = split_even_odd(make_uint2(v.x, v.y));
+            const uint2 b = split_even_odd(make_uint2(v.z, v.w));
+            *(uint2 *)(qb + 8 * h) = make_uint2(a.x, b.x);
+            *(uint2 *)(qb + 16 + 8 * h) = make_uint2(a.y, b.y);
+        }
+    };
     for (int pb = 0; pb < nt; pb += P) {
         const int pn = min(P, nt - pb);                   // tiles in this pass
         const int nunits = (pn + 1) >> 1;
@@ -312,60 +341,49 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
         // wave are then all in flight while the activations are staged.
         Unit<QT> u[D];
         if constexpr (XT < 0) {
-            constexpr int XB = 4;                         // 16-byte q chunks per thread and batch
-            const int nq = MM * pn * 2, nd = MM * pn;
-            uint4 qv[XB];
-            uint16_t dv[2];
-            auto qchunk = [&](int c) {                    // 16-byte chunk c (clamped) of the pass
-                c = min(c, nq - 1);
-                const int m = c / (pn * 2), o = c - m * pn * 2;
-                return *(const uint4 *)(act.q + m * K + (int64_t)(kt0 + pb) * 32 + o * 16);
+            // per row m: 16-byte chunks o < 2 pn of q, scales o < pn
+            const int64_t q0 = (int64_t)(kt0 + pb) * 32;
+            auto qload = [&](int m, int o) {
+                return *(const uint4 *)(act.q + m * K + q0 + 16 * min(o, 2 * pn - 1));
             };
-            auto dval = [&](int c) -> uint16_t {
-                c = min(c, nd - 1);
-                const int m = c / pn, o = c - m * pn;
-                return DOTS ? (uint16_t)0 : act.d[m * nb + kt0 + pb + o];
+            auto dload = [&](int m, int o) -> uint16_t {
+                return DOTS ? (uint16_t)0 : act.d[m * nb + kt0 + pb + min(o, pn - 1)];
             };
-            auto qput = [&](int c, const uint4 &v) {
-                if (c < nq) {
-                    const int m = c / (pn * 2), o = c - m * pn * 2;
-                    *(uint4 *)(qs + m * P * 32 + o * 16) = v;
-                }
-            };
-            auto dput = [&](int c, uint16_t v) {
-                if (c < nd) {
-                    const int m = c / pn, o = c - m * pn;
-                    ds[m * P + o] = v;
-                }
-            };
+            const int o = threadIdx.x;
+            uint4 qv[MM];
+            uint16_t dv[MM];
 #pragma unroll
-            for (int i = 0; i < XB; i++)
-                qv[i] = qchunk(threadIdx.x + i * NW * 64);
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-                dv[i] = dval(threadIdx.x + i * NW * 64);
+            for (int m = 0; m < MM; m++) {
+                qv[m] = qload(m, o);
+                dv[m] = dload(m, o);
+            }
 #pragma unroll
             for (int r = 0; r < D; r++)
                 load_stage(u[r], r);
 #pragma unroll
-            for (int i = 0; i < XB; i++)
-                qput(threadIdx.x + i * NW * 64, qv[i]);
+            for (int m = 0; m < MM; m++) {
+                if (o < 2 * pn)
+                    put_chunk(o >> 1, m, o & 1, qv[m]);
+                if (o < pn)
+                    ds[o * MM + m] = f16_bits_to_f32(dv[m]);
+            }
+            for (int o2 = o + NW * 64; o2 < 2 * pn; o2 += NW * 64) {
 #pragma unroll
-            for (int i = 0; i < 2; i++)
-                dput(threadIdx.x + i * NW * 64, dv[i]);
-            for (int c = threadIdx.x + XB * NW * 64; c < nq; c += NW * 64)
-                qput(c, qchunk(c));
-            for (int c = threadIdx.x + 2 * NW * 64; c < nd; c += NW * 64)
-                dput(c, dval(c));
+                for (int m = 0; m < MM; m++) {
+                    put_chunk(o2 >> 1, m, o2 & 1, qload(m, o2));
+                    if (o2 < pn)
+                        ds[o2 * MM + m] = f16_bits_to_f32(dload(m, o2));
+                }
+            }
         } else {
             // one 32-element block per quad of lanes, 8 elements per lane
-            // (quant_quad); QB blocks per batch
+            // (quant_quad); block b = tp * MM + m, QB blocks per batch
             constexpr int QB = NW * 16;
             const int nblk = MM * pn;
             const int c = lane & 3, bq = threadIdx.x >> 2;
             auto xload = [&](float (&v)[8], int b) {
                 b = min(b, nblk - 1);
-                const int m = b / pn, tp = b - m * pn;
+                const int tp = b / MM, m = b - tp * MM;
                 load_x8<XT>(v, act.x, m * act.ldx + (int64_t)(kt0 + pb + tp) * 32 + 8 * c);
             };
             // quantized unconditionally (a branch here would let the compiler
@@ -375,10 +393,16 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                 uint16_t db;
                 quant_quad(v, qv, db);
                 if (b < nblk) {
-                    const int m = b / pn, tp = b - m * pn;
-                    *(uint2 *)(qs + m * P * 32 + tp * 32 + 8 * c) = qv;
+                    int8_t *qb = qs + b * 32;
+                    if constexpr (QT == TQ_Q8_0) {
+                        *(uint2 *)(qb + 8 * c) = qv;
+                    } else {
+                        const uint2 eo = split_even_odd(qv);
+                        *(uint32_t *)(qb + 4 * c) = eo.x;
+                        *(uint32_t *)(qb + 16 + 4 * c) = eo.y;
+                    }
                     if (c == 0)
-                        ds[m * P + tp] = db;
+                        ds[b] = f16_bits_to_f32(db);
                 }
             };
             float v[8];
@@ -401,7 +425,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
             TileRegs<QT> w;
             lds_tile<QT>(w, my + half * TS, l);
             ActRegs<QT, MM> x;
-            lds_act<QT, MM>(x, qs, ds, P, tp, l);
+            lds_act<QT, MM>(x, qs, ds, tp, l);
             int s[MM];
             block_dots<QT, MM>(s, w, x, sel0, sel1, lut);
             if constexpr (DOTS) {
@@ -419,7 +443,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                 dw = valid ? dw : 0.0f;                       // a missing second tile adds 0
 #pragma unroll
                 for (int m = 0; m < MM; m++)
-                    acc[m] = fmaf((float)s[m], dw * f16_bits_to_f32(x.d[m]), acc[m]);
+                    acc[m] = fmaf((float)s[m], dw * x.d[m], acc[m]);
             }
         };
         // A ring of D unit buffers: buffer r holds the wave's units r, r + D,
