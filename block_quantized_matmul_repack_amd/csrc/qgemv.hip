@@ -72,6 +72,61 @@ constexpr int ring_depth()
     return QT == TQ_Q8_0 ? TQ_GEMV_DEPTH_Q8 : TQ_GEMV_DEPTH_Q4;
 }
 
+// 4-bit tiles with at least this many activation rows go through the int8
+// matrix cores (one v_mfma_i32_32x32x32_i8 per tile, rows past M zero)
+// instead of v_dot4; fewer rows stay on v_dot4, where the matrix core would
+// mostly multiply zeros.
+#ifndef TQ_GEMV_MMA_MIN_M
+#define TQ_GEMV_MMA_MIN_M 2
+#endif
+template <int QT, int MM>
+constexpr bool use_mma()
+{
+    return QT != TQ_Q8_0 && MM >= TQ_GEMV_MMA_MIN_M;
+}
+
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef int v16i_t __attribute__((ext_vector_type(16)));
+
+// Matrix-core operand of a staged 4-bit tile.  ds_read_b64_tr_b8 hands lane
+// j of each 16-lane group byte j % 8 of the 8-byte rows that lanes 2i + (j
+// >= 8) of the group point at (i = 0..7).  Pointing lane 2i + p of group G
+// at the tile's 8 bytes (column pair 8 (G / 2) + i, rows 8 (2 (G % 2) + p)
+// ..) gives lane l the column pairs 16 (l / 32) / 2 .. + 7 of row l % 32: its
+// 16 K values K0 + 0 .. 15, K0 = 16 (l / 32), as nibbles.  The byte offset
+// of that row in the tile:
+__device__ __forceinline__ int tr8_offset(int lane)
+{
+    const int G = lane >> 4, s = lane & 15;
+    return (8 * (G >> 1) + (s >> 1)) * 32 + 8 * (2 * (G & 1) + (s & 1));
+}
+
+// The 16 int8 of that operand, in the matrix-core K order used throughout:
+// K0 + {0, 2, 4, 6}, {8, .., 14}, {1, .., 7}, {9, .., 15} (the activations
+// are staged in the same order).  Q4_0 values are 16 (code - 8), like the
+// v_dot4 path.
+template <int QT>
+__device__ __forceinline__ v4i_t tile_operand(const uint8_t *tile, int off, const Lut &lut)
+{
+    const v2i_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i_t *)(tile + off));
+    uint32_t lo[2], hi[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const uint32_t x = (uint32_t)w[i];
+        if constexpr (QT == TQ_Q4_0) {
+            const uint32_t t = x ^ 0x88888888u;
+            lo[i] = (t << 4) & 0xF0F0F0F0u;
+            hi[i] = t & 0xF0F0F0F0u;
+        } else {
+            lo[i] = lut16(x & 0x0F0F0F0Fu, lut);
+            hi[i] = lut16((x >> 4) & 0x0F0F0F0Fu, lut);
+        }
+    }
+    return v4i_t{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
+}
+
 template <int QT>
 struct TileRegs;
 
@@ -259,10 +314,18 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     constexpr int TS = Fmt<QT>::tile;
     constexpr int UB = Unit<QT>::BYTES;
     constexpr int D = ring_depth<QT>();
+    constexpr bool MMA = use_mma<QT, MM>();
+    constexpr int ACC = MMA ? 4 : MM;                     // fp32 sums per lane
+    constexpr int NSLOT = MMA ? NW : 2 * NW;              // partial sums per output
+    // staged 4-bit activations: the even K of a 16-K half at HS * h, the odd
+    // K ODD bytes further (v_dot4: all even K, then all odd K; matrix cores:
+    // each 16-K half as 8 even then 8 odd)
+    constexpr int HS = MMA ? 16 : 8, ODD = MMA ? 8 : 16;
     static_assert(NW * 64 >= MM * 32, "one thread per output of the stripe");
     __shared__ __attribute__((aligned(16))) uint8_t stage[NW][UB];
     __shared__ __attribute__((aligned(16))) uint8_t act_lds[act_lds_bytes<MM>()];
-    __shared__ float red[2 * NW][MM][32];
+    __shared__ float red[NSLOT][MM][32];
+    __shared__ __attribute__((aligned(16))) uint32_t zero16[4];   // A rows past M
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, l = lane & 31;
@@ -288,12 +351,15 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
         sel1 = b2 | ((4 + b2) << 8) | (b3 << 16) | ((4 + b3) << 24);
     }
 
-    float acc[MM];
+    float acc[ACC];
 #pragma unroll
-    for (int m = 0; m < MM; m++)
+    for (int m = 0; m < ACC; m++)
         acc[m] = 0.0f;
+    if (threadIdx.x < 4)
+        zero16[threadIdx.x] = 0;                          // read after the staging barrier
 
     uint8_t *my = stage[wave];
+    const int tro = tr8_offset(lane);                     // matrix-core path only
     // Weight loads are raw buffer loads over this workgroup's tiles: a unit
     // or chunk past the range gets offset BUF_OOB, which returns zeros and
     // moves no data, so every load is issued unconditionally.
@@ -312,8 +378,8 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
         } else {
             const uint2 a = split_even_odd(make_uint2(v.x, v.y));
             const uint2 b = split_even_odd(make_uint2(v.z, v.w));
-            *(uint2 *)(qb + 8 * h) = make_uint2(a.x, b.x);
-            *(uint2 *)(qb + 16 + 8 * h) = make_uint2(a.y, b.y);
+            *(uint2 *)(qb + HS * h) = make_uint2(a.x, b.x);
+            *(uint2 *)(qb + HS * h + ODD) = make_uint2(a.y, b.y);
         }
     };
     for (int pb = 0; pb < nt; pb += P) {
@@ -398,8 +464,8 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                         *(uint2 *)(qb + 8 * c) = qv;
                     } else {
                         const uint2 eo = split_even_odd(qv);
-                        *(uint32_t *)(qb + 4 * c) = eo.x;
-                        *(uint32_t *)(qb + 16 + 4 * c) = eo.y;
+                        *(uint32_t *)(qb + HS * (c >> 1) + 4 * (c & 1)) = eo.x;
+                        *(uint32_t *)(qb + HS * (c >> 1) + 4 * (c & 1) + ODD) = eo.y;
                     }
                     if (c == 0)
                         ds[b] = f16_bits_to_f32(db);
@@ -420,30 +486,74 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
 
         auto process = [&](const Unit<QT> &un, int j) {
             store_unit<QT>(un, my, min(2, pn - 2 * j) * (TS / 16), lane);
-            const int tp = min(2 * j + half, pn - 1);         // this half's tile, pass-local
-            const bool valid = 2 * j + half < pn;
-            TileRegs<QT> w;
-            lds_tile<QT>(w, my + half * TS, l);
-            ActRegs<QT, MM> x;
-            lds_act<QT, MM>(x, qs, ds, tp, l);
-            int s[MM];
-            block_dots<QT, MM>(s, w, x, sel0, sel1, lut);
-            if constexpr (DOTS) {
-                const int64_t n = 32 * ct + l;
-                if (valid && n < N) {
+            if constexpr (MMA) {
+                // the whole wave takes each tile of the unit: lane l holds
+                // output row n = l % 32 for activation rows 4 (l / 32) + r
 #pragma unroll
-                    for (int m = 0; m < MM; m++)
-                        isum[((int64_t)m * N + n) * nb + kt0 + pb + tp] =
-                            (QT == TQ_Q4_0) ? (s[m] >> 4) : s[m];
+                for (int t = 0; t < 2; t++) {
+                    const int tp = min(2 * j + t, pn - 1);
+                    const bool valid = 2 * j + t < pn;
+                    const uint8_t *tile = my + t * TS;
+                    const v4i_t b = tile_operand<QT>(tile, tro, lut);
+                    const int8_t *ap = l < MM ? qs + (tp * MM + l) * 32 + 16 * half
+                                              : (const int8_t *)zero16;
+                    const v4i_t a = *(const v4i_t *)ap;
+                    const v16i_t dot = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, v16i_t{}, 0, 0, 0);
+                    // Only dot[0..3] are used, but the MFMA writes all 16
+                    // registers.  Reading them all here keeps the compiler
+                    // from handing the unused ones to other values before the
+                    // MFMA has finished writing them (a variant without this
+                    // gave wrong sums at M = 8).
+                    asm volatile("" ::"v"(dot));
+                    if constexpr (DOTS) {
+                        const int64_t n = 32 * ct + l;
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            const int m = 4 * half + r;
+                            if (valid && m < MM && n < N)
+                                isum[((int64_t)m * N + n) * nb + kt0 + pb + tp] =
+                                    (QT == TQ_Q4_0) ? (dot[r] >> 4) : dot[r];
+                        }
+                    } else {
+                        float dw = f16_bits_to_f32(
+                            ((const uint16_t *)(tile + Fmt<QT>::scale_off))[l]);
+                        if constexpr (QT == TQ_Q4_0)
+                            dw *= 0.0625f;
+                        dw = valid ? dw : 0.0f;               // a missing second tile adds 0
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            const int m = 4 * half + r;
+                            const float da = m < MM ? ds[tp * MM + min(m, MM - 1)] : 0.0f;
+                            acc[r] = fmaf((float)dot[r], dw * da, acc[r]);
+                        }
+                    }
                 }
             } else {
-                float dw = f16_bits_to_f32(w.sc);
-                if constexpr (QT == TQ_Q4_0)
-                    dw *= 0.0625f;
-                dw = valid ? dw : 0.0f;                       // a missing second tile adds 0
+                const int tp = min(2 * j + half, pn - 1);     // this half's tile, pass-local
+                const bool valid = 2 * j + half < pn;
+                TileRegs<QT> w;
+                lds_tile<QT>(w, my + half * TS, l);
+                ActRegs<QT, MM> x;
+                lds_act<QT, MM>(x, qs, ds, tp, l);
+                int s[MM];
+                block_dots<QT, MM>(s, w, x, sel0, sel1, lut);
+                if constexpr (DOTS) {
+                    const int64_t n = 32 * ct + l;
+                    if (valid && n < N) {
 #pragma unroll
-                for (int m = 0; m < MM; m++)
-                    acc[m] = fmaf((float)s[m], dw * x.d[m], acc[m]);
+                        for (int m = 0; m < MM; m++)
+                            isum[((int64_t)m * N + n) * nb + kt0 + pb + tp] =
+                                (QT == TQ_Q4_0) ? (s[m] >> 4) : s[m];
+                    }
+                } else {
+                    float dw = f16_bits_to_f32(w.sc);
+                    if constexpr (QT == TQ_Q4_0)
+                        dw *= 0.0625f;
+                    dw = valid ? dw : 0.0f;                   // a missing second tile adds 0
+#pragma unroll
+                    for (int m = 0; m < MM; m++)
+                        acc[m] = fmaf((float)s[m], dw * x.d[m], acc[m]);
+                }
             }
         };
         // A ring of D unit buffers: buffer r holds the wave's units r, r + D,
@@ -463,16 +573,24 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     if constexpr (DOTS)
         return;
 
+    if constexpr (MMA) {
 #pragma unroll
-    for (int m = 0; m < MM; m++)
-        red[hs][m][l] = acc[m];
+        for (int r = 0; r < 4; r++) {
+            if (4 * half + r < MM)
+                red[wave][min(4 * half + r, MM - 1)][l] = acc[r];
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < MM; m++)
+            red[hs][m][l] = acc[m];
+    }
     __syncthreads();
     const int i = threadIdx.x;
     const int m = i >> 5, r = i & 31;
     float part = 0.0f;
     if (i < MM * 32) {
 #pragma unroll
-        for (int c = 0; c < 2 * NW; c++)
+        for (int c = 0; c < NSLOT; c++)
             part += red[c][m][r];
     }
     const int64_t n = 32 * ct + r;
