@@ -45,12 +45,12 @@ ROTATE_BYTES = 1 << 30         # defeat the 256 MB Infinity Cache
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "decode": {"fetch_kib": 8800.01, "write_kib": 112.0,
-               "src": "5d3d160ec6b7c826abeb384a368f5408e462aecf08881cfe559e7961da1f2b73"},
-    "gemm": {"fetch_kib": 13372.03, "write_kib": 8192.0,
-             "src": "a40974dde259adcd55e77d23c28bbade68e77fb96952905afc3e11677c5f914e"},
-    "repack": {"fetch_kib": 16147.18, "write_kib": 32256.0,
-               "src": "13f67fc23bdb53a872fa4d68cba950443435a92c9b34cc58fa3a145511c45c34"},
+    "decode": {"fetch_kib": 8779.52, "write_kib": 112.0,
+               "src": "65a452c120782a67bcb7a698c21d5e409ef84d53e0f04baadc3a5e0d607ed904"},
+    "gemm": {"fetch_kib": 13363.18, "write_kib": 8192.0,
+             "src": "cad6aa91d9b39e2d1ff51229686e2593aa22682e90886692d124690d34599749"},
+    "repack": {"fetch_kib": 16161.07, "write_kib": 32256.0,
+               "src": "400031de737dc36b1f2b468107153240bb35e2de939add632c5a18dbf5c3b773"},
 }
 KERNEL_SOURCES = {
     "decode": ("qgemv.hip", "tq_internal.h"),
@@ -254,6 +254,67 @@ def measure_repack(torch, tq, synth, n=50):
                          "bytes_per_launch": fb + w.weight_bytes}}
 
 
+def measure_others(torch, tq, synth):
+    """The other decode / prefill workloads, timed like the roofline kernel
+    (graph of 50 steps, HIP events); weights rotate over >= 1 GiB.  Decode
+    steps are timed both fused (qgemv_x) and as quantize_act + qgemv; GB/s
+    counts tiles + fp32 x + fp32 y over the faster one."""
+    import numpy as np
+    res = {}
+    cases = [("q4_0_gemv_k4096_n14336_m1", 1), ("q4_0_gemv_k4096_n14336_m1", 4),
+             ("q4_0_gemv_k4096_n14336_m1", 8), ("q8_0_lmhead_k4096_n128001_m1", 1),
+             ("q8_0_lmhead_k4096_n128001_m128", 128)]
+    tiles_cache = {}
+    for name, M in cases:
+        w = synth.WORKLOADS[name]
+        key = (w.qtype, w.K, w.N)
+        if key not in tiles_cache:
+            inp = synth.make_inputs(w, M=1)
+            flat = torch.from_numpy(inp.flat).cuda()
+            R = max(2, -(-ROTATE_BYTES // w.weight_bytes))
+            tiles_cache.clear()
+            tiles_cache[key] = [tq.repack_tiles(w.qtype, flat, w.K, w.N) for _ in range(R)]
+            del flat
+        tiles = tiles_cache[key]
+        R = len(tiles)
+        rng = np.random.default_rng(M)
+        x = torch.from_numpy(rng.standard_normal((M, w.K), dtype=np.float32)).cuda()
+        if M <= 8:
+            q = torch.empty((M, w.K), dtype=torch.int8, device="cuda")
+            d = torch.empty((M, w.K // 32), dtype=torch.float16, device="cuda")
+            y = torch.empty((M, w.N), dtype=torch.float32, device="cuda")
+            fused = lambda i: tq.qgemv_x(w.qtype, tiles[i % R], w.K, w.N, x, out=y)
+
+            def two(i):
+                tq.quantize_act(x, q=q, d=d)
+                tq.qgemv(w.qtype, tiles[i % R], w.K, w.N, q, d, out=y)
+            label = f"{name.rsplit('_m', 1)[0]}_m{M}"
+            nbytes = w.weight_bytes + 4 * M * w.K + 4 * M * w.N
+            for i in range(5):
+                fused(i)
+                two(i)
+            us_f = kernel_us(torch, fused, 50)
+            us_2 = kernel_us(torch, two, 50)
+            us = min(us_f, us_2)
+            res[label] = {"step_us": round(us, 3),
+                          "path": "qgemv_x (fused)" if us_f <= us_2 else "quantize_act + qgemv",
+                          "qgemv_x_us": round(us_f, 3), "quantize_act_qgemv_us": round(us_2, 3),
+                          "GB_s": round(nbytes / us / 1e3, 1),
+                          "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        else:
+            q, d = tq.quantize_act(x)
+            f = lambda i: tq.qgemm(w.qtype, tiles[i % R], w.K, w.N, q, d)
+            nbytes = w.weight_bytes + M * w.K + 2 * M * (w.K // 32) + 4 * M * w.N
+            for i in range(5):
+                f(i)
+            us = kernel_us(torch, f, 50)
+            res[f"{name} qgemm"] = {"kernel_us": round(us, 3), "GB_s": round(nbytes / us / 1e3, 1),
+                                    "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                                    "TOPS": round(2.0 * M * w.N * w.K / us / 1e6, 2)}
+    tiles_cache.clear()
+    return res
+
+
 def launch_only(torch, tq, synth, kernel, n):
     """Launch one kernel n times, eagerly, untimed (counter collection)."""
     if kernel == "decode":
@@ -334,6 +395,7 @@ def main():
     if not args.no_extra:
         line["qgemm"] = measure_gemm(torch, tq, synth)
         line["repack"] = measure_repack(torch, tq, synth)
+        line["other_workloads"] = measure_others(torch, tq, synth)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(synth, w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

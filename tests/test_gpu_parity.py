@@ -198,6 +198,25 @@ def test_qgemv_split_and_unsplit(tq, qtype, M, K, N):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M", [2, 5, 6, 7])
+@pytest.mark.parametrize("K,N", [(2048, 96), (4064, 33)])
+def test_qgemv_every_row_count(tq, qtype, M, K, N):
+    """Row counts between the ones above, with many tiles per workgroup
+    (split and unsplit): for 4-bit tiles these take the matrix-core path,
+    where rows 4..7 come from the second half of the wave."""
+    inp = make(qtype, K, N, M, seed=M * 11 + K + N)
+    tiles, tdev = _dev(inp, qtype, K, N)
+    q, d = oracle.quantize_act(inp.x)
+    y_ref, acond = oracle.matmul(qtype, tiles, K, N, q, d, LUT)
+    qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+    for split in (True, False):
+        y = tq.qgemv(qtype, tdev, K, N, qd, dd, lut=LUT, split=split)
+        check_y(y.cpu().numpy(), y_ref, acond, (qtype, M, K, N, split))
+    yx = tq.qgemv_x(qtype, tdev, K, N, torch.from_numpy(inp.x).cuda(), lut=LUT)
+    check_y(yx.cpu().numpy(), y_ref, acond, (qtype, M, K, N, "fused"))
+
+
 def test_qgemv_workspace_reused_across_shapes(tq):
     """One workspace serves calls of different shapes in a row (its counter
     and partial offsets depend on the shape): every call must leave it zero."""
