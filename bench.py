@@ -191,6 +191,16 @@ def measure_gemv(torch, tq, synth, args):
         "quantize_act_us": kernel_us(torch, parts["quantize_act"]),
         "two_launch_step_us": two_us,
     }
+    # references at this size: an (almost) empty launch, and a plain device
+    # copy of the same number of bytes (read + write), both graph-replayed
+    tiny = torch.zeros(1, device="cuda")
+    detail["empty_launch_us"] = kernel_us(torch, lambda i: tiny.add_(1.0))
+    src = [torch.ones(w.weight_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    dst = torch.empty_like(src[0])
+    cu = kernel_us(torch, lambda i: dst.copy_(src[i % R]))
+    del src
+    detail["copy_same_bytes_us"] = cu
+    detail["copy_same_bytes_GB_s"] = 2 * w.weight_bytes / cu / 1e3
     return w, R, dt, detail
 
 
@@ -333,6 +343,13 @@ def launch_only(torch, tq, synth, kernel, n):
     print(f"launched {kernel} x{n}", flush=True)
 
 
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2**30, 1)}
+
+
 def cpu_baseline(synth, w, seconds):
     """The oracle as it stands (single-threaded C), timed on this host."""
     import oracle
@@ -391,6 +408,7 @@ def main():
                      "kernel_us": round(det["qgemv_x_us"], 3),
                      "bytes_per_launch": gemv_x_bytes(w)},
         "decode_detail_us": {k: round(v, 3) for k, v in det.items()},
+        "device": device_info(torch),
     }
     if not args.no_extra:
         line["qgemm"] = measure_gemm(torch, tq, synth)

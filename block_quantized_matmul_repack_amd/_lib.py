@@ -28,6 +28,7 @@ SIGNATURES = {
     "tq_qgemv": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P, SZ, P]),
     "tq_qgemv_x": (INT, [INT, P, I64, I64, INT, P, I64, I64, P, P, I64, P, SZ, P]),
     "tq_qgemm": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
+    "tq_matmul": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P, SZ, P]),
     "tq_block_dots": (INT, [INT, P, I64, I64, P, I64, P, P, INT, P]),
 }
 

@@ -207,6 +207,16 @@ int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
         tq::launch_qgemm(type, tiles, K, N, q, d, M, pack_lut(lut), y, ldy, nullptr, stream));
 }
 
+int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
+              const uint16_t *d, int64_t M, const int8_t *lut, float *y, int64_t ldy,
+              void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (M <= 8)
+        return tq_qgemv(type, tiles, K, N, q, d, M, lut, y, ldy, workspace, workspace_bytes,
+                        stream);
+    return tq_qgemm(type, tiles, K, N, q, d, M, lut, y, ldy, stream);
+}
+
 int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
                   int64_t M, const int8_t *lut, int32_t *isum, int path, hipStream_t stream)
 {

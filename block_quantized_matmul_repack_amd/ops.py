@@ -160,6 +160,19 @@ def qgemm(qtype, tiles, K, N, q, d, lut=None, out=None):
     return out
 
 
+def matmul(qtype, tiles, K, N, q, d, lut=None, out=None):
+    """y [M, N] for any M: the library picks qgemv (M <= 8) or qgemm."""
+    _need_cuda(tiles, q, d, out)
+    out = _out("tq_matmul", q, N, out)
+    M = q.shape[0]
+    st = _stream(q)
+    need = lib().tq_qgemv_workspace_bytes(qtype, K, N, M) if M <= 8 else 0
+    ws = workspace(q.device, st.value, need) if need else None
+    check(lib().tq_matmul(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut),
+                          _ptr(out), out.stride(0), _ptr(ws), need, st), "tq_matmul")
+    return out
+
+
 def block_dots(qtype, tiles, K, N, q, lut=None, path=PATH_GEMV, out=None):
     """Integer block dots int32 [M, N, K/32] as computed inside qgemv / qgemm."""
     _need_cuda(tiles, q, out)

@@ -173,6 +173,15 @@ int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N,
              const int8_t *q, const uint16_t *d, int64_t M,
              const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
 
+/* The product for any M, dispatched on M: tq_qgemv (with the workspace) for
+ * M <= 8, where one pass over the tiles serves all rows, else tq_qgemm.
+ * Arguments as tq_qgemv, except that M >= 0 is unbounded (TQ_E_SHAPE only
+ * for the limits of the calling convention). */
+int tq_matmul(int type, const void *tiles, int64_t K, int64_t N,
+              const int8_t *q, const uint16_t *d, int64_t M,
+              const int8_t *lut, float *y, int64_t ldy,
+              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Test instrument: run the tq_qgemv (path TQ_PATH_GEMV, M <= 8) or tq_qgemm
  * (TQ_PATH_GEMM) kernel with the integer block dots as output instead of y:
  * isum[(m*N + n)*(K/32) + kt] (int32, device, 4-byte aligned) =

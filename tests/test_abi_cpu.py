@@ -107,11 +107,11 @@ def test_quantize_validation(L):
     assert L.tq_quantize_act(0, NUL, 0, 64, 64, NUL, NUL, NUL) == 0
 
 
-@pytest.mark.parametrize("fn", ["tq_qgemv", "tq_qgemm"])
+@pytest.mark.parametrize("fn", ["tq_qgemv", "tq_qgemm", "tq_matmul"])
 def test_matmul_validation(L, fn):
-    if fn == "tq_qgemv":
+    if fn in ("tq_qgemv", "tq_matmul"):
         def f(*a):
-            return L.tq_qgemv(*a[:10], None, 0, a[10])
+            return getattr(L, fn)(*a[:10], None, 0, a[10])
     else:
         f = L.tq_qgemm
     assert f(9, A16, 64, 32, A16, A16, 1, NUL, A16, 32, NUL) == 2
@@ -141,6 +141,14 @@ def test_qgemv_x_validation(L):
     assert f(0, A16, 64, 32, 0, A2, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 4       # fp32 x at 2 B
     assert f(2, A16, 64, 32, 1, A16, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 1      # IQ4_NL, no table
     assert f(0, NUL, 64, 0, 0, NUL, 64, 1, NUL, NUL, 0, NUL, 0, NUL) == 0        # N == 0
+
+
+def test_matmul_dispatch_validation(L):
+    # M > 8 goes to the GEMM's checks: no M limit, same shape / pointer rules
+    f = L.tq_matmul
+    assert f(0, A16, 64, 32, A16, A16, 9, NUL, A16, 31, NUL, 0, NUL) == 3        # ldy < N
+    assert f(0, A16, 64, 32, A16, NUL, 9, NUL, A16, 32, NUL, 0, NUL) == 1        # d NULL
+    assert f(0, NUL, 64, 0, NUL, NUL, 9, NUL, NUL, 0, NUL, 0, NUL) == 0          # N == 0
 
 
 def test_gemv_m_limit(L):

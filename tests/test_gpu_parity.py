@@ -217,6 +217,19 @@ def test_qgemv_every_row_count(tq, qtype, M, K, N):
     check_y(yx.cpu().numpy(), y_ref, acond, (qtype, M, K, N, "fused"))
 
 
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M", [1, 8, 9, 40])
+def test_matmul_dispatch(tq, qtype, M):
+    """tq_matmul is bitwise the GEMV for M <= 8 and the GEMM above."""
+    K, N = 512, 100
+    inp = make(qtype, K, N, M, seed=M + 3)
+    tiles, tdev = _dev(inp, qtype, K, N)
+    qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+    y = tq.matmul(qtype, tdev, K, N, qd, dd, lut=LUT)
+    ref = (tq.qgemv if M <= 8 else tq.qgemm)(qtype, tdev, K, N, qd, dd, lut=LUT)
+    assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
+
+
 def test_qgemv_workspace_reused_across_shapes(tq):
     """One workspace serves calls of different shapes in a row (its counter
     and partial offsets depend on the shape): every call must leave it zero."""
