@@ -11,7 +11,8 @@ the reading taken wherever the page is silent.  Arrays are numpy, C-contiguous.
 
 Parity pins: see tests/test_oracle_*.py.  The flat GGML block nibble order
 (flat_decode, and through it the input side of repack) is "parity unpinned":
-the page does not print the flat layout.
+the page does not print the flat layout; for MXFP4 the flat block (one E8M0
+byte, then 16 nibble bytes) is unpinned for the same reason.
 """
 import ctypes
 import os
@@ -20,7 +21,7 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, Q8_0, IQ4_NL = 0, 1, 2
+Q4_0, Q8_0, IQ4_NL, MXFP4 = 0, 1, 2, 3
 F32, BF16, F16 = 0, 1, 2
 
 _lib = None
@@ -30,8 +31,7 @@ def lib():
     global _lib
     if _lib is None:
         path = _build.LIB
-        if not os.path.exists(path):
-            _build.build()
+        _build.build(force=False)
         L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         l = ctypes.c_long
@@ -59,6 +59,8 @@ def lib():
         L.or_block_dots.restype = ctypes.c_int
         L.or_matmul.argtypes = [ctypes.c_int, P, l, l, P, P, l, P, l, l, P, P, l]
         L.or_matmul.restype = None
+        L.or_row_scale.argtypes = [ctypes.c_int, ctypes.c_uint16]
+        L.or_row_scale.restype = ctypes.c_double
         _lib = L
     return _lib
 
@@ -108,6 +110,12 @@ def tiled_bytes(t, K, N):
 
 def flat_bytes(t, K, N):
     return lib().or_flat_bytes(t, K, N)
+
+
+def row_scale(t, s):
+    """The factor one tile row scale s contributes to y (fp64): the fp16 value
+    of s, or for MXFP4 half the power of two the E8M0 byte s stands for."""
+    return lib().or_row_scale(t, int(s))
 
 
 def flat_decode(t, flat, K, N):

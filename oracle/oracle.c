@@ -9,7 +9,7 @@
  * Source of every definition: the page "Hexagon backend developer details"
  * (llama.cpp docs/backend/snapdragon/developer.md), section "Tiled Weight
  * Formats" with its subsections "Tile Dimensions and Grid Layout" and
- * "Block-32 Quantized Formats" (Q4_0, Q8_0, IQ4_NL), and section "Memory
+ * "Block-32 Quantized Formats" (Q4_0, Q8_0, IQ4_NL, MXFP4), and section "Memory
  * buffers" (dynamically quantized activations).  Where the page is silent the
  * reading taken is stated at the function.
  *
@@ -27,7 +27,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_IQ4_NL = 2 };
+enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_IQ4_NL = 2, OR_MXFP4 = 3 };
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
 
 /* ---------------------------------------------------------------------------
@@ -106,6 +106,7 @@ long or_tile_bytes(int type)
     case OR_Q4_0: return 576;
     case OR_Q8_0: return 1088;
     case OR_IQ4_NL: return 576;
+    case OR_MXFP4: return 544;
     }
     return 0;
 }
@@ -116,6 +117,7 @@ long or_block_bytes(int type)
     case OR_Q4_0: return 18;
     case OR_Q8_0: return 34;
     case OR_IQ4_NL: return 18;
+    case OR_MXFP4: return 17;
     }
     return 0;
 }
@@ -138,12 +140,20 @@ long or_flat_bytes(int type, long K, long N)
  * taken is GGML's own block-32 layout: row n holds K/32 consecutive blocks;
  * a Q4_0 / IQ4_NL block is an fp16 scale followed by 16 bytes whose low
  * nibbles are elements 0..15 and high nibbles elements 16..31; a Q8_0 block is
- * an fp16 scale followed by 32 int8 elements.
+ * an fp16 scale followed by 32 int8 elements; an MXFP4 block is one E8M0
+ * scale byte followed by 16 bytes with the Q4_0 nibble order.
  *
  * codes[n*K + k] receives the raw code of element k of row n: 0..15 for the
  * 4-bit types, the int8 byte (as uint8) for Q8_0.  scales[n*(K/32) + b]
- * receives the fp16 bits of block b of row n.
+ * receives the fp16 bits of block b of row n (MXFP4: the E8M0 byte).
  * ------------------------------------------------------------------------- */
+static long quant_offset(int type) { return type == OR_MXFP4 ? 1 : 2; }
+
+static uint16_t block_scale(int type, const uint8_t *blk)
+{
+    return type == OR_MXFP4 ? blk[0] : (uint16_t)(blk[0] | (blk[1] << 8));
+}
+
 void or_flat_decode(int type, const uint8_t *flat, long K, long N,
                     uint8_t *codes, uint16_t *scales)
 {
@@ -151,15 +161,16 @@ void or_flat_decode(int type, const uint8_t *flat, long K, long N,
     for (long n = 0; n < N; n++) {
         for (long b = 0; b < nb; b++) {
             const uint8_t *blk = flat + (n * nb + b) * bb;
-            scales[n * nb + b] = (uint16_t)(blk[0] | (blk[1] << 8));
+            const uint8_t *qs = blk + quant_offset(type);
+            scales[n * nb + b] = block_scale(type, blk);
             for (int j = 0; j < 32; j++) {
                 uint8_t c;
                 if (type == OR_Q8_0)
-                    c = blk[2 + j];
+                    c = qs[j];
                 else if (j < 16)
-                    c = blk[2 + j] & 0x0f;
+                    c = qs[j] & 0x0f;
                 else
-                    c = blk[2 + (j - 16)] >> 4;
+                    c = qs[j - 16] >> 4;
                 codes[n * K + b * 32 + j] = c;
             }
         }
@@ -185,18 +196,40 @@ void or_flat_decode(int type, const uint8_t *flat, long K, long N,
 static uint8_t code_at(int type, const uint8_t *flat, long K, long n, long k)
 {
     long nb = K / 32, bb = or_block_bytes(type);
-    const uint8_t *blk = flat + (n * nb + k / 32) * bb;
+    const uint8_t *qs = flat + (n * nb + k / 32) * bb + quant_offset(type);
     int j = (int)(k % 32);
     if (type == OR_Q8_0)
-        return blk[2 + j];
-    return j < 16 ? (blk[2 + j] & 0x0f) : (blk[2 + j - 16] >> 4);
+        return qs[j];
+    return j < 16 ? (qs[j] & 0x0f) : (qs[j - 16] >> 4);
 }
 
 static uint16_t scale_at(int type, const uint8_t *flat, long K, long n, long kt)
 {
     long nb = K / 32, bb = or_block_bytes(type);
-    const uint8_t *blk = flat + (n * nb + kt) * bb;
-    return (uint16_t)(blk[0] | (blk[1] << 8));
+    return block_scale(type, flat + (n * nb + kt) * bb);
+}
+
+/* Tile scale bytes: 32 fp16 at 512 (Q4_0, IQ4_NL) or 1024 (Q8_0); MXFP4: 32
+ * single E8M0 bytes at 512 ("MXFP4": bytes 512..543). */
+static long scale_offset(int type) { return type == OR_Q8_0 ? 1024 : 512; }
+
+static void put_tile_scale(int type, uint8_t *tile, int row, uint16_t s)
+{
+    if (type == OR_MXFP4) {
+        tile[512 + row] = (uint8_t)s;
+    } else {
+        long so = scale_offset(type);
+        tile[so + 2 * row + 0] = (uint8_t)(s & 0xff);
+        tile[so + 2 * row + 1] = (uint8_t)(s >> 8);
+    }
+}
+
+static uint16_t get_tile_scale(int type, const uint8_t *tile, int row)
+{
+    if (type == OR_MXFP4)
+        return tile[512 + row];
+    long so = scale_offset(type);
+    return (uint16_t)(tile[so + 2 * row] | (tile[so + 2 * row + 1] << 8));
 }
 
 void or_repack(int type, const uint8_t *flat, long K, long N, uint8_t *tiles)
@@ -220,10 +253,7 @@ void or_repack(int type, const uint8_t *flat, long K, long N, uint8_t *tiles)
                         tile[cp * 32 + row] = (uint8_t)((c1 << 4) | c0);
                     }
                 }
-                uint16_t s = valid ? scale_at(type, flat, K, n, kt) : 0;
-                long so = (type == OR_Q8_0) ? 1024 : 512;
-                tile[so + 2 * row + 0] = (uint8_t)(s & 0xff);
-                tile[so + 2 * row + 1] = (uint8_t)(s >> 8);
+                put_tile_scale(type, tile, row, valid ? scale_at(type, flat, K, n, kt) : 0);
             }
         }
     }
@@ -249,9 +279,7 @@ void or_unpack(int type, const uint8_t *tiles, long K, long N,
                     c = (col & 1) ? (tile[cp * 32 + row] >> 4) : (tile[cp * 32 + row] & 0x0f);
                 codes[n * K + kt * 32 + col] = c;
             }
-            long so = (type == OR_Q8_0) ? 1024 : 512;
-            scales[n * n_k_tiles + kt] =
-                (uint16_t)(tile[so + 2 * row] | (tile[so + 2 * row + 1] << 8));
+            scales[n * n_k_tiles + kt] = get_tile_scale(type, tile, row);
         }
     }
 }
@@ -263,16 +291,45 @@ void or_unpack(int type, const uint8_t *tiles, long K, long N,
  * half-range offsets for Q2_0 ("codes 0..3 representing signed values -1..2")
  * and Q3_K ("low2 - 4").  IQ4_NL: the code indexes a 16-entry non-linear
  * table (the page names it but does not print it); here the table is an
- * int8[16] supplied by the caller.
+ * int8[16] supplied by the caller.  MXFP4 ("MXFP4": 4-bit OCP Microscaling
+ * FP4, E2M1): the code is sign (bit 3), exponent (bits 2..1, bias 1) and
+ * mantissa (bit 0); its value is +-0.5*m for exponent 0 and
+ * +-2^(e-1) * (1 + m/2) otherwise.  The integer weight is twice that value
+ * (0, 1, 2, 3, 4, 6, 8, 12 with sign), the factor 1/2 going to the scale.
  * ------------------------------------------------------------------------- */
+static int e2m1_twice(uint8_t code)
+{
+    int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    int v = (e == 0) ? m : (1 << (e - 1)) * (2 + m);
+    return sign ? -v : v;
+}
+
 static int weight_value(int type, uint8_t code, const int8_t *lut)
 {
     switch (type) {
     case OR_Q4_0: return (int)code - 8;
     case OR_Q8_0: return (int)(int8_t)code;
     case OR_IQ4_NL: return (int)lut[code & 0x0f];
+    case OR_MXFP4: return e2m1_twice(code & 0x0f);
     }
     return 0;
+}
+
+/* The row scale that multiplies the integer weight.  fp16 types: the fp16
+ * value.  MXFP4 ("MXFP4", Dequantization): the E8M0 byte e becomes the FP16
+ * power of two with exponent bits clamp(e - 112, 0, 30), i.e. 2^(e-127) for
+ * 113 <= e <= 142, 0 for e <= 112 and 2^15 for e >= 142; halved here because
+ * the integer weight is twice the FP4 value. */
+double or_row_scale(int type, uint16_t s)
+{
+    if (type != OR_MXFP4)
+        return (double)or_f16_to_f32(s);
+    int ex = (int)s - 112;
+    if (ex < 0)
+        ex = 0;
+    if (ex > 30)
+        ex = 30;
+    return 0.5 * (double)or_f16_to_f32((uint16_t)(ex << 10));
 }
 
 /* ---------------------------------------------------------------------------
@@ -382,7 +439,6 @@ void or_matmul(int type, const uint8_t *tiles, long K, long N,
 {
     long nb = K / 32;
     long ts = or_tile_bytes(type);
-    long so = (type == OR_Q8_0) ? 1024 : 512;
     if (n1 > N)
         n1 = N;
     double *wrow = malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
@@ -391,8 +447,7 @@ void or_matmul(int type, const uint8_t *tiles, long K, long N,
         int row = (int)(n % 32);
         for (long kt = 0; kt < nb; kt++) {
             const uint8_t *tile = tiles + (ct * nb + kt) * ts;
-            double dw = (double)or_f16_to_f32(
-                (uint16_t)(tile[so + 2 * row] | (tile[so + 2 * row + 1] << 8)));
+            double dw = or_row_scale(type, get_tile_scale(type, tile, row));
             for (int col = 0; col < 32; col++) {
                 int cp = col / 2;
                 uint8_t c = (type == OR_Q8_0)

@@ -11,15 +11,18 @@ weight codes, then weight scales, then activations.
 Flat layout written here (GGML block-32, little-endian): row n holds K/32
 consecutive blocks; a Q4_0 / IQ4_NL block is 2 bytes of fp16 scale followed by
 16 bytes whose low nibbles are elements 0..15 and high nibbles elements
-16..31; a Q8_0 block is 2 bytes of fp16 scale followed by 32 int8 elements.
+16..31; a Q8_0 block is 2 bytes of fp16 scale followed by 32 int8 elements;
+an MXFP4 block is 1 byte of E8M0 scale followed by 16 nibble bytes ordered
+as in Q4_0.
 """
 import dataclasses
 
 import numpy as np
 
-Q4_0, Q8_0, IQ4_NL = 0, 1, 2
-TYPE_NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", IQ4_NL: "iq4_nl"}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, IQ4_NL: 18}
+Q4_0, Q8_0, IQ4_NL, MXFP4 = 0, 1, 2, 3
+TYPE_NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", IQ4_NL: "iq4_nl", MXFP4: "mxfp4"}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, IQ4_NL: 18, MXFP4: 17}
+TILE_BYTES = {Q4_0: 576, Q8_0: 1088, IQ4_NL: 576, MXFP4: 544}
 
 # Stand-in for the 16-entry non-linear IQ4_NL table.  The page names the table
 # but does not print its values; any 16 int8 entries keep the integer path
@@ -47,10 +50,14 @@ def draw_codes(rng, qtype, N, K):
 
 
 def draw_scales(rng, dist, N, K):
-    """fp16 scale bits [N, K/32].  dist: 'uniform' -> U[1e-3, 1e-2);
-    'absnormal' -> |N(0,1)| * 0.01.  Drawn in float64, cast to float32, then
-    to fp16 by numpy (round to nearest even)."""
+    """Scale bits [N, K/32] (uint16).  dist: 'uniform' -> fp16 of U[1e-3, 1e-2);
+    'absnormal' -> fp16 of |N(0,1)| * 0.01 (drawn in float64, cast to float32,
+    then to fp16 by numpy, round to nearest even); 'e8m0' -> MXFP4 E8M0 bytes
+    uniform in [118, 124], power-of-two scales 2^-9 .. 2^-3 (with E2M1 values
+    up to 6, weights of magnitude up to about 0.75)."""
     shape = (N, K // 32)
+    if dist == "e8m0":
+        return rng.integers(118, 125, size=shape).astype(np.uint16)
     if dist == "uniform":
         s = rng.uniform(1e-3, 1e-2, size=shape)
     elif dist == "absnormal":
@@ -61,20 +68,23 @@ def draw_scales(rng, dist, N, K):
 
 
 def pack_flat(qtype, codes, scale_bits):
-    """Write codes [N, K] and fp16 scale bits [N, K/32] as flat GGML blocks."""
+    """Write codes [N, K] and scale bits [N, K/32] (fp16, or E8M0 bytes for
+    MXFP4) as flat GGML blocks."""
     N, K = codes.shape
     nb = K // 32
     bb = BLOCK_BYTES[qtype]
     out = np.empty((N, nb, bb), np.uint8)
     sb = np.ascontiguousarray(scale_bits, dtype=np.uint16).reshape(N, nb)
     out[:, :, 0] = (sb & 0xFF).astype(np.uint8)
-    out[:, :, 1] = (sb >> 8).astype(np.uint8)
+    if qtype != MXFP4:
+        out[:, :, 1] = (sb >> 8).astype(np.uint8)
+    q0 = 1 if qtype == MXFP4 else 2
     c = codes.reshape(N, nb, 32)
     if qtype == Q8_0:
-        out[:, :, 2:] = c.view(np.uint8)
+        out[:, :, q0:] = c.view(np.uint8)
     else:
         c = c.astype(np.uint8)
-        out[:, :, 2:] = c[:, :, :16] | (c[:, :, 16:] << 4)
+        out[:, :, q0:] = c[:, :, :16] | (c[:, :, 16:] << 4)
     return out.reshape(-1)
 
 
@@ -112,7 +122,7 @@ class Workload:
 
     @property
     def tile_bytes(self):
-        return {Q4_0: 576, Q8_0: 1088, IQ4_NL: 576}[self.qtype]
+        return TILE_BYTES[self.qtype]
 
     @property
     def weight_bytes(self):
