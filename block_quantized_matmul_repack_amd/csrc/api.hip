@@ -16,7 +16,10 @@ constexpr int64_t MAX_M = int64_t(1) << 20;
 constexpr int64_t MAX_PROD = int64_t(1) << 40;
 constexpr int64_t MAX_MK = int64_t(1) << 36;
 
-bool valid_type(int t) { return t == TQ_Q4_0 || t == TQ_Q8_0 || t == TQ_IQ4_NL; }
+bool valid_type(int t)
+{
+    return t == TQ_Q4_0 || t == TQ_Q8_0 || t == TQ_IQ4_NL || t == TQ_MXFP4;
+}
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -29,8 +32,20 @@ bool valid_mk(int64_t M, int64_t K) { return M >= 0 && M <= MAX_M && M * K < MAX
 
 int launch_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_E_LAUNCH; }
 
-tq::Lut pack_lut(const int8_t *lut)
+// Twice the OCP Microscaling FP4 (E2M1) values of codes 0..15 ("MXFP4":
+// the nibbles are E2M1 codes): 0, 0.5, 1, 1.5, 2, 3, 4, 6, then the same
+// negated.  Doubled they are int8, and the kernels' int8 path stays exact.
+constexpr int8_t MXFP4_TWICE_E2M1[16] = {0, 1, 2, 3, 4, 6, 8, 12,
+                                         0, -1, -2, -3, -4, -6, -8, -12};
+
+// The table a launch of `type` uses: the caller's for IQ4_NL, the fixed one
+// for MXFP4, none for the others.
+tq::Lut pack_lut(int type, const int8_t *lut)
 {
+    if (type == TQ_MXFP4)
+        lut = MXFP4_TWICE_E2M1;
+    else if (type != TQ_IQ4_NL)
+        lut = nullptr;
     tq::Lut t{};
     if (lut)
         for (int i = 0; i < 16; i++)
@@ -66,6 +81,7 @@ size_t tq_tile_bytes(int type)
     case TQ_Q4_0: return tq::Fmt<TQ_Q4_0>::tile;
     case TQ_Q8_0: return tq::Fmt<TQ_Q8_0>::tile;
     case TQ_IQ4_NL: return tq::Fmt<TQ_IQ4_NL>::tile;
+    case TQ_MXFP4: return tq::Fmt<TQ_MXFP4>::tile;
     }
     return 0;
 }
@@ -76,6 +92,7 @@ size_t tq_block_bytes(int type)
     case TQ_Q4_0: return tq::Fmt<TQ_Q4_0>::block;
     case TQ_Q8_0: return tq::Fmt<TQ_Q8_0>::block;
     case TQ_IQ4_NL: return tq::Fmt<TQ_IQ4_NL>::block;
+    case TQ_MXFP4: return tq::Fmt<TQ_MXFP4>::block;
     }
     return 0;
 }
@@ -127,7 +144,7 @@ int tq_repack_tiles(int type, const void *flat, int64_t K, int64_t N, void *tile
         return TQ_OK;
     if (!flat || !tiles)
         return TQ_E_NULL;
-    if (!aligned(flat, 2) || !aligned(tiles, 16))
+    if (!aligned(flat, type == TQ_MXFP4 ? 4 : 2) || !aligned(tiles, 16))
         return TQ_E_ALIGN;
     return launch_status(tq::launch_repack(type, flat, K, N, tiles, stream));
 }
@@ -168,7 +185,7 @@ int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
     if (workspace && !aligned(workspace, 256))
         return TQ_E_ALIGN;
     const tq::Act act{q, d, nullptr, -1, 0};
-    return launch_status(tq::launch_qgemv(type, tiles, K, N, act, M, pack_lut(lut), y, ldy,
+    return launch_status(tq::launch_qgemv(type, tiles, K, N, act, M, pack_lut(type, lut), y, ldy,
                                           nullptr, workspace, workspace_bytes, stream));
 }
 
@@ -192,7 +209,7 @@ int tq_qgemv_x(int type, const void *tiles, int64_t K, int64_t N, int dtype, con
     if (!aligned(x, dtype == TQ_F32 ? 4 : 2) || (workspace && !aligned(workspace, 256)))
         return TQ_E_ALIGN;
     const tq::Act act{nullptr, nullptr, x, dtype, ldx};
-    return launch_status(tq::launch_qgemv(type, tiles, K, N, act, M, pack_lut(lut), y, ldy,
+    return launch_status(tq::launch_qgemv(type, tiles, K, N, act, M, pack_lut(type, lut), y, ldy,
                                           nullptr, workspace, workspace_bytes, stream));
 }
 
@@ -204,7 +221,7 @@ int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
     if (st != TQ_OK || M == 0 || N == 0)
         return st;
     return launch_status(
-        tq::launch_qgemm(type, tiles, K, N, q, d, M, pack_lut(lut), y, ldy, nullptr, stream));
+        tq::launch_qgemm(type, tiles, K, N, q, d, M, pack_lut(type, lut), y, ldy, nullptr, stream));
 }
 
 int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
@@ -229,7 +246,7 @@ int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N, const int8_
         return st;
     if ((int64_t)M * N * (K / 32) >= MAX_PROD)
         return TQ_E_SHAPE;
-    const tq::Lut t = pack_lut(lut);
+    const tq::Lut t = pack_lut(type, lut);
     const tq::Act act{q, nullptr, nullptr, -1, 0};
     hipError_t e = (path == TQ_PATH_GEMV)
                        ? tq::launch_qgemv(type, tiles, K, N, act, M, t, nullptr, N, isum,

@@ -14,7 +14,9 @@
 // LDS is double-buffered and the global loads run two steps ahead of the
 // MFMAs (two register stages), with one barrier per step.  Q4_0 weights are
 // staged as 16 * (code - 8) (two bit operations per 4 weights); the 16 is
-// taken out of the fp32 result at the end, exactly.
+// taken out of the fp32 result at the end, exactly, as is MXFP4's 2 (its
+// weights staged as the integers 2 * E2M1, its E8M0 row bytes as the fp16
+// powers of two they stand for).
 //
 // Per k-block each wave runs one v_mfma_i32_32x32x32_i8, whose K depth equals
 // the block size, so its int32 result is exactly the per-block integer dot.
@@ -103,7 +105,7 @@ __device__ __forceinline__ Offs<QT> make_offs(int64_t nkt, int64_t K, int tid)
         for (int i = 0; i < 2; i++)
             o.w[i] = tile + ((4 * c + 2 * hh + i) * 8 + g) * 4;
     }
-    o.dw = tile + Fmt<QT>::scale_off + 2 * l;
+    o.dw = tile + Fmt<QT>::scale_off + (QT == TQ_MXFP4 ? l : 2 * l);
     return o;
 }
 
@@ -113,7 +115,7 @@ struct StageRegs {
     uint16_t da;              // one activation block scale
     uint32_t w[Offs<QT>::NWD];// weight dwords (4-bit: rows 4g..4g+3 at column pairs
                               // 4c+2hh, 4c+2hh+1; Q8_0: rows 2p, 2p+1 at 8h+4hh .. +3)
-    uint16_t dw;              // weight row scale
+    uint16_t dw;              // weight row scale (MXFP4: its E8M0 byte)
     bool da_ok, dw_ok;        // the scales' k-blocks lie inside K
 };
 
@@ -140,7 +142,10 @@ __device__ __forceinline__ void load_step(StageRegs<QT> &s, const Ranges &rg, co
         // zeroed for blocks past K at store time (a select here would wait
         // for the load)
         s.da = __builtin_amdgcn_raw_buffer_load_b16(rg.d, o.da + kt0 * 2, 0, 0);
-        s.dw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + kt0 * TS, 0, 0);
+        if constexpr (QT == TQ_MXFP4)
+            s.dw = __builtin_amdgcn_raw_buffer_load_b8(rg.w, o.dw + kt0 * TS, 0, 0);
+        else
+            s.dw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + kt0 * TS, 0, 0);
         s.da_ok = kt0 + o.kba < nkt;
         s.dw_ok = kt0 + o.kbw < nkt;
     }
@@ -199,7 +204,8 @@ __device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds &L, int b
     }
     // both halves of the wave hold the same row scale: the duplicate store
     // writes the same bits and keeps the step free of branches
-    ((uint16_t *)&L.dw[buf][0][32 * tt + l])[kb] = s.dw_ok ? s.dw : (uint16_t)0;
+    const uint16_t dwb = (QT == TQ_MXFP4) ? e8m0_f16_bits(s.dw) : s.dw;
+    ((uint16_t *)&L.dw[buf][0][32 * tt + l])[kb] = s.dw_ok ? dwb : (uint16_t)0;
 }
 
 template <int QT, bool DOTS>
@@ -356,7 +362,7 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
         for (int r = 0; r < 16; r++) {
             const int64_t m = m0 + 32 * wm + 8 * (r >> 2) + 4 * lk + (r & 3);
             if (m < M)
-                y[m * ldy + n] = (QT == TQ_Q4_0) ? acc[r] * 0.0625f : acc[r];
+                y[m * ldy + n] = acc[r] * weight_unscale<QT>();
         }
     }
 }
@@ -392,6 +398,7 @@ hipError_t launch_qgemm(int type, const void *tiles, int64_t K, int64_t N, const
     case TQ_Q4_0: return launch_t<TQ_Q4_0>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
     case TQ_Q8_0: return launch_t<TQ_Q8_0>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
     case TQ_IQ4_NL: return launch_t<TQ_IQ4_NL>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_MXFP4: return launch_t<TQ_MXFP4>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
     }
     return hipErrorInvalidValue;
 }

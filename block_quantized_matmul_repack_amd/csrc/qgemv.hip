@@ -16,8 +16,10 @@
 // a quarter / half of the tile's column pairs, transposes bytes with
 // v_perm_b32, forms partial dots with v_dot4_i32_i8 and finishes each row's
 // 32-element block dot with quad DPP adds.  Lane l of the half then holds the
-// exact int32 block dot of row l, scales it by its fp16 row scale times the
-// fp16 activation scale (exact in fp32) and accumulates in fp32.
+// exact int32 block dot of row l, scales it by its fp16 row scale (MXFP4:
+// the power of two of its E8M0 byte) times the fp16 activation scale (exact
+// in fp32) and accumulates in fp32.  IQ4_NL and MXFP4 codes become int8
+// through a 16-entry table (MXFP4: 2 * E2M1, its half going to the scale).
 //   4-bit lanes: l = 4g + c reads rows 4g..4g+3 at column pairs 4c..4c+3
 //   (K 8c..8c+7).  Q8_0 lanes: l = 2p + h reads rows 2p, 2p+1 at column
 //   pairs 8h..8h+7 (K 16h..16h+15).  Each lane keeps its rows in slots
@@ -138,6 +140,8 @@ struct TileRegs<TQ_Q4_0> {
 };
 template <>
 struct TileRegs<TQ_IQ4_NL> : TileRegs<TQ_Q4_0> {};
+template <>
+struct TileRegs<TQ_MXFP4> : TileRegs<TQ_Q4_0> {};
 // Q8_0 tiles: 8 dwords (rows 2p, 2p+1 at column pairs 8h+i) and the row scale.
 template <>
 struct TileRegs<TQ_Q8_0> {
@@ -161,7 +165,7 @@ __device__ __forceinline__ void lds_tile(TileRegs<QT> &r, const uint8_t *tile, i
         for (int i = 0; i < 4; i++)
             r.a[i] = t[(4 * c + i) * 8 + g];
     }
-    r.sc = ((const uint16_t *)(tile + Fmt<QT>::scale_off))[l];
+    r.sc = tile_scale_bits<QT>(tile, l);
 }
 
 template <int QT, int MM>
@@ -173,6 +177,8 @@ struct ActRegs<TQ_Q4_0, MM> {
 };
 template <int MM>
 struct ActRegs<TQ_IQ4_NL, MM> : ActRegs<TQ_Q4_0, MM> {};
+template <int MM>
+struct ActRegs<TQ_MXFP4, MM> : ActRegs<TQ_Q4_0, MM> {};
 template <int MM>
 struct ActRegs<TQ_Q8_0, MM> {
     uint32_t v[MM][4];       // 16 consecutive K
@@ -283,9 +289,9 @@ __device__ __forceinline__ void block_dots(int (&s)[MM], const TileRegs<QT> &w,
 // unit goes to lane i % 64, register slot i / 64.
 template <int QT>
 struct Unit {
-    static constexpr int BYTES = 2 * Fmt<QT>::tile;       // 1152 (4-bit), 2176 (Q8_0)
-    static constexpr int CHUNKS = BYTES / 16;             // 72, 136
-    static constexpr int SLOTS = (CHUNKS + 63) / 64;      // 2, 3
+    static constexpr int BYTES = 2 * Fmt<QT>::tile;       // 1152 (4-bit), 2176 (Q8_0), 1088 (MXFP4)
+    static constexpr int CHUNKS = BYTES / 16;             // 72, 136, 68
+    static constexpr int SLOTS = (CHUNKS + 63) / 64;      // 2, 3, 2
     v4u c[SLOTS];
 };
 
@@ -515,10 +521,8 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                                     (QT == TQ_Q4_0) ? (dot[r] >> 4) : dot[r];
                         }
                     } else {
-                        float dw = f16_bits_to_f32(
-                            ((const uint16_t *)(tile + Fmt<QT>::scale_off))[l]);
-                        if constexpr (QT == TQ_Q4_0)
-                            dw *= 0.0625f;
+                        float dw = f16_bits_to_f32(tile_scale_bits<QT>(tile, l)) *
+                                   weight_unscale<QT>();
                         dw = valid ? dw : 0.0f;               // a missing second tile adds 0
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
@@ -546,9 +550,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                                 (QT == TQ_Q4_0) ? (s[m] >> 4) : s[m];
                     }
                 } else {
-                    float dw = f16_bits_to_f32(w.sc);
-                    if constexpr (QT == TQ_Q4_0)
-                        dw *= 0.0625f;
+                    float dw = f16_bits_to_f32(w.sc) * weight_unscale<QT>();
                     dw = valid ? dw : 0.0f;                   // a missing second tile adds 0
 #pragma unroll
                     for (int m = 0; m < MM; m++)
@@ -729,6 +731,7 @@ hipError_t launch_qgemv(int type, const void *tiles, int64_t K, int64_t N, const
     case TQ_Q4_0: return launch_t<TQ_Q4_0>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
     case TQ_Q8_0: return launch_t<TQ_Q8_0>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
     case TQ_IQ4_NL: return launch_t<TQ_IQ4_NL>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
+    case TQ_MXFP4: return launch_t<TQ_MXFP4>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
     }
     return hipErrorInvalidValue;
 }

@@ -10,10 +10,17 @@
 // is what both tile formats need:
 //   Q8_0: tile dword (cp, rp) = halfword cp of rows 2rp and 2rp+1, so a
 //         16-byte tile chunk is a 16-byte LDS read, stored as is;
-//   Q4_0 / IQ4_NL: tile byte (cp, r) = one nibble of each of quant bytes
-//         2h, 2h+1 of row r (h = cp mod 8; low nibbles for cp < 8, high for
-//         cp >= 8), built two rows at a time with shifts and masks.
+//   Q4_0 / IQ4_NL / MXFP4: tile byte (cp, r) = one nibble of each of quant
+//         bytes 2h, 2h+1 of row r (h = cp mod 8; low nibbles for cp < 8,
+//         high for cp >= 8), built two rows at a time with shifts and masks.
 // Store: every thread writes whole 16-byte chunks of the tiles.
+//
+// MXFP4 blocks are 17 bytes (one E8M0 byte, then the 16 quant bytes), so
+// most of them start at odd addresses: a block is read as the 5 aligned
+// dwords that cover it (the flat buffer is 4-byte aligned) and shifted into
+// place.
+#include <type_traits>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -24,22 +31,55 @@ constexpr int THREADS = 256;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// The MXFP4 block at byte a of the flat buffer (total bytes long): its E8M0
+// byte and its 8 quant halfwords.  The 5 covering dwords start at a & ~3;
+// the first four end before a + 16, inside the block; the fifth can pass the
+// end of the buffer only for its last block, and is then read bytewise.
+__device__ __forceinline__ void load_mx_block(const uint8_t *__restrict__ flat, int64_t a,
+                                              int64_t total, uint16_t (&q)[8], uint16_t &e)
+{
+    const int64_t A = a & ~int64_t(3);
+    const int sh = (int)(a - A);
+    uint32_t w[5];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        w[i] = *(const uint32_t *)(flat + A + 4 * i);
+    if (A + 20 <= total) {
+        w[4] = *(const uint32_t *)(flat + A + 16);
+    } else {
+        w[4] = 0;
+        for (int j = 0; j < 4 && A + 16 + j < total; j++)
+            w[4] |= (uint32_t)flat[A + 16 + j] << (8 * j);
+    }
+    e = (uint16_t)((w[0] >> (8 * sh)) & 0xFFu);
+    const int s1 = 8 * (sh + 1);                  // quants start 1..4 bytes into w[0]
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t v = (uint32_t)((((uint64_t)w[k + 1] << 32) | w[k]) >> s1);
+        q[2 * k] = (uint16_t)v;
+        q[2 * k + 1] = (uint16_t)(v >> 16);
+    }
+}
+
 template <int QT>
 __global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ flat,
                                                     int64_t nb, int64_t N,
                                                     uint8_t *__restrict__ tiles)
 {
-    constexpr int BB = Fmt<QT>::block;          // flat block bytes (fp16 d + quants)
-    constexpr int QH = (BB - 2) / 2;            // quant halfwords per block: 8 or 16
+    constexpr bool MX = QT == TQ_MXFP4;
+    constexpr int BB = Fmt<QT>::block;          // flat block bytes (scale + quants)
+    constexpr int QH = MX ? 8 : (BB - 2) / 2;   // quant halfwords per block: 8 or 16
     constexpr int TS = Fmt<QT>::tile;
-    constexpr int CH = TS / 16;                 // 16-byte chunks per tile: 36 or 68
-    constexpr int QCH = CH - 4;                 // chunks of quants (the last 4 hold scales)
+    constexpr int CH = TS / 16;                 // 16-byte chunks per tile: 36, 68 or 34
+    constexpr int QCH = Fmt<QT>::scale_off / 16;// chunks of quants (the rest hold scales)
+    using Scale = std::conditional_t<MX, uint8_t, uint16_t>;
+    constexpr int SPC = 16 / (int)sizeof(Scale);// row scales per 16-byte chunk
     // each tile's halfword columns padded by 16 bytes: the lanes of a store
     // differ in t, and a tile stride of 16 mod 256 bytes spreads them over
     // the LDS banks
     constexpr int TP = QH * 32 + 8;
     __shared__ __attribute__((aligned(16))) uint16_t qs[KT][TP];
-    __shared__ __attribute__((aligned(16))) uint16_t sc[KT][32];
+    __shared__ __attribute__((aligned(16))) Scale sc[KT][32];
 
     const int64_t ct = blockIdx.x;
     const int64_t kt0 = (int64_t)blockIdx.y * KT;
@@ -53,14 +93,18 @@ __global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ 
         uint16_t q[QH];
         uint16_t d = 0;
         if (n < N) {
-            const uint8_t *blk = flat + (n * nb + kt0 + t) * BB;
-            d = *(const uint16_t *)blk;
+            if constexpr (MX) {
+                load_mx_block(flat, (n * nb + kt0 + t) * BB, N * nb * BB, q, d);
+            } else {
+                const uint8_t *blk = flat + (n * nb + kt0 + t) * BB;
+                d = *(const uint16_t *)blk;
 #pragma unroll
-            for (int v = 0; v < QH / 8; v++) {
-                const u16x8u w = *(const u16x8u *)(blk + 2 + 16 * v);
+                for (int v = 0; v < QH / 8; v++) {
+                    const u16x8u w = *(const u16x8u *)(blk + 2 + 16 * v);
 #pragma unroll
-                for (int e = 0; e < 8; e++)
-                    q[8 * v + e] = w[e];
+                    for (int e = 0; e < 8; e++)
+                        q[8 * v + e] = w[e];
+                }
             }
         } else {
 #pragma unroll
@@ -70,7 +114,7 @@ __global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ 
 #pragma unroll
         for (int h = 0; h < QH; h++)
             qs[t][32 * h + r] = q[h];
-        sc[t][r] = d;
+        sc[t][r] = (Scale)d;
     }
     __syncthreads();
 
@@ -79,8 +123,8 @@ __global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ 
         const int t = i / CH, c = i - t * CH;
         u32x4 out;
         if (c >= QCH) {
-            // scale chunk: dwords of rows 8j .. 8j + 7
-            out = *(const u32x4 *)&sc[t][8 * (c - QCH)];
+            // scale chunk: rows SPC j .. SPC j + SPC - 1
+            out = *(const u32x4 *)&sc[t][SPC * (c - QCH)];
         } else if constexpr (QT == TQ_Q8_0) {
             // dwords (cp, rp .. rp + 3): halfword cp of rows 8j .. 8j + 7
             out = *(const u32x4 *)&qs[t][32 * (c >> 2) + 8 * (c & 3)];
@@ -123,6 +167,7 @@ hipError_t launch_repack(int type, const void *flat, int64_t K, int64_t N, void 
     case TQ_Q4_0: k_repack<TQ_Q4_0><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
     case TQ_IQ4_NL: k_repack<TQ_IQ4_NL><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
     case TQ_Q8_0: k_repack<TQ_Q8_0><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
+    case TQ_MXFP4: k_repack<TQ_MXFP4><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

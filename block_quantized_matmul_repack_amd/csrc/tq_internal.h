@@ -8,8 +8,9 @@
 
 namespace tq {
 
-// Tile geometry ("Block-32 Quantized Formats"): quant bytes, then 32 fp16
-// row scales at scale_off + 2*row.
+// Tile geometry ("Block-32 Quantized Formats"): quant bytes, then 32 row
+// scales at scale_off: fp16 at scale_off + 2*row, or for MXFP4 one E8M0 byte
+// at scale_off + row.  block = bytes of one flat GGML block.
 template <int QT> struct Fmt;
 template <> struct Fmt<TQ_Q4_0> {
     static constexpr int tile = 576, scale_off = 512, block = 18;
@@ -19,6 +20,9 @@ template <> struct Fmt<TQ_IQ4_NL> {
 };
 template <> struct Fmt<TQ_Q8_0> {
     static constexpr int tile = 1088, scale_off = 1024, block = 34;
+};
+template <> struct Fmt<TQ_MXFP4> {
+    static constexpr int tile = 544, scale_off = 512, block = 17;
 };
 
 // Raw buffer loads (CDNA buffer resource descriptor, stride 0): a load whose
@@ -43,7 +47,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                              0x00020000);
 }
 
-// IQ4_NL table as four little-endian dwords (entries 4i..4i+3 in dword i).
+// 16-entry int8 table of a 4-bit type (IQ4_NL: the caller's; MXFP4: 2 *
+// E2M1) as four little-endian dwords (entries 4i..4i+3 in dword i).
 struct Lut {
     uint32_t w[4];
 };
@@ -90,6 +95,32 @@ __device__ __forceinline__ float quad_max(float v)
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, true)));
     const int c = __builtin_bit_cast(int, v);
     return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, c, 0x4E, 0xF, 0xF, true)));
+}
+
+// MXFP4 ("MXFP4", Dequantization): the E8M0 row byte e as the fp16 power of
+// two whose exponent bits are clamp(e - 112, 0, 30) (field 0: +0.0).
+__device__ __forceinline__ uint16_t e8m0_f16_bits(uint32_t e)
+{
+    return (uint16_t)(min(max((int)e - 112, 0), 30) << 10);
+}
+
+// fp16 bits of tile row l's scale, read from the tile (LDS or global).
+template <int QT>
+__device__ __forceinline__ uint16_t tile_scale_bits(const uint8_t *tile, int l)
+{
+    if constexpr (QT == TQ_MXFP4)
+        return e8m0_f16_bits(tile[Fmt<QT>::scale_off + l]);
+    else
+        return ((const uint16_t *)(tile + Fmt<QT>::scale_off))[l];
+}
+
+// The kernels multiply integer weights that are a fixed power of two times
+// the format's: Q4_0 as 16 (code - 8) (the nibble in the high half of a
+// byte), MXFP4 as 2 * E2M1 (integers).  This factor undoes it, exactly.
+template <int QT>
+constexpr float weight_unscale()
+{
+    return QT == TQ_Q4_0 ? 0.0625f : (QT == TQ_MXFP4 ? 0.5f : 1.0f);
 }
 
 // Dynamic activation quantization of one 32-element K block ("Memory

@@ -20,12 +20,20 @@
  *            bytes 1024 + 2*row hold the fp16 scale d.  Weight = d * quant.
  *     IQ4_NL 576 B: the Q4_0 layout, each nibble an index into a 16-entry
  *            table.  Weight = d * lut[index].
+ *     MXFP4  544 B: the Q4_0 nibble layout of OCP FP4 (E2M1) codes; byte
+ *            512 + row holds row's E8M0 scale byte e.  Weight =
+ *            E2M1(code) * s(e), s(e) the fp16 power of two with exponent
+ *            bits clamp(e - 112, 0, 30): 2^(e-127) for 113 <= e <= 142, 0
+ *            for e <= 112, 2^15 for e > 142.  The kernels multiply the
+ *            integers 2 * E2M1(code) (0, 1, 2, 3, 4, 6, 8, 12 and their
+ *            negatives) by s(e) / 2, exactly.
  *   Rows n >= N of the last row-tile are zero (codes 0, scale +0.0).
  *
  *   Flat source ("repacked from flat row-major GGML layouts"): row n holds
  *   K/32 consecutive GGML blocks: Q4_0 / IQ4_NL = fp16 d + 16 bytes (low
  *   nibbles elements 0..15, high nibbles 16..31), 18 B; Q8_0 = fp16 d + 32
- *   int8, 34 B.
+ *   int8, 34 B; MXFP4 = E8M0 byte e + 16 bytes in the Q4_0 nibble order,
+ *   17 B.
  *
  *   Activations (section "Memory buffers": dynamically quantized activations,
  *   used as Q8_0 activation tiles by the vector dot of "Q2_0 Format"): per
@@ -68,7 +76,7 @@
 extern "C" {
 #endif
 
-typedef enum { TQ_Q4_0 = 0, TQ_Q8_0 = 1, TQ_IQ4_NL = 2 } tq_type;
+typedef enum { TQ_Q4_0 = 0, TQ_Q8_0 = 1, TQ_IQ4_NL = 2, TQ_MXFP4 = 3 } tq_type;
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 typedef enum {
     TQ_OK = 0,
@@ -82,11 +90,11 @@ typedef enum {
 /* Which kernel family tq_block_dots runs. */
 typedef enum { TQ_PATH_GEMV = 0, TQ_PATH_GEMM = 1 } tq_path;
 
-/* Bytes of one tile ("Block-32 Quantized Formats"): 576, 1088, 576; 0 for an
- * unknown type. */
+/* Bytes of one tile ("Block-32 Quantized Formats"): 576, 1088, 576, 544; 0
+ * for an unknown type. */
 size_t tq_tile_bytes(int type);
 
-/* Bytes of one flat GGML block: 18, 34, 18; 0 for an unknown type. */
+/* Bytes of one flat GGML block: 18, 34, 18, 17; 0 for an unknown type. */
 size_t tq_block_bytes(int type);
 
 /* (K/32) * ((N+31)/32) * tq_tile_bytes(type) ("Tile Dimensions and Grid
@@ -105,7 +113,8 @@ const char *tq_status_string(int status);
 
 /* Repack flat GGML blocks into tiles ("Tiled Weight Formats": repacking at
  * model load or at run time).
- *   flat  : device, tq_flat_bytes(type, K, N) bytes, 2-byte aligned.
+ *   flat  : device, tq_flat_bytes(type, K, N) bytes, 2-byte aligned
+ *           (TQ_MXFP4: 4-byte aligned).
  *   tiles : device, tq_tiled_bytes(type, K, N) bytes, 16-byte aligned; fully
  *           written, padding rows included.  Must not overlap `flat`.
  * Bit-exact byte permutation; deterministic. */
@@ -133,7 +142,8 @@ size_t tq_qgemv_workspace_bytes(int type, int64_t K, int64_t N, int64_t M);
  *           aligned, d 2-byte aligned.
  *   M     : 1..8 (else TQ_E_SHAPE).
  *   lut   : host, 16 int8 table entries for TQ_IQ4_NL (required), ignored
- *           (may be NULL) for the other types.
+ *           (may be NULL) for the other types (TQ_MXFP4's values are fixed
+ *           by E2M1).
  *   y     : device fp32, y[m*ldy + n] written for m < M, n < N only;
  *           ldy >= N; 4-byte aligned.
  *   workspace, workspace_bytes : optional device scratch, 256-byte aligned,
@@ -185,7 +195,9 @@ int tq_matmul(int type, const void *tiles, int64_t K, int64_t N,
 /* Test instrument: run the tq_qgemv (path TQ_PATH_GEMV, M <= 8) or tq_qgemm
  * (TQ_PATH_GEMM) kernel with the integer block dots as output instead of y:
  * isum[(m*N + n)*(K/32) + kt] (int32, device, 4-byte aligned) =
- * sum_{j<32} w_int[n][32kt+j] * q[m][32kt+j], for m < M, n < N. */
+ * sum_{j<32} w_int[n][32kt+j] * q[m][32kt+j], for m < M, n < N, with w_int
+ * = code - 8 (Q4_0), the int8 (Q8_0), lut[code] (IQ4_NL) or 2 * E2M1(code)
+ * (MXFP4). */
 int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N,
                   const int8_t *q, int64_t M, const int8_t *lut,
                   int32_t *isum, int path, hipStream_t stream);

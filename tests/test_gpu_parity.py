@@ -15,8 +15,8 @@ from gpu_helpers import check_y, make, tiles_slice, to_dev_act
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-Q4_0, Q8_0, IQ4_NL = synth.Q4_0, synth.Q8_0, synth.IQ4_NL
-TYPES = [Q4_0, Q8_0, IQ4_NL]
+Q4_0, Q8_0, IQ4_NL, MXFP4 = synth.Q4_0, synth.Q8_0, synth.IQ4_NL, synth.MXFP4
+TYPES = [Q4_0, Q8_0, IQ4_NL, MXFP4]
 LUT = synth.IQ4_NL_STANDIN_LUT
 
 
@@ -282,3 +282,40 @@ def test_qgemv_x_row_stride(tq):
     qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
     y2 = tq.qgemv(Q8_0, tdev, K, N, qd, dd)
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("offset", [4, 8, 12])
+def test_mxfp4_repack_flat_offsets(tq, offset):
+    """17-byte MXFP4 blocks start at every byte phase; moving the whole flat
+    buffer by 4..12 bytes changes the phase of every dword the kernel reads,
+    and the buffer ends exactly at its last block."""
+    K, N = 96, 35
+    inp = make(MXFP4, K, N, 1, seed=offset)
+    ref = oracle.repack(MXFP4, inp.flat, K, N)
+    big = torch.zeros(inp.flat.size + offset, dtype=torch.uint8, device="cuda")
+    big[offset:] = torch.from_numpy(inp.flat).cuda()
+    got = tq.repack_tiles(MXFP4, big[offset:], K, N).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_mxfp4_every_scale_byte(tq):
+    """Every E8M0 byte 0..255 (the zero, normal and clamped ranges) and every
+    code, through both kernels: block dots bit-exact, y within tolerance."""
+    K, N, M = 64, 256, 3
+    rng = np.random.default_rng(17)
+    codes = synth.draw_codes(rng, MXFP4, N, K)
+    e = np.stack([np.arange(256), np.arange(256)[::-1]], axis=1).astype(np.uint16)
+    flat = synth.pack_flat(MXFP4, codes, e)
+    x = synth.draw_activations(rng, M, K)
+    tiles = oracle.repack(MXFP4, flat, K, N)
+    q, d = oracle.quantize_act(x)
+    tdev = tq.repack_tiles(MXFP4, torch.from_numpy(flat).cuda(), K, N)
+    assert np.array_equal(tdev.cpu().numpy(), tiles)
+    qd, dd = tq.quantize_act(torch.from_numpy(x).cuda())
+    ref = oracle.block_dots(MXFP4, tiles, K, N, q)
+    y_ref, acond = oracle.matmul(MXFP4, tiles, K, N, q, d)
+    for path, fn in ((tq.PATH_GEMV, tq.qgemv), (tq.PATH_GEMM, tq.qgemm)):
+        got = tq.block_dots(MXFP4, tdev, K, N, qd, path=path).cpu().numpy()
+        assert np.array_equal(got, ref), path
+        y = fn(MXFP4, tdev, K, N, qd, dd).cpu().numpy()
+        check_y(y, y_ref, acond, ("mxfp4 scales", path))
