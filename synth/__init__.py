@@ -161,4 +161,7 @@ WORKLOADS = {
     "q8_0_lmhead_k4096_n128001_m1": Workload("q8_0_lmhead_k4096_n128001_m1", Q8_0, 4096, 128001, 1, "absnormal"),
     "q8_0_lmhead_k4096_n128001_m128": Workload("q8_0_lmhead_k4096_n128001_m128", Q8_0, 4096, 128001, 128,
                                                "absnormal", path="qgemm"),
+    "mxfp4_gemv_k4096_n14336_m1": Workload("mxfp4_gemv_k4096_n14336_m1", MXFP4, 4096, 14336, 1, "e8m0"),
+    "mxfp4_gemm_m512_k4096_n4096": Workload("mxfp4_gemm_m512_k4096_n4096", MXFP4, 4096, 4096, 512,
+                                            "e8m0", act_dtype="bf16", path="qgemm"),
 }
