@@ -193,8 +193,7 @@ __device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds &L, int b
                 lo = (t << 4) & 0xF0F0F0F0u;              // 16 * (even-column code - 8)
                 hi = t & 0xF0F0F0F0u;                     // 16 * (odd-column code - 8)
             } else {
-                lo = lut16(pr & 0x0F0F0F0Fu, lut);
-                hi = lut16((pr >> 4) & 0x0F0F0F0Fu, lut);
+                lut16x2(pr, lut, lo, hi);
             }
             const uint32_t r0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // row 2r:   K +0..+3
             const uint32_t r1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // row 2r+1: K +0..+3

@@ -122,8 +122,7 @@ __device__ __forceinline__ v4i_t tile_operand(const uint8_t *tile, int off, cons
             lo[i] = (t << 4) & 0xF0F0F0F0u;
             hi[i] = t & 0xF0F0F0F0u;
         } else {
-            lo[i] = lut16(x & 0x0F0F0F0Fu, lut);
-            hi[i] = lut16((x >> 4) & 0x0F0F0F0Fu, lut);
+            lut16x2(x, lut, lo[i], hi[i]);
         }
     }
     return v4i_t{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
@@ -160,10 +159,14 @@ __device__ __forceinline__ void lds_tile(TileRegs<QT> &r, const uint8_t *tile, i
         for (int i = 0; i < 8; i++)
             r.a[i] = t[(8 * h + i) * 16 + p];
     } else {
+        // slot i holds column pair 4c + ((i + c) & 3): the 4 lanes of a quad
+        // (c = 0..3) read 4 different bank groups instead of one address 32
+        // dwords apart each, so the 32 lanes of a half read 32 banks; the
+        // staged activations carry the same rotation (rot_act)
         const int g = l >> 2, c = l & 3;
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            r.a[i] = t[(4 * c + i) * 8 + g];
+            r.a[i] = t[(4 * c + ((i + c) & 3)) * 8 + g];
     }
     r.sc = tile_scale_bits<QT>(tile, l);
 }
@@ -187,8 +190,9 @@ struct ActRegs<TQ_Q8_0, MM> {
 
 // Staged activations of one pass: tile tp's 32 int8 of row m at
 // qs[(tp * MM + m) * 32] -- for 4-bit weights as the 16 even K then the 16
-// odd K, so that a lane's even and odd words come out of LDS ready for the
-// nibble dot products -- and its scale, as fp32, at ds[tp * MM + m].
+// odd K, each word c rotated by rot_act, so that a lane's even and odd words
+// come out of LDS ready for the nibble dot products -- and its scale, as
+// fp32, at ds[tp * MM + m].
 template <int QT, int MM>
 __device__ __forceinline__ void lds_act(ActRegs<QT, MM> &r, const int8_t *qs, const float *ds,
                                         int tp, int l)
@@ -208,6 +212,15 @@ __device__ __forceinline__ void lds_act(ActRegs<QT, MM> &r, const int8_t *qs, co
         }
         r.d[m] = ds[tp * MM + m];
     }
+}
+
+// Activation word c (4 even or 4 odd K of K 8c .. 8c + 7) of a tile, as the
+// v_dot4 path stages it for 4-bit weights: rotated right by c bytes, so that
+// its byte b meets the weights of column pair 4c + ((b + c) & 3), the order
+// in which lds_tile reads them.
+__device__ __forceinline__ uint32_t rot_act(uint32_t w, int c)
+{
+    return __builtin_amdgcn_alignbyte(w, w, (uint32_t)c);
 }
 
 // Even-K / odd-K split of 8 consecutive int8 (K 8c .. 8c + 7) into the two
@@ -264,8 +277,7 @@ __device__ __forceinline__ void block_dots(int (&s)[MM], const TileRegs<QT> &w,
                 ev[j] = (t << 4) & 0xF0F0F0F0u;               // 16 * (even-column code - 8)
                 od[j] = t & 0xF0F0F0F0u;                      // 16 * (odd-column code - 8)
             } else {
-                ev[j] = lut16(tr[j] & 0x0F0F0F0Fu, lut);
-                od[j] = lut16((tr[j] >> 4) & 0x0F0F0F0Fu, lut);
+                lut16x2(tr[j], lut, ev[j], od[j]);
             }
         }
 #pragma unroll
@@ -382,8 +394,12 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
         if constexpr (QT == TQ_Q8_0) {
             *(uint4 *)(qb + 16 * h) = v;
         } else {
-            const uint2 a = split_even_odd(make_uint2(v.x, v.y));
-            const uint2 b = split_even_odd(make_uint2(v.z, v.w));
+            uint2 a = split_even_odd(make_uint2(v.x, v.y));     // words 2h
+            uint2 b = split_even_odd(make_uint2(v.z, v.w));     // and 2h + 1
+            if constexpr (!MMA) {
+                a = make_uint2(rot_act(a.x, 2 * h), rot_act(a.y, 2 * h));
+                b = make_uint2(rot_act(b.x, 2 * h + 1), rot_act(b.y, 2 * h + 1));
+            }
             *(uint2 *)(qb + HS * h) = make_uint2(a.x, b.x);
             *(uint2 *)(qb + HS * h + ODD) = make_uint2(a.y, b.y);
         }
@@ -469,7 +485,9 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                     if constexpr (QT == TQ_Q8_0) {
                         *(uint2 *)(qb + 8 * c) = qv;
                     } else {
-                        const uint2 eo = split_even_odd(qv);
+                        uint2 eo = split_even_odd(qv);
+                        if constexpr (!MMA)
+                            eo = make_uint2(rot_act(eo.x, c), rot_act(eo.y, c));
                         *(uint32_t *)(qb + HS * (c >> 1) + 4 * (c & 1)) = eo.x;
                         *(uint32_t *)(qb + HS * (c >> 1) + 4 * (c & 1) + ODD) = eo.y;
                     }

@@ -150,21 +150,32 @@ __device__ __forceinline__ void quant_quad(const float (&v)[8], uint2 &q, uint16
 
 typedef uint32_t u32x2u __attribute__((ext_vector_type(2), aligned(4)));
 
-// 4 table lookups at once: idx holds four byte indices 0..15; returns the four
-// int8 table entries in the same byte positions.  v_perm_b32 selects any byte
-// of an 8-byte pair, so the two table halves are looked up separately and
-// merged on bit 3 of each index.
-__device__ __forceinline__ uint32_t lut16(uint32_t idx, const Lut &t)
+// 0xFF in each byte of v whose bit 7 is set, else 0x00: v_perm_b32's sign
+// selectors (8, 9: bits 15, 31 of the second operand; 10, 11: of the first)
+// read bytes 1 and 3 only, so v << 8 brings bytes 0 and 2 there.
+__device__ __forceinline__ uint32_t byte_sign_mask(uint32_t v)
 {
-    const uint32_t sel = idx & 0x07070707u;
-    const uint32_t lo = __builtin_amdgcn_perm(t.w[1], t.w[0], sel);
-    const uint32_t hi = __builtin_amdgcn_perm(t.w[3], t.w[2], sel);
-    // m = 0xFF in the bytes whose index has bit 3 set: shifted to each byte's
-    // sign bit, then replicated by v_perm's sign selectors (8, 9: signs of
-    // bytes 1, 3 of the second operand; 10, 11: of bytes 1, 3 of the first)
-    const uint32_t sb = idx << 4;
-    const uint32_t m = __builtin_amdgcn_perm(sb, sb << 8, 0x0B090A08u);
-    return (hi & m) | (lo & ~m);
+    return __builtin_amdgcn_perm(v, v << 8, 0x0B090A08u);
+}
+
+// Table lookups of the 8 nibbles of x at once: ev gets the int8 table entries
+// of the low nibbles (byte b: entry of bits 4b..4b+3), od those of the high
+// nibbles.  v_perm_b32 picks any byte of an 8-byte pair, so each half of the
+// table is looked up with the nibble's low 3 bits and the two results are
+// merged on its bit 3 (bit 7 of the byte for a high nibble, bit 3 shifted
+// there for a low one).  14 VALU operations for 8 lookups.
+__device__ __forceinline__ void lut16x2(uint32_t x, const Lut &t, uint32_t &ev, uint32_t &od)
+{
+    const uint32_t se = x & 0x07070707u;
+    const uint32_t so = (x >> 4) & 0x07070707u;
+    const uint32_t me = byte_sign_mask(x << 4);
+    const uint32_t mo = byte_sign_mask(x);
+    const uint32_t le = __builtin_amdgcn_perm(t.w[1], t.w[0], se);
+    const uint32_t he = __builtin_amdgcn_perm(t.w[3], t.w[2], se);
+    const uint32_t lo = __builtin_amdgcn_perm(t.w[1], t.w[0], so);
+    const uint32_t ho = __builtin_amdgcn_perm(t.w[3], t.w[2], so);
+    ev = (he & me) | (le & ~me);
+    od = (ho & mo) | (lo & ~mo);
 }
 
 // K-split of the decode GEMV: S workgroups per stripe (a power of two),
