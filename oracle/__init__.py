@@ -12,7 +12,8 @@ the reading taken wherever the page is silent.  Arrays are numpy, C-contiguous.
 Parity pins: see tests/test_oracle_*.py.  The flat GGML block nibble order
 (flat_decode, and through it the input side of repack) is "parity unpinned":
 the page does not print the flat layout; for MXFP4 the flat block (one E8M0
-byte, then 16 nibble bytes) is unpinned for the same reason.
+byte, then 16 nibble bytes) and for Q4_1 (fp16 d, fp16 m, then 16 nibble
+bytes) are unpinned for the same reason.
 """
 import ctypes
 import os
@@ -21,7 +22,7 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, Q8_0, IQ4_NL, MXFP4 = 0, 1, 2, 3
+Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1 = 0, 1, 2, 3, 4
 F32, BF16, F16 = 0, 1, 2
 
 _lib = None
@@ -41,7 +42,7 @@ def lib():
         L.or_f32_to_f16.restype = ctypes.c_uint16
         L.or_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.or_bf16_to_f32.restype = ctypes.c_float
-        for f in ("or_tile_bytes", "or_block_bytes"):
+        for f in ("or_tile_bytes", "or_block_bytes", "or_scale_count"):
             getattr(L, f).argtypes = [ctypes.c_int]
             getattr(L, f).restype = l
         for f in ("or_tiled_bytes", "or_flat_bytes"):
@@ -118,12 +119,22 @@ def row_scale(t, s):
     return lib().or_row_scale(t, int(s))
 
 
+def scale_count(t):
+    return lib().or_scale_count(t)
+
+
+def _scales_array(t, N, nb):
+    ns = scale_count(t)
+    return np.zeros((N, nb) if ns == 1 else (N, nb, ns), np.uint16)
+
+
 def flat_decode(t, flat, K, N):
-    """Flat GGML blocks -> (codes uint8 [N,K], scale bits uint16 [N,K/32])."""
+    """Flat GGML blocks -> (codes uint8 [N,K], scale bits uint16 [N,K/32]);
+    for Q4_1 the scales are [N,K/32,2] (d, m)."""
     flat = _c(flat, np.uint8)
     assert flat.size == flat_bytes(t, K, N)
     codes = np.zeros((N, K), np.uint8)
-    scales = np.zeros((N, K // 32), np.uint16)
+    scales = _scales_array(t, N, K // 32)
     lib().or_flat_decode(t, _p(flat), K, N, _p(codes), _p(scales))
     return codes, scales
 
@@ -138,11 +149,11 @@ def repack(t, flat, K, N):
 
 
 def unpack(t, tiles, K, N):
-    """Tiled bytes -> (codes uint8 [N,K], scale bits uint16 [N,K/32])."""
+    """Tiled bytes -> (codes uint8 [N,K], scale bits as flat_decode)."""
     tiles = _c(tiles, np.uint8)
     assert tiles.size == tiled_bytes(t, K, N)
     codes = np.zeros((N, K), np.uint8)
-    scales = np.zeros((N, K // 32), np.uint16)
+    scales = _scales_array(t, N, K // 32)
     lib().or_unpack(t, _p(tiles), K, N, _p(codes), _p(scales))
     return codes, scales
 

@@ -9,7 +9,7 @@
  * Source of every definition: the page "Hexagon backend developer details"
  * (llama.cpp docs/backend/snapdragon/developer.md), section "Tiled Weight
  * Formats" with its subsections "Tile Dimensions and Grid Layout" and
- * "Block-32 Quantized Formats" (Q4_0, Q8_0, IQ4_NL, MXFP4), and section "Memory
+ * "Block-32 Quantized Formats" (Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1), and section "Memory
  * buffers" (dynamically quantized activations).  Where the page is silent the
  * reading taken is stated at the function.
  *
@@ -27,7 +27,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_IQ4_NL = 2, OR_MXFP4 = 3 };
+enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_IQ4_NL = 2, OR_MXFP4 = 3, OR_Q4_1 = 4 };
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
 
 /* ---------------------------------------------------------------------------
@@ -107,6 +107,7 @@ long or_tile_bytes(int type)
     case OR_Q8_0: return 1088;
     case OR_IQ4_NL: return 576;
     case OR_MXFP4: return 544;
+    case OR_Q4_1: return 640;
     }
     return 0;
 }
@@ -118,9 +119,13 @@ long or_block_bytes(int type)
     case OR_Q8_0: return 34;
     case OR_IQ4_NL: return 18;
     case OR_MXFP4: return 17;
+    case OR_Q4_1: return 20;
     }
     return 0;
 }
+
+/* Scale values per row and block: Q4_1 keeps a pair (d, m), the others one. */
+long or_scale_count(int type) { return type == OR_Q4_1 ? 2 : 1; }
 
 /* "Tile Dimensions and Grid Layout": n_k_tiles = ne0 / 32, n_col_tiles =
  * (ne1 + 31) / 32, with ne0 = K and ne1 = N. */
@@ -141,28 +146,36 @@ long or_flat_bytes(int type, long K, long N)
  * a Q4_0 / IQ4_NL block is an fp16 scale followed by 16 bytes whose low
  * nibbles are elements 0..15 and high nibbles elements 16..31; a Q8_0 block is
  * an fp16 scale followed by 32 int8 elements; an MXFP4 block is one E8M0
- * scale byte followed by 16 bytes with the Q4_0 nibble order.
+ * scale byte followed by 16 bytes with the Q4_0 nibble order; a Q4_1 block is
+ * the fp16 scale d, the fp16 min m, then 16 bytes with the Q4_0 nibble order.
  *
  * codes[n*K + k] receives the raw code of element k of row n: 0..15 for the
- * 4-bit types, the int8 byte (as uint8) for Q8_0.  scales[n*(K/32) + b]
- * receives the fp16 bits of block b of row n (MXFP4: the E8M0 byte).
+ * 4-bit types, the int8 byte (as uint8) for Q8_0.  scales[(n*(K/32) + b)*ns
+ * + i], ns = or_scale_count(type), receives scale value i of block b of row
+ * n: the fp16 bits (MXFP4: the E8M0 byte; Q4_1: i = 0 is d, i = 1 is m).
  * ------------------------------------------------------------------------- */
-static long quant_offset(int type) { return type == OR_MXFP4 ? 1 : 2; }
-
-static uint16_t block_scale(int type, const uint8_t *blk)
+static long quant_offset(int type)
 {
-    return type == OR_MXFP4 ? blk[0] : (uint16_t)(blk[0] | (blk[1] << 8));
+    return type == OR_MXFP4 ? 1 : (type == OR_Q4_1 ? 4 : 2);
+}
+
+static uint16_t block_scale(int type, const uint8_t *blk, int i)
+{
+    if (type == OR_MXFP4)
+        return blk[0];
+    return (uint16_t)(blk[2 * i] | (blk[2 * i + 1] << 8));
 }
 
 void or_flat_decode(int type, const uint8_t *flat, long K, long N,
                     uint8_t *codes, uint16_t *scales)
 {
-    long nb = K / 32, bb = or_block_bytes(type);
+    long nb = K / 32, bb = or_block_bytes(type), ns = or_scale_count(type);
     for (long n = 0; n < N; n++) {
         for (long b = 0; b < nb; b++) {
             const uint8_t *blk = flat + (n * nb + b) * bb;
             const uint8_t *qs = blk + quant_offset(type);
-            scales[n * nb + b] = block_scale(type, blk);
+            for (int i = 0; i < ns; i++)
+                scales[(n * nb + b) * ns + i] = block_scale(type, blk, i);
             for (int j = 0; j < 32; j++) {
                 uint8_t c;
                 if (type == OR_Q8_0)
@@ -203,33 +216,40 @@ static uint8_t code_at(int type, const uint8_t *flat, long K, long n, long k)
     return j < 16 ? (qs[j] & 0x0f) : (qs[j - 16] >> 4);
 }
 
-static uint16_t scale_at(int type, const uint8_t *flat, long K, long n, long kt)
+static uint16_t scale_at(int type, const uint8_t *flat, long K, long n, long kt, int i)
 {
     long nb = K / 32, bb = or_block_bytes(type);
-    return block_scale(type, flat + (n * nb + kt) * bb);
+    return block_scale(type, flat + (n * nb + kt) * bb, i);
 }
 
 /* Tile scale bytes: 32 fp16 at 512 (Q4_0, IQ4_NL) or 1024 (Q8_0); MXFP4: 32
- * single E8M0 bytes at 512 ("MXFP4": bytes 512..543). */
-static long scale_offset(int type) { return type == OR_Q8_0 ? 1024 : 512; }
-
-static void put_tile_scale(int type, uint8_t *tile, int row, uint16_t s)
+ * single E8M0 bytes at 512 ("MXFP4": bytes 512..543); Q4_1: 32 fp16 pairs at
+ * 512, d of row r at 512 + 4r and m at 512 + 4r + 2 ("Q4_1": scale[2*row] =
+ * d, scale[2*row + 1] = m). */
+static long scale_byte(int type, int row, int i)
 {
-    if (type == OR_MXFP4) {
-        tile[512 + row] = (uint8_t)s;
-    } else {
-        long so = scale_offset(type);
-        tile[so + 2 * row + 0] = (uint8_t)(s & 0xff);
-        tile[so + 2 * row + 1] = (uint8_t)(s >> 8);
+    switch (type) {
+    case OR_MXFP4: return 512 + row;
+    case OR_Q4_1: return 512 + 4 * row + 2 * i;
+    case OR_Q8_0: return 1024 + 2 * row;
     }
+    return 512 + 2 * row;
 }
 
-static uint16_t get_tile_scale(int type, const uint8_t *tile, int row)
+static void put_tile_scale(int type, uint8_t *tile, int row, int i, uint16_t s)
 {
+    long o = scale_byte(type, row, i);
+    tile[o] = (uint8_t)(s & 0xff);
+    if (type != OR_MXFP4)
+        tile[o + 1] = (uint8_t)(s >> 8);
+}
+
+static uint16_t get_tile_scale(int type, const uint8_t *tile, int row, int i)
+{
+    long o = scale_byte(type, row, i);
     if (type == OR_MXFP4)
-        return tile[512 + row];
-    long so = scale_offset(type);
-    return (uint16_t)(tile[so + 2 * row] | (tile[so + 2 * row + 1] << 8));
+        return tile[o];
+    return (uint16_t)(tile[o] | (tile[o + 1] << 8));
 }
 
 void or_repack(int type, const uint8_t *flat, long K, long N, uint8_t *tiles)
@@ -253,13 +273,15 @@ void or_repack(int type, const uint8_t *flat, long K, long N, uint8_t *tiles)
                         tile[cp * 32 + row] = (uint8_t)((c1 << 4) | c0);
                     }
                 }
-                put_tile_scale(type, tile, row, valid ? scale_at(type, flat, K, n, kt) : 0);
+                for (int i = 0; i < or_scale_count(type); i++)
+                    put_tile_scale(type, tile, row, i, valid ? scale_at(type, flat, K, n, kt, i) : 0);
             }
         }
     }
 }
 
-/* Inverse of or_repack for rows n < N: codes[n*K + k], scales[n*(K/32)+kt]. */
+/* Inverse of or_repack for rows n < N: codes[n*K + k], scales[(n*(K/32) +
+ * kt)*ns + i] as or_flat_decode. */
 void or_unpack(int type, const uint8_t *tiles, long K, long N,
                uint8_t *codes, uint16_t *scales)
 {
@@ -279,7 +301,9 @@ void or_unpack(int type, const uint8_t *tiles, long K, long N,
                     c = (col & 1) ? (tile[cp * 32 + row] >> 4) : (tile[cp * 32 + row] & 0x0f);
                 codes[n * K + kt * 32 + col] = c;
             }
-            scales[n * n_k_tiles + kt] = get_tile_scale(type, tile, row);
+            for (int i = 0; i < or_scale_count(type); i++)
+                scales[(n * n_k_tiles + kt) * or_scale_count(type) + i] =
+                    get_tile_scale(type, tile, row, i);
         }
     }
 }
@@ -296,6 +320,9 @@ void or_unpack(int type, const uint8_t *tiles, long K, long N,
  * mantissa (bit 0); its value is +-0.5*m for exponent 0 and
  * +-2^(e-1) * (1 + m/2) otherwise.  The integer weight is twice that value
  * (0, 1, 2, 3, 4, 6, 8, 12 with sign), the factor 1/2 going to the scale.
+ * Q4_1 ("Q4_1": a scale d and a min m per row): the integer weight is the
+ * code itself, 0..15, and the weight value d * code + m (GGML's Q4_1); the
+ * block dot is that of the codes, the min enters only the matmul.
  * ------------------------------------------------------------------------- */
 static int e2m1_twice(uint8_t code)
 {
@@ -311,6 +338,7 @@ static int weight_value(int type, uint8_t code, const int8_t *lut)
     case OR_Q8_0: return (int)(int8_t)code;
     case OR_IQ4_NL: return (int)lut[code & 0x0f];
     case OR_MXFP4: return e2m1_twice(code & 0x0f);
+    case OR_Q4_1: return (int)code;
     }
     return 0;
 }
@@ -447,13 +475,17 @@ void or_matmul(int type, const uint8_t *tiles, long K, long N,
         int row = (int)(n % 32);
         for (long kt = 0; kt < nb; kt++) {
             const uint8_t *tile = tiles + (ct * nb + kt) * ts;
-            double dw = or_row_scale(type, get_tile_scale(type, tile, row));
+            double dw = or_row_scale(type, get_tile_scale(type, tile, row, 0));
+            /* Q4_1: w = d * code + m (GGML's Q4_1; "Q4_1" names the pair d,
+             * the scale, and m, the min) */
+            double mw = (type == OR_Q4_1)
+                ? (double)or_f16_to_f32(get_tile_scale(type, tile, row, 1)) : 0.0;
             for (int col = 0; col < 32; col++) {
                 int cp = col / 2;
                 uint8_t c = (type == OR_Q8_0)
                     ? tile[cp * 64 + 2 * row + (col & 1)]
                     : ((col & 1) ? (tile[cp * 32 + row] >> 4) : (tile[cp * 32 + row] & 0x0f));
-                wrow[kt * 32 + col] = dw * (double)weight_value(type, c, lut);
+                wrow[kt * 32 + col] = dw * (double)weight_value(type, c, lut) + mw;
             }
         }
         for (long m = 0; m < M; m++) {

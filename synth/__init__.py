@@ -13,16 +13,17 @@ consecutive blocks; a Q4_0 / IQ4_NL block is 2 bytes of fp16 scale followed by
 16 bytes whose low nibbles are elements 0..15 and high nibbles elements
 16..31; a Q8_0 block is 2 bytes of fp16 scale followed by 32 int8 elements;
 an MXFP4 block is 1 byte of E8M0 scale followed by 16 nibble bytes ordered
-as in Q4_0.
+as in Q4_0; a Q4_1 block is 2 bytes of fp16 scale d, 2 bytes of fp16 min m,
+then 16 nibble bytes ordered as in Q4_0.
 """
 import dataclasses
 
 import numpy as np
 
-Q4_0, Q8_0, IQ4_NL, MXFP4 = 0, 1, 2, 3
-TYPE_NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", IQ4_NL: "iq4_nl", MXFP4: "mxfp4"}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, IQ4_NL: 18, MXFP4: 17}
-TILE_BYTES = {Q4_0: 576, Q8_0: 1088, IQ4_NL: 576, MXFP4: 544}
+Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1 = 0, 1, 2, 3, 4
+TYPE_NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", IQ4_NL: "iq4_nl", MXFP4: "mxfp4", Q4_1: "q4_1"}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, IQ4_NL: 18, MXFP4: 17, Q4_1: 20}
+TILE_BYTES = {Q4_0: 576, Q8_0: 1088, IQ4_NL: 576, MXFP4: 544, Q4_1: 640}
 
 # Stand-in for the 16-entry non-linear IQ4_NL table.  The page names the table
 # but does not print its values; any 16 int8 entries keep the integer path
@@ -54,10 +55,17 @@ def draw_scales(rng, dist, N, K):
     'absnormal' -> fp16 of |N(0,1)| * 0.01 (drawn in float64, cast to float32,
     then to fp16 by numpy, round to nearest even); 'e8m0' -> MXFP4 E8M0 bytes
     uniform in [118, 124], power-of-two scales 2^-9 .. 2^-3 (with E2M1 values
-    up to 6, weights of magnitude up to about 0.75)."""
+    up to 6, weights of magnitude up to about 0.75); 'minmax' -> Q4_1 pairs
+    [N, K/32, 2]: d = fp16 of U[1e-3, 1e-2), m = fp16 of -d * U[6, 10] (a
+    block min below zero, codes 0..15 spanning [m, m + 15 d])."""
     shape = (N, K // 32)
     if dist == "e8m0":
         return rng.integers(118, 125, size=shape).astype(np.uint16)
+    if dist == "minmax":
+        d = rng.uniform(1e-3, 1e-2, size=shape)
+        m = -d * rng.uniform(6.0, 10.0, size=shape)
+        pair = np.stack([d, m], axis=-1)
+        return pair.astype(np.float32).astype(np.float16).view(np.uint16)
     if dist == "uniform":
         s = rng.uniform(1e-3, 1e-2, size=shape)
     elif dist == "absnormal":
@@ -68,17 +76,19 @@ def draw_scales(rng, dist, N, K):
 
 
 def pack_flat(qtype, codes, scale_bits):
-    """Write codes [N, K] and scale bits [N, K/32] (fp16, or E8M0 bytes for
-    MXFP4) as flat GGML blocks."""
+    """Write codes [N, K] and scale bits [N, K/32] (fp16, E8M0 bytes for
+    MXFP4, [N, K/32, 2] fp16 (d, m) pairs for Q4_1) as flat GGML blocks."""
     N, K = codes.shape
     nb = K // 32
     bb = BLOCK_BYTES[qtype]
+    ns = 2 if qtype == Q4_1 else 1
     out = np.empty((N, nb, bb), np.uint8)
-    sb = np.ascontiguousarray(scale_bits, dtype=np.uint16).reshape(N, nb)
-    out[:, :, 0] = (sb & 0xFF).astype(np.uint8)
-    if qtype != MXFP4:
-        out[:, :, 1] = (sb >> 8).astype(np.uint8)
-    q0 = 1 if qtype == MXFP4 else 2
+    sb = np.ascontiguousarray(scale_bits, dtype=np.uint16).reshape(N, nb, ns)
+    for i in range(ns):
+        out[:, :, 2 * i] = (sb[:, :, i] & 0xFF).astype(np.uint8)
+        if qtype != MXFP4:
+            out[:, :, 2 * i + 1] = (sb[:, :, i] >> 8).astype(np.uint8)
+    q0 = {MXFP4: 1, Q4_1: 4}.get(qtype, 2)
     c = codes.reshape(N, nb, 32)
     if qtype == Q8_0:
         out[:, :, q0:] = c.view(np.uint8)
