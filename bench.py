@@ -274,7 +274,9 @@ def measure_others(torch, tq, synth):
     cases = [("q4_0_gemv_k4096_n14336_m1", 1), ("q4_0_gemv_k4096_n14336_m1", 4),
              ("q4_0_gemv_k4096_n14336_m1", 8), ("q8_0_lmhead_k4096_n128001_m1", 1),
              ("q8_0_lmhead_k4096_n128001_m128", 128), ("mxfp4_gemv_k4096_n14336_m1", 1),
-             ("mxfp4_gemv_k4096_n14336_m1", 4), ("mxfp4_gemm_m512_k4096_n4096", 512)]
+             ("mxfp4_gemv_k4096_n14336_m1", 4), ("mxfp4_gemm_m512_k4096_n4096", 512),
+             ("q4_1_gemv_k4096_n14336_m1", 1), ("q4_1_gemv_k4096_n14336_m1", 4),
+             ("q4_1_gemm_m512_k4096_n4096", 512)]
     tiles_cache = {}
     for name, M in cases:
         w = synth.WORKLOADS[name]

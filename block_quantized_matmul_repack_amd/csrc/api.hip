@@ -18,7 +18,7 @@ constexpr int64_t MAX_MK = int64_t(1) << 36;
 
 bool valid_type(int t)
 {
-    return t == TQ_Q4_0 || t == TQ_Q8_0 || t == TQ_IQ4_NL || t == TQ_MXFP4;
+    return t == TQ_Q4_0 || t == TQ_Q8_0 || t == TQ_IQ4_NL || t == TQ_MXFP4 || t == TQ_Q4_1;
 }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -82,6 +82,7 @@ size_t tq_tile_bytes(int type)
     case TQ_Q8_0: return tq::Fmt<TQ_Q8_0>::tile;
     case TQ_IQ4_NL: return tq::Fmt<TQ_IQ4_NL>::tile;
     case TQ_MXFP4: return tq::Fmt<TQ_MXFP4>::tile;
+    case TQ_Q4_1: return tq::Fmt<TQ_Q4_1>::tile;
     }
     return 0;
 }
@@ -93,6 +94,7 @@ size_t tq_block_bytes(int type)
     case TQ_Q8_0: return tq::Fmt<TQ_Q8_0>::block;
     case TQ_IQ4_NL: return tq::Fmt<TQ_IQ4_NL>::block;
     case TQ_MXFP4: return tq::Fmt<TQ_MXFP4>::block;
+    case TQ_Q4_1: return tq::Fmt<TQ_Q4_1>::block;
     }
     return 0;
 }
@@ -144,7 +146,7 @@ int tq_repack_tiles(int type, const void *flat, int64_t K, int64_t N, void *tile
         return TQ_OK;
     if (!flat || !tiles)
         return TQ_E_NULL;
-    if (!aligned(flat, type == TQ_MXFP4 ? 4 : 2) || !aligned(tiles, 16))
+    if (!aligned(flat, (type == TQ_MXFP4 || type == TQ_Q4_1) ? 4 : 2) || !aligned(tiles, 16))
         return TQ_E_ALIGN;
     return launch_status(tq::launch_repack(type, flat, K, N, tiles, stream));
 }

@@ -48,7 +48,7 @@ constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
 // lanes of a b128 read of 16 consecutive rows hit 16 different bank groups.
 constexpr int LDS_ROW = 144;
 
-struct Lds {
+struct LdsMain {
     uint8_t A[2][BM * LDS_ROW];
     uint8_t B[2][BN * LDS_ROW];
     // rank-1 MFMA operands: [0][row] = the row's KB fp16 scales of the step,
@@ -56,6 +56,17 @@ struct Lds {
     uint64_t da[2][2][BM];
     uint64_t dw[2][2][BN];
 };
+// Q4_1's min term, sum_b m_w[n][b] * da[m][b] * asum[m][b], is a product
+// over the k-blocks: the step's block sums of each activation row and fp16
+// row mins of each weight row feed fp32 MFMAs that accumulate it.
+struct LdsMin {
+    float asum[2][BM][KB];
+    uint64_t mw[2][BN];
+};
+template <int QT>
+struct Lds : LdsMain {};
+template <>
+struct Lds<TQ_Q4_1> : LdsMain, LdsMin {};
 
 // Buffer ranges of one workgroup: its activation rows, their scales, and its
 // two weight stripes.  Loads past them return zero.
@@ -105,7 +116,7 @@ __device__ __forceinline__ Offs<QT> make_offs(int64_t nkt, int64_t K, int tid)
         for (int i = 0; i < 2; i++)
             o.w[i] = tile + ((4 * c + 2 * hh + i) * 8 + g) * 4;
     }
-    o.dw = tile + Fmt<QT>::scale_off + (QT == TQ_MXFP4 ? l : 2 * l);
+    o.dw = tile + Fmt<QT>::scale_off + (QT == TQ_MXFP4 ? l : (QT == TQ_Q4_1 ? 4 * l : 2 * l));
     return o;
 }
 
@@ -116,6 +127,7 @@ struct StageRegs {
     uint32_t w[Offs<QT>::NWD];// weight dwords (4-bit: rows 4g..4g+3 at column pairs
                               // 4c+2hh, 4c+2hh+1; Q8_0: rows 2p, 2p+1 at 8h+4hh .. +3)
     uint16_t dw;              // weight row scale (MXFP4: its E8M0 byte)
+    uint16_t mw;              // Q4_1: weight row min
     bool da_ok, dw_ok;        // the scales' k-blocks lie inside K
 };
 
@@ -146,6 +158,8 @@ __device__ __forceinline__ void load_step(StageRegs<QT> &s, const Ranges &rg, co
             s.dw = __builtin_amdgcn_raw_buffer_load_b8(rg.w, o.dw + kt0 * TS, 0, 0);
         else
             s.dw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + kt0 * TS, 0, 0);
+        if constexpr (QT == TQ_Q4_1)
+            s.mw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + 2 + kt0 * TS, 0, 0);
         s.da_ok = kt0 + o.kba < nkt;
         s.dw_ok = kt0 + o.kbw < nkt;
     }
@@ -154,8 +168,8 @@ __device__ __forceinline__ void load_step(StageRegs<QT> &s, const Ranges &rg, co
         s.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rg.w, o.w[i] + kt0 * TS, 0, BUF_NT);
 }
 
-template <int QT>
-__device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds &L, int buf,
+template <int QT, bool DOTS>
+__device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds<QT> &L, int buf,
                                            const Lut &lut, int tid)
 {
 #pragma unroll
@@ -163,6 +177,16 @@ __device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds &L, int b
         const int ch = tid + THREADS * i;
         const int row = ch >> 3, kb = (ch >> 1) & 3, h = ch & 1;
         *(uint4 *)(L.A[buf] + row * LDS_ROW + 32 * kb + 16 * h) = s.a[i];
+        if constexpr (QT == TQ_Q4_1 && !DOTS) {
+            // block sum: this chunk's 16 int8 plus the other half's, held by
+            // the neighbouring thread (ch ^ 1); both threads store the same
+            // value (a branch here would split the loop body).  Blocks past
+            // K get sums of whatever was read there, but their scales are 0.
+            const uint4 a = s.a[i];
+            int p = byte_sum(a.x, byte_sum(a.y, byte_sum(a.z, byte_sum(a.w, 0))));
+            p += __builtin_amdgcn_update_dpp(0, p, 0xB1, 0xF, 0xF, true);
+            L.asum[buf][row][kb] = (float)p;
+        }
     }
     ((uint16_t *)&L.da[buf][0][tid >> 2])[tid & 3] = s.da_ok ? s.da : (uint16_t)0;
     const int wave = tid >> 6, lane = tid & 63;
@@ -192,6 +216,9 @@ __device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds &L, int b
                 const uint32_t t = pr ^ 0x88888888u;      // nibble c -> c - 8 (4-bit two's complement)
                 lo = (t << 4) & 0xF0F0F0F0u;              // 16 * (even-column code - 8)
                 hi = t & 0xF0F0F0F0u;                     // 16 * (odd-column code - 8)
+            } else if constexpr (QT == TQ_Q4_1) {
+                lo = pr & 0x0F0F0F0Fu;                    // the codes themselves
+                hi = (pr >> 4) & 0x0F0F0F0Fu;
             } else {
                 lut16x2(pr, lut, lo, hi);
             }
@@ -205,6 +232,8 @@ __device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds &L, int b
     // writes the same bits and keeps the step free of branches
     const uint16_t dwb = (QT == TQ_MXFP4) ? e8m0_f16_bits(s.dw) : s.dw;
     ((uint16_t *)&L.dw[buf][0][32 * tt + l])[kb] = s.dw_ok ? dwb : (uint16_t)0;
+    if constexpr (QT == TQ_Q4_1)
+        ((uint16_t *)&L.mw[buf][32 * tt + l])[kb] = s.dw_ok ? s.mw : (uint16_t)0;
 }
 
 template <int QT, bool DOTS>
@@ -215,7 +244,7 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
                                                    int64_t K, Lut lut, float *__restrict__ y,
                                                    int64_t ldy, int32_t *__restrict__ isum)
 {
-    __shared__ __attribute__((aligned(16))) Lds L;
+    __shared__ __attribute__((aligned(16))) Lds<QT> L;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -243,6 +272,7 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
 #pragma unroll
     for (int r = 0; r < 16; r++)
         acc[r] = 0.0f;
+    v16f mt = {};                        // Q4_1: the min term
 
     // One k-block: the int8 MFMA (exact block dots) and, for y, the rank-1
     // fp16 MFMA giving sc[m][n] = da[m] * dw[n] (exact in fp32).  Its A
@@ -324,6 +354,23 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
             __builtin_amdgcn_sched_group_barrier(SG_VALU, 32, 0);
             // the weight decode that follows is scheduled on its own
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (QT == TQ_Q4_1) {
+                // min term of the step's KB blocks, two per fp32 MFMA: lane
+                // (li, lk) holds k = lk, i.e. block 2j + lk, with A = da *
+                // asum of activation row li (exact in fp32) and B = the min
+                // of weight row li
+                const int ra = 32 * wm + li;
+                const uint64_t dav = L.da[buf][0][ra];
+                const uint64_t mwv = L.mw[buf][32 * wn + li];
+#pragma unroll
+                for (int j = 0; j < KB / 2; j++) {
+                    const int kb = 2 * j + lk;
+                    const float a = f16_bits_to_f32((uint16_t)(dav >> (16 * kb))) *
+                                    L.asum[buf][ra][kb];
+                    const float b = f16_bits_to_f32((uint16_t)(mwv >> (16 * kb)));
+                    mt = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, mt, 0, 0, 0);
+                }
+            }
         }
     };
 
@@ -338,18 +385,18 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
     const int64_t nsteps2 = (nsteps + 1) & ~int64_t(1);
     load_step<QT, DOTS>(r0, rg, o, (int)nkt, 0);
     load_step<QT, DOTS>(r1, rg, o, (int)nkt, KB);
-    store_step<QT>(r0, L, 0, lut, tid);
+    store_step<QT, DOTS>(r0, L, 0, lut, tid);
     __syncthreads();
     for (int64_t step = 0; step < nsteps2; step += 2) {
         // even step: buffer 0 is computed, r1 holds step+1, r0 is free
         load_step<QT, DOTS>(r0, rg, o, (int)nkt, (int)(step + 2) * KB);
         compute(0, step);
-        store_step<QT>(r1, L, 1, lut, tid);
+        store_step<QT, DOTS>(r1, L, 1, lut, tid);
         __syncthreads();
         // odd step: buffer 1 is computed, r0 holds step+2, r1 is free
         load_step<QT, DOTS>(r1, rg, o, (int)nkt, (int)(step + 3) * KB);
         compute(1, step + 1);
-        store_step<QT>(r0, L, 0, lut, tid);
+        store_step<QT, DOTS>(r0, L, 0, lut, tid);
         __syncthreads();
     }
     epilogue(carry.kt, carry.dot, carry.sc);
@@ -361,7 +408,7 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
         for (int r = 0; r < 16; r++) {
             const int64_t m = m0 + 32 * wm + 8 * (r >> 2) + 4 * lk + (r & 3);
             if (m < M)
-                y[m * ldy + n] = acc[r] * weight_unscale<QT>();
+                y[m * ldy + n] = acc[r] * weight_unscale<QT>() + (QT == TQ_Q4_1 ? mt[r] : 0.0f);
         }
     }
 }
@@ -398,6 +445,7 @@ hipError_t launch_qgemm(int type, const void *tiles, int64_t K, int64_t N, const
     case TQ_Q8_0: return launch_t<TQ_Q8_0>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
     case TQ_IQ4_NL: return launch_t<TQ_IQ4_NL>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
     case TQ_MXFP4: return launch_t<TQ_MXFP4>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_Q4_1: return launch_t<TQ_Q4_1>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
     }
     return hipErrorInvalidValue;
 }

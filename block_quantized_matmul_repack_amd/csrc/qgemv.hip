@@ -121,6 +121,9 @@ __device__ __forceinline__ v4i_t tile_operand(const uint8_t *tile, int off, cons
             const uint32_t t = x ^ 0x88888888u;
             lo[i] = (t << 4) & 0xF0F0F0F0u;
             hi[i] = t & 0xF0F0F0F0u;
+        } else if constexpr (QT == TQ_Q4_1) {
+            lo[i] = x & 0x0F0F0F0Fu;
+            hi[i] = (x >> 4) & 0x0F0F0F0Fu;
         } else {
             lut16x2(x, lut, lo[i], hi[i]);
         }
@@ -141,6 +144,10 @@ template <>
 struct TileRegs<TQ_IQ4_NL> : TileRegs<TQ_Q4_0> {};
 template <>
 struct TileRegs<TQ_MXFP4> : TileRegs<TQ_Q4_0> {};
+template <>
+struct TileRegs<TQ_Q4_1> : TileRegs<TQ_Q4_0> {
+    uint16_t mn;             // the row's min
+};
 // Q8_0 tiles: 8 dwords (rows 2p, 2p+1 at column pairs 8h+i) and the row scale.
 template <>
 struct TileRegs<TQ_Q8_0> {
@@ -169,6 +176,8 @@ __device__ __forceinline__ void lds_tile(TileRegs<QT> &r, const uint8_t *tile, i
             r.a[i] = t[(4 * c + ((i + c) & 3)) * 8 + g];
     }
     r.sc = tile_scale_bits<QT>(tile, l);
+    if constexpr (QT == TQ_Q4_1)
+        r.mn = tile_min_bits(tile, l);
 }
 
 template <int QT, int MM>
@@ -183,6 +192,10 @@ struct ActRegs<TQ_IQ4_NL, MM> : ActRegs<TQ_Q4_0, MM> {};
 template <int MM>
 struct ActRegs<TQ_MXFP4, MM> : ActRegs<TQ_Q4_0, MM> {};
 template <int MM>
+struct ActRegs<TQ_Q4_1, MM> : ActRegs<TQ_Q4_0, MM> {
+    float s[MM];             // da * (sum of the block's 32 int8), exact
+};
+template <int MM>
 struct ActRegs<TQ_Q8_0, MM> {
     uint32_t v[MM][4];       // 16 consecutive K
     float d[MM];
@@ -192,10 +205,11 @@ struct ActRegs<TQ_Q8_0, MM> {
 // qs[(tp * MM + m) * 32] -- for 4-bit weights as the 16 even K then the 16
 // odd K, each word c rotated by rot_act, so that a lane's even and odd words
 // come out of LDS ready for the nibble dot products -- and its scale, as
-// fp32, at ds[tp * MM + m].
+// fp32, at ds[tp * MM + m]; for Q4_1 also da times the sum of its 32 int8
+// at ss[tp * MM + m].
 template <int QT, int MM>
 __device__ __forceinline__ void lds_act(ActRegs<QT, MM> &r, const int8_t *qs, const float *ds,
-                                        int tp, int l)
+                                        const float *ss, int tp, int l)
 {
 #pragma unroll
     for (int m = 0; m < MM; m++) {
@@ -211,6 +225,8 @@ __device__ __forceinline__ void lds_act(ActRegs<QT, MM> &r, const int8_t *qs, co
             r.v[m].y = *(const uint32_t *)(qb + 16 + 4 * (l & 3));
         }
         r.d[m] = ds[tp * MM + m];
+        if constexpr (QT == TQ_Q4_1)
+            r.s[m] = ss[tp * MM + m];
     }
 }
 
@@ -276,6 +292,9 @@ __device__ __forceinline__ void block_dots(int (&s)[MM], const TileRegs<QT> &w,
                 const uint32_t t = tr[j] ^ 0x88888888u;       // nibble c -> c - 8 (4-bit two's complement)
                 ev[j] = (t << 4) & 0xF0F0F0F0u;               // 16 * (even-column code - 8)
                 od[j] = t & 0xF0F0F0F0u;                      // 16 * (odd-column code - 8)
+            } else if constexpr (QT == TQ_Q4_1) {
+                ev[j] = tr[j] & 0x0F0F0F0Fu;                  // the codes themselves
+                od[j] = (tr[j] >> 4) & 0x0F0F0F0Fu;
             } else {
                 lut16x2(tr[j], lut, ev[j], od[j]);
             }
@@ -301,7 +320,7 @@ __device__ __forceinline__ void block_dots(int (&s)[MM], const TileRegs<QT> &w,
 // unit goes to lane i % 64, register slot i / 64.
 template <int QT>
 struct Unit {
-    static constexpr int BYTES = 2 * Fmt<QT>::tile;       // 1152 (4-bit), 2176 (Q8_0), 1088 (MXFP4)
+    static constexpr int BYTES = 2 * Fmt<QT>::tile;       // 1152 (4-bit), 2176 (Q8_0), 1088 (MXFP4), 1280 (Q4_1)
     static constexpr int CHUNKS = BYTES / 16;             // 72, 136, 68
     static constexpr int SLOTS = (CHUNKS + 63) / 64;      // 2, 3, 2
     v4u c[SLOTS];
@@ -385,9 +404,12 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     // The chunk is processed in passes of up to P tiles.  Each pass first
     // stages the pass's int8 activations and scales of all M rows in LDS
     // (layout at lds_act), so the unit loop has only weight loads in flight.
-    constexpr int P = act_lds_bytes<MM>() / (MM * 36) & ~1;
+    // per tile and row: 32 int8, the fp32 scale and, for Q4_1, the block sum
+    constexpr int PB = QT == TQ_Q4_1 ? 40 : 36;
+    constexpr int P = act_lds_bytes<MM>() / (MM * PB) & ~1;
     int8_t *qs = (int8_t *)act_lds;
     float *ds = (float *)(act_lds + MM * P * 32);
+    float *ss = ds + MM * P;                              // Q4_1 only
     // one 16-byte chunk (K 16 h .. 16 h + 15 of a tile) of row m into qs
     auto put_chunk = [&](int tp, int m, int h, uint4 v) {
         int8_t *qb = qs + (tp * MM + m) * 32;
@@ -448,19 +470,32 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
 #pragma unroll
             for (int r = 0; r < D; r++)
                 load_stage(u[r], r);
+            // Q4_1: the sum of a tile's 32 int8 from its two chunks, held by
+            // neighbouring threads (o, o ^ 1; pairs are in range together)
+            auto put_sum = [&](int m, int oo, const uint4 &v) {
+                if constexpr (QT == TQ_Q4_1 && !DOTS) {
+                    int p = byte_sum(v.x, byte_sum(v.y, byte_sum(v.z, byte_sum(v.w, 0))));
+                    p += dpp_xor1(p);
+                    if (oo < 2 * pn && (oo & 1) == 0)
+                        ss[(oo >> 1) * MM + m] = (float)p;
+                }
+            };
 #pragma unroll
             for (int m = 0; m < MM; m++) {
                 if (o < 2 * pn)
                     put_chunk(o >> 1, m, o & 1, qv[m]);
                 if (o < pn)
                     ds[o * MM + m] = f16_bits_to_f32(dv[m]);
+                put_sum(m, o, qv[m]);
             }
             for (int o2 = o + NW * 64; o2 < 2 * pn; o2 += NW * 64) {
 #pragma unroll
                 for (int m = 0; m < MM; m++) {
-                    put_chunk(o2 >> 1, m, o2 & 1, qload(m, o2));
+                    const uint4 v2 = qload(m, o2);
+                    put_chunk(o2 >> 1, m, o2 & 1, v2);
                     if (o2 < pn)
                         ds[o2 * MM + m] = f16_bits_to_f32(dload(m, o2));
+                    put_sum(m, o2, v2);
                 }
             }
         } else {
@@ -480,6 +515,13 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                 uint2 qv;
                 uint16_t db;
                 quant_quad(v, qv, db);
+                if constexpr (QT == TQ_Q4_1) {
+                    int p = byte_sum(qv.x, byte_sum(qv.y, 0));
+                    p += dpp_xor1(p);                     // the quad's 32 int8
+                    p += dpp_xor2(p);
+                    if (b < nblk && c == 0)
+                        ss[b] = (float)p;
+                }
                 if (b < nblk) {
                     int8_t *qb = qs + b * 32;
                     if constexpr (QT == TQ_Q8_0) {
@@ -542,11 +584,17 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                         float dw = f16_bits_to_f32(tile_scale_bits<QT>(tile, l)) *
                                    weight_unscale<QT>();
                         dw = valid ? dw : 0.0f;               // a missing second tile adds 0
+                        float mw = 0.0f;
+                        if constexpr (QT == TQ_Q4_1)
+                            mw = valid ? f16_bits_to_f32(tile_min_bits(tile, l)) : 0.0f;
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
                             const int m = 4 * half + r;
-                            const float da = m < MM ? ds[tp * MM + min(m, MM - 1)] : 0.0f;
+                            const int mi = tp * MM + min(m, MM - 1);
+                            const float da = m < MM ? ds[mi] : 0.0f;
                             acc[r] = fmaf((float)dot[r], dw * da, acc[r]);
+                            if constexpr (QT == TQ_Q4_1)
+                                acc[r] = fmaf(mw, da * ss[mi], acc[r]);   // the min
                         }
                     }
                 }
@@ -556,7 +604,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                 TileRegs<QT> w;
                 lds_tile<QT>(w, my + half * TS, l);
                 ActRegs<QT, MM> x;
-                lds_act<QT, MM>(x, qs, ds, tp, l);
+                lds_act<QT, MM>(x, qs, ds, ss, tp, l);
                 int s[MM];
                 block_dots<QT, MM>(s, w, x, sel0, sel1, lut);
                 if constexpr (DOTS) {
@@ -573,6 +621,13 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
 #pragma unroll
                     for (int m = 0; m < MM; m++)
                         acc[m] = fmaf((float)s[m], dw * x.d[m], acc[m]);
+                    if constexpr (QT == TQ_Q4_1) {
+                        // the min: m_w * da * sum(q), da * sum exact in fp32
+                        const float mw = valid ? f16_bits_to_f32(w.mn) : 0.0f;
+#pragma unroll
+                        for (int m = 0; m < MM; m++)
+                            acc[m] = fmaf(mw, x.d[m] * x.s[m], acc[m]);
+                    }
                 }
             }
         };
@@ -750,6 +805,7 @@ hipError_t launch_qgemv(int type, const void *tiles, int64_t K, int64_t N, const
     case TQ_Q8_0: return launch_t<TQ_Q8_0>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
     case TQ_IQ4_NL: return launch_t<TQ_IQ4_NL>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
     case TQ_MXFP4: return launch_t<TQ_MXFP4>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
+    case TQ_Q4_1: return launch_t<TQ_Q4_1>(tiles, K, N, act, M, lut, y, ldy, isum, sp, s);
     }
     return hipErrorInvalidValue;
 }

@@ -10,7 +10,7 @@
 // is what both tile formats need:
 //   Q8_0: tile dword (cp, rp) = halfword cp of rows 2rp and 2rp+1, so a
 //         16-byte tile chunk is a 16-byte LDS read, stored as is;
-//   Q4_0 / IQ4_NL / MXFP4: tile byte (cp, r) = one nibble of each of quant
+//   Q4_0 / IQ4_NL / MXFP4 / Q4_1: tile byte (cp, r) = one nibble of each of quant
 //         bytes 2h, 2h+1 of row r (h = cp mod 8; low nibbles for cp < 8,
 //         high for cp >= 8), built two rows at a time with shifts and masks.
 // Store: every thread writes whole 16-byte chunks of the tiles.
@@ -67,12 +67,15 @@ __global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ 
                                                     uint8_t *__restrict__ tiles)
 {
     constexpr bool MX = QT == TQ_MXFP4;
-    constexpr int BB = Fmt<QT>::block;          // flat block bytes (scale + quants)
-    constexpr int QH = MX ? 8 : (BB - 2) / 2;   // quant halfwords per block: 8 or 16
+    constexpr bool Q41 = QT == TQ_Q4_1;
+    constexpr int BB = Fmt<QT>::block;          // flat block bytes (scales + quants)
+    constexpr int QOFF = MX ? 1 : (Q41 ? 4 : 2);// offset of the quants in a block
+    constexpr int QH = (BB - QOFF) / 2;         // quant halfwords per block: 8 or 16
     constexpr int TS = Fmt<QT>::tile;
     constexpr int CH = TS / 16;                 // 16-byte chunks per tile: 36, 68 or 34
     constexpr int QCH = Fmt<QT>::scale_off / 16;// chunks of quants (the rest hold scales)
-    using Scale = std::conditional_t<MX, uint8_t, uint16_t>;
+    // a row's scale bytes in the tile: E8M0 byte, fp16 d, or fp16 pair (d, m)
+    using Scale = std::conditional_t<MX, uint8_t, std::conditional_t<Q41, uint32_t, uint16_t>>;
     constexpr int SPC = 16 / (int)sizeof(Scale);// row scales per 16-byte chunk
     // each tile's halfword columns padded by 16 bytes: the lanes of a store
     // differ in t, and a tile stride of 16 mod 256 bytes spreads them over
@@ -91,16 +94,20 @@ __global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ 
         const int r = i / te, t = i - r * te;
         const int64_t n = 32 * ct + r;
         uint16_t q[QH];
-        uint16_t d = 0;
+        Scale d = 0;
         if (n < N) {
             if constexpr (MX) {
-                load_mx_block(flat, (n * nb + kt0 + t) * BB, N * nb * BB, q, d);
+                uint16_t e;
+                load_mx_block(flat, (n * nb + kt0 + t) * BB, N * nb * BB, q, e);
+                d = (Scale)e;
             } else {
+                // Q4_1 blocks are 20 bytes and the flat buffer 4-byte aligned,
+                // so (d, m) is one aligned dword
                 const uint8_t *blk = flat + (n * nb + kt0 + t) * BB;
-                d = *(const uint16_t *)blk;
+                d = *(const Scale *)blk;
 #pragma unroll
                 for (int v = 0; v < QH / 8; v++) {
-                    const u16x8u w = *(const u16x8u *)(blk + 2 + 16 * v);
+                    const u16x8u w = *(const u16x8u *)(blk + QOFF + 16 * v);
 #pragma unroll
                     for (int e = 0; e < 8; e++)
                         q[8 * v + e] = w[e];
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ 
 #pragma unroll
         for (int h = 0; h < QH; h++)
             qs[t][32 * h + r] = q[h];
-        sc[t][r] = (Scale)d;
+        sc[t][r] = d;
     }
     __syncthreads();
 
@@ -168,6 +175,7 @@ hipError_t launch_repack(int type, const void *flat, int64_t K, int64_t N, void 
     case TQ_IQ4_NL: k_repack<TQ_IQ4_NL><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
     case TQ_Q8_0: k_repack<TQ_Q8_0><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
     case TQ_MXFP4: k_repack<TQ_MXFP4><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
+    case TQ_Q4_1: k_repack<TQ_Q4_1><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

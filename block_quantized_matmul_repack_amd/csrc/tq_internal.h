@@ -9,8 +9,9 @@
 namespace tq {
 
 // Tile geometry ("Block-32 Quantized Formats"): quant bytes, then 32 row
-// scales at scale_off: fp16 at scale_off + 2*row, or for MXFP4 one E8M0 byte
-// at scale_off + row.  block = bytes of one flat GGML block.
+// scales at scale_off: fp16 at scale_off + 2*row, for MXFP4 one E8M0 byte at
+// scale_off + row, for Q4_1 the fp16 pair (d, m) at scale_off + 4*row.
+// block = bytes of one flat GGML block.
 template <int QT> struct Fmt;
 template <> struct Fmt<TQ_Q4_0> {
     static constexpr int tile = 576, scale_off = 512, block = 18;
@@ -23,6 +24,9 @@ template <> struct Fmt<TQ_Q8_0> {
 };
 template <> struct Fmt<TQ_MXFP4> {
     static constexpr int tile = 544, scale_off = 512, block = 17;
+};
+template <> struct Fmt<TQ_Q4_1> {
+    static constexpr int tile = 640, scale_off = 512, block = 20;
 };
 
 // Raw buffer loads (CDNA buffer resource descriptor, stride 0): a load whose
@@ -110,8 +114,22 @@ __device__ __forceinline__ uint16_t tile_scale_bits(const uint8_t *tile, int l)
 {
     if constexpr (QT == TQ_MXFP4)
         return e8m0_f16_bits(tile[Fmt<QT>::scale_off + l]);
+    else if constexpr (QT == TQ_Q4_1)
+        return ((const uint16_t *)(tile + Fmt<QT>::scale_off))[2 * l];
     else
         return ((const uint16_t *)(tile + Fmt<QT>::scale_off))[l];
+}
+
+// fp16 bits of tile row l's min (Q4_1 only).
+__device__ __forceinline__ uint16_t tile_min_bits(const uint8_t *tile, int l)
+{
+    return ((const uint16_t *)(tile + Fmt<TQ_Q4_1>::scale_off))[2 * l + 1];
+}
+
+// acc + the sum of the 4 int8 of a (activation block sums for Q4_1's min).
+__device__ __forceinline__ int byte_sum(uint32_t a, int acc)
+{
+    return __builtin_amdgcn_sdot4((int)a, 0x01010101, acc, false);
 }
 
 // The kernels multiply integer weights that are a fixed power of two times

@@ -27,13 +27,16 @@
  *            for e <= 112, 2^15 for e > 142.  The kernels multiply the
  *            integers 2 * E2M1(code) (0, 1, 2, 3, 4, 6, 8, 12 and their
  *            negatives) by s(e) / 2, exactly.
+ *     Q4_1   640 B: the Q4_0 nibble layout of codes 0..15; bytes 512 + 4*row
+ *            hold row's fp16 scale d, bytes 514 + 4*row its fp16 min m.
+ *            Weight = d * quant + m.
  *   Rows n >= N of the last row-tile are zero (codes 0, scale +0.0).
  *
  *   Flat source ("repacked from flat row-major GGML layouts"): row n holds
  *   K/32 consecutive GGML blocks: Q4_0 / IQ4_NL = fp16 d + 16 bytes (low
  *   nibbles elements 0..15, high nibbles 16..31), 18 B; Q8_0 = fp16 d + 32
  *   int8, 34 B; MXFP4 = E8M0 byte e + 16 bytes in the Q4_0 nibble order,
- *   17 B.
+ *   17 B; Q4_1 = fp16 d + fp16 m + 16 bytes in the Q4_0 nibble order, 20 B.
  *
  *   Activations (section "Memory buffers": dynamically quantized activations,
  *   used as Q8_0 activation tiles by the vector dot of "Q2_0 Format"): per
@@ -46,7 +49,8 @@
  *   dst = src0^T * src1).  Per 32-element block the integer dot
  *   isum = sum_j w_int * q is formed exactly in int32, then scaled by the
  *   fp16 row scale times the fp16 activation scale (exact in fp32) and
- *   summed in fp32 over blocks.
+ *   summed in fp32 over blocks.  Q4_1's min adds m * da * sum_j q per block
+ *   (the activation sum exact in int32, times da exact in fp32).
  *
  * Calling convention (all entry points):
  *   - Data pointers are DEVICE pointers, except `lut`, which is a HOST
@@ -76,7 +80,7 @@
 extern "C" {
 #endif
 
-typedef enum { TQ_Q4_0 = 0, TQ_Q8_0 = 1, TQ_IQ4_NL = 2, TQ_MXFP4 = 3 } tq_type;
+typedef enum { TQ_Q4_0 = 0, TQ_Q8_0 = 1, TQ_IQ4_NL = 2, TQ_MXFP4 = 3, TQ_Q4_1 = 4 } tq_type;
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 typedef enum {
     TQ_OK = 0,
@@ -90,11 +94,11 @@ typedef enum {
 /* Which kernel family tq_block_dots runs. */
 typedef enum { TQ_PATH_GEMV = 0, TQ_PATH_GEMM = 1 } tq_path;
 
-/* Bytes of one tile ("Block-32 Quantized Formats"): 576, 1088, 576, 544; 0
- * for an unknown type. */
+/* Bytes of one tile ("Block-32 Quantized Formats"): 576, 1088, 576, 544,
+ * 640; 0 for an unknown type. */
 size_t tq_tile_bytes(int type);
 
-/* Bytes of one flat GGML block: 18, 34, 18, 17; 0 for an unknown type. */
+/* Bytes of one flat GGML block: 18, 34, 18, 17, 20; 0 for an unknown type. */
 size_t tq_block_bytes(int type);
 
 /* (K/32) * ((N+31)/32) * tq_tile_bytes(type) ("Tile Dimensions and Grid
@@ -114,7 +118,7 @@ const char *tq_status_string(int status);
 /* Repack flat GGML blocks into tiles ("Tiled Weight Formats": repacking at
  * model load or at run time).
  *   flat  : device, tq_flat_bytes(type, K, N) bytes, 2-byte aligned
- *           (TQ_MXFP4: 4-byte aligned).
+ *           (TQ_MXFP4, TQ_Q4_1: 4-byte aligned).
  *   tiles : device, tq_tiled_bytes(type, K, N) bytes, 16-byte aligned; fully
  *           written, padding rows included.  Must not overlap `flat`.
  * Bit-exact byte permutation; deterministic. */
@@ -196,8 +200,8 @@ int tq_matmul(int type, const void *tiles, int64_t K, int64_t N,
  * (TQ_PATH_GEMM) kernel with the integer block dots as output instead of y:
  * isum[(m*N + n)*(K/32) + kt] (int32, device, 4-byte aligned) =
  * sum_{j<32} w_int[n][32kt+j] * q[m][32kt+j], for m < M, n < N, with w_int
- * = code - 8 (Q4_0), the int8 (Q8_0), lut[code] (IQ4_NL) or 2 * E2M1(code)
- * (MXFP4). */
+ * = code - 8 (Q4_0), the int8 (Q8_0), lut[code] (IQ4_NL), 2 * E2M1(code)
+ * (MXFP4) or the code itself (Q4_1, whose min is not part of the block dot). */
 int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N,
                   const int8_t *q, int64_t M, const int8_t *lut,
                   int32_t *isum, int path, hipStream_t stream);

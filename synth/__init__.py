@@ -174,4 +174,7 @@ WORKLOADS = {
     "mxfp4_gemv_k4096_n14336_m1": Workload("mxfp4_gemv_k4096_n14336_m1", MXFP4, 4096, 14336, 1, "e8m0"),
     "mxfp4_gemm_m512_k4096_n4096": Workload("mxfp4_gemm_m512_k4096_n4096", MXFP4, 4096, 4096, 512,
                                             "e8m0", act_dtype="bf16", path="qgemm"),
+    "q4_1_gemv_k4096_n14336_m1": Workload("q4_1_gemv_k4096_n14336_m1", Q4_1, 4096, 14336, 1, "minmax"),
+    "q4_1_gemm_m512_k4096_n4096": Workload("q4_1_gemm_m512_k4096_n4096", Q4_1, 4096, 4096, 512,
+                                           "minmax", act_dtype="bf16", path="qgemm"),
 }

@@ -127,6 +127,19 @@ def test_mxfp4_m512_k4096_n4096(tq):
     _check_dots(tq, c, tq.PATH_GEMM)
 
 
+@pytest.mark.parametrize("M", [1, 8])
+def test_q4_1_k4096_n14336(tq, M):
+    c = Case(tq, "q4_1_gemv_k4096_n14336_m1", M=M)
+    _check_case(tq, c, tq.qgemv, full_y=True)
+    _check_dots(tq, c, tq.PATH_GEMV)
+
+
+def test_q4_1_m512_k4096_n4096(tq):
+    c = Case(tq, "q4_1_gemm_m512_k4096_n4096")
+    _check_case(tq, c, tq.qgemm, full_y=False)
+    _check_dots(tq, c, tq.PATH_GEMM)
+
+
 @pytest.fixture(scope="module")
 def lmhead(tq):
     return Case(tq, "q8_0_lmhead_k4096_n128001_m128")

@@ -15,8 +15,8 @@ from gpu_helpers import check_y, make, tiles_slice, to_dev_act
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-Q4_0, Q8_0, IQ4_NL, MXFP4 = synth.Q4_0, synth.Q8_0, synth.IQ4_NL, synth.MXFP4
-TYPES = [Q4_0, Q8_0, IQ4_NL, MXFP4]
+Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1 = synth.Q4_0, synth.Q8_0, synth.IQ4_NL, synth.MXFP4, synth.Q4_1
+TYPES = [Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1]
 LUT = synth.IQ4_NL_STANDIN_LUT
 
 
@@ -319,3 +319,32 @@ def test_mxfp4_every_scale_byte(tq):
         assert np.array_equal(got, ref), path
         y = fn(MXFP4, tdev, K, N, qd, dd).cpu().numpy()
         check_y(y, y_ref, acond, ("mxfp4 scales", path))
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 40, 130])
+def test_q4_1_min_term(tq, M):
+    """Q4_1 with all codes 0 is the min term alone (m * da * sum(q) per
+    block); with large activations the block sums reach +-4064.  Both
+    kernels, and the fused decode, against the oracle."""
+    K, N = 320, 70
+    rng = np.random.default_rng(M)
+    codes = np.zeros((N, K), np.uint8)
+    codes[:, ::7] = 15
+    pairs = synth.draw_scales(rng, "minmax", N, K)
+    flat = synth.pack_flat(Q4_1, codes, pairs)
+    x = synth.draw_activations(rng, M, K)
+    x[:, :64] = np.abs(x[:, :64]) + 3.0          # blocks 0, 1: all of one sign
+    x[0, 64:96] = -1.0                            # block 2 of row 0: q = -127 throughout
+    tiles = oracle.repack(Q4_1, flat, K, N)
+    q, d = oracle.quantize_act(x)
+    assert q[0, 64:96].sum() == -127 * 32
+    y_ref, acond = oracle.matmul(Q4_1, tiles, K, N, q, d)
+    tdev = tq.repack_tiles(Q4_1, torch.from_numpy(flat).cuda(), K, N)
+    assert np.array_equal(tdev.cpu().numpy(), tiles)
+    qd, dd = tq.quantize_act(torch.from_numpy(x).cuda())
+    fns = [tq.qgemm] + ([tq.qgemv] if M <= 8 else [])
+    for fn in fns:
+        check_y(fn(Q4_1, tdev, K, N, qd, dd).cpu().numpy(), y_ref, acond, ("q4_1 min", fn.__name__, M))
+    if M <= 8:
+        yx = tq.qgemv_x(Q4_1, tdev, K, N, torch.from_numpy(x).cuda())
+        check_y(yx.cpu().numpy(), y_ref, acond, ("q4_1 min fused", M))
