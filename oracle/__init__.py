@@ -13,7 +13,8 @@ Parity pins: see tests/test_oracle_*.py.  The flat GGML block nibble order
 (flat_decode, and through it the input side of repack) is "parity unpinned":
 the page does not print the flat layout; for MXFP4 the flat block (one E8M0
 byte, then 16 nibble bytes) and for Q4_1 (fp16 d, fp16 m, then 16 nibble
-bytes) are unpinned for the same reason.
+bytes) and for Q4_K (the 144-byte super-block with 6-bit scales and mins) are
+unpinned for the same reason.
 """
 import ctypes
 import os
@@ -22,7 +23,7 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1 = 0, 1, 2, 3, 4
+Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1, Q4_K = 0, 1, 2, 3, 4, 5
 F32, BF16, F16 = 0, 1, 2
 
 _lib = None
@@ -42,7 +43,7 @@ def lib():
         L.or_f32_to_f16.restype = ctypes.c_uint16
         L.or_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.or_bf16_to_f32.restype = ctypes.c_float
-        for f in ("or_tile_bytes", "or_block_bytes", "or_scale_count"):
+        for f in ("or_tile_bytes", "or_block_bytes", "or_scale_count", "or_block_elems"):
             getattr(L, f).argtypes = [ctypes.c_int]
             getattr(L, f).restype = l
         for f in ("or_tiled_bytes", "or_flat_bytes"):
@@ -121,6 +122,10 @@ def row_scale(t, s):
 
 def scale_count(t):
     return lib().or_scale_count(t)
+
+
+def block_elems(t):
+    return lib().or_block_elems(t)
 
 
 def _scales_array(t, N, nb):

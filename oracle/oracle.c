@@ -27,7 +27,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_IQ4_NL = 2, OR_MXFP4 = 3, OR_Q4_1 = 4 };
+enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_IQ4_NL = 2, OR_MXFP4 = 3, OR_Q4_1 = 4, OR_Q4_K = 5 };
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
 
 /* ---------------------------------------------------------------------------
@@ -108,6 +108,7 @@ long or_tile_bytes(int type)
     case OR_IQ4_NL: return 576;
     case OR_MXFP4: return 544;
     case OR_Q4_1: return 640;
+    case OR_Q4_K: return 640;
     }
     return 0;
 }
@@ -120,12 +121,17 @@ long or_block_bytes(int type)
     case OR_IQ4_NL: return 18;
     case OR_MXFP4: return 17;
     case OR_Q4_1: return 20;
+    case OR_Q4_K: return 144;   /* one 256-element super-block */
     }
     return 0;
 }
 
-/* Scale values per row and block: Q4_1 keeps a pair (d, m), the others one. */
-long or_scale_count(int type) { return type == OR_Q4_1 ? 2 : 1; }
+/* Elements of one flat block: 256 for the K-quant Q4_K, 32 for the others. */
+long or_block_elems(int type) { return type == OR_Q4_K ? 256 : 32; }
+
+/* Scale values per row and 32-element block in a tile: Q4_1 and Q4_K keep a
+ * pair, the others one. */
+long or_scale_count(int type) { return (type == OR_Q4_1 || type == OR_Q4_K) ? 2 : 1; }
 
 /* "Tile Dimensions and Grid Layout": n_k_tiles = ne0 / 32, n_col_tiles =
  * (ne1 + 31) / 32, with ne0 = K and ne1 = N. */
@@ -136,7 +142,7 @@ long or_tiled_bytes(int type, long K, long N)
 
 long or_flat_bytes(int type, long K, long N)
 {
-    return N * (K / 32) * or_block_bytes(type);
+    return N * (K / or_block_elems(type)) * or_block_bytes(type);
 }
 
 /* ---------------------------------------------------------------------------
@@ -166,9 +172,71 @@ static uint16_t block_scale(int type, const uint8_t *blk, int i)
     return (uint16_t)(blk[2 * i] | (blk[2 * i + 1] << 8));
 }
 
+/* ---------------------------------------------------------------------------
+ * Q4_K flat super-blocks ("K-Quants": GGML packs 256 elements per super-block;
+ * the page splits each into 8 tiles of 32 k whose row pairs are (d * sc,
+ * -dmin * m)).  The page does not print the flat super-block; the reading
+ * taken is GGML's: fp16 d, fp16 dmin, 12 bytes holding eight 6-bit scales sc
+ * and eight 6-bit mins m, then 128 bytes of nibbles in which 64-element
+ * chunk c owns bytes 32c..32c+31, element 64c + i (i < 32) in the low nibble
+ * of byte 32c + i and element 64c + 32 + i in its high nibble.
+ *
+ * The 6-bit values of sub-block j: for j < 4, sc = low 6 bits of byte j and
+ * m = low 6 bits of byte j + 4; for j >= 4 the low 4 bits come from byte
+ * j + 4 (sc in its low nibble, m in its high one) and the top 2 bits from
+ * the top 2 bits of byte j - 4 (sc) and byte j (m).
+ * ------------------------------------------------------------------------- */
+static void q4k_scale_min(const uint8_t *sb, int j, int *sc, int *m)
+{
+    if (j < 4) {
+        *sc = sb[j] & 63;
+        *m = sb[j + 4] & 63;
+    } else {
+        *sc = (sb[j + 4] & 0x0f) | ((sb[j - 4] >> 6) << 4);
+        *m = (sb[j + 4] >> 4) | ((sb[j] >> 6) << 4);
+    }
+}
+
+static const uint8_t *q4k_block(const uint8_t *flat, long K, long n, long k)
+{
+    return flat + (n * (K / 256) + k / 256) * 144;
+}
+
+static uint8_t q4k_code(const uint8_t *flat, long K, long n, long k)
+{
+    const uint8_t *qs = q4k_block(flat, K, n, k) + 16;
+    int e = (int)(k % 256), c = e / 64, i = e % 64;
+    uint8_t byte = qs[32 * c + (i % 32)];
+    return i < 32 ? (byte & 0x0f) : (byte >> 4);
+}
+
+/* The tile pair of 32-element block kt of row n: i = 0 gives d * sc, i = 1
+ * gives -(dmin * m), each product formed in fp32 (exact: an fp16 times a
+ * 6-bit integer) and rounded to fp16 nearest-even (the tile holds FP16). */
+static uint16_t q4k_pair(const uint8_t *flat, long K, long n, long kt, int i)
+{
+    const uint8_t *blk = q4k_block(flat, K, n, 32 * kt);
+    int sc, m;
+    q4k_scale_min(blk + 4, (int)(kt % 8), &sc, &m);
+    float d = or_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+    float dmin = or_f16_to_f32((uint16_t)(blk[2] | (blk[3] << 8)));
+    return i == 0 ? or_f32_to_f16(d * (float)sc) : or_f32_to_f16(-(dmin * (float)m));
+}
+
 void or_flat_decode(int type, const uint8_t *flat, long K, long N,
                     uint8_t *codes, uint16_t *scales)
 {
+    if (type == OR_Q4_K) {
+        long nb = K / 32;
+        for (long n = 0; n < N; n++) {
+            for (long k = 0; k < K; k++)
+                codes[n * K + k] = q4k_code(flat, K, n, k);
+            for (long b = 0; b < nb; b++)
+                for (int i = 0; i < 2; i++)
+                    scales[(n * nb + b) * 2 + i] = q4k_pair(flat, K, n, b, i);
+        }
+        return;
+    }
     long nb = K / 32, bb = or_block_bytes(type), ns = or_scale_count(type);
     for (long n = 0; n < N; n++) {
         for (long b = 0; b < nb; b++) {
@@ -208,6 +276,8 @@ void or_flat_decode(int type, const uint8_t *flat, long K, long N,
  * ------------------------------------------------------------------------- */
 static uint8_t code_at(int type, const uint8_t *flat, long K, long n, long k)
 {
+    if (type == OR_Q4_K)
+        return q4k_code(flat, K, n, k);
     long nb = K / 32, bb = or_block_bytes(type);
     const uint8_t *qs = flat + (n * nb + k / 32) * bb + quant_offset(type);
     int j = (int)(k % 32);
@@ -218,6 +288,8 @@ static uint8_t code_at(int type, const uint8_t *flat, long K, long n, long k)
 
 static uint16_t scale_at(int type, const uint8_t *flat, long K, long n, long kt, int i)
 {
+    if (type == OR_Q4_K)
+        return q4k_pair(flat, K, n, kt, i);
     long nb = K / 32, bb = or_block_bytes(type);
     return block_scale(type, flat + (n * nb + kt) * bb, i);
 }
@@ -230,7 +302,8 @@ static long scale_byte(int type, int row, int i)
 {
     switch (type) {
     case OR_MXFP4: return 512 + row;
-    case OR_Q4_1: return 512 + 4 * row + 2 * i;
+    case OR_Q4_1:
+    case OR_Q4_K: return 512 + 4 * row + 2 * i;
     case OR_Q8_0: return 1024 + 2 * row;
     }
     return 512 + 2 * row;
@@ -322,7 +395,9 @@ void or_unpack(int type, const uint8_t *tiles, long K, long N,
  * (0, 1, 2, 3, 4, 6, 8, 12 with sign), the factor 1/2 going to the scale.
  * Q4_1 ("Q4_1": a scale d and a min m per row): the integer weight is the
  * code itself, 0..15, and the weight value d * code + m (GGML's Q4_1); the
- * block dot is that of the codes, the min enters only the matmul.
+ * block dot is that of the codes, the min enters only the matmul.  Q4_K
+ * tiles are Q4_1 tiles ("K-Quants": same layout as the Q4_1 tile) whose pair
+ * is (d * sc, -dmin * m), so the same holds with those two values.
  * ------------------------------------------------------------------------- */
 static int e2m1_twice(uint8_t code)
 {
@@ -338,7 +413,8 @@ static int weight_value(int type, uint8_t code, const int8_t *lut)
     case OR_Q8_0: return (int)(int8_t)code;
     case OR_IQ4_NL: return (int)lut[code & 0x0f];
     case OR_MXFP4: return e2m1_twice(code & 0x0f);
-    case OR_Q4_1: return (int)code;
+    case OR_Q4_1:
+    case OR_Q4_K: return (int)code;
     }
     return 0;
 }
@@ -478,7 +554,7 @@ void or_matmul(int type, const uint8_t *tiles, long K, long N,
             double dw = or_row_scale(type, get_tile_scale(type, tile, row, 0));
             /* Q4_1: w = d * code + m (GGML's Q4_1; "Q4_1" names the pair d,
              * the scale, and m, the min) */
-            double mw = (type == OR_Q4_1)
+            double mw = (type == OR_Q4_1 || type == OR_Q4_K)
                 ? (double)or_f16_to_f32(get_tile_scale(type, tile, row, 1)) : 0.0;
             for (int col = 0; col < 32; col++) {
                 int cp = col / 2;

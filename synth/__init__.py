@@ -14,16 +14,27 @@ consecutive blocks; a Q4_0 / IQ4_NL block is 2 bytes of fp16 scale followed by
 16..31; a Q8_0 block is 2 bytes of fp16 scale followed by 32 int8 elements;
 an MXFP4 block is 1 byte of E8M0 scale followed by 16 nibble bytes ordered
 as in Q4_0; a Q4_1 block is 2 bytes of fp16 scale d, 2 bytes of fp16 min m,
-then 16 nibble bytes ordered as in Q4_0.
+then 16 nibble bytes ordered as in Q4_0.  A Q4_K super-block (256 elements)
+is fp16 d, fp16 dmin, 12 bytes packing eight 6-bit scales and eight 6-bit
+mins, then 128 bytes in which 64-element chunk c owns bytes 32c..32c+31
+(element 64c + i in the low nibble of byte 32c + i, element 64c + 32 + i in
+its high nibble).
 """
+import collections
 import dataclasses
 
 import numpy as np
 
-Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1 = 0, 1, 2, 3, 4
-TYPE_NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", IQ4_NL: "iq4_nl", MXFP4: "mxfp4", Q4_1: "q4_1"}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, IQ4_NL: 18, MXFP4: 17, Q4_1: 20}
-TILE_BYTES = {Q4_0: 576, Q8_0: 1088, IQ4_NL: 576, MXFP4: 544, Q4_1: 640}
+Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1, Q4_K = 0, 1, 2, 3, 4, 5
+TYPE_NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", IQ4_NL: "iq4_nl", MXFP4: "mxfp4", Q4_1: "q4_1",
+              Q4_K: "q4_k"}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, IQ4_NL: 18, MXFP4: 17, Q4_1: 20, Q4_K: 144}
+BLOCK_ELEMS = {Q4_K: 256}          # elements per flat block; 32 for the others
+TILE_BYTES = {Q4_0: 576, Q8_0: 1088, IQ4_NL: 576, MXFP4: 544, Q4_1: 640, Q4_K: 640}
+
+# Q4_K super-block parameters: fp16 bits of d and dmin [N, K/256], 6-bit
+# scale and min of each 32-element sub-block [N, K/32].
+Q4KScales = collections.namedtuple("Q4KScales", "d dmin sc m")
 
 # Stand-in for the 16-entry non-linear IQ4_NL table.  The page names the table
 # but does not print its values; any 16 int8 entries keep the integer path
@@ -57,10 +68,19 @@ def draw_scales(rng, dist, N, K):
     uniform in [118, 124], power-of-two scales 2^-9 .. 2^-3 (with E2M1 values
     up to 6, weights of magnitude up to about 0.75); 'minmax' -> Q4_1 pairs
     [N, K/32, 2]: d = fp16 of U[1e-3, 1e-2), m = fp16 of -d * U[6, 10] (a
-    block min below zero, codes 0..15 spanning [m, m + 15 d])."""
+    block min below zero, codes 0..15 spanning [m, m + 15 d]); 'q4k' -> a
+    Q4KScales of d, dmin = fp16 of U[1e-4, 1e-3) per super-block and 6-bit
+    scales and mins uniform 0..63 per sub-block."""
     shape = (N, K // 32)
     if dist == "e8m0":
         return rng.integers(118, 125, size=shape).astype(np.uint16)
+    if dist == "q4k":
+        nsb = K // 256
+        d = rng.uniform(1e-4, 1e-3, size=(N, nsb)).astype(np.float32).astype(np.float16)
+        dmin = rng.uniform(1e-4, 1e-3, size=(N, nsb)).astype(np.float32).astype(np.float16)
+        sc = rng.integers(0, 64, size=shape).astype(np.uint8)
+        m = rng.integers(0, 64, size=shape).astype(np.uint8)
+        return Q4KScales(d.view(np.uint16), dmin.view(np.uint16), sc, m)
     if dist == "minmax":
         d = rng.uniform(1e-3, 1e-2, size=shape)
         m = -d * rng.uniform(6.0, 10.0, size=shape)
@@ -75,9 +95,37 @@ def draw_scales(rng, dist, N, K):
     return s.astype(np.float32).astype(np.float16).view(np.uint16)
 
 
+def _pack_q4k(codes, p):
+    """GGML Q4_K super-blocks from codes [N, K] and a Q4KScales."""
+    N, K = codes.shape
+    nsb = K // 256
+    out = np.zeros((N, nsb, 144), np.uint8)
+    d = np.ascontiguousarray(p.d, dtype=np.uint16).reshape(N, nsb)
+    dmin = np.ascontiguousarray(p.dmin, dtype=np.uint16).reshape(N, nsb)
+    out[:, :, 0], out[:, :, 1] = d & 0xFF, d >> 8
+    out[:, :, 2], out[:, :, 3] = dmin & 0xFF, dmin >> 8
+    sc = np.asarray(p.sc, dtype=np.uint8).reshape(N, nsb, 8)
+    m = np.asarray(p.m, dtype=np.uint8).reshape(N, nsb, 8)
+    sb = out[:, :, 4:16]
+    for j in range(8):
+        if j < 4:
+            sb[:, :, j] |= sc[:, :, j]
+            sb[:, :, j + 4] |= m[:, :, j]
+        else:
+            sb[:, :, j + 4] = (sc[:, :, j] & 0xF) | ((m[:, :, j] & 0xF) << 4)
+            sb[:, :, j - 4] |= (sc[:, :, j] >> 4) << 6
+            sb[:, :, j] |= (m[:, :, j] >> 4) << 6
+    c = codes.astype(np.uint8).reshape(N, nsb, 4, 64)
+    out[:, :, 16:] = (c[:, :, :, :32] | (c[:, :, :, 32:] << 4)).reshape(N, nsb, 128)
+    return out.reshape(-1)
+
+
 def pack_flat(qtype, codes, scale_bits):
     """Write codes [N, K] and scale bits [N, K/32] (fp16, E8M0 bytes for
-    MXFP4, [N, K/32, 2] fp16 (d, m) pairs for Q4_1) as flat GGML blocks."""
+    MXFP4, [N, K/32, 2] fp16 (d, m) pairs for Q4_1, a Q4KScales for Q4_K) as
+    flat GGML blocks."""
+    if qtype == Q4_K:
+        return _pack_q4k(codes, scale_bits)
     N, K = codes.shape
     nb = K // 32
     bb = BLOCK_BYTES[qtype]
