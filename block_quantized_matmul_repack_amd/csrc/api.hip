@@ -18,8 +18,12 @@ constexpr int64_t MAX_MK = int64_t(1) << 36;
 
 bool valid_type(int t)
 {
-    return t == TQ_Q4_0 || t == TQ_Q8_0 || t == TQ_IQ4_NL || t == TQ_MXFP4 || t == TQ_Q4_1;
+    return t == TQ_Q4_0 || t == TQ_Q8_0 || t == TQ_IQ4_NL || t == TQ_MXFP4 || t == TQ_Q4_1 ||
+           t == TQ_Q4_K;
 }
+
+// The tile kernels a type runs on: Q4_K tiles are Q4_1 tiles.
+int kernel_type(int t) { return t == TQ_Q4_K ? TQ_Q4_1 : t; }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -29,6 +33,12 @@ bool valid_kn(int64_t K, int64_t N)
 }
 
 bool valid_mk(int64_t M, int64_t K) { return M >= 0 && M <= MAX_M && M * K < MAX_MK; }
+
+// K, N valid for `type`: Q4_K also needs whole 256-element super-blocks.
+bool valid_tkn(int type, int64_t K, int64_t N)
+{
+    return valid_kn(K, N) && (type != TQ_Q4_K || K % 256 == 0);
+}
 
 int launch_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_E_LAUNCH; }
 
@@ -59,7 +69,7 @@ int check_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t
 {
     if (!valid_type(type))
         return TQ_E_TYPE;
-    if (!valid_kn(K, N) || !valid_mk(M, K) || ldy < N)
+    if (!valid_tkn(type, K, N) || !valid_mk(M, K) || ldy < N)
         return TQ_E_SHAPE;
     if (M == 0 || N == 0)
         return TQ_OK;
@@ -83,6 +93,7 @@ size_t tq_tile_bytes(int type)
     case TQ_IQ4_NL: return tq::Fmt<TQ_IQ4_NL>::tile;
     case TQ_MXFP4: return tq::Fmt<TQ_MXFP4>::tile;
     case TQ_Q4_1: return tq::Fmt<TQ_Q4_1>::tile;
+    case TQ_Q4_K: return tq::Fmt<TQ_Q4_K>::tile;
     }
     return 0;
 }
@@ -95,27 +106,28 @@ size_t tq_block_bytes(int type)
     case TQ_IQ4_NL: return tq::Fmt<TQ_IQ4_NL>::block;
     case TQ_MXFP4: return tq::Fmt<TQ_MXFP4>::block;
     case TQ_Q4_1: return tq::Fmt<TQ_Q4_1>::block;
+    case TQ_Q4_K: return tq::Fmt<TQ_Q4_K>::block;
     }
     return 0;
 }
 
 size_t tq_tiled_bytes(int type, int64_t K, int64_t N)
 {
-    if (!valid_type(type) || !valid_kn(K, N))
+    if (!valid_type(type) || !valid_tkn(type, K, N))
         return 0;
     return (size_t)(K / 32) * (size_t)((N + 31) / 32) * tq_tile_bytes(type);
 }
 
 size_t tq_flat_bytes(int type, int64_t K, int64_t N)
 {
-    if (!valid_type(type) || !valid_kn(K, N))
+    if (!valid_type(type) || !valid_tkn(type, K, N))
         return 0;
-    return (size_t)N * (size_t)(K / 32) * tq_block_bytes(type);
+    return (size_t)N * (size_t)(K / (type == TQ_Q4_K ? 256 : 32)) * tq_block_bytes(type);
 }
 
 int tq_supported(int type, int64_t K, int64_t N, int64_t M, int path)
 {
-    if (!valid_type(type) || !valid_kn(K, N) || !valid_mk(M, K))
+    if (!valid_type(type) || !valid_tkn(type, K, N) || !valid_mk(M, K))
         return 0;
     if (path == TQ_PATH_GEMV)
         return M <= 8;
@@ -140,13 +152,14 @@ int tq_repack_tiles(int type, const void *flat, int64_t K, int64_t N, void *tile
 {
     if (!valid_type(type))
         return TQ_E_TYPE;
-    if (!valid_kn(K, N))
+    if (!valid_tkn(type, K, N))
         return TQ_E_SHAPE;
     if (N == 0)
         return TQ_OK;
     if (!flat || !tiles)
         return TQ_E_NULL;
-    if (!aligned(flat, (type == TQ_MXFP4 || type == TQ_Q4_1) ? 4 : 2) || !aligned(tiles, 16))
+    const uintptr_t fa = type == TQ_Q4_K ? 16 : ((type == TQ_MXFP4 || type == TQ_Q4_1) ? 4 : 2);
+    if (!aligned(flat, fa) || !aligned(tiles, 16))
         return TQ_E_ALIGN;
     return launch_status(tq::launch_repack(type, flat, K, N, tiles, stream));
 }
@@ -170,7 +183,7 @@ int tq_quantize_act(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
 
 size_t tq_qgemv_workspace_bytes(int type, int64_t K, int64_t N, int64_t M)
 {
-    if (!valid_type(type) || !valid_kn(K, N) || N == 0 || M < 1 || M > 8)
+    if (!valid_type(type) || !valid_tkn(type, K, N) || N == 0 || M < 1 || M > 8)
         return 0;
     return tq::gemv_workspace_bytes(K, N, M);
 }
@@ -187,7 +200,7 @@ int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
     if (workspace && !aligned(workspace, 256))
         return TQ_E_ALIGN;
     const tq::Act act{q, d, nullptr, -1, 0};
-    return launch_status(tq::launch_qgemv(type, tiles, K, N, act, M, pack_lut(type, lut), y, ldy,
+    return launch_status(tq::launch_qgemv(kernel_type(type), tiles, K, N, act, M, pack_lut(type, lut), y, ldy,
                                           nullptr, workspace, workspace_bytes, stream));
 }
 
@@ -211,7 +224,7 @@ int tq_qgemv_x(int type, const void *tiles, int64_t K, int64_t N, int dtype, con
     if (!aligned(x, dtype == TQ_F32 ? 4 : 2) || (workspace && !aligned(workspace, 256)))
         return TQ_E_ALIGN;
     const tq::Act act{nullptr, nullptr, x, dtype, ldx};
-    return launch_status(tq::launch_qgemv(type, tiles, K, N, act, M, pack_lut(type, lut), y, ldy,
+    return launch_status(tq::launch_qgemv(kernel_type(type), tiles, K, N, act, M, pack_lut(type, lut), y, ldy,
                                           nullptr, workspace, workspace_bytes, stream));
 }
 
@@ -223,7 +236,7 @@ int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
     if (st != TQ_OK || M == 0 || N == 0)
         return st;
     return launch_status(
-        tq::launch_qgemm(type, tiles, K, N, q, d, M, pack_lut(type, lut), y, ldy, nullptr, stream));
+        tq::launch_qgemm(kernel_type(type), tiles, K, N, q, d, M, pack_lut(type, lut), y, ldy, nullptr, stream));
 }
 
 int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
@@ -251,9 +264,9 @@ int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N, const int8_
     const tq::Lut t = pack_lut(type, lut);
     const tq::Act act{q, nullptr, nullptr, -1, 0};
     hipError_t e = (path == TQ_PATH_GEMV)
-                       ? tq::launch_qgemv(type, tiles, K, N, act, M, t, nullptr, N, isum,
+                       ? tq::launch_qgemv(kernel_type(type), tiles, K, N, act, M, t, nullptr, N, isum,
                                           nullptr, 0, stream)
-                       : tq::launch_qgemm(type, tiles, K, N, q, nullptr, M, t, nullptr, N,
+                       : tq::launch_qgemm(kernel_type(type), tiles, K, N, q, nullptr, M, t, nullptr, N,
                                           isum, stream);
     return launch_status(e);
 }

@@ -61,6 +61,54 @@ __device__ __forceinline__ void load_mx_block(const uint8_t *__restrict__ flat, 
     }
 }
 
+// One Q4_K super-block of row r (16-byte aligned, 144 bytes) into the 8
+// tiles' LDS staging of k_repack: for sub-block j, the 16 bytes of a flat
+// 32-element block (element e low, e + 16 high nibble, as Q4_0) and the pair
+// (fp16 d * sc_j, fp16 -(dmin * m_j)), products exact in fp32, rounded to
+// nearest even.  valid = false stages zeros.
+template <int TP>
+__device__ __forceinline__ void stage_q4k(const uint8_t *__restrict__ blk, bool valid, int r,
+                                          uint16_t (*qs)[TP], uint32_t (*sc)[32])
+{
+    uint32_t w[36];
+#pragma unroll
+    for (int v = 0; v < 9; v++) {
+        const u32x4 x = valid ? *(const u32x4 *)(blk + 16 * v) : u32x4{0, 0, 0, 0};
+        w[4 * v] = x.x;
+        w[4 * v + 1] = x.y;
+        w[4 * v + 2] = x.z;
+        w[4 * v + 3] = x.w;
+    }
+    const float d = f16_bits_to_f32((uint16_t)w[0]);
+    const float dmin = f16_bits_to_f32((uint16_t)(w[0] >> 16));
+    auto sbyte = [&](int k) { return (w[1 + k / 4] >> (8 * (k % 4))) & 0xFFu; };   // scales[k]
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        uint32_t s6, m6;
+        if (j < 4) {
+            s6 = sbyte(j) & 63u;
+            m6 = sbyte(j + 4) & 63u;
+        } else {
+            s6 = (sbyte(j + 4) & 15u) | ((sbyte(j - 4) >> 6) << 4);
+            m6 = (sbyte(j + 4) >> 4) | ((sbyte(j) >> 6) << 4);
+        }
+        // -dmin * m is -(dmin * m) bit for bit, signed zeros included
+        const uint32_t a = f16_of_product(d, (float)s6);
+        const uint32_t b = f16_of_product(-dmin, (float)m6);
+        sc[j][r] = valid ? (a | (b << 16)) : 0u;
+        // sub-block j = nibble j % 2 of 64-element chunk j / 2
+        const int c = j >> 1;
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const uint32_t lo = w[4 + 8 * c + v], hi = w[4 + 8 * c + 4 + v];   // elements v.., 16 + v..
+            const uint32_t o = (j & 1) ? (((lo >> 4) & 0x0F0F0F0Fu) | (hi & 0xF0F0F0F0u))
+                                       : ((lo & 0x0F0F0F0Fu) | ((hi & 0x0F0F0F0Fu) << 4));
+            qs[j][32 * (2 * v) + r] = (uint16_t)o;
+            qs[j][32 * (2 * v + 1) + r] = (uint16_t)(o >> 16);
+        }
+    }
+}
+
 template <int QT>
 __global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ flat,
                                                     int64_t nb, int64_t N,
@@ -68,14 +116,16 @@ __global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ 
 {
     constexpr bool MX = QT == TQ_MXFP4;
     constexpr bool Q41 = QT == TQ_Q4_1;
+    constexpr bool Q4K = QT == TQ_Q4_K;
     constexpr int BB = Fmt<QT>::block;          // flat block bytes (scales + quants)
     constexpr int QOFF = MX ? 1 : (Q41 ? 4 : 2);// offset of the quants in a block
-    constexpr int QH = (BB - QOFF) / 2;         // quant halfwords per block: 8 or 16
+    constexpr int QH = Q4K ? 8 : (BB - QOFF) / 2;   // quant halfwords per tile row: 8 or 16
     constexpr int TS = Fmt<QT>::tile;
     constexpr int CH = TS / 16;                 // 16-byte chunks per tile: 36, 68 or 34
     constexpr int QCH = Fmt<QT>::scale_off / 16;// chunks of quants (the rest hold scales)
     // a row's scale bytes in the tile: E8M0 byte, fp16 d, or fp16 pair (d, m)
-    using Scale = std::conditional_t<MX, uint8_t, std::conditional_t<Q41, uint32_t, uint16_t>>;
+    using Scale =
+        std::conditional_t<MX, uint8_t, std::conditional_t<Q41 || Q4K, uint32_t, uint16_t>>;
     constexpr int SPC = 16 / (int)sizeof(Scale);// row scales per 16-byte chunk
     // each tile's halfword columns padded by 16 bytes: the lanes of a store
     // differ in t, and a tile stride of 16 mod 256 bytes spreads them over
@@ -88,9 +138,19 @@ __global__ __launch_bounds__(THREADS) void k_repack(const uint8_t *__restrict__ 
     const int64_t kt0 = (int64_t)blockIdx.y * KT;
     const int te = (int)min<int64_t>(KT, nb - kt0);
 
+    if constexpr (Q4K) {
+        // item = (row r, super-block): 8 tiles at once (te is a multiple of 8)
+        const int nsb = te / 8;
+        for (int i = threadIdx.x; i < nsb * 32; i += THREADS) {
+            const int r = i / nsb, sb = i - r * nsb;
+            const int64_t n = 32 * ct + r;
+            const uint8_t *blk = flat + ((n < N ? n : 0) * (nb / 8) + kt0 / 8 + sb) * BB;
+            stage_q4k<TP>(blk, n < N, r, &qs[8 * sb], &sc[8 * sb]);
+        }
+    }
     // Load: item i = (row r = i / te, tile t = i % te), so a wave reads a few
     // contiguous runs of blocks; rows past N are zero.
-    for (int i = threadIdx.x; i < te * 32; i += THREADS) {
+    for (int i = threadIdx.x; i < (Q4K ? 0 : te * 32); i += THREADS) {
         const int r = i / te, t = i - r * te;
         const int64_t n = 32 * ct + r;
         uint16_t q[QH];
@@ -176,6 +236,7 @@ hipError_t launch_repack(int type, const void *flat, int64_t K, int64_t N, void 
     case TQ_Q8_0: k_repack<TQ_Q8_0><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
     case TQ_MXFP4: k_repack<TQ_MXFP4><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
     case TQ_Q4_1: k_repack<TQ_Q4_1><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
+    case TQ_Q4_K: k_repack<TQ_Q4_K><<<grid, THREADS, 0, s>>>(f, nb, N, t); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

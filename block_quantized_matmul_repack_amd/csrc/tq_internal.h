@@ -28,6 +28,10 @@ template <> struct Fmt<TQ_MXFP4> {
 template <> struct Fmt<TQ_Q4_1> {
     static constexpr int tile = 640, scale_off = 512, block = 20;
 };
+// Q4_K: Q4_1 tiles; `block` is one 256-element flat super-block
+template <> struct Fmt<TQ_Q4_K> {
+    static constexpr int tile = 640, scale_off = 512, block = 144;
+};
 
 // Raw buffer loads (CDNA buffer resource descriptor, stride 0): a load whose
 // byte offset lies outside [0, bytes) returns zero, so out-of-range operands
@@ -65,6 +69,17 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b)
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
 {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// fp16 bits of the product a * b, formed in fp32 and rounded once to nearest
+// even, with IEEE signed zeros.  The empty asm keeps the product an fp32
+// value: otherwise the compiler fuses multiply and conversion into a mixed
+// fma with a +0 addend (v_fma_mixlo_f16), which turns a -0 product into +0.
+__device__ __forceinline__ uint16_t f16_of_product(float a, float b)
+{
+    float p = a * b;
+    asm volatile("" : "+v"(p));
+    return f32_to_f16_bits(p);
 }
 
 // Eight consecutive activation elements of dtype DT from index i, converted

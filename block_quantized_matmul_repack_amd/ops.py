@@ -10,7 +10,7 @@ import torch
 
 from ._lib import TiledqError, check, lib
 
-Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1 = 0, 1, 2, 3, 4
+Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1, Q4_K = 0, 1, 2, 3, 4, 5
 F32, BF16, F16 = 0, 1, 2
 PATH_GEMV, PATH_GEMM = 0, 1
 

@@ -30,6 +30,9 @@
  *     Q4_1   640 B: the Q4_0 nibble layout of codes 0..15; bytes 512 + 4*row
  *            hold row's fp16 scale d, bytes 514 + 4*row its fp16 min m.
  *            Weight = d * quant + m.
+ *     Q4_K   640 B: a Q4_1 tile ("K-Quants") whose pair is (d * sc, -dmin * m)
+ *            of the 32-k sub-block: fp32 products rounded to fp16
+ *            nearest-even.  Computed exactly like Q4_1.
  *   Rows n >= N of the last row-tile are zero (codes 0, scale +0.0).
  *
  *   Flat source ("repacked from flat row-major GGML layouts"): row n holds
@@ -37,6 +40,12 @@
  *   nibbles elements 0..15, high nibbles 16..31), 18 B; Q8_0 = fp16 d + 32
  *   int8, 34 B; MXFP4 = E8M0 byte e + 16 bytes in the Q4_0 nibble order,
  *   17 B; Q4_1 = fp16 d + fp16 m + 16 bytes in the Q4_0 nibble order, 20 B.
+ *   Q4_K: 256-element super-blocks of 144 B (K % 256 == 0, else
+ *   TQ_E_SHAPE): fp16 d, fp16 dmin, 12 bytes of eight 6-bit scales sc and
+ *   mins m (sub-block j < 4: low 6 bits of bytes j, j + 4; j >= 4: the low /
+ *   high nibble of byte j + 4 plus the top 2 bits of byte j - 4 / j), then
+ *   128 nibble bytes: 64-element chunk c at bytes 32c.., its first 32
+ *   elements in the low nibbles.
  *
  *   Activations (section "Memory buffers": dynamically quantized activations,
  *   used as Q8_0 activation tiles by the vector dot of "Q2_0 Format"): per
@@ -65,7 +74,8 @@
  *     every output untouched.  M == 0 or N == 0 is TQ_OK with no launch.
  *   - The library is stateless; calls on different streams may run
  *     concurrently.  Outputs of concurrent calls must not overlap.
- *   - Shapes: 32 <= K <= 2^20 with K % 32 == 0; 0 <= N <= 2^30;
+ *   - Shapes: 32 <= K <= 2^20 with K % 32 == 0 (Q4_K: K % 256 == 0);
+ *     0 <= N <= 2^30;
  *     0 <= M <= 2^20; K*N and M*K each below 2^40.
  */
 #ifndef TILEDQ_H
@@ -80,7 +90,9 @@
 extern "C" {
 #endif
 
-typedef enum { TQ_Q4_0 = 0, TQ_Q8_0 = 1, TQ_IQ4_NL = 2, TQ_MXFP4 = 3, TQ_Q4_1 = 4 } tq_type;
+typedef enum {
+    TQ_Q4_0 = 0, TQ_Q8_0 = 1, TQ_IQ4_NL = 2, TQ_MXFP4 = 3, TQ_Q4_1 = 4, TQ_Q4_K = 5
+} tq_type;
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 typedef enum {
     TQ_OK = 0,
@@ -95,17 +107,19 @@ typedef enum {
 typedef enum { TQ_PATH_GEMV = 0, TQ_PATH_GEMM = 1 } tq_path;
 
 /* Bytes of one tile ("Block-32 Quantized Formats"): 576, 1088, 576, 544,
- * 640; 0 for an unknown type. */
+ * 640, 640; 0 for an unknown type. */
 size_t tq_tile_bytes(int type);
 
-/* Bytes of one flat GGML block: 18, 34, 18, 17, 20; 0 for an unknown type. */
+/* Bytes of one flat GGML block: 18, 34, 18, 17, 20 (32 elements each), and
+ * 144 for a 256-element Q4_K super-block; 0 for an unknown type. */
 size_t tq_block_bytes(int type);
 
 /* (K/32) * ((N+31)/32) * tq_tile_bytes(type) ("Tile Dimensions and Grid
  * Layout"); 0 if the shape or type is invalid. */
 size_t tq_tiled_bytes(int type, int64_t K, int64_t N);
 
-/* N * (K/32) * tq_block_bytes(type); 0 if the shape or type is invalid. */
+/* N * (K/32) * tq_block_bytes(type) (Q4_K: N * (K/256) * 144); 0 if the
+ * shape or type is invalid. */
 size_t tq_flat_bytes(int type, int64_t K, int64_t N);
 
 /* 1 if (type, K, N, M) is supported by `path` (TQ_PATH_GEMV needs
@@ -118,7 +132,7 @@ const char *tq_status_string(int status);
 /* Repack flat GGML blocks into tiles ("Tiled Weight Formats": repacking at
  * model load or at run time).
  *   flat  : device, tq_flat_bytes(type, K, N) bytes, 2-byte aligned
- *           (TQ_MXFP4, TQ_Q4_1: 4-byte aligned).
+ *           (TQ_MXFP4, TQ_Q4_1: 4-byte aligned; TQ_Q4_K: 16-byte aligned).
  *   tiles : device, tq_tiled_bytes(type, K, N) bytes, 16-byte aligned; fully
  *           written, padding rows included.  Must not overlap `flat`.
  * Bit-exact byte permutation; deterministic. */
@@ -201,7 +215,8 @@ int tq_matmul(int type, const void *tiles, int64_t K, int64_t N,
  * isum[(m*N + n)*(K/32) + kt] (int32, device, 4-byte aligned) =
  * sum_{j<32} w_int[n][32kt+j] * q[m][32kt+j], for m < M, n < N, with w_int
  * = code - 8 (Q4_0), the int8 (Q8_0), lut[code] (IQ4_NL), 2 * E2M1(code)
- * (MXFP4) or the code itself (Q4_1, whose min is not part of the block dot). */
+ * (MXFP4) or the code itself (Q4_1 and Q4_K, whose min is not part of the
+ * block dot). */
 int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N,
                   const int8_t *q, int64_t M, const int8_t *lut,
                   int32_t *isum, int path, hipStream_t stream);

@@ -23,7 +23,7 @@ def seed_for(*parts):
 
 def make(qtype, K, N, M, seed=0, dist=None, act="f32"):
     dist = dist or {synth.Q8_0: "absnormal", synth.MXFP4: "e8m0",
-                    synth.Q4_1: "minmax"}.get(qtype, "uniform")
+                    synth.Q4_1: "minmax", synth.Q4_K: "q4k"}.get(qtype, "uniform")
     w = synth.Workload("t", qtype, K, N, M, dist, act_dtype=act, seed=seed)
     return synth.make_inputs(w)
 

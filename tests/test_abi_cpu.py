@@ -42,10 +42,13 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_sizes_match_oracle(L, orc):
-    for t in (0, 1, 2, 3, 4):
+    for t in (0, 1, 2, 3, 4, 5):
         assert L.tq_tile_bytes(t) == orc.tile_bytes(t)
         assert L.tq_block_bytes(t) == orc.block_bytes(t)
-        for K, N in ((32, 1), (4096, 4096), (4096, 14336), (4096, 128001), (96, 70)):
+        for K, N in ((32, 1), (4096, 4096), (4096, 14336), (4096, 128001), (96, 70), (768, 3)):
+            if t == 5 and K % 256:
+                assert L.tq_tiled_bytes(t, K, N) == 0 and L.tq_flat_bytes(t, K, N) == 0
+                continue
             assert L.tq_tiled_bytes(t, K, N) == orc.tiled_bytes(t, K, N)
             assert L.tq_flat_bytes(t, K, N) == orc.flat_bytes(t, K, N)
     assert L.tq_tile_bytes(7) == 0
@@ -58,7 +61,9 @@ def test_supported_static_properties(L):
     assert L.tq_supported(2, 4096, 4096, 512, 1) == 1
     assert L.tq_supported(3, 4096, 4096, 1, 0) == 1          # MXFP4
     assert L.tq_supported(4, 4096, 4096, 1, 0) == 1          # Q4_1
-    assert L.tq_supported(5, 4096, 4096, 1, 0) == 0
+    assert L.tq_supported(5, 4096, 4096, 1, 0) == 1          # Q4_K
+    assert L.tq_supported(5, 4128, 4096, 1, 0) == 0          # K % 256 != 0
+    assert L.tq_supported(6, 4096, 4096, 1, 0) == 0
     assert L.tq_supported(0, 4001, 4096, 1, 0) == 0
     assert L.tq_supported(0, 4096, 4096, 1, 5) == 0
 
@@ -98,6 +103,9 @@ def test_repack_validation(L):
     assert L.tq_repack_tiles(0, NUL, 64, 0, NUL, NUL) == 0       # empty: OK, no launch
     assert L.tq_repack_tiles(3, A2, 64, 32, A16, NUL) == 4       # MXFP4 flat: 4-byte aligned
     assert L.tq_repack_tiles(4, A2, 64, 32, A16, NUL) == 4       # Q4_1 flat: 4-byte aligned
+    assert L.tq_repack_tiles(5, ctypes.c_void_p(0x10004), 256, 32, A16, NUL) == 4   # Q4_K: 16
+    assert L.tq_repack_tiles(5, A16, 288, 32, A16, NUL) == 3     # Q4_K: K % 256
+    assert L.tq_qgemv(5, A16, 288, 32, A16, A16, 1, NUL, A16, 32, NUL, 0, NUL) == 3
 
 
 def test_quantize_validation(L):

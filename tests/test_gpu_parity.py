@@ -16,6 +16,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1 = synth.Q4_0, synth.Q8_0, synth.IQ4_NL, synth.MXFP4, synth.Q4_1
+Q4_K = synth.Q4_K
 TYPES = [Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1]
 LUT = synth.IQ4_NL_STANDIN_LUT
 
@@ -348,3 +349,60 @@ def test_q4_1_min_term(tq, M):
     if M <= 8:
         yx = tq.qgemv_x(Q4_1, tdev, K, N, torch.from_numpy(x).cuda())
         check_y(yx.cpu().numpy(), y_ref, acond, ("q4_1 min fused", M))
+
+
+Q4K_SHAPES = [(256, 1), (256, 33), (512, 65), (1024, 97), (4096, 100)]
+
+
+@pytest.mark.parametrize("K,N", Q4K_SHAPES)
+def test_q4_k_repack_bitexact(tq, K, N):
+    """Q4_K super-blocks -> tiles: quant bytes and the fp16 pair products."""
+    inp = make(Q4_K, K, N, 1, seed=K + N)
+    ref = oracle.repack(Q4_K, inp.flat, K, N)
+    out = torch.full((ref.size + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    tq.repack_tiles(Q4_K, torch.from_numpy(inp.flat).cuda(), K, N, out=out[:ref.size])
+    got = out.cpu().numpy()
+    bad = np.nonzero(got[:ref.size] != ref)[0]
+    assert bad.size == 0, [(int(b) // 640, int(b) % 640, int(got[b]), int(ref[b])) for b in bad[:12]]
+    assert (got[ref.size:] == 0xA5).all()
+
+
+def test_q4_k_extreme_scales(tq):
+    """All 6-bit scale / min values, d and dmin from subnormal to large and of
+    either sign, zeros included (the fp16 products round, overflow to inf,
+    or are zeros of either sign)."""
+    K, N = 256, 64
+    rng = np.random.default_rng(5)
+    codes = synth.draw_codes(rng, Q4_K, N, K)
+    p = synth.draw_scales(rng, "q4k", N, K)
+    p.sc[:] = np.arange(N * 8).reshape(N, 8) % 64
+    p.m[:] = (np.arange(N * 8).reshape(N, 8) * 5) % 64
+    vals = np.array([2.0 ** -24, 6.1e-5, 0.0999, 1.0, 1000.0, 2000.0, 65504.0, 0.0,
+                     -0.0, -1.0, -0.375, -2.0 ** -20], np.float16)
+    p.d[:, 0] = vals[np.arange(N) % len(vals)].view(np.uint16)
+    p.dmin[:, 0] = vals[(np.arange(N) * 5) % len(vals)].view(np.uint16)
+    flat = synth.pack_flat(Q4_K, codes, p)
+    ref = oracle.repack(Q4_K, flat, K, N)
+    got = tq.repack_tiles(Q4_K, torch.from_numpy(flat).cuda(), K, N).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 9, 130])
+@pytest.mark.parametrize("K,N", [(256, 33), (1024, 97), (4096, 100)])
+def test_q4_k_products(tq, M, K, N):
+    """Block dots (both kernels) bit-exact, y within tolerance, fused decode."""
+    inp = make(Q4_K, K, N, M, seed=M * 17 + K + N)
+    tiles, tdev = _dev(inp, Q4_K, K, N)
+    q, d = oracle.quantize_act(inp.x)
+    qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+    ref = oracle.block_dots(Q4_K, tiles, K, N, q)
+    paths = [tq.PATH_GEMM] + ([tq.PATH_GEMV] if M <= 8 else [])
+    for path in paths:
+        got = tq.block_dots(Q4_K, tdev, K, N, qd, path=path).cpu().numpy()
+        assert np.array_equal(got, ref), path
+    y_ref, acond = oracle.matmul(Q4_K, tiles, K, N, q, d)
+    check_y(tq.matmul(Q4_K, tdev, K, N, qd, dd).cpu().numpy(), y_ref, acond, ("q4_k", M, K, N))
+    check_y(tq.qgemm(Q4_K, tdev, K, N, qd, dd).cpu().numpy(), y_ref, acond, ("q4_k gemm", M, K, N))
+    if M <= 8:
+        yx = tq.qgemv_x(Q4_K, tdev, K, N, torch.from_numpy(inp.x).cuda())
+        check_y(yx.cpu().numpy(), y_ref, acond, ("q4_k fused", M, K, N))
