@@ -45,12 +45,12 @@ ROTATE_BYTES = 1 << 30         # defeat the 256 MB Infinity Cache
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "decode": {"fetch_kib": 8779.52, "write_kib": 112.0,
-               "src": "65a452c120782a67bcb7a698c21d5e409ef84d53e0f04baadc3a5e0d607ed904"},
-    "gemm": {"fetch_kib": 13363.18, "write_kib": 8192.0,
-             "src": "cad6aa91d9b39e2d1ff51229686e2593aa22682e90886692d124690d34599749"},
-    "repack": {"fetch_kib": 16161.07, "write_kib": 32256.0,
-               "src": "400031de737dc36b1f2b468107153240bb35e2de939add632c5a18dbf5c3b773"},
+    "decode": {"fetch_kib": 8779.91, "write_kib": 112.0,
+              "src": "9167a7389661e2092b8c44984affcf77aca9c3c33ef66a8c0f09febffe36ebf7"},
+    "gemm": {"fetch_kib": 13368.15, "write_kib": 8192.0,
+            "src": "b0b552de170f56cdfee02de99d977245410e88562483a47a7b9c6cbe487370c2"},
+    "repack": {"fetch_kib": 16143.81, "write_kib": 32256.0,
+              "src": "2cb14a99a3044ab768aa5099b093a2d3a1c6cfb56ddc8dc09e1368e7f1e1646a"},
 }
 KERNEL_SOURCES = {
     "decode": ("qgemv.hip", "tq_internal.h"),
@@ -276,7 +276,7 @@ def measure_others(torch, tq, synth):
              ("q8_0_lmhead_k4096_n128001_m128", 128), ("mxfp4_gemv_k4096_n14336_m1", 1),
              ("mxfp4_gemv_k4096_n14336_m1", 4), ("mxfp4_gemm_m512_k4096_n4096", 512),
              ("q4_1_gemv_k4096_n14336_m1", 1), ("q4_1_gemv_k4096_n14336_m1", 4),
-             ("q4_1_gemm_m512_k4096_n4096", 512)]
+             ("q4_1_gemm_m512_k4096_n4096", 512), ("q4_k_gemv_k4096_n14336_m1", 1)]
     tiles_cache = {}
     for name, M in cases:
         w = synth.WORKLOADS[name]
@@ -325,6 +325,23 @@ def measure_others(torch, tq, synth):
                                     "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                                     "TOPS": round(2.0 * M * w.N * w.K / us / 1e6, 2)}
     tiles_cache.clear()
+    # repack of every type at the FFN shape (flat copies rotate over >= 1 GiB)
+    for qtype in (synth.Q8_0, synth.IQ4_NL, synth.MXFP4, synth.Q4_1, synth.Q4_K):
+        w = synth.Workload("repack", qtype, 4096, 14336, 1,
+                           {synth.Q8_0: "absnormal", synth.MXFP4: "e8m0", synth.Q4_1: "minmax",
+                            synth.Q4_K: "q4k"}.get(qtype, "uniform"))
+        inp = synth.make_inputs(w)
+        fb = inp.flat.size
+        flats = [torch.from_numpy(inp.flat).cuda() for _ in range(min(32, max(2, -(-ROTATE_BYTES // fb))))]
+        out = torch.empty(w.weight_bytes, dtype=torch.uint8, device="cuda")
+        f = lambda i: tq.repack_tiles(qtype, flats[i % len(flats)], w.K, w.N, out=out)
+        for i in range(3):
+            f(i)
+        us = kernel_us(torch, f, 30)
+        gbs = (fb + w.weight_bytes) / us / 1e3
+        res[f"repack {synth.TYPE_NAMES[qtype]}_k4096_n14336"] = {
+            "kernel_us": round(us, 3), "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del flats, out
     return res
 
 
