@@ -61,6 +61,10 @@ def lib():
         L.or_block_dots.restype = ctypes.c_int
         L.or_matmul.argtypes = [ctypes.c_int, P, l, l, P, P, l, P, l, l, P, P, l]
         L.or_matmul.restype = None
+        L.or_block_dots_flat.argtypes = [ctypes.c_int, P, l, l, P, l, P, P]
+        L.or_block_dots_flat.restype = ctypes.c_int
+        L.or_matmul_flat.argtypes = [ctypes.c_int, P, l, l, P, P, l, P, l, l, P, P, l]
+        L.or_matmul_flat.restype = None
         L.or_row_scale.argtypes = [ctypes.c_int, ctypes.c_uint16]
         L.or_row_scale.restype = ctypes.c_double
         _lib = L
@@ -204,3 +208,32 @@ def matmul(t, tiles, K, N, q, d, lut=None, n0=0, n1=None):
     lib().or_matmul(t, _p(tiles), K, N, _p(q), _p(d), M, _p(lut), n0, n1,
                     _p(y), _p(acond), N)
     return y, acond
+
+
+def block_dots_flat(t, flat, K, N, q, lut=None):
+    """Integer block dots int32 [M, N, K/32] over flat GGML blocks."""
+    flat = _c(flat, np.uint8)
+    assert flat.size == flat_bytes(t, K, N)
+    q = _c(q, np.int8)
+    M = q.shape[0]
+    lut = None if lut is None else _c(lut, np.int8)
+    isum = np.zeros((M, N, K // 32), np.int32)
+    if lib().or_block_dots_flat(t, _p(flat), K, N, _p(q), M, _p(lut), _p(isum)) != 0:
+        raise ValueError("block_dots_flat: int32 overflow")
+    return isum
+
+
+def matmul_flat(t, flat, K, N, q, d, lut=None, n0=0, n1=None):
+    """As matmul, over flat GGML blocks."""
+    flat = _c(flat, np.uint8)
+    assert flat.size == flat_bytes(t, K, N)
+    q = _c(q, np.int8)
+    d = _c(d, np.uint16)
+    M = q.shape[0]
+    n1 = N if n1 is None else min(n1, N)
+    lut = None if lut is None else _c(lut, np.int8)
+    y = np.zeros((M, N), np.float64)
+    acond = np.zeros((M, N), np.float64)
+    lib().or_matmul_flat(t, _p(flat), K, N, _p(q), _p(d), M, _p(lut), n0, n1, _p(y), _p(acond), N)
+    return y, acond
+

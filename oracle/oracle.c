@@ -579,3 +579,68 @@ void or_matmul(int type, const uint8_t *tiles, long K, long N,
     }
     free(wrow);
 }
+
+/* ---------------------------------------------------------------------------
+ * The same products over flat GGML blocks ("supports_op Independence from
+ * Buffer and Repack State": a supported type must work tiled and flat, the
+ * flat form being what test harnesses and non-weight tensors use).  Weights
+ * are read from the flat blocks directly (code_at, scale_at), with the
+ * values a tile of the same data holds; so the results equal those of
+ * or_block_dots / or_matmul on or_repack's tiles.
+ * ------------------------------------------------------------------------- */
+static double flat_weight(int type, const uint8_t *flat, long K, long n, long k,
+                          const int8_t *lut)
+{
+    long kt = k / 32;
+    uint8_t c = code_at(type, flat, K, n, k);
+    double dw = or_row_scale(type, scale_at(type, flat, K, n, kt, 0));
+    double mw = (type == OR_Q4_1 || type == OR_Q4_K)
+        ? (double)or_f16_to_f32(scale_at(type, flat, K, n, kt, 1)) : 0.0;
+    return dw * (double)weight_value(type, c, lut) + mw;
+}
+
+int or_block_dots_flat(int type, const uint8_t *flat, long K, long N,
+                       const int8_t *q, long M, const int8_t *lut, int32_t *isum)
+{
+    long nb = K / 32;
+    for (long n = 0; n < N; n++)
+        for (long m = 0; m < M; m++)
+            for (long kt = 0; kt < nb; kt++) {
+                int64_t s = 0;
+                for (int j = 0; j < 32; j++)
+                    s += (int64_t)weight_value(type, code_at(type, flat, K, n, 32 * kt + j), lut) *
+                         (int64_t)q[m * K + kt * 32 + j];
+                if (s > INT32_MAX || s < INT32_MIN)
+                    return -1;
+                isum[(m * N + n) * nb + kt] = (int32_t)s;
+            }
+    return 0;
+}
+
+void or_matmul_flat(int type, const uint8_t *flat, long K, long N,
+                    const int8_t *q, const uint16_t *d, long M, const int8_t *lut,
+                    long n0, long n1, double *y, double *acond, long ldy)
+{
+    long nb = K / 32;
+    if (n1 > N)
+        n1 = N;
+    double *wrow = malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    for (long n = n0; n < n1; n++) {
+        for (long k = 0; k < K; k++)
+            wrow[k] = flat_weight(type, flat, K, n, k, lut);
+        for (long m = 0; m < M; m++) {
+            double s = 0.0, a = 0.0;
+            for (long k = 0; k < K; k++) {
+                double act = (double)or_f16_to_f32(d[m * nb + k / 32]) * (double)q[m * K + k];
+                double t = wrow[k] * act;
+                s += t;
+                a += fabs(t);
+            }
+            y[m * ldy + n] = s;
+            if (acond)
+                acond[m * ldy + n] = a;
+        }
+    }
+    free(wrow);
+}
+
