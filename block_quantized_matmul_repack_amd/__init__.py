@@ -3,7 +3,8 @@
 The computation lives in libtiledq.so (HIP kernels for gfx950 behind a C ABI
 declared in include/tiledq.h); this package is its thin torch binding.
 """
-from .ops import (BF16, F16, F32, IQ4_NL, MXFP4, PATH_GEMM, Q4_1, Q4_K, PATH_GEMV, Q4_0, Q8_0,  # noqa: F401
-                  block_bytes, block_dots, flat_bytes, matmul, qgemm, qgemv, qgemv_x, quantize_act,
-                  repack_tiles, supported, tile_bytes, tiled_bytes)
+from .ops import (BF16, F16, F32, IQ4_NL, MXFP4, PATH_GEMM, PATH_GEMM_FLAT, PATH_GEMV,  # noqa: F401
+                  PATH_GEMV_FLAT, Q4_0, Q4_1, Q4_K, Q8_0, block_bytes, block_dots, flat_bytes,
+                  matmul, matmul_flat, qgemm, qgemm_flat, qgemv, qgemv_flat, qgemv_x,
+                  quantize_act, repack_tiles, supported, tile_bytes, tiled_bytes, unpack_tiles)
 from ._lib import TiledqError, lib  # noqa: F401

@@ -30,6 +30,10 @@ SIGNATURES = {
     "tq_qgemm": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_matmul": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P, SZ, P]),
     "tq_block_dots": (INT, [INT, P, I64, I64, P, I64, P, P, INT, P]),
+    "tq_unpack_tiles": (INT, [INT, P, I64, I64, P, P]),
+    "tq_qgemv_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
+    "tq_qgemm_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
+    "tq_matmul_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
 }
 
 

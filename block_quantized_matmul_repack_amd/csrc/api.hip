@@ -63,9 +63,18 @@ tq::Lut pack_lut(int type, const int8_t *lut)
     return t;
 }
 
+// Alignment a flat block buffer of `type` needs: 2 bytes (fp16 scales), 4
+// for the 17-byte MXFP4 and 20-byte Q4_1 blocks (read through aligned
+// dwords), 16 for Q4_K's 144-byte super-blocks (read as 16-byte vectors).
+uintptr_t flat_align(int type)
+{
+    return type == TQ_Q4_K ? 16 : ((type == TQ_MXFP4 || type == TQ_Q4_1) ? 4 : 2);
+}
+
+// `wa`: the alignment the weight buffer needs (16 for tiles).
 int check_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
                  const uint16_t *d, int64_t M, const int8_t *lut, const void *out, int64_t ldy,
-                 bool need_d)
+                 bool need_d, uintptr_t wa = 16)
 {
     if (!valid_type(type))
         return TQ_E_TYPE;
@@ -75,7 +84,7 @@ int check_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t
         return TQ_OK;
     if (!tiles || !q || (need_d && !d) || !out || (type == TQ_IQ4_NL && !lut))
         return TQ_E_NULL;
-    if (!aligned(tiles, 16) || !aligned(q, 16) || (need_d && !aligned(d, 2)) ||
+    if (!aligned(tiles, wa) || !aligned(q, 16) || (need_d && !aligned(d, 2)) ||
         !aligned(out, 4))
         return TQ_E_ALIGN;
     return TQ_OK;
@@ -158,8 +167,7 @@ int tq_repack_tiles(int type, const void *flat, int64_t K, int64_t N, void *tile
         return TQ_OK;
     if (!flat || !tiles)
         return TQ_E_NULL;
-    const uintptr_t fa = type == TQ_Q4_K ? 16 : ((type == TQ_MXFP4 || type == TQ_Q4_1) ? 4 : 2);
-    if (!aligned(flat, fa) || !aligned(tiles, 16))
+    if (!aligned(flat, flat_align(type)) || !aligned(tiles, 16))
         return TQ_E_ALIGN;
     return launch_status(tq::launch_repack(type, flat, K, N, tiles, stream));
 }
@@ -252,23 +260,87 @@ int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q
 int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
                   int64_t M, const int8_t *lut, int32_t *isum, int path, hipStream_t stream)
 {
-    if (path != TQ_PATH_GEMV && path != TQ_PATH_GEMM)
+    if (path < TQ_PATH_GEMV || path > TQ_PATH_GEMM_FLAT)
         return TQ_E_TYPE;
-    if (path == TQ_PATH_GEMV && valid_type(type) && M > 8)
+    const bool flat = path == TQ_PATH_GEMV_FLAT || path == TQ_PATH_GEMM_FLAT;
+    const bool gemv = path == TQ_PATH_GEMV || path == TQ_PATH_GEMV_FLAT;
+    if (gemv && valid_type(type) && M > 8)
         return TQ_E_SHAPE;
-    int st = check_matmul(type, tiles, K, N, q, nullptr, M, lut, isum, N, false);
+    int st = check_matmul(type, tiles, K, N, q, nullptr, M, lut, isum, N, false,
+                          flat ? flat_align(type) : 16);
     if (st != TQ_OK || M == 0 || N == 0)
         return st;
     if ((int64_t)M * N * (K / 32) >= MAX_PROD)
         return TQ_E_SHAPE;
     const tq::Lut t = pack_lut(type, lut);
     const tq::Act act{q, nullptr, nullptr, -1, 0};
-    hipError_t e = (path == TQ_PATH_GEMV)
-                       ? tq::launch_qgemv(kernel_type(type), tiles, K, N, act, M, t, nullptr, N, isum,
-                                          nullptr, 0, stream)
-                       : tq::launch_qgemm(kernel_type(type), tiles, K, N, q, nullptr, M, t, nullptr, N,
-                                          isum, stream);
+    hipError_t e;
+    switch (path) {
+    case TQ_PATH_GEMV:
+        e = tq::launch_qgemv(kernel_type(type), tiles, K, N, act, M, t, nullptr, N, isum, nullptr,
+                             0, stream);
+        break;
+    case TQ_PATH_GEMM:
+        e = tq::launch_qgemm(kernel_type(type), tiles, K, N, q, nullptr, M, t, nullptr, N, isum,
+                             stream);
+        break;
+    case TQ_PATH_GEMV_FLAT:
+        e = tq::launch_qgemv_flat(type, tiles, K, N, q, nullptr, M, t, nullptr, N, isum, stream);
+        break;
+    default:
+        e = tq::launch_qgemm_flat(type, tiles, K, N, q, nullptr, M, t, nullptr, N, isum, stream);
+        break;
+    }
     return launch_status(e);
+}
+
+int tq_unpack_tiles(int type, const void *tiles, int64_t K, int64_t N, void *flat,
+                    hipStream_t stream)
+{
+    if (!valid_type(type) || type == TQ_Q4_K)
+        return TQ_E_TYPE;
+    if (!valid_tkn(type, K, N))
+        return TQ_E_SHAPE;
+    if (N == 0)
+        return TQ_OK;
+    if (!flat || !tiles)
+        return TQ_E_NULL;
+    if (!aligned(flat, flat_align(type)) || !aligned(tiles, 16))
+        return TQ_E_ALIGN;
+    return launch_status(tq::launch_unpack(type, tiles, K, N, flat, stream));
+}
+
+int tq_qgemv_flat(int type, const void *flat, int64_t K, int64_t N, const int8_t *q,
+                  const uint16_t *d, int64_t M, const int8_t *lut, float *y, int64_t ldy,
+                  hipStream_t stream)
+{
+    if (valid_type(type) && M > 8)
+        return TQ_E_SHAPE;
+    int st = check_matmul(type, flat, K, N, q, d, M, lut, y, ldy, true, flat_align(type));
+    if (st != TQ_OK || M == 0 || N == 0)
+        return st;
+    return launch_status(tq::launch_qgemv_flat(type, flat, K, N, q, d, M, pack_lut(type, lut),
+                                               y, ldy, nullptr, stream));
+}
+
+int tq_qgemm_flat(int type, const void *flat, int64_t K, int64_t N, const int8_t *q,
+                  const uint16_t *d, int64_t M, const int8_t *lut, float *y, int64_t ldy,
+                  hipStream_t stream)
+{
+    int st = check_matmul(type, flat, K, N, q, d, M, lut, y, ldy, true, flat_align(type));
+    if (st != TQ_OK || M == 0 || N == 0)
+        return st;
+    return launch_status(tq::launch_qgemm_flat(type, flat, K, N, q, d, M, pack_lut(type, lut),
+                                               y, ldy, nullptr, stream));
+}
+
+int tq_matmul_flat(int type, const void *flat, int64_t K, int64_t N, const int8_t *q,
+                   const uint16_t *d, int64_t M, const int8_t *lut, float *y, int64_t ldy,
+                   hipStream_t stream)
+{
+    if (M <= 8)
+        return tq_qgemv_flat(type, flat, K, N, q, d, M, lut, y, ldy, stream);
+    return tq_qgemm_flat(type, flat, K, N, q, d, M, lut, y, ldy, stream);
 }
 
 }  // extern "C"

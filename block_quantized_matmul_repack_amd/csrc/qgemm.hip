@@ -81,18 +81,24 @@ struct Ranges {
 // two per thread, plus one block scale per thread (row t/4, block t%4).
 // Weights: wave w takes the tile of stripe w/4, block w%4; lane 32*hh + l
 // reads, for tile lane l, half hh of that lane's column pairs.
-template <int QT>
+// FT: -1 = weights as tiles; else weights as flat GGML blocks of type FT
+// (row n's blocks contiguous; FT = TQ_Q4_K runs with QT = TQ_Q4_1).  Flat
+// thread roles: weight row tid / 8 (of the 64), k-block (tid / 2) % 4, half
+// tid % 2 of the block's quant bytes (4-bit: 8 bytes = elements 8h .. 8h + 7
+// and 16 + 8h ..; Q8_0 and Q4_K: 16 elements from 16h).
+template <int QT, int FT>
 struct Offs {
-    static constexpr int NWD = QT == TQ_Q8_0 ? 4 : 2;
+    static constexpr int NWD = (QT == TQ_Q8_0 || FT == TQ_Q4_K) ? 4 : 2;
     int a[2], da, w[NWD], dw;
     int kba, kbw;                 // k-block of this thread's activation / weight scale
+    int hw, rowsb;                // flat: half, and (Q4_K) the row's first super-block
 };
 
-template <int QT>
-__device__ __forceinline__ Offs<QT> make_offs(int64_t nkt, int64_t K, int tid)
+template <int QT, int FT>
+__device__ __forceinline__ Offs<QT, FT> make_offs(int64_t nkt, int64_t K, int tid)
 {
     constexpr int TS = Fmt<QT>::tile;
-    Offs<QT> o;
+    Offs<QT, FT> o;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int ch = tid + THREADS * i;
@@ -101,6 +107,22 @@ __device__ __forceinline__ Offs<QT> make_offs(int64_t nkt, int64_t K, int tid)
     }
     o.kba = tid & 3;
     o.da = (int)((tid >> 2) * nkt + o.kba) * 2;
+    if constexpr (FT >= 0) {
+        constexpr int BB = Fmt<FT>::block;
+        const int rr = tid >> 3, kb = (tid >> 1) & 3, h = tid & 1;
+        o.kbw = kb;
+        o.hw = h;
+        if constexpr (FT == TQ_Q4_K) {
+            o.rowsb = (int)(rr * (nkt / 8)) * BB;
+            o.w[0] = o.dw = 0;                    // per step: super-block of kt0 + kb
+        } else {
+            const int blk = (int)(rr * nkt + kb) * BB;
+            constexpr int QOFF = FT == TQ_MXFP4 ? 1 : (FT == TQ_Q4_1 ? 4 : 2);
+            o.w[0] = blk + QOFF + (FT == TQ_Q8_0 ? 16 : 8) * h;
+            o.dw = blk;
+        }
+        return o;
+    }
     const int wave = tid >> 6, lane = tid & 63;
     const int tt = wave >> 2, l = lane & 31, hh = lane >> 5;
     o.kbw = wave & 3;
@@ -120,14 +142,17 @@ __device__ __forceinline__ Offs<QT> make_offs(int64_t nkt, int64_t K, int tid)
     return o;
 }
 
-template <int QT>
+template <int QT, int FT>
 struct StageRegs {
     uint4 a[2];               // activations: 2 x 16 bytes
     uint16_t da;              // one activation block scale
-    uint32_t w[Offs<QT>::NWD];// weight dwords (4-bit: rows 4g..4g+3 at column pairs
-                              // 4c+2hh, 4c+2hh+1; Q8_0: rows 2p, 2p+1 at 8h+4hh .. +3)
+    uint32_t w[Offs<QT, FT>::NWD]; // weight dwords (tiles, 4-bit: rows 4g..4g+3 at column
+                              // pairs 4c+2hh, 4c+2hh+1; Q8_0: rows 2p, 2p+1 at 8h+4hh ..
+                              // +3; flat: the thread's quant bytes in order)
     uint16_t dw;              // weight row scale (MXFP4: its E8M0 byte)
     uint16_t mw;              // Q4_1: weight row min
+    uint4 hdr;                // flat Q4_K: the super-block's d, dmin and scale bytes
+    int sub;                  // flat Q4_K: sub-block (0..7) of this step's block
     bool da_ok, dw_ok;        // the scales' k-blocks lie inside K
 };
 
@@ -136,9 +161,9 @@ struct StageRegs {
 // last step reads finite bytes of the next row / stripe or zero, and its two
 // scales are forced to zero, so it adds exactly 0; so there are no branches
 // around loads and the compiler can wait for exactly the older stage.
-template <int QT, bool DOTS>
-__device__ __forceinline__ void load_step(StageRegs<QT> &s, const Ranges &rg, const Offs<QT> &o,
-                                          int nkt, int kt0)
+template <int QT, bool DOTS, int FT>
+__device__ __forceinline__ void load_step(StageRegs<QT, FT> &s, const Ranges &rg,
+                                          const Offs<QT, FT> &o, int nkt, int kt0)
 {
     constexpr int TS = Fmt<QT>::tile;
 #pragma unroll
@@ -154,22 +179,83 @@ __device__ __forceinline__ void load_step(StageRegs<QT> &s, const Ranges &rg, co
         // zeroed for blocks past K at store time (a select here would wait
         // for the load)
         s.da = __builtin_amdgcn_raw_buffer_load_b16(rg.d, o.da + kt0 * 2, 0, 0);
+        s.da_ok = kt0 + o.kba < nkt;
+        s.dw_ok = kt0 + o.kbw < nkt;
+    }
+    if constexpr (FT >= 0) {
+        // flat blocks: this thread's quant bytes and the block's scales
+        constexpr int BB = Fmt<FT>::block;
+        if constexpr (FT == TQ_Q4_K) {
+            const int kk = kt0 + o.kbw;
+            s.sub = kk & 7;
+            const int sbo = o.rowsb + (kk >> 3) * BB;
+            const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
+                rg.w, sbo + 16 + 32 * ((kk & 7) >> 1) + 16 * o.hw, 0, BUF_NT);
+            s.w[0] = v.x, s.w[1] = v.y, s.w[2] = v.z, s.w[3] = v.w;
+            if constexpr (!DOTS) {
+                const v4i h = __builtin_amdgcn_raw_buffer_load_b128(rg.w, sbo, 0, 0);
+                s.hdr = make_uint4(h.x, h.y, h.z, h.w);
+            }
+        } else if constexpr (FT == TQ_MXFP4) {
+            // 17-byte blocks start at any byte: byte loads
+            uint32_t b[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                b[i] = __builtin_amdgcn_raw_buffer_load_b8(rg.w, o.w[0] + kt0 * BB + i, 0, 0);
+            s.w[0] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+            s.w[1] = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+            if constexpr (!DOTS)
+                s.dw = __builtin_amdgcn_raw_buffer_load_b8(rg.w, o.dw + kt0 * BB, 0, 0);
+        } else if constexpr (FT == TQ_Q8_0) {
+            const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rg.w, o.w[0] + kt0 * BB, 0, BUF_NT);
+            s.w[0] = v.x, s.w[1] = v.y, s.w[2] = v.z, s.w[3] = v.w;
+            if constexpr (!DOTS)
+                s.dw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + kt0 * BB, 0, 0);
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rg.w, o.w[0] + kt0 * BB, 0, BUF_NT);
+            s.w[0] = (uint32_t)v[0], s.w[1] = (uint32_t)v[1];
+            if constexpr (!DOTS) {
+                s.dw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + kt0 * BB, 0, 0);
+                if constexpr (FT == TQ_Q4_1)
+                    s.mw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + 2 + kt0 * BB, 0, 0);
+            }
+        }
+        return;
+    }
+    if constexpr (!DOTS) {
         if constexpr (QT == TQ_MXFP4)
             s.dw = __builtin_amdgcn_raw_buffer_load_b8(rg.w, o.dw + kt0 * TS, 0, 0);
         else
             s.dw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + kt0 * TS, 0, 0);
         if constexpr (QT == TQ_Q4_1)
             s.mw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + 2 + kt0 * TS, 0, 0);
-        s.da_ok = kt0 + o.kba < nkt;
-        s.dw_ok = kt0 + o.kbw < nkt;
     }
 #pragma unroll
-    for (int i = 0; i < Offs<QT>::NWD; i++)
+    for (int i = 0; i < Offs<QT, FT>::NWD; i++)
         s.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rg.w, o.w[i] + kt0 * TS, 0, BUF_NT);
 }
 
-template <int QT, bool DOTS>
-__device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds<QT> &L, int buf,
+// 8 quant bytes of a flat 4-bit block half (elements 8h .. 8h + 7 in the
+// low nibbles, 16 + 8h .. in the high ones) as int8 weights: lo / hi dwords
+// for K 8h + 4i .. and 16 + 8h + 4i .., i = 0, 1.
+template <int QT>
+__device__ __forceinline__ void decode_flat4(uint32_t v, const Lut &lut, uint32_t &lo,
+                                             uint32_t &hi)
+{
+    if constexpr (QT == TQ_Q4_0) {
+        const uint32_t t = v ^ 0x88888888u;
+        lo = (t << 4) & 0xF0F0F0F0u;
+        hi = t & 0xF0F0F0F0u;
+    } else if constexpr (QT == TQ_Q4_1) {
+        lo = v & 0x0F0F0F0Fu;
+        hi = (v >> 4) & 0x0F0F0F0Fu;
+    } else {
+        lut16x2(v, lut, lo, hi);
+    }
+}
+
+template <int QT, bool DOTS, int FT>
+__device__ __forceinline__ void store_step(const StageRegs<QT, FT> &s, Lds<QT> &L, int buf,
                                            const Lut &lut, int tid)
 {
 #pragma unroll
@@ -189,6 +275,42 @@ __device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds<QT> &L, i
         }
     }
     ((uint16_t *)&L.da[buf][0][tid >> 2])[tid & 3] = s.da_ok ? s.da : (uint16_t)0;
+    if constexpr (FT >= 0) {
+        // flat: weight row rr's block kb in [row][K] order (both halves of a
+        // block store its scales: the same bits, no branch)
+        const int rr = tid >> 3, kb = (tid >> 1) & 3, h = tid & 1;
+        uint8_t *B = L.B[buf] + rr * LDS_ROW + 32 * kb;
+        uint16_t dwb = s.dw, mwb = s.mw;
+        if constexpr (FT == TQ_Q8_0) {
+            *(uint4 *)(B + 16 * h) = make_uint4(s.w[0], s.w[1], s.w[2], s.w[3]);
+        } else if constexpr (FT == TQ_Q4_K) {
+            // sub-block `sub` = nibble sub % 2 of its chunk's bytes
+            uint32_t e[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                e[i] = (s.sub & 1) ? ((s.w[i] >> 4) & 0x0F0F0F0Fu) : (s.w[i] & 0x0F0F0F0Fu);
+            *(uint4 *)(B + 16 * h) = make_uint4(e[0], e[1], e[2], e[3]);
+            if constexpr (!DOTS) {
+                const uint32_t s3[3] = {s.hdr.y, s.hdr.z, s.hdr.w};
+                uint32_t sc, mn;
+                q4k_scale_min(s3, s.sub, sc, mn);
+                dwb = f16_of_product(f16_bits_to_f32((uint16_t)s.hdr.x), (float)sc);
+                mwb = f16_of_product(-f16_bits_to_f32((uint16_t)(s.hdr.x >> 16)), (float)mn);
+            }
+        } else {
+            uint32_t lo0, hi0, lo1, hi1;
+            decode_flat4<QT>(s.w[0], lut, lo0, hi0);
+            decode_flat4<QT>(s.w[1], lut, lo1, hi1);
+            *(uint2 *)(B + 8 * h) = make_uint2(lo0, lo1);
+            *(uint2 *)(B + 16 + 8 * h) = make_uint2(hi0, hi1);
+            if constexpr (FT == TQ_MXFP4)
+                dwb = e8m0_f16_bits(s.dw);
+        }
+        ((uint16_t *)&L.dw[buf][0][rr])[kb] = s.dw_ok ? dwb : (uint16_t)0;
+        if constexpr (QT == TQ_Q4_1)
+            ((uint16_t *)&L.mw[buf][rr])[kb] = s.dw_ok ? mwb : (uint16_t)0;
+        return;
+    }
     const int wave = tid >> 6, lane = tid & 63;
     const int tt = wave >> 2, kb = wave & 3, l = lane & 31, hh = lane >> 5;
     uint8_t *B = L.B[buf] + (32 * tt) * LDS_ROW + 32 * kb;
@@ -236,7 +358,7 @@ __device__ __forceinline__ void store_step(const StageRegs<QT> &s, Lds<QT> &L, i
         ((uint16_t *)&L.mw[buf][32 * tt + l])[kb] = s.dw_ok ? s.mw : (uint16_t)0;
 }
 
-template <int QT, bool DOTS>
+template <int QT, bool DOTS, int FT>
 __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uint8_t *__restrict__ tiles,
                                                    int64_t nkt, int64_t N,
                                                    const int8_t *__restrict__ q,
@@ -259,9 +381,15 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
     rg.q = make_rsrc(q + m0 * K, min<int64_t>(M - m0, BM) * K);
     rg.d = make_rsrc(DOTS ? (const void *)q : (const void *)(d + m0 * nkt),
                      DOTS ? 0 : min<int64_t>(M - m0, BM) * nkt * 2);
-    rg.w = make_rsrc(tiles + ct0 * nkt * TS, min<int64_t>(nct - ct0, BN / 32) * nkt * TS);
+    if constexpr (FT >= 0) {
+        // flat: the workgroup's 64 weight rows, each nkt / (block elements / 32) blocks
+        const int64_t rb = (FT == TQ_Q4_K ? nkt / 8 : nkt) * Fmt<FT>::block;
+        rg.w = make_rsrc(tiles + 32 * ct0 * rb, min<int64_t>(N - 32 * ct0, BN) * rb);
+    } else {
+        rg.w = make_rsrc(tiles + ct0 * nkt * TS, min<int64_t>(nct - ct0, BN / 32) * nkt * TS);
+    }
 
-    const Offs<QT> o = make_offs<QT>(nkt, K, tid);
+    const Offs<QT, FT> o = make_offs<QT, FT>(nkt, K, tid);
     // the all-zero halves of the scale operands are never written again
     for (int i = tid; i < 2 * BM; i += THREADS)
         L.da[i / BM][1][i % BM] = 0;
@@ -376,27 +504,27 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
 
     // Two register stages: step s+1's data is in flight while step s+2 is
     // issued.
-    StageRegs<QT> r0, r1;
+    StageRegs<QT, FT> r0, r1;
     // The loop body is one basic block (two steps, no exit in between), so the
     // compiler tracks the two stages without conservative waits.  An odd step
     // count gets one trailing step whose k-blocks all lie past K: its scales
     // are zero, so it adds exactly 0, and its loads (like every prefetch past
     // the end) are range-checked by the buffer descriptors.
     const int64_t nsteps2 = (nsteps + 1) & ~int64_t(1);
-    load_step<QT, DOTS>(r0, rg, o, (int)nkt, 0);
-    load_step<QT, DOTS>(r1, rg, o, (int)nkt, KB);
-    store_step<QT, DOTS>(r0, L, 0, lut, tid);
+    load_step<QT, DOTS, FT>(r0, rg, o, (int)nkt, 0);
+    load_step<QT, DOTS, FT>(r1, rg, o, (int)nkt, KB);
+    store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
     __syncthreads();
     for (int64_t step = 0; step < nsteps2; step += 2) {
         // even step: buffer 0 is computed, r1 holds step+1, r0 is free
-        load_step<QT, DOTS>(r0, rg, o, (int)nkt, (int)(step + 2) * KB);
+        load_step<QT, DOTS, FT>(r0, rg, o, (int)nkt, (int)(step + 2) * KB);
         compute(0, step);
-        store_step<QT, DOTS>(r1, L, 1, lut, tid);
+        store_step<QT, DOTS, FT>(r1, L, 1, lut, tid);
         __syncthreads();
         // odd step: buffer 1 is computed, r0 holds step+2, r1 is free
-        load_step<QT, DOTS>(r1, rg, o, (int)nkt, (int)(step + 3) * KB);
+        load_step<QT, DOTS, FT>(r1, rg, o, (int)nkt, (int)(step + 3) * KB);
         compute(1, step + 1);
-        store_step<QT, DOTS>(r0, L, 0, lut, tid);
+        store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
         __syncthreads();
     }
     epilogue(carry.kt, carry.dot, carry.sc);
@@ -413,8 +541,8 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
     }
 }
 
-template <int QT>
-hipError_t launch_t(const void *tiles, int64_t K, int64_t N, const int8_t *q, const uint16_t *d,
+template <int QT, int FT>
+hipError_t launch_t(const void *w, int64_t K, int64_t N, const int8_t *q, const uint16_t *d,
                     int64_t M, const Lut &lut, float *y, int64_t ldy, int32_t *isum,
                     hipStream_t s)
 {
@@ -426,11 +554,11 @@ hipError_t launch_t(const void *tiles, int64_t K, int64_t N, const int8_t *q, co
     // on one XCD and each weight tile is fetched into a single L2.
     dim3 grid((unsigned)((nct + BN / 32 - 1) / (BN / 32)), (unsigned)((M + BM - 1) / BM));
     if (isum)
-        k_qgemm<QT, true><<<grid, THREADS, 0, s>>>((const uint8_t *)tiles, nkt, N, q, d, M, K,
-                                                   lut, y, ldy, isum);
+        k_qgemm<QT, true, FT><<<grid, THREADS, 0, s>>>((const uint8_t *)w, nkt, N, q, d, M, K,
+                                                       lut, y, ldy, isum);
     else
-        k_qgemm<QT, false><<<grid, THREADS, 0, s>>>((const uint8_t *)tiles, nkt, N, q, d, M, K,
-                                                    lut, y, ldy, isum);
+        k_qgemm<QT, false, FT><<<grid, THREADS, 0, s>>>((const uint8_t *)w, nkt, N, q, d, M, K,
+                                                        lut, y, ldy, isum);
     return hipGetLastError();
 }
 
@@ -441,11 +569,27 @@ hipError_t launch_qgemm(int type, const void *tiles, int64_t K, int64_t N, const
                         int32_t *isum, hipStream_t s)
 {
     switch (type) {
-    case TQ_Q4_0: return launch_t<TQ_Q4_0>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
-    case TQ_Q8_0: return launch_t<TQ_Q8_0>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
-    case TQ_IQ4_NL: return launch_t<TQ_IQ4_NL>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
-    case TQ_MXFP4: return launch_t<TQ_MXFP4>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
-    case TQ_Q4_1: return launch_t<TQ_Q4_1>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_Q4_0: return launch_t<TQ_Q4_0, -1>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_Q8_0: return launch_t<TQ_Q8_0, -1>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_IQ4_NL: return launch_t<TQ_IQ4_NL, -1>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_MXFP4: return launch_t<TQ_MXFP4, -1>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_Q4_1: return launch_t<TQ_Q4_1, -1>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_qgemm_flat(int type, const void *flat, int64_t K, int64_t N, const int8_t *q,
+                             const uint16_t *d, int64_t M, const Lut &lut, float *y,
+                             int64_t ldy, int32_t *isum, hipStream_t s)
+{
+    switch (type) {
+    case TQ_Q4_0: return launch_t<TQ_Q4_0, TQ_Q4_0>(flat, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_Q8_0: return launch_t<TQ_Q8_0, TQ_Q8_0>(flat, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_IQ4_NL:
+        return launch_t<TQ_IQ4_NL, TQ_IQ4_NL>(flat, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_MXFP4: return launch_t<TQ_MXFP4, TQ_MXFP4>(flat, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_Q4_1: return launch_t<TQ_Q4_1, TQ_Q4_1>(flat, K, N, q, d, M, lut, y, ldy, isum, s);
+    case TQ_Q4_K: return launch_t<TQ_Q4_1, TQ_Q4_K>(flat, K, N, q, d, M, lut, y, ldy, isum, s);
     }
     return hipErrorInvalidValue;
 }

@@ -31,36 +31,6 @@ constexpr int THREADS = 256;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// The MXFP4 block at byte a of the flat buffer (total bytes long): its E8M0
-// byte and its 8 quant halfwords.  The 5 covering dwords start at a & ~3;
-// the first four end before a + 16, inside the block; the fifth can pass the
-// end of the buffer only for its last block, and is then read bytewise.
-__device__ __forceinline__ void load_mx_block(const uint8_t *__restrict__ flat, int64_t a,
-                                              int64_t total, uint16_t (&q)[8], uint16_t &e)
-{
-    const int64_t A = a & ~int64_t(3);
-    const int sh = (int)(a - A);
-    uint32_t w[5];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-        w[i] = *(const uint32_t *)(flat + A + 4 * i);
-    if (A + 20 <= total) {
-        w[4] = *(const uint32_t *)(flat + A + 16);
-    } else {
-        w[4] = 0;
-        for (int j = 0; j < 4 && A + 16 + j < total; j++)
-            w[4] |= (uint32_t)flat[A + 16 + j] << (8 * j);
-    }
-    e = (uint16_t)((w[0] >> (8 * sh)) & 0xFFu);
-    const int s1 = 8 * (sh + 1);                  // quants start 1..4 bytes into w[0]
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        const uint32_t v = (uint32_t)((((uint64_t)w[k + 1] << 32) | w[k]) >> s1);
-        q[2 * k] = (uint16_t)v;
-        q[2 * k + 1] = (uint16_t)(v >> 16);
-    }
-}
-
 // One Q4_K super-block of row r (16-byte aligned, 144 bytes) into the 8
 // tiles' LDS staging of k_repack: for sub-block j, the 16 bytes of a flat
 // 32-element block (element e low, e + 16 high nibble, as Q4_0) and the pair

@@ -211,6 +211,54 @@ __device__ __forceinline__ void lut16x2(uint32_t x, const Lut &t, uint32_t &ev, 
     od = (ho & mo) | (lo & ~mo);
 }
 
+// The MXFP4 block at byte a of the flat buffer (total bytes long): its E8M0
+// byte and its 8 quant halfwords.  The 5 covering dwords start at a & ~3;
+// the first four end before a + 16, inside the block; the fifth can pass the
+// end of the buffer only for its last block, and is then read bytewise.
+__device__ __forceinline__ void load_mx_block(const uint8_t *__restrict__ flat, int64_t a,
+                                              int64_t total, uint16_t (&q)[8], uint16_t &e)
+{
+    const int64_t A = a & ~int64_t(3);
+    const int sh = (int)(a - A);
+    uint32_t w[5];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        w[i] = *(const uint32_t *)(flat + A + 4 * i);
+    if (A + 20 <= total) {
+        w[4] = *(const uint32_t *)(flat + A + 16);
+    } else {
+        w[4] = 0;
+        for (int j = 0; j < 4 && A + 16 + j < total; j++)
+            w[4] |= (uint32_t)flat[A + 16 + j] << (8 * j);
+    }
+    e = (uint16_t)((w[0] >> (8 * sh)) & 0xFFu);
+    const int s1 = 8 * (sh + 1);                  // quants start 1..4 bytes into w[0]
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t v = (uint32_t)((((uint64_t)w[k + 1] << 32) | w[k]) >> s1);
+        q[2 * k] = (uint16_t)v;
+        q[2 * k + 1] = (uint16_t)(v >> 16);
+    }
+}
+
+// Q4_K: 6-bit scale and min of sub-block j from the 12 scale bytes (three
+// dwords), as the repack decodes them (Q4_K layout in tiledq.h).
+__device__ __forceinline__ void q4k_scale_min(const uint32_t (&s3)[3], int j, uint32_t &sc,
+                                              uint32_t &m)
+{
+    auto sb = [&](int k) {
+        const uint32_t v = k < 4 ? s3[0] : (k < 8 ? s3[1] : s3[2]);
+        return (v >> (8 * (k & 3))) & 0xFFu;
+    };
+    if (j < 4) {
+        sc = sb(j) & 63u;
+        m = sb(j + 4) & 63u;
+    } else {
+        sc = (sb(j + 4) & 15u) | ((sb(j - 4) >> 6) << 4);
+        m = (sb(j + 4) >> 4) | ((sb(j) >> 6) << 4);
+    }
+}
+
 // K-split of the decode GEMV: S workgroups per stripe (a power of two),
 // `chunk` k-tiles each; slots points into the caller's workspace when S > 1.
 struct Split {
@@ -240,5 +288,14 @@ hipError_t launch_qgemv(int type, const void *tiles, int64_t K, int64_t N, const
 hipError_t launch_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
                         const uint16_t *d, int64_t M, const Lut &lut, float *y, int64_t ldy,
                         int32_t *isum, hipStream_t s);
+// Flat (un-repacked) GGML blocks: unpack of tiles, and the two products.
+hipError_t launch_unpack(int type, const void *tiles, int64_t K, int64_t N, void *flat,
+                         hipStream_t s);
+hipError_t launch_qgemv_flat(int type, const void *flat, int64_t K, int64_t N, const int8_t *q,
+                             const uint16_t *d, int64_t M, const Lut &lut, float *y,
+                             int64_t ldy, int32_t *isum, hipStream_t s);
+hipError_t launch_qgemm_flat(int type, const void *flat, int64_t K, int64_t N, const int8_t *q,
+                             const uint16_t *d, int64_t M, const Lut &lut, float *y,
+                             int64_t ldy, int32_t *isum, hipStream_t s);
 
 }  // namespace tq

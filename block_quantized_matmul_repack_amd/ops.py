@@ -12,7 +12,7 @@ from ._lib import TiledqError, check, lib
 
 Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1, Q4_K = 0, 1, 2, 3, 4, 5
 F32, BF16, F16 = 0, 1, 2
-PATH_GEMV, PATH_GEMM = 0, 1
+PATH_GEMV, PATH_GEMM, PATH_GEMV_FLAT, PATH_GEMM_FLAT = 0, 1, 2, 3
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
@@ -173,8 +173,46 @@ def matmul(qtype, tiles, K, N, q, d, lut=None, out=None):
     return out
 
 
+def unpack_tiles(qtype, tiles, K, N, out=None):
+    """Tiles (uint8 GPU tensor) -> flat GGML blocks (uint8 GPU tensor)."""
+    _need_cuda(tiles, out)
+    nbytes = flat_bytes(qtype, K, N)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=tiles.device)
+    if tiles.numel() * tiles.element_size() < tiled_bytes(qtype, K, N) or \
+            out.numel() * out.element_size() < nbytes:
+        raise TiledqError("unpack_tiles: buffer too small")
+    check(lib().tq_unpack_tiles(qtype, _ptr(tiles), K, N, _ptr(out), _stream(tiles)),
+          "tq_unpack_tiles")
+    return out[:nbytes]
+
+
+def _flat_product(name, qtype, flat, K, N, q, d, lut, out):
+    _need_cuda(flat, q, d, out)
+    out = _out(name, q, N, out)
+    check(getattr(lib(), name)(qtype, _ptr(flat), K, N, _ptr(q), _ptr(d), q.shape[0],
+                               _lut_arg(lut), _ptr(out), out.stride(0), _stream(q)), name)
+    return out
+
+
+def qgemv_flat(qtype, flat, K, N, q, d, lut=None, out=None):
+    """Decode product over flat (un-repacked) GGML blocks, M <= 8."""
+    return _flat_product("tq_qgemv_flat", qtype, flat, K, N, q, d, lut, out)
+
+
+def qgemm_flat(qtype, flat, K, N, q, d, lut=None, out=None):
+    """Prefill product over flat GGML blocks, any M."""
+    return _flat_product("tq_qgemm_flat", qtype, flat, K, N, q, d, lut, out)
+
+
+def matmul_flat(qtype, flat, K, N, q, d, lut=None, out=None):
+    """Product over flat GGML blocks for any M (qgemv_flat for M <= 8)."""
+    return _flat_product("tq_matmul_flat", qtype, flat, K, N, q, d, lut, out)
+
+
 def block_dots(qtype, tiles, K, N, q, lut=None, path=PATH_GEMV, out=None):
-    """Integer block dots int32 [M, N, K/32] as computed inside qgemv / qgemm."""
+    """Integer block dots int32 [M, N, K/32] as computed inside qgemv / qgemm
+    (paths PATH_GEMV_FLAT / PATH_GEMM_FLAT: `tiles` holds flat blocks)."""
     _need_cuda(tiles, q, out)
     M = q.shape[0]
     if out is None:

@@ -103,8 +103,11 @@ typedef enum {
     TQ_E_LAUNCH = 5   /* the HIP runtime rejected a launch                    */
 } tq_status;
 
-/* Which kernel family tq_block_dots runs. */
-typedef enum { TQ_PATH_GEMV = 0, TQ_PATH_GEMM = 1 } tq_path;
+/* Which kernel family tq_block_dots runs, and whether its weights are tiles
+ * or flat GGML blocks. */
+typedef enum {
+    TQ_PATH_GEMV = 0, TQ_PATH_GEMM = 1, TQ_PATH_GEMV_FLAT = 2, TQ_PATH_GEMM_FLAT = 3
+} tq_path;
 
 /* Bytes of one tile ("Block-32 Quantized Formats"): 576, 1088, 576, 544,
  * 640, 640; 0 for an unknown type. */
@@ -210,8 +213,39 @@ int tq_matmul(int type, const void *tiles, int64_t K, int64_t N,
               const int8_t *lut, float *y, int64_t ldy,
               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Flat (un-repacked) weights ("supports_op Independence from Buffer and
+ * Repack State": every supported type must work tiled and stored flat).
+ *
+ * tq_unpack_tiles: the inverse of tq_repack_tiles, rows n < N only.
+ *   tiles : device, tq_tiled_bytes(type, K, N) bytes, 16-byte aligned.
+ *   flat  : device, tq_flat_bytes(type, K, N) bytes, aligned as for
+ *           tq_repack_tiles; fully written.  Must not overlap `tiles`.
+ *   TQ_Q4_K is rejected (TQ_E_TYPE): its tiles keep d * sc and -dmin * m,
+ *   not the super-block's fields.  Bit-exact; deterministic. */
+int tq_unpack_tiles(int type, const void *tiles, int64_t K, int64_t N,
+                    void *flat, hipStream_t stream);
+
+/* Products over flat GGML blocks, with the same results as over the tiles
+ * of the same data (each weight the value its tile holds; Q4_K with the
+ * fp16 pairs of its tile).  Arguments as tq_qgemv / tq_qgemm / tq_matmul,
+ * with `flat` (device, tq_flat_bytes(type, K, N) bytes, aligned as for
+ * tq_repack_tiles) in place of the tiles and no workspace.
+ * tq_qgemv_flat: M <= 8 (else TQ_E_SHAPE); tq_qgemm_flat: any M;
+ * tq_matmul_flat: dispatched on M as tq_matmul. */
+int tq_qgemv_flat(int type, const void *flat, int64_t K, int64_t N,
+                  const int8_t *q, const uint16_t *d, int64_t M,
+                  const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
+int tq_qgemm_flat(int type, const void *flat, int64_t K, int64_t N,
+                  const int8_t *q, const uint16_t *d, int64_t M,
+                  const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
+int tq_matmul_flat(int type, const void *flat, int64_t K, int64_t N,
+                   const int8_t *q, const uint16_t *d, int64_t M,
+                   const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
+
 /* Test instrument: run the tq_qgemv (path TQ_PATH_GEMV, M <= 8) or tq_qgemm
- * (TQ_PATH_GEMM) kernel with the integer block dots as output instead of y:
+ * (TQ_PATH_GEMM) kernel, or their flat forms (TQ_PATH_GEMV_FLAT,
+ * TQ_PATH_GEMM_FLAT; `tiles` then holds flat blocks, aligned as for
+ * tq_repack_tiles), with the integer block dots as output instead of y:
  * isum[(m*N + n)*(K/32) + kt] (int32, device, 4-byte aligned) =
  * sum_{j<32} w_int[n][32kt+j] * q[m][32kt+j], for m < M, n < N, with w_int
  * = code - 8 (Q4_0), the int8 (Q8_0), lut[code] (IQ4_NL), 2 * E2M1(code)

@@ -188,3 +188,28 @@ def test_product_code_never_touches_oracle():
                 src = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in src.lower(), fn
                 assert "synth" not in src, fn
+
+
+def test_flat_validation(L):
+    A4 = ctypes.c_void_p(0x10004)
+    # unpack: Q4_K has no inverse; alignment as the repack's flat buffer
+    assert L.tq_unpack_tiles(5, A16, 256, 32, A16, NUL) == 2
+    assert L.tq_unpack_tiles(9, A16, 64, 32, A16, NUL) == 2
+    assert L.tq_unpack_tiles(0, A16, 48, 32, A16, NUL) == 3
+    assert L.tq_unpack_tiles(0, A2, 64, 32, A16, NUL) == 4          # tiles need 16
+    assert L.tq_unpack_tiles(4, A16, 64, 32, A2, NUL) == 4          # Q4_1 flat needs 4
+    assert L.tq_unpack_tiles(0, NUL, 64, 0, NUL, NUL) == 0
+    for fn in ("tq_qgemv_flat", "tq_qgemm_flat", "tq_matmul_flat"):
+        f = getattr(L, fn)
+        # (type, flat, K, N, q, d, M, lut, y, ldy, stream)
+        assert f(9, A16, 64, 32, A16, A16, 1, NUL, A16, 32, NUL) == 2, fn
+        assert f(5, A16, 288, 32, A16, A16, 1, NUL, A16, 32, NUL) == 3, fn     # Q4_K: K % 256
+        assert f(5, A4, 256, 32, A16, A16, 1, NUL, A16, 32, NUL) == 4, fn      # Q4_K flat: 16
+        assert f(3, A2, 64, 32, A16, A16, 1, NUL, A16, 32, NUL) == 4, fn       # MXFP4 flat: 4
+        assert f(2, A16, 64, 32, A16, A16, 1, NUL, A16, 32, NUL) == 1, fn      # IQ4_NL table
+        assert f(0, A16, 64, 32, A16, A16, 1, NUL, A16, 31, NUL) == 3, fn      # ldy < N
+        assert f(0, NUL, 64, 0, NUL, NUL, 3, NUL, NUL, 0, NUL) == 0, fn
+    assert L.tq_qgemv_flat(0, A16, 64, 32, A16, A16, 9, NUL, A16, 32, NUL) == 3
+    assert L.tq_block_dots(0, A16, 64, 32, A16, 1, NUL, A16, 4, NUL) == 2       # unknown path
+    assert L.tq_block_dots(0, A16, 64, 32, A16, 9, NUL, A16, 2, NUL) == 3       # flat GEMV, M > 8
+    assert L.tq_block_dots(5, A4, 256, 32, A16, 1, NUL, A16, 3, NUL) == 4       # Q4_K flat: 16

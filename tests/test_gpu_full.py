@@ -140,6 +140,12 @@ def test_q4_1_m512_k4096_n4096(tq):
     _check_dots(tq, c, tq.PATH_GEMM)
 
 
+def test_q4_k_k4096_n14336_m1(tq):
+    c = Case(tq, "q4_k_gemv_k4096_n14336_m1")
+    _check_case(tq, c, tq.qgemv, full_y=True)
+    _check_dots(tq, c, tq.PATH_GEMV)
+
+
 @pytest.fixture(scope="module")
 def lmhead(tq):
     return Case(tq, "q8_0_lmhead_k4096_n128001_m128")
