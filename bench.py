@@ -342,6 +342,43 @@ def measure_others(torch, tq, synth):
         res[f"repack {synth.TYPE_NAMES[qtype]}_k4096_n14336"] = {
             "kernel_us": round(us, 3), "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
         del flats, out
+    # flat (un-repacked) weights beside the tiled ones, and the device unpack
+    for name, M in (("q4_0_gemv_k4096_n14336_m1", 1), ("q4_0_gemv_k4096_n14336_m1", 8),
+                    ("q8_0_gemv_k4096_n4096_m1", 1), ("iq4_nl_gemm_m512_k4096_n4096", 512)):
+        w = synth.WORKLOADS[name]
+        inp = synth.make_inputs(w, M=1)
+        fb = inp.flat.size
+        R = min(32, max(2, -(-ROTATE_BYTES // fb)))
+        flats = [torch.from_numpy(inp.flat).cuda() for _ in range(R)]
+        tiles = [tq.repack_tiles(w.qtype, f, w.K, w.N) for f in flats]
+        rng = np.random.default_rng(M)
+        x = torch.from_numpy(rng.standard_normal((M, w.K), dtype=np.float32)).cuda()
+        q, d = tq.quantize_act(x)
+        y = torch.empty((M, w.N), dtype=torch.float32, device="cuda")
+        lut = inp.lut
+        if M <= 8:
+            ft = lambda i: tq.qgemv(w.qtype, tiles[i % R], w.K, w.N, q, d, lut=lut, out=y)
+            ff = lambda i: tq.qgemv_flat(w.qtype, flats[i % R], w.K, w.N, q, d, lut=lut, out=y)
+        else:
+            ft = lambda i: tq.qgemm(w.qtype, tiles[i % R], w.K, w.N, q, d, lut=lut, out=y)
+            ff = lambda i: tq.qgemm_flat(w.qtype, flats[i % R], w.K, w.N, q, d, lut=lut, out=y)
+        for i in range(3):
+            ft(i)
+            ff(i)
+        ut, uf = kernel_us(torch, ft, 30), kernel_us(torch, ff, 30)
+        label = f"flat {name.rsplit('_m', 1)[0]}_m{M}"
+        res[label] = {"flat_us": round(uf, 3), "tiled_us": round(ut, 3),
+                      "flat_GB_s_of_weights": round(fb / uf / 1e3, 1)}
+        if M > 8:
+            res[label]["flat_TOPS"] = round(2.0 * M * w.N * w.K / uf / 1e6, 2)
+        if name.startswith("q4_0"):
+            out = torch.empty(fb, dtype=torch.uint8, device="cuda")
+            fu = lambda i: tq.unpack_tiles(w.qtype, tiles[i % R], w.K, w.N, out=out)
+            fu(0)
+            uu = kernel_us(torch, fu, 30)
+            res[f"unpack {name.rsplit('_m', 1)[0]}"] = {
+                "kernel_us": round(uu, 3), "GB_s": round((fb + w.weight_bytes) / uu / 1e3, 1)}
+        del flats, tiles
     return res
 
 
