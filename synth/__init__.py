@@ -225,4 +225,5 @@ WORKLOADS = {
     "q4_1_gemv_k4096_n14336_m1": Workload("q4_1_gemv_k4096_n14336_m1", Q4_1, 4096, 14336, 1, "minmax"),
     "q4_1_gemm_m512_k4096_n4096": Workload("q4_1_gemm_m512_k4096_n4096", Q4_1, 4096, 4096, 512,
                                            "minmax", act_dtype="bf16", path="qgemm"),
+    "q4_k_gemv_k4096_n14336_m1": Workload("q4_k_gemv_k4096_n14336_m1", Q4_K, 4096, 14336, 1, "q4k"),
 }
