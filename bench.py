@@ -45,12 +45,12 @@ ROTATE_BYTES = 1 << 30         # defeat the 256 MB Infinity Cache
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "decode": {"fetch_kib": 8779.91, "write_kib": 112.0,
-              "src": "9167a7389661e2092b8c44984affcf77aca9c3c33ef66a8c0f09febffe36ebf7"},
-    "gemm": {"fetch_kib": 13368.15, "write_kib": 8192.0,
-            "src": "b0b552de170f56cdfee02de99d977245410e88562483a47a7b9c6cbe487370c2"},
-    "repack": {"fetch_kib": 16143.81, "write_kib": 32256.0,
-              "src": "2cb14a99a3044ab768aa5099b093a2d3a1c6cfb56ddc8dc09e1368e7f1e1646a"},
+    "decode": {"fetch_kib": 8779.82, "write_kib": 112.0,
+              "src": "b5373a8ae12e50ccff175640a47fa8d316c314fdecdb8e5e30d464d2296fa432"},
+    "gemm": {"fetch_kib": 13367.21, "write_kib": 8192.0,
+            "src": "36ca0fc8939a075bb2ea00ddb280f4a3eb98c3a83672c6d8f0c602afd225d379"},
+    "repack": {"fetch_kib": 16143.79, "write_kib": 32256.0,
+              "src": "c7731d535cab20731010497bbc0a3d1e000150808057ba5a6c0f9dbfd08771ac"},
 }
 KERNEL_SOURCES = {
     "decode": ("qgemv.hip", "tq_internal.h"),

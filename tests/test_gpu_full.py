@@ -146,6 +146,29 @@ def test_q4_k_k4096_n14336_m1(tq):
     _check_dots(tq, c, tq.PATH_GEMV)
 
 
+@pytest.mark.parametrize("name", ["q4_0_gemv_k4096_n14336_m1", "q8_0_gemv_k4096_n4096_m1"])
+def test_flat_full_size(tq, name):
+    """The flat path at full size: device unpack of the repacked tiles gives
+    the flat bytes back; the flat GEMV's y against the oracle (in full) and
+    its block dots on sampled stripes."""
+    c = Case(tq, name)
+    w = c.w
+    flat = torch.from_numpy(c.inp.flat).cuda()
+    assert np.array_equal(tq.unpack_tiles(w.qtype, c.tiles, w.K, w.N).cpu().numpy(), c.inp.flat)
+    y = tq.qgemv_flat(w.qtype, flat, w.K, w.N, c.q, c.d, lut=c.inp.lut).cpu().numpy()
+    y_ref, acond = oracle.matmul_flat(w.qtype, c.inp.flat, w.K, w.N, c.q_ref, c.d_ref, c.inp.lut)
+    check_y(y, y_ref, acond, ("flat", w.name))
+    nb = w.K // 32
+    bb = oracle.block_bytes(w.qtype)
+    for s in _stripes(w):
+        n0, n1 = 32 * s, min(32 * s + 32, w.N)
+        sl = c.inp.flat[n0 * nb * bb:n1 * nb * bb]
+        got = tq.block_dots(w.qtype, flat[n0 * nb * bb:n1 * nb * bb], w.K, n1 - n0, c.q,
+                            lut=c.inp.lut, path=tq.PATH_GEMV_FLAT).cpu().numpy()
+        assert np.array_equal(got, oracle.block_dots_flat(w.qtype, sl, w.K, n1 - n0, c.q_ref,
+                                                          c.inp.lut)), (w.name, s)
+
+
 @pytest.fixture(scope="module")
 def lmhead(tq):
     return Case(tq, "q8_0_lmhead_k4096_n128001_m128")
