@@ -13,7 +13,7 @@ LIB = os.path.join(PKG, "libtiledq.so")
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-function",
-    # packed fp32 VALU ops stay disabled ("Build")
+    # packed fp32 VALU instructions (v_pk_*_f32) are not generated
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
