@@ -138,9 +138,9 @@ int tq_supported(int type, int64_t K, int64_t N, int64_t M, int path)
 {
     if (!valid_type(type) || !valid_tkn(type, K, N) || !valid_mk(M, K))
         return 0;
-    if (path == TQ_PATH_GEMV)
+    if (path == TQ_PATH_GEMV || path == TQ_PATH_GEMV_FLAT)
         return M <= 8;
-    return path == TQ_PATH_GEMM;
+    return path == TQ_PATH_GEMM || path == TQ_PATH_GEMM_FLAT;
 }
 
 const char *tq_status_string(int status)

@@ -125,8 +125,9 @@ size_t tq_tiled_bytes(int type, int64_t K, int64_t N);
  * shape or type is invalid. */
 size_t tq_flat_bytes(int type, int64_t K, int64_t N);
 
-/* 1 if (type, K, N, M) is supported by `path` (TQ_PATH_GEMV needs
- * M <= 8), judged from these static properties alone; 0 otherwise. */
+/* 1 if (type, K, N, M) is supported by `path` (TQ_PATH_GEMV and
+ * TQ_PATH_GEMV_FLAT need M <= 8; Q4_K needs K % 256 == 0), judged from
+ * these static properties alone; 0 otherwise. */
 int tq_supported(int type, int64_t K, int64_t N, int64_t M, int path);
 
 /* Static, NUL-terminated name of a status code. */
