@@ -27,6 +27,8 @@
 // k = 4..7), so the vector ALU only converts each dot and adds it into the
 // fp32 accumulator (2 operations per output per block).  Load offsets are
 // computed once per thread; a step adds only the k offset.
+#include <type_traits>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -37,7 +39,15 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
+// THREADS = the 8 waves that stage a step's data and own the 8 32 x 32
+// output sub-blocks; KSW groups of them split each step's KB k-blocks.
+#ifndef TQ_GEMM_KSPLIT
+#define TQ_GEMM_KSPLIT 2
+#endif
 constexpr int BM = 128, BN = 64, KB = 4, THREADS = 512;
+constexpr int KSW = TQ_GEMM_KSPLIT, KBW = KB / KSW;   // wave groups, k-blocks per group
+constexpr int WG_THREADS = THREADS * KSW;
+static_assert(KB % KSW == 0 && KBW % 2 == 0, "k-blocks split evenly, in pairs");
 #ifndef TQ_GEMM_MIN_BLOCKS
 #define TQ_GEMM_MIN_BLOCKS 1      // workgroups per CU the register budget is sized for
 #endif
@@ -359,7 +369,7 @@ __device__ __forceinline__ void store_step(const StageRegs<QT, FT> &s, Lds<QT> &
 }
 
 template <int QT, bool DOTS, int FT>
-__global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uint8_t *__restrict__ tiles,
+__global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uint8_t *__restrict__ tiles,
                                                    int64_t nkt, int64_t N,
                                                    const int8_t *__restrict__ q,
                                                    const uint16_t *__restrict__ d, int64_t M,
@@ -369,7 +379,8 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
     __shared__ __attribute__((aligned(16))) Lds<QT> L;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = (tid >> 6) & 7;
+    const int grp = tid / THREADS;       // wave group: k-blocks KBW * grp .. of each step
     const int wm = wave & 3, wn = wave >> 2;
     const int li = lane & 31, lk = lane >> 5;
     const int64_t nct = (N + 31) / 32;
@@ -391,16 +402,15 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
 
     const Offs<QT, FT> o = make_offs<QT, FT>(nkt, K, tid);
     // the all-zero halves of the scale operands are never written again
-    for (int i = tid; i < 2 * BM; i += THREADS)
+    for (int i = tid; i < 2 * BM; i += WG_THREADS)
         L.da[i / BM][1][i % BM] = 0;
-    for (int i = tid; i < 2 * BN; i += THREADS)
+    for (int i = tid; i < 2 * BN; i += WG_THREADS)
         L.dw[i / BN][1][i % BN] = 0;
 
-    float acc[16];
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-        acc[r] = 0.0f;
-    v16f mt = {};                        // Q4_1: the min term
+    // fp32 sums of this wave's 32 x 32 sub-block (Q4_1: the min term's
+    // MFMAs accumulate into it too, which needs no final rescale)
+    v16f acc = {};
+    static_assert(QT != TQ_Q4_1 || weight_unscale<QT>() == 1.0f, "min term shares acc");
 
     // One k-block: the int8 MFMA (exact block dots) and, for y, the rank-1
     // fp16 MFMA giving sc[m][n] = da[m] * dw[n] (exact in fp32).  Its A
@@ -437,106 +447,110 @@ __global__ __launch_bounds__(THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const uin
                 acc[r] = fmaf((float)dot[r], sc[r], acc[r]);
         }
     };
-    // Software pipeline over k-blocks, across steps: block kb's vector
-    // epilogue runs after block kb + 1's MFMAs are issued, so the matrix
-    // cores and the vector ALU work at the same time; the last block of a
-    // step (dot, sc, kt in `carry`) is finished during the next step's first
-    // MFMAs.  The scheduling group barriers keep that order (by default the
-    // compiler issues all MFMAs first, and a wave's vector work then waits
-    // behind its own matrix work).
-    struct Carry {
-        v16i dot;
-        v16f sc;
-        int64_t kt;
-    };
-    Carry carry;
-    carry.dot = v16i{};
-    carry.sc = v16f{};
-    carry.kt = -1;                       // nothing pending: adds 0 * 0, writes nothing
+    // Per step a wave takes its group's KBW k-blocks, each MFMA pair followed
+    // by its vector epilogue; the other waves of the SIMD (4 per SIMD) fill
+    // the MFMA latency.  (Keeping two blocks' results live, to hide it within
+    // the wave, does not fit the 128 registers a wave has at 4 per SIMD.)
     auto compute = [&](int buf, int64_t step) {
         const v4h ua = __builtin_bit_cast(v4h, L.da[buf][lk][32 * wm + li]);
         const uint64_t wv = L.dw[buf][lk][32 * wn + li];
-        v16i dot[2];
-        v16f sc[2];
-        mfmas(buf, 0, ua, wv, dot[0], sc[0]);
-        epilogue(carry.kt, carry.dot, carry.sc);
+        const int kb0 = KBW * grp;
 #pragma unroll
-        for (int kb = 1; kb < KB; kb++) {
-            mfmas(buf, kb, ua, wv, dot[kb & 1], sc[kb & 1]);
-            epilogue(step * KB + kb - 1, dot[(kb - 1) & 1], sc[(kb - 1) & 1]);
+        for (int j = 0; j < KBW; j++) {
+            v16i dot;
+            v16f sc;
+            mfmas(buf, kb0 + j, ua, wv, dot, sc);
+            epilogue(step * KB + kb0 + j, dot, sc);
         }
-        carry.dot = dot[(KB - 1) & 1];
-        carry.sc = sc[(KB - 1) & 1];
-        carry.kt = step * KB + KB - 1;
         if constexpr (!DOTS) {
-            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
-#pragma unroll
-            for (int kb = 1; kb < KB; kb++) {
-                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_VALU, 16, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_VALU, 16, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(SG_VALU, 32, 0);
-            // the weight decode that follows is scheduled on its own
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (QT == TQ_Q4_1) {
-                // min term of the step's KB blocks, two per fp32 MFMA: lane
-                // (li, lk) holds k = lk, i.e. block 2j + lk, with A = da *
-                // asum of activation row li (exact in fp32) and B = the min
-                // of weight row li
+                // min term of the group's k-blocks, two per fp32 MFMA: lane
+                // (li, lk) holds k = lk, i.e. block kb0 + 2j + lk, with A = da
+                // * asum of activation row li (exact in fp32) and B = the
+                // min of weight row li
                 const int ra = 32 * wm + li;
                 const uint64_t dav = L.da[buf][0][ra];
                 const uint64_t mwv = L.mw[buf][32 * wn + li];
 #pragma unroll
-                for (int j = 0; j < KB / 2; j++) {
-                    const int kb = 2 * j + lk;
+                for (int j = 0; j < KBW / 2; j++) {
+                    const int kb = kb0 + 2 * j + lk;
                     const float a = f16_bits_to_f32((uint16_t)(dav >> (16 * kb))) *
                                     L.asum[buf][ra][kb];
                     const float b = f16_bits_to_f32((uint16_t)(mwv >> (16 * kb)));
-                    mt = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, mt, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
                 }
             }
         }
     };
 
     // Two register stages: step s+1's data is in flight while step s+2 is
-    // issued.
-    StageRegs<QT, FT> r0, r1;
-    // The loop body is one basic block (two steps, no exit in between), so the
-    // compiler tracks the two stages without conservative waits.  An odd step
-    // count gets one trailing step whose k-blocks all lie past K: its scales
-    // are zero, so it adds exactly 0, and its loads (like every prefetch past
-    // the end) are range-checked by the buffer descriptors.
+    // issued.  Only wave group 0 stages; the groups run the same loop with the
+    // same barriers, each as one basic block (two steps, no exit in between),
+    // so the compiler tracks the two stages without conservative waits.  An
+    // odd step count gets one trailing step whose k-blocks all lie past K: its
+    // scales are zero, so it adds exactly 0, and its loads (like every
+    // prefetch past the end) are range-checked by the buffer descriptors.
     const int64_t nsteps2 = (nsteps + 1) & ~int64_t(1);
-    load_step<QT, DOTS, FT>(r0, rg, o, (int)nkt, 0);
-    load_step<QT, DOTS, FT>(r1, rg, o, (int)nkt, KB);
-    store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
-    __syncthreads();
-    for (int64_t step = 0; step < nsteps2; step += 2) {
-        // even step: buffer 0 is computed, r1 holds step+1, r0 is free
-        load_step<QT, DOTS, FT>(r0, rg, o, (int)nkt, (int)(step + 2) * KB);
-        compute(0, step);
-        store_step<QT, DOTS, FT>(r1, L, 1, lut, tid);
+    auto run = [&](auto stage) {
+        constexpr bool ST = decltype(stage)::value;
+        StageRegs<QT, FT> r0, r1;
+        if constexpr (ST) {
+            load_step<QT, DOTS, FT>(r0, rg, o, (int)nkt, 0);
+            load_step<QT, DOTS, FT>(r1, rg, o, (int)nkt, KB);
+            store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
+        }
         __syncthreads();
-        // odd step: buffer 1 is computed, r0 holds step+2, r1 is free
-        load_step<QT, DOTS, FT>(r1, rg, o, (int)nkt, (int)(step + 3) * KB);
-        compute(1, step + 1);
-        store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
-        __syncthreads();
-    }
-    epilogue(carry.kt, carry.dot, carry.sc);
+        for (int64_t step = 0; step < nsteps2; step += 2) {
+            // even step: buffer 0 is computed, r1 holds step+1, r0 is free
+            if constexpr (ST)
+                load_step<QT, DOTS, FT>(r0, rg, o, (int)nkt, (int)(step + 2) * KB);
+            compute(0, step);
+            if constexpr (ST)
+                store_step<QT, DOTS, FT>(r1, L, 1, lut, tid);
+            __syncthreads();
+            // odd step: buffer 1 is computed, r0 holds step+2, r1 is free
+            if constexpr (ST)
+                load_step<QT, DOTS, FT>(r1, rg, o, (int)nkt, (int)(step + 3) * KB);
+            compute(1, step + 1);
+            if constexpr (ST)
+                store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
+            __syncthreads();
+        }
+    };
+    if (grp == 0)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
     if constexpr (DOTS)
         return;
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+        v[r] = acc[r] * weight_unscale<QT>();
+    if constexpr (KSW > 1) {
+        // the groups' partial sums meet in LDS (the A buffers, done with)
+        static_assert(KSW == 2 && 16 * THREADS * 4 <= (int)sizeof(L.A), "reduction space");
+        float *red = (float *)L.A[0];
+        if (grp == 1) {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                red[r * THREADS + (tid - THREADS)] = v[r];
+        }
+        __syncthreads();
+        if (grp == 1)
+            return;
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+            v[r] += red[r * THREADS + tid];
+    }
     const int64_t n = 32 * (ct0 + wn) + li;
     if (n < N) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int64_t m = m0 + 32 * wm + 8 * (r >> 2) + 4 * lk + (r & 3);
             if (m < M)
-                y[m * ldy + n] = acc[r] * weight_unscale<QT>() + (QT == TQ_Q4_1 ? mt[r] : 0.0f);
+                y[m * ldy + n] = v[r];
         }
     }
 }
@@ -554,10 +568,10 @@ hipError_t launch_t(const void *w, int64_t K, int64_t N, const int8_t *q, const 
     // on one XCD and each weight tile is fetched into a single L2.
     dim3 grid((unsigned)((nct + BN / 32 - 1) / (BN / 32)), (unsigned)((M + BM - 1) / BM));
     if (isum)
-        k_qgemm<QT, true, FT><<<grid, THREADS, 0, s>>>((const uint8_t *)w, nkt, N, q, d, M, K,
+        k_qgemm<QT, true, FT><<<grid, WG_THREADS, 0, s>>>((const uint8_t *)w, nkt, N, q, d, M, K,
                                                        lut, y, ldy, isum);
     else
-        k_qgemm<QT, false, FT><<<grid, THREADS, 0, s>>>((const uint8_t *)w, nkt, N, q, d, M, K,
+        k_qgemm<QT, false, FT><<<grid, WG_THREADS, 0, s>>>((const uint8_t *)w, nkt, N, q, d, M, K,
                                                         lut, y, ldy, isum);
     return hipGetLastError();
 }
