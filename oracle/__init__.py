@@ -65,6 +65,12 @@ def lib():
         L.or_block_dots_flat.restype = ctypes.c_int
         L.or_matmul_flat.argtypes = [ctypes.c_int, P, l, l, P, P, l, P, l, l, P, P, l]
         L.or_matmul_flat.restype = None
+        L.or_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.or_e4m3_value.restype = ctypes.c_double
+        L.or_quantize_act_mx.argtypes = [ctypes.c_int, P, l, l, l, P, P]
+        L.or_quantize_act_mx.restype = None
+        L.or_matmul_mx.argtypes = [P, l, l, P, P, l, l, l, P, P, l]
+        L.or_matmul_mx.restype = None
         L.or_row_scale.argtypes = [ctypes.c_int, ctypes.c_uint16]
         L.or_row_scale.restype = ctypes.c_double
         _lib = L
@@ -237,3 +243,35 @@ def matmul_flat(t, flat, K, N, q, d, lut=None, n0=0, n1=None):
     lib().or_matmul_flat(t, _p(flat), K, N, _p(q), _p(d), M, _p(lut), n0, n1, _p(y), _p(acond), N)
     return y, acond
 
+
+
+def e4m3_value(code):
+    """Value of an OCP FP8 E4M3 code (0x7F / 0xFF, NaN, excluded)."""
+    return lib().or_e4m3_value(int(code))
+
+
+def quantize_act_mx(x, dtype=F32, K=None):
+    """MXFP8 activations: x [M, K] float32 (F32) or uint16 bits (BF16 / F16).
+
+    Returns (q uint8 E4M3 codes [M,K], e uint8 E8M0 scales [M,K/32])."""
+    x = np.ascontiguousarray(x, dtype=np.float32 if dtype == F32 else np.uint16)
+    M, Kx = x.shape
+    K = Kx if K is None else K
+    q = np.zeros((M, K), np.uint8)
+    e = np.zeros((M, K // 32), np.uint8)
+    lib().or_quantize_act_mx(dtype, _p(x), M, K, Kx, _p(q), _p(e))
+    return q, e
+
+
+def matmul_mx(tiles, K, N, q, e, n0=0, n1=None):
+    """MXFP4 tiles x MXFP8 activations: y[m, n] (fp64) and acond[m, n] =
+    sum |W*A| for n0 <= n < n1."""
+    tiles = _c(tiles, np.uint8)
+    q = _c(q, np.uint8)
+    e = _c(e, np.uint8)
+    M = q.shape[0]
+    n1 = N if n1 is None else min(n1, N)
+    y = np.zeros((M, N), np.float64)
+    acond = np.zeros((M, N), np.float64)
+    lib().or_matmul_mx(_p(tiles), K, N, _p(q), _p(e), M, n0, n1, _p(y), _p(acond), N)
+    return y, acond

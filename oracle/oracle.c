@@ -11,7 +11,9 @@
  * Formats" with its subsections "Tile Dimensions and Grid Layout" and
  * "Block-32 Quantized Formats" (Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1), and section "Memory
  * buffers" (dynamically quantized activations).  Where the page is silent the
- * reading taken is stated at the function.
+ * reading taken is stated at the function.  The MXFP8 activation side of the
+ * MXFP4 block-scaled product (or_quantize_act_mx, or_matmul_mx) follows the
+ * OCP Microscaling Formats specification v1.0, stated at the functions.
  *
  * Everything is scalar C, one element at a time, in the order the page states
  * it.  Floating-point results are fp64 unless the data format fixes the
@@ -644,3 +646,121 @@ void or_matmul_flat(int type, const uint8_t *flat, long K, long N,
     free(wrow);
 }
 
+
+/* ---------------------------------------------------------------------------
+ * MXFP8 activations for MXFP4 weights (OCP Microscaling Formats v1.0: a block
+ * of 32 elements shares one E8M0 scale X = 2^(e - 127); the elements are
+ * FP8 E4M3 codes).  The page's MXFP4 tiles carry exactly such per-32 E8M0
+ * scales ("MXFP4"); this is the activation side that pairs with them on
+ * matrix hardware that applies per-32 power-of-two scales itself.  Reading
+ * (the page quantizes activations to Q8_0 and says nothing of MX
+ * activations), following the OCP conversion:
+ *   amax = max_j |x_j| (inputs converted exactly to fp32);
+ *   X    = 2^(floor(log2 amax) - 8)   (8 = the largest E4M3 exponent),
+ *          the biased exponent clamped to 0..254; amax = 0 gives e = 0;
+ *   P_j  = the E4M3 value nearest to x_j / X, ties to the even code,
+ *          magnitudes above 448 (the largest finite E4M3) saturating to 448;
+ *          the code's sign bit is the sign bit of x_j.
+ * E4M3 (OCP FP8): sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ * field 0 is subnormal (m/8 * 2^-6); codes 0x7F and 0xFF are NaN and never
+ * produced.
+ * ------------------------------------------------------------------------- */
+double or_e4m3_value(uint8_t code)
+{
+    int e = (code >> 3) & 0x0f, m = code & 7;
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return (code & 0x80) ? -v : v;
+}
+
+/* Nearest non-negative E4M3 code (0..0x7E) to v >= 0, ties to the even
+ * code: a walk over the 127 finite values in increasing order. */
+static int e4m3_nearest(double v)
+{
+    int best = 0;
+    double bd = fabs(v);
+    for (int c = 1; c <= 0x7e; c++) {
+        double dist = fabs(v - or_e4m3_value((uint8_t)c));
+        if (dist < bd || (dist == bd && (c & 1) == 0 && (best & 1) != 0)) {
+            best = c;
+            bd = dist;
+        }
+    }
+    return best;
+}
+
+void or_quantize_act_mx(int dtype, const void *x, long M, long K, long ldx,
+                        uint8_t *q, uint8_t *e)
+{
+    long nb = K / 32;
+    for (long m = 0; m < M; m++) {
+        for (long kt = 0; kt < nb; kt++) {
+            double amax = 0.0;
+            for (int j = 0; j < 32; j++) {
+                double v = fabs((double)load_act(dtype, x, m * ldx + kt * 32 + j));
+                if (v > amax)
+                    amax = v;
+            }
+            int eb = 0;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);           /* amax = f * 2^ex, 0.5 <= f < 1 */
+                eb = (ex - 1) - 8 + 127;    /* floor(log2 amax) - 8, biased */
+                if (eb < 0)
+                    eb = 0;
+                if (eb > 254)
+                    eb = 254;
+            }
+            e[m * nb + kt] = (uint8_t)eb;
+            for (int j = 0; j < 32; j++) {
+                float xv = load_act(dtype, x, m * ldx + kt * 32 + j);
+                double r = ldexp(fabs((double)xv), 127 - eb);   /* |x| / X, exact */
+                int c = (r >= 448.0) ? 0x7e : e4m3_nearest(r);
+                q[m * K + kt * 32 + j] = (uint8_t)(c | (signbit(xv) ? 0x80 : 0));
+            }
+        }
+    }
+}
+
+/* The MXFP4 x MXFP8 product from its plain definition:
+ *   y[m][n] = sum_k W[n][k] * A[m][k],
+ *   W[n][k] = s(e_w[n][kt]) * E2M1(code)  -- the page's MXFP4 dequantization,
+ *             s(e) = the FP16 power of two with exponent bits clamp(e-112, 0, 30);
+ *   A[m][k] = 2^(e_a[m][kt] - 127) * E4M3(q[m][k]).
+ * fp64, output rows n0 <= n < n1; acond as in or_matmul. */
+void or_matmul_mx(const uint8_t *tiles, long K, long N, const uint8_t *q, const uint8_t *e,
+                  long M, long n0, long n1, double *y, double *acond, long ldy)
+{
+    long nb = K / 32;
+    long ts = or_tile_bytes(OR_MXFP4);
+    if (n1 > N)
+        n1 = N;
+    double *wrow = malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    for (long n = n0; n < n1; n++) {
+        long ct = n / 32;
+        int row = (int)(n % 32);
+        for (long kt = 0; kt < nb; kt++) {
+            const uint8_t *tile = tiles + (ct * nb + kt) * ts;
+            /* or_row_scale halves the power of two for the doubled integer
+             * weight; the E2M1 value is half that integer: together s * E2M1 */
+            double dw = or_row_scale(OR_MXFP4, get_tile_scale(OR_MXFP4, tile, row, 0));
+            for (int col = 0; col < 32; col++) {
+                int cp = col / 2;
+                uint8_t c = (col & 1) ? (tile[cp * 32 + row] >> 4) : (tile[cp * 32 + row] & 0x0f);
+                wrow[kt * 32 + col] = dw * (double)e2m1_twice(c);
+            }
+        }
+        for (long m = 0; m < M; m++) {
+            double s = 0.0, a = 0.0;
+            for (long k = 0; k < K; k++) {
+                double act = ldexp(or_e4m3_value(q[m * K + k]), (int)e[m * nb + k / 32] - 127);
+                double t = wrow[k] * act;
+                s += t;
+                a += fabs(t);
+            }
+            y[m * ldy + n] = s;
+            if (acond)
+                acond[m * ldy + n] = a;
+        }
+    }
+    free(wrow);
+}
