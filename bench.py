@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (fp8 x fp4 issues at the fp8 rate)
 ROTATE_BYTES = 1 << 30         # defeat the 256 MB Infinity Cache
 
 # HBM traffic of the kernels, from rocprofv3 --pmc passes (FETCH_SIZE, then
@@ -56,8 +57,9 @@ KERNEL_SOURCES = {
     "decode": ("qgemv.hip", "tq_internal.h"),
     "gemm": ("qgemm.hip", "tq_internal.h"),
     "repack": ("repack.hip", "tq_internal.h"),
+    "mx": ("mx.hip", "tq_internal.h"),
 }
-LAUNCH_ONLY = ("decode", "gemm", "repack", "copy")
+LAUNCH_ONLY = ("decode", "gemm", "repack", "mx", "copy")
 
 
 def source_hash(kernel):
@@ -283,6 +285,45 @@ def measure_gemm(torch, tq, synth, n=200):
                          "traffic": tb, "bytes_per_launch": gemm_bytes(w)}}
 
 
+def setup_mx(torch, tq, synth):
+    """MXFP4 M=512 K=N=4096 on the block-scaled matrix cores (MXFP8
+    activations from bf16, like the int8 GEMM workload's)."""
+    import numpy as np
+    w = synth.WORKLOADS["mxfp4_gemm_m512_k4096_n4096"]
+    inp = synth.make_inputs(w)
+    flat = torch.from_numpy(inp.flat).cuda()
+    R = max(2, -(-ROTATE_BYTES // w.weight_bytes))
+    tiles = [tq.repack_tiles(w.qtype, flat, w.K, w.N) for _ in range(R)]
+    x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
+    q, e = tq.quantize_act_mx(x)
+    y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    f = lambda i: tq.qgemm_mx(tiles[i % R], w.K, w.N, q, e, out=y)
+    quant = lambda i: tq.quantize_act_mx(x, q=q, e=e)
+    q8, d8 = tq.quantize_act(x)
+    f8 = lambda i: tq.qgemm(w.qtype, tiles[i % R], w.K, w.N, q8, d8, out=y)
+    return w, f, quant, f8
+
+
+def measure_mx(torch, tq, synth, n=200):
+    w, f, quant, f8 = setup_mx(torch, tq, synth)
+    for i in range(20):
+        f(i)
+        f8(i)
+    us = kernel_us(torch, f, n)
+    quant_us = kernel_us(torch, quant, 50)
+    us8 = kernel_us(torch, f8, n)
+    tflops = 2.0 * w.M * w.N * w.K / us / 1e6
+    nbytes = w.weight_bytes + w.M * w.K + w.M * (w.K // 32) + 4 * w.M * w.N
+    return {"workload": w.name + " (MXFP8 activations, block-scaled MFMA)",
+            "metric": "qgemm_mx fp8 x fp4 TFLOP/s", "value": round(tflops, 2), "unit": "TFLOP/s",
+            "kernel_us": round(us, 3), "quantize_act_mx_us": round(quant_us, 3),
+            "int8_path_same_tiles_us": round(us8, 3),
+            "hbm_GB_s": round(nbytes / us / 1e3, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / FP8_PEAK_TFLOPS, 4),
+                         "traffic": traffic_bytes("mx"), "bytes_per_launch": nbytes}}
+
+
 def setup_repack(torch, tq, synth):
     w = synth.WORKLOADS["q4_0_gemv_k4096_n14336_m1"]
     inp = synth.make_inputs(w)
@@ -433,6 +474,8 @@ def launch_only(torch, tq, synth, kernel, n):
         f = setup_gemm(torch, tq, synth)[1]
     elif kernel == "repack":
         f = setup_repack(torch, tq, synth)[1]
+    elif kernel == "mx":
+        f = setup_mx(torch, tq, synth)[1]
     else:                                   # calibration: a plain 256 MiB copy
         a = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -550,6 +593,7 @@ def main():
     }
     if not args.no_extra:
         line["qgemm"] = measure_gemm(torch, tq, synth)
+        line["qgemm_mx"] = measure_mx(torch, tq, synth)
         line["repack"] = measure_repack(torch, tq, synth)
         line["other_workloads"] = measure_others(torch, tq, synth)
     if not args.no_cpu_baseline:

@@ -31,6 +31,8 @@ SIGNATURES = {
     "tq_matmul": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P, SZ, P]),
     "tq_block_dots": (INT, [INT, P, I64, I64, P, I64, P, P, INT, P]),
     "tq_unpack_tiles": (INT, [INT, P, I64, I64, P, P]),
+    "tq_quantize_act_mx": (INT, [INT, P, I64, I64, I64, P, P, P]),
+    "tq_qgemm_mx": (INT, [P, I64, I64, P, P, I64, P, I64, P]),
     "tq_qgemv_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_qgemm_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_matmul_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),

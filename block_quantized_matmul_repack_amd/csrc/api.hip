@@ -343,4 +343,35 @@ int tq_matmul_flat(int type, const void *flat, int64_t K, int64_t N, const int8_
     return tq_qgemm_flat(type, flat, K, N, q, d, M, lut, y, ldy, stream);
 }
 
+int tq_quantize_act_mx(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx, uint8_t *q,
+                       uint8_t *e, hipStream_t stream)
+{
+    if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16)
+        return TQ_E_TYPE;
+    if (K < 32 || K > MAX_K || K % 32 != 0 || !valid_mk(M, K) || ldx < K ||
+        M * ldx >= MAX_PROD)
+        return TQ_E_SHAPE;
+    if (M == 0)
+        return TQ_OK;
+    if (!x || !q || !e)
+        return TQ_E_NULL;
+    if (!aligned(x, dtype == TQ_F32 ? 4 : 2) || !aligned(q, 8))
+        return TQ_E_ALIGN;
+    return launch_status(tq::launch_quantize_mx(dtype, x, M, K, ldx, q, e, stream));
+}
+
+int tq_qgemm_mx(const void *tiles, int64_t K, int64_t N, const uint8_t *q, const uint8_t *e,
+                int64_t M, float *y, int64_t ldy, hipStream_t stream)
+{
+    if (!valid_kn(K, N) || !valid_mk(M, K) || ldy < N)
+        return TQ_E_SHAPE;
+    if (M == 0 || N == 0)
+        return TQ_OK;
+    if (!tiles || !q || !e || !y)
+        return TQ_E_NULL;
+    if (!aligned(tiles, 16) || !aligned(q, 16) || !aligned(y, 4))
+        return TQ_E_ALIGN;
+    return launch_status(tq::launch_qgemm_mx(tiles, K, N, q, e, M, y, ldy, stream));
+}
+
 }  // extern "C"

@@ -297,5 +297,10 @@ hipError_t launch_qgemv_flat(int type, const void *flat, int64_t K, int64_t N, c
 hipError_t launch_qgemm_flat(int type, const void *flat, int64_t K, int64_t N, const int8_t *q,
                              const uint16_t *d, int64_t M, const Lut &lut, float *y,
                              int64_t ldy, int32_t *isum, hipStream_t s);
+// MXFP4 tiles x MXFP8 activations on the block-scaled matrix cores.
+hipError_t launch_quantize_mx(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
+                              uint8_t *q, uint8_t *e, hipStream_t s);
+hipError_t launch_qgemm_mx(const void *tiles, int64_t K, int64_t N, const uint8_t *q,
+                           const uint8_t *e, int64_t M, float *y, int64_t ldy, hipStream_t s);
 
 }  // namespace tq

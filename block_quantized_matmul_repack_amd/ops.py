@@ -187,6 +187,41 @@ def unpack_tiles(qtype, tiles, K, N, out=None):
     return out[:nbytes]
 
 
+def quantize_act_mx(x, K=None, q=None, e=None):
+    """x [M, >=K] fp32 / bf16 / fp16 -> MXFP8 (q uint8 E4M3 codes [M, K],
+    e uint8 E8M0 scales [M, K/32])."""
+    if x.dim() != 2 or x.dtype not in _DTYPES:
+        raise TiledqError("quantize_act_mx: x must be 2-D fp32, bf16 or fp16")
+    if not x.is_cuda or x.stride(1) != 1:
+        raise TiledqError("quantize_act_mx: x must be a GPU tensor with unit column stride")
+    M, Kx = x.shape
+    K = Kx if K is None else K
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if e is None:
+        e = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _need_cuda(q, e)
+    if q.numel() < M * K or e.numel() < M * (K // 32):
+        raise TiledqError("quantize_act_mx: output too small")
+    check(lib().tq_quantize_act_mx(_DTYPES[x.dtype], _ptr(x), M, K, x.stride(0), _ptr(q),
+                                   _ptr(e), _stream(x)), "tq_quantize_act_mx")
+    return q, e
+
+
+def qgemm_mx(tiles, K, N, q, e, out=None):
+    """MXFP4 tiles x MXFP8 activations on the block-scaled matrix cores:
+    y [M, N] fp32, any M."""
+    _need_cuda(tiles, q, e, out)
+    M = q.shape[0]
+    if tiles.numel() * tiles.element_size() < tiled_bytes(MXFP4, K, N) or \
+            q.numel() < M * K or e.numel() < M * (K // 32):
+        raise TiledqError("qgemm_mx: buffer too small")
+    out = _out("tq_qgemm_mx", q, N, out)
+    check(lib().tq_qgemm_mx(_ptr(tiles), K, N, _ptr(q), _ptr(e), M, _ptr(out), out.stride(0),
+                            _stream(q)), "tq_qgemm_mx")
+    return out
+
+
 def _flat_product(name, qtype, flat, K, N, q, d, lut, out):
     _need_cuda(flat, q, d, out)
     out = _out(name, q, N, out)

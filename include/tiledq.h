@@ -243,6 +243,44 @@ int tq_matmul_flat(int type, const void *flat, int64_t K, int64_t N,
                    const int8_t *q, const uint16_t *d, int64_t M,
                    const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
 
+/* MXFP4 on block-scaled matrix cores.  The page's MXFP4 tiles ("MXFP4":
+ * E2M1 codes with one E8M0 scale per row and 32-element block) multiplied by
+ * activations in the matching OCP Microscaling format, MXFP8: FP8 E4M3 codes
+ * with one E8M0 scale per 32 elements, so that the matrix core applies both
+ * power-of-two scales itself.  This is a second activation format beside the
+ * page's Q8_0 one (tq_quantize_act); results differ from tq_qgemm on the
+ * same MXFP4 tiles by the activation rounding.
+ *
+ * tq_quantize_act_mx: per 32-element block of each row (OCP Microscaling
+ * v1.0 conversion): e = floor(log2 amax) - 8 + 127, clamped to 0..254 (0 for
+ * an all-zero block); q = the E4M3 code nearest to x / 2^(e - 127), ties to
+ * even, magnitudes above 448 saturating to 448, sign bit = x's sign bit.
+ * Never writes the NaN codes 0x7F / 0xFF.  Bit-exact, deterministic.
+ *   x : device, dtype TQ_F32 / TQ_BF16 / TQ_F16, row m at x + m*ldx
+ *       elements (ldx >= K), aligned to its element size.
+ *   q : device, uint8 [M][K] E4M3 codes, 8-byte aligned.
+ *   e : device, uint8 [M][K/32] E8M0 bytes.
+ *   K % 32 == 0 (else TQ_E_SHAPE); M == 0 returns TQ_OK with no launch.
+ *
+ * tq_qgemm_mx: y[m*ldy + n] = sum_k W[n][k] * A[m][k] for m < M, n < N, with
+ * W the MXFP4 tile weights (E2M1 value times the FP16 power of two of
+ * exponent bits clamp(e - 112, 0, 30), exactly as the page converts the
+ * E8M0 byte: rows with e <= 112 weigh 0) and A[m][k] = E4M3(q[m][k]) *
+ * 2^(e[m][k/32] - 127).  Any M >= 1; fp32 sums in the matrix core (not
+ * bit-reproducible against a sequential fp32 sum: see the tolerance the
+ * tests state).
+ *   tiles : device, tq_tiled_bytes(TQ_MXFP4, K, N) bytes, 16-byte aligned.
+ *   q, e  : device, as written by tq_quantize_act_mx (q 16-byte aligned);
+ *           q must hold no NaN code.
+ *   y     : device fp32, row stride ldy >= N, 4-byte aligned; only n < N,
+ *           m < M written.
+ *   Errors as tq_qgemm.  Deterministic. */
+int tq_quantize_act_mx(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
+                       uint8_t *q, uint8_t *e, hipStream_t stream);
+int tq_qgemm_mx(const void *tiles, int64_t K, int64_t N, const uint8_t *q,
+                const uint8_t *e, int64_t M, float *y, int64_t ldy,
+                hipStream_t stream);
+
 /* Test instrument: run the tq_qgemv (path TQ_PATH_GEMV, M <= 8) or tq_qgemm
  * (TQ_PATH_GEMM) kernel, or their flat forms (TQ_PATH_GEMV_FLAT,
  * TQ_PATH_GEMM_FLAT; `tiles` then holds flat blocks, aligned as for

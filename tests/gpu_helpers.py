@@ -35,10 +35,10 @@ def to_dev_act(x, act):
     return t.view(torch.bfloat16 if act == "bf16" else torch.float16)
 
 
-def check_y(y, y_ref, acond, what=""):
+def check_y(y, y_ref, acond, what="", floor=FLOOR):
     y = np.asarray(y, dtype=np.float64)
     err = np.abs(y - y_ref)
-    bound = TOL * np.maximum(np.abs(y_ref), FLOOR * acond)
+    bound = TOL * np.maximum(np.abs(y_ref), floor * acond)
     bad = np.nonzero(err > bound)
     assert bad[0].size == 0, (what, [(int(i), int(j), float(y[i, j]), float(y_ref[i, j]))
                                      for i, j in zip(*bad)][:5])

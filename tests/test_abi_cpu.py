@@ -217,3 +217,27 @@ def test_flat_validation(L):
     assert L.tq_block_dots(0, A16, 64, 32, A16, 1, NUL, A16, 4, NUL) == 2       # unknown path
     assert L.tq_block_dots(0, A16, 64, 32, A16, 9, NUL, A16, 2, NUL) == 3       # flat GEMV, M > 8
     assert L.tq_block_dots(5, A4, 256, 32, A16, 1, NUL, A16, 3, NUL) == 4       # Q4_K flat: 16
+
+
+def test_mx_validation(L):
+    q = L.tq_quantize_act_mx
+    assert q(5, A16, 1, 64, 64, A16, A16, NUL) == 2
+    assert q(0, A16, 1, 60, 64, A16, A16, NUL) == 3
+    assert q(0, A16, 1, 64, 32, A16, A16, NUL) == 3         # ldx < K
+    assert q(0, NUL, 1, 64, 64, A16, A16, NUL) == 1
+    assert q(0, A16, 1, 64, 64, A16, NUL, NUL) == 1
+    assert q(0, A2, 1, 64, 64, A16, A16, NUL) == 4          # fp32 needs 4 B
+    assert q(0, A16, 1, 64, 64, A2, A16, NUL) == 4          # q needs 8 B
+    assert q(0, NUL, 0, 64, 64, NUL, NUL, NUL) == 0
+    g = L.tq_qgemm_mx
+    assert g(A16, 48, 32, A16, A16, 1, A16, 32, NUL) == 3
+    assert g(A16, 64, 32, A16, A16, 1, A16, 31, NUL) == 3   # ldy < N
+    assert g(NUL, 64, 32, A16, A16, 1, A16, 32, NUL) == 1
+    assert g(A16, 64, 32, NUL, A16, 1, A16, 32, NUL) == 1
+    assert g(A16, 64, 32, A16, NUL, 1, A16, 32, NUL) == 1
+    assert g(A16, 64, 32, A16, A16, 1, NUL, 32, NUL) == 1
+    assert g(A2, 64, 32, A16, A16, 1, A16, 32, NUL) == 4
+    assert g(A16, 64, 32, A2, A16, 1, A16, 32, NUL) == 4
+    assert g(A16, 64, 32, A16, A16, 1, A2, 32, NUL) == 4
+    assert g(NUL, 64, 32, NUL, NUL, 0, NUL, 32, NUL) == 0   # M == 0
+    assert g(NUL, 64, 0, NUL, NUL, 4, NUL, 0, NUL) == 0     # N == 0

@@ -127,6 +127,24 @@ def test_mxfp4_m512_k4096_n4096(tq):
     _check_dots(tq, c, tq.PATH_GEMM)
 
 
+def test_mxfp4_mx_m512_k4096_n4096(tq):
+    """The same workload on the block-scaled matrix cores: MXFP8 activations
+    bit for bit in full, y on the sampled stripes."""
+    c = Case(tq, "mxfp4_gemm_m512_k4096_n4096")
+    w = c.w
+    assert np.array_equal(c.tiles.cpu().numpy(), c.tiles_ref), "repack differs"
+    qr, er = oracle.quantize_act_mx(c.inp.x, _DT[w.act_dtype])
+    print(f"[full] {w.name}: quantize_act_mx + qgemm_mx", flush=True)
+    q, e = tq.quantize_act_mx(to_dev_act(c.inp.x, w.act_dtype))
+    assert np.array_equal(q.cpu().numpy(), qr) and np.array_equal(e.cpu().numpy(), er)
+    y = tq.qgemm_mx(c.tiles, w.K, w.N, q, e).cpu().numpy()
+    for s in _stripes(w):
+        n0, n1 = 32 * s, min(32 * s + 32, w.N)
+        y_ref, acond = oracle.matmul_mx(c.tiles_ref, w.K, w.N, qr, er, n0=n0, n1=n1)
+        # the block-scaled matrix core's tolerance (see test_gpu_mx)
+        check_y(y[:, n0:n1], y_ref[:, n0:n1], acond[:, n0:n1], (w.name, "mx", s), floor=0.25)
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_q4_1_k4096_n14336(tq, M):
     c = Case(tq, "q4_1_gemv_k4096_n14336_m1", M=M)

@@ -1,0 +1,150 @@
+"""MXFP4 tiles x MXFP8 activations on the block-scaled matrix cores, against
+the oracle: the MXFP8 quantizer bit-exact, the product elementwise within
+|y - y_ref| <= 1e-3 * max(|y_ref|, 0.25 * A) (A = sum of |terms|) and
+normwise within 1e-4.
+
+The floor is wider than the int8 path's 1e-2 * A because of how the
+block-scaled matrix core adds: it sums each instruction's scaled products
+with about 16 significant bits, not fp32's 24 (most sums come out exact; the
+largest errors measured on these inputs were 2.6e-5 * A, at small K where a
+single instruction makes up the sum; normwise errors were about 4e-6).
+0.25 * A keeps a tenfold margin over that, while any layout, scale or
+indexing mistake gives errors of the order of A itself."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import check_y, make, to_dev_act
+
+pytestmark = pytest.mark.gpu
+MXFP4 = synth.MXFP4
+MX_FLOOR = 0.25
+
+
+def check_mx(y, y_ref, acond, what):
+    check_y(y, y_ref, acond, what, floor=MX_FLOOR)
+    assert np.linalg.norm(y - y_ref) <= 1e-4 * np.linalg.norm(y_ref), what
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_quantized_matmul_repack_amd as tq
+    tq.lib()
+    return tq
+
+
+def specials(x):
+    """Blocks that exercise the scale rule, ties, saturation and signs."""
+    K = x.shape[1]
+    x[0, :32] = 0.0                                  # all-zero block: e = 0
+    if K >= 128:
+        x[0, 32:64] = 1.5                            # constant block
+        x[0, 64:96] = np.float32(2.0 ** -120)        # scale clamped to e = 0
+        x[0, 96] = 511.0                             # X = 1 for the rest of the block
+        x[0, 97:106] = [448.0, 460.0, 479.0, -490.0, -0.0, 0.0029296875, 0.0009765625,
+                        9.0, 13.0]                   # saturation, signed zero, ties
+    return x
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 256), (8, 4096), (37, 1024), (130, 96)])
+def test_quantize_mx_bitexact(tq, act, M, K):
+    inp = make(MXFP4, K, 1, M, seed=M * 100 + K, act=act)
+    x = inp.x.copy()
+    if act == "f32":
+        x = specials(x)
+    dt = {"f32": oracle.F32, "bf16": oracle.BF16, "f16": oracle.F16}[act]
+    qr, er = oracle.quantize_act_mx(x, dt)
+    q, e = tq.quantize_act_mx(to_dev_act(x, act))
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(e.cpu().numpy(), er)
+
+
+def test_quantize_mx_row_stride(tq):
+    inp = make(MXFP4, 256, 1, 5, seed=3)
+    wide = np.concatenate([inp.x, np.full((5, 64), 9e5, np.float32)], axis=1)
+    qr, er = oracle.quantize_act_mx(wide, oracle.F32, K=256)
+    q, e = tq.quantize_act_mx(torch.from_numpy(wide).cuda(), K=256)
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(e.cpu().numpy(), er)
+
+
+def mx_case(tq, M, K, N, seed, ebytes=None):
+    inp = make(MXFP4, K, N, M, seed=seed)
+    flat = inp.flat
+    if ebytes is not None:
+        flat = synth.pack_flat(MXFP4, inp.codes, ebytes.astype(np.uint16))
+    tiles = oracle.repack(MXFP4, flat, K, N)
+    q, e = oracle.quantize_act_mx(inp.x)
+    y_ref, acond = oracle.matmul_mx(tiles, K, N, q, e)
+    qd, ed = tq.quantize_act_mx(torch.from_numpy(inp.x).cuda())
+    out = torch.full((M, N + 16), 7.0, dtype=torch.float32, device="cuda")
+    tq.qgemm_mx(torch.from_numpy(tiles).cuda(), K, N, qd, ed, out=out)
+    got = out.cpu().numpy()
+    assert (got[:, N:] == 7.0).all()                 # columns beyond N untouched
+    return got[:, :N], y_ref, acond
+
+
+@pytest.mark.parametrize("M", [1, 5, 128, 130, 300])
+@pytest.mark.parametrize("K,N", [(32, 1), (96, 33), (256, 64), (1024, 97), (2048, 300),
+                                 (4064, 65)])
+def test_qgemm_mx_y(tq, M, K, N):
+    got, y_ref, acond = mx_case(tq, M, K, N, seed=M * 7 + K + N)
+    check_mx(got, y_ref, acond, ("mx", M, K, N))
+
+
+def test_qgemm_mx_scale_edges(tq):
+    """Rows whose E8M0 byte the page maps to 0 (e <= 112) contribute exactly
+    nothing; e >= 142 saturates at 2^15 -- mixed with ordinary rows."""
+    K, N, M = 256, 70, 40
+    rng = np.random.default_rng(9)
+    e = rng.integers(118, 125, (N, K // 32)).astype(np.uint8)
+    e[0, :] = 0
+    e[1, :] = 112
+    e[2, ::2] = 113
+    e[3, :] = 142
+    e[4, :] = 200
+    e[5, 1::3] = 255
+    e[69, :] = 100
+    got, y_ref, acond = mx_case(tq, M, K, N, seed=5, ebytes=e)
+    assert (got[:, 0] == 0).all() and (got[:, 1] == 0).all() and (got[:, 69] == 0).all()
+    check_mx(got, y_ref, acond, "mx scale edges")
+
+
+def test_qgemm_mx_deterministic(tq):
+    K, N, M = 1024, 200, 130
+    inp = make(MXFP4, K, N, M, seed=1)
+    tiles = torch.from_numpy(oracle.repack(MXFP4, inp.flat, K, N)).cuda()
+    q, e = tq.quantize_act_mx(torch.from_numpy(inp.x).cuda())
+    a = tq.qgemm_mx(tiles, K, N, q, e)
+    b = tq.qgemm_mx(tiles, K, N, q, e)
+    assert torch.equal(a, b)
+
+
+def test_qgemm_mx_close_to_int8_path(tq):
+    """The same MXFP4 tiles through the page's Q8_0 activations (tq_qgemm):
+    both approximate the same real product, each within its activation
+    rounding (E4M3 keeps 3 mantissa bits, so this is loose)."""
+    K, N, M = 1024, 96, 64
+    inp = make(MXFP4, K, N, M, seed=4)
+    tiles = torch.from_numpy(oracle.repack(MXFP4, inp.flat, K, N)).cuda()
+    x = torch.from_numpy(inp.x).cuda()
+    q, e = tq.quantize_act_mx(x)
+    y_mx = tq.qgemm_mx(tiles, K, N, q, e).cpu().numpy().astype(np.float64)
+    q8, d8 = tq.quantize_act(x)
+    y_i8 = tq.qgemm(MXFP4, tiles, K, N, q8, d8).cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(y_mx - y_i8) / np.linalg.norm(y_i8) < 0.1
+
+
+def test_mx_empty_shapes(tq):
+    t = torch.zeros(1088, dtype=torch.uint8, device="cuda")
+    q = torch.zeros((0, 64), dtype=torch.uint8, device="cuda")
+    e = torch.zeros((0, 2), dtype=torch.uint8, device="cuda")
+    out = tq.qgemm_mx(t, 64, 32, q, e)
+    assert out.shape == (0, 32)
+    qq, ee = tq.quantize_act_mx(torch.zeros((0, 64), device="cuda"))
+    assert qq.shape == (0, 64) and ee.shape == (0, 2)
