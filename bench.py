@@ -46,12 +46,14 @@ ROTATE_BYTES = 1 << 30         # defeat the 256 MB Infinity Cache
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "decode": {"fetch_kib": 8779.82, "write_kib": 112.0,
-              "src": "b5373a8ae12e50ccff175640a47fa8d316c314fdecdb8e5e30d464d2296fa432"},
-    "gemm": {"fetch_kib": 13369.16, "write_kib": 8192.0,
-            "src": "6ae1fe76c8a1668e6150bd2a776b68b370fc82cf8f98fcf0c4e5000309835a32"},
-    "repack": {"fetch_kib": 16143.79, "write_kib": 32256.0,
-              "src": "c7731d535cab20731010497bbc0a3d1e000150808057ba5a6c0f9dbfd08771ac"},
+    "decode": {"fetch_kib": 8779.81, "write_kib": 112.00,
+             "src": "55b2e5cfc488b70b6ac82f4971120ec01ad77bdf202d81f3923c58d573de87c7"},
+    "gemm": {"fetch_kib": 13369.53, "write_kib": 8192.00,
+           "src": "ffaf03ca0cef80b39ffa637f26ec8f0417089ad91034c7db7ac0b60c7b0c975b"},
+    "repack": {"fetch_kib": 16143.86, "write_kib": 32256.00,
+             "src": "b079be5257f056c8da28b20e2af048e64ed280c21bc08e26b4d0bcc56e7546db"},
+    "mx": {"fetch_kib": 12871.01, "write_kib": 8192.00,
+         "src": "b3a202fe6dad40862634398f75f9c071091839e4933f34c28661ddeceab4e348"},
 }
 KERNEL_SOURCES = {
     "decode": ("qgemv.hip", "tq_internal.h"),

@@ -97,22 +97,29 @@ __global__ __launch_bounds__(QTHREADS) void k_quantize_mx(const void *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// Block-scaled GEMM.  A workgroup of 8 waves owns BM x BN = 128 x 64
-// outputs, in two groups of 4 that own the same outputs and split each
-// stage's MFMA steps (two waves per SIMD, so one wave's waits for loads and
-// LDS overlap the other's work; at the end group 1 hands its sums to group 0
-// through LDS): wave (g, w) takes activation rows 32w .. 32w + 31 against
-// both 32-row weight stripes (two accumulators).  A stage covers SKT = 8
-// k-tiles (256 K, four MFMA steps of 64), staged by all 512 threads: the
-// activation rows (256 bytes each, padded to 272 so that b128 reads of 16
-// consecutive rows hit 16 different bank groups), their E8M0 bytes, the 16
-// tiles' quant bytes as stored and their row scales converted once.
+// Block-scaled GEMM.  A workgroup of 8 waves owns BM x BN = 64 x 128
+// outputs (64 activation rows, four 32-row weight stripes: the 8-bit
+// activations are the larger operand, so a workgroup spans more weights
+// than activations), in two groups of 4 that own the same outputs and split
+// each stage's MFMA steps (two waves per SIMD, so one wave's waits for
+// loads and LDS overlap the other's work; at the end group 1 hands its sums
+// to group 0 through LDS): wave (g, w) takes activation rows 32 (w % 2) ..
+// + 31 against stripes 2 (w / 2) and 2 (w / 2) + 1 (two accumulators).  A
+// stage covers SKT = 8 k-tiles (256 K, four MFMA steps of 64), staged by all
+// 512 threads: the activation rows (256 bytes each, padded to 272 so that
+// b128 reads of 16 consecutive rows hit 16 different bank groups), their
+// E8M0 bytes, the 32 tiles' quant bytes as stored and their row scales
+// converted once.  (Stages of 512 K measured the same.)
 //
-// Scales sit in LDS as two dwords per row, k-tiles 2s + h in byte s of dword
-// h: a lane of half h reads its dword once per stage and the MFMA's byte
-// select (a constant, the step) picks the step's scale.  The page's E8M0
+// Scales sit in LDS as SKT / 4 dwords per row, k-tile 2s + h in byte s % 4
+// of dword h + 2 (s / 4): a lane of half h reads its dwords once per stage
+// and the MFMA's byte select (a constant) picks the step's scale.  The page's E8M0
 // conversion is applied when staging: min(e, 142), with the codes of rows
-// whose e <= 112 (and of tiles past K) staged as zeros.
+// whose e <= 112 (and of tiles past K) staged as zeros.  Which rows to zero
+// comes from one wave ballot: the lane that loads row r's scale byte of a
+// tile votes for it, and the lanes holding that tile's quant chunks read
+// their 16 rows' votes; when every row is kept (the common case) the whole
+// wave skips the masking.
 //
 // LDS is double-buffered and the global loads run two stages ahead in
 // registers, one barrier per stage.  The buffer descriptors advance by one
@@ -122,24 +129,31 @@ __global__ __launch_bounds__(QTHREADS) void k_quantize_mx(const void *__restrict
 // padded with a stage whose k-tiles all lie past K (zeroed, it adds exactly
 // 0; its loads are range-checked or land in zeroed rows).
 // ---------------------------------------------------------------------------
-constexpr int BM = 128, BN = 64, SKT = 8;
+#ifndef TQ_MX_SKT
+#define TQ_MX_SKT 8
+#endif
+constexpr int BM = 64, BN = 128, SKT = TQ_MX_SKT;
 constexpr int KSW = 2;                  // wave groups splitting a stage's steps
 constexpr int THREADS = 256 * KSW;
 constexpr int SPG = SKT / 2 / KSW;      // MFMA steps (64 K) per group and stage
 constexpr int A_ROW = 32 * SKT + 16;
 constexpr int TB = 544;                 // MXFP4 tile bytes: 512 quant + 32 E8M0
-constexpr int NT = 2 * SKT;             // tiles per stage (two stripes)
+constexpr int NSTR = BN / 32;           // weight stripes per workgroup
+constexpr int NT = NSTR * SKT;          // tiles per stage
 constexpr int NA = BM * SKT * 2 / THREADS;     // 16-byte activation chunks per thread
 constexpr int NS = BM * SKT / THREADS;         // activation scale bytes per thread
 constexpr int NB = NT * 32 / THREADS;          // 16-byte tile chunks per thread
 static_assert(NA * THREADS == BM * SKT * 2 && NS * THREADS == BM * SKT &&
-              NB * THREADS == NT * 32 && SPG * KSW * 2 == SKT && SKT == 8, "stage split");
+              NB * THREADS == NT * 32 && SPG * KSW * 2 == SKT && SKT % 8 == 0, "stage split");
+constexpr int SDW = SKT / 4;            // scale dwords per row
+constexpr int CPR = 2 * SKT;            // 16-byte chunks per staged activation row
 
 struct LdsMx {
     uint8_t A[2][BM * A_ROW];
     uint8_t B[2][NT * 512];             // tile (stripe c, k-tile j) at (c * SKT + j) * 512
-    uint32_t sa[2][BM][2];              // activation row: k-tile 2s + h in byte s of dword h
-    uint32_t sb[2][BN][2];              // weight row, converted, same arrangement
+    uint32_t sa[2][BM][SDW];            // activation row: k-tile 2s + h in byte s % 4 of
+                                        // dword h + 2 (s / 4)
+    uint32_t sb[2][BN][SDW];            // weight row, converted, same arrangement
 };
 
 // f(integral_constant<int, I>) for I = I0 .. N - 1: a loop whose index is a
@@ -154,7 +168,11 @@ __device__ __forceinline__ void static_for(F &&f)
 }
 
 // Byte of k-tile j in a row's two scale dwords.
-__device__ __forceinline__ int scale_byte(int j) { return 4 * (j & 1) + (j >> 1); }
+__device__ __forceinline__ int scale_byte(int j)
+{
+    const int s = j >> 1;
+    return 4 * ((j & 1) + 2 * (s >> 2)) + (s & 3);
+}
 
 struct RangesMx {
     __amdgpu_buffer_rsrc_t q, e, w;
@@ -163,24 +181,24 @@ struct RangesMx {
 struct StageMx {
     v4i a[NA];
     v4i b[NB];
-    v4i eb[NB];                         // the E8M0 bytes of the 16 rows of b
     uint32_t sa[NS];
     uint32_t sb[NB];
 };
 
 // Per-thread load offsets, relative to the stage's descriptors (thread tid
 // of 512):
-//   activation chunk ch = tid + 512 i (i < 4): row ch / 16, 16 bytes at 16 (ch % 16);
-//   activation scale byte g = tid + 512 i (i < 2) of the stage's 128 x 8:
-//     row g / 8, k-tile g % 8 (byte loads, each range-checked on its own;
-//     eight consecutive lanes read one row's eight bytes, so a wave's load
-//     touches 8 cache lines, not 64);
-//   tile chunk ch = tid: tile t = ch / 32 (stripe t / 8, k-tile t % 8), 16
-//     quant bytes at 16 (ch % 32) -- column pair (ch % 32) / 2, rows 16 (ch %
-//     2) .. + 15 -- with the E8M0 bytes of those 16 rows, and that tile's
-//     scale of row ch % 32.
+//   activation chunk ch = tid + 512 i (i < NA): row ch / CPR, 16 bytes at
+//     16 (ch % CPR);
+//   activation scale byte g = tid + 512 i (i < NS) of the stage's 64 x SKT:
+//     row g / SKT, k-tile g % SKT (byte loads, each range-checked on its
+//     own; consecutive lanes read one row's bytes, so a wave's load touches
+//     a few cache lines, not 64);
+//   tile chunk ch = tid + 512 i (i < NB): tile t = ch / 32 (stripe t / SKT,
+//     k-tile t % SKT), 16 quant bytes at 16 (ch % 32) -- column pair (ch % 32)
+//     / 2, rows 16 (ch % 2) .. + 15 -- and that tile's scale of row ch % 32
+//     (so the 32 lanes of a tile hold all its row scales).
 struct OffsMx {
-    int a[NA], sa[NS], b[NB], eb[NB], sb[NB];
+    int a[NA], sa[NS], b[NB], sb[NB];
 };
 
 __device__ __forceinline__ OffsMx make_offs_mx(int tid, int K, int nkt)
@@ -189,12 +207,12 @@ __device__ __forceinline__ OffsMx make_offs_mx(int tid, int K, int nkt)
 #pragma unroll
     for (int i = 0; i < NA; i++) {
         const int ch = tid + THREADS * i;
-        o.a[i] = (ch >> 4) * K + 16 * (ch & 15);
+        o.a[i] = (ch / CPR) * K + 16 * (ch % CPR);
     }
 #pragma unroll
     for (int i = 0; i < NS; i++) {
         const int g = tid + THREADS * i;
-        o.sa[i] = (g >> 3) * nkt + (g & 7);
+        o.sa[i] = (g / SKT) * nkt + g % SKT;
     }
 #pragma unroll
     for (int i = 0; i < NB; i++) {
@@ -202,7 +220,6 @@ __device__ __forceinline__ OffsMx make_offs_mx(int tid, int K, int nkt)
         const int t = ch >> 5;
         const int tile = ((t / SKT) * nkt + t % SKT) * TB;
         o.b[i] = tile + 16 * (ch & 31);
-        o.eb[i] = tile + 512 + 16 * (ch & 1);
         o.sb[i] = tile + 512 + (ch & 31);
     }
     return o;
@@ -233,17 +250,15 @@ __device__ __forceinline__ void load_stage(StageMx &s, const RangesMx &rg, const
 #pragma unroll
     for (int i = 0; i < NB; i++) {
         s.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rg.w, o.b[i], 0, BUF_NT);
-        s.eb[i] = __builtin_amdgcn_raw_buffer_load_b128(rg.w, o.eb[i], 0, 0);
         s.sb[i] = __builtin_amdgcn_raw_buffer_load_b8(rg.w, o.sb[i], 0, 0);
     }
 }
 
-// Per byte of x: 0xFF where the byte (an E8M0 e) is >= 113, else 0 (each
-// byte's low 7 bits plus 15 reach bit 7 without carrying into the next).
-__device__ __forceinline__ uint32_t keep_mask(uint32_t x)
+// Four keep bits (bit i: byte i) as a byte mask: 0xFF in byte i where bit i
+// is set (the product spreads bit i to bit 8i with no carries).
+__device__ __forceinline__ uint32_t spread4(uint32_t n)
 {
-    const uint32_t h = (x | ((x & 0x7F7F7F7Fu) + 0x0F0F0F0Fu)) & 0x80808080u;
-    return (h >> 7) * 0xFFu;
+    return ((n * 0x00204081u) & 0x01010101u) * 0xFFu;
 }
 
 __device__ __forceinline__ void store_stage(const StageMx &s, LdsMx &L, int buf, int tid,
@@ -252,35 +267,35 @@ __device__ __forceinline__ void store_stage(const StageMx &s, LdsMx &L, int buf,
 #pragma unroll
     for (int i = 0; i < NA; i++) {
         const int ch = tid + THREADS * i;
-        *(v4i *)(L.A[buf] + (ch >> 4) * A_ROW + 16 * (ch & 15)) = s.a[i];
+        *(v4i *)(L.A[buf] + (ch / CPR) * A_ROW + 16 * (ch % CPR)) = s.a[i];
     }
     // byte stores: no arithmetic on the loaded values, which the compiler
     // could hoist above the stage's MFMAs (and with it a wait for the loads)
 #pragma unroll
     for (int i = 0; i < NS; i++) {
         const int g = tid + THREADS * i;
-        ((uint8_t *)L.sa[buf])[(g >> 3) * 8 + scale_byte(g & 7)] = (uint8_t)s.sa[i];
+        ((uint8_t *)L.sa[buf])[(g / SKT) * SKT + scale_byte(g % SKT)] = (uint8_t)s.sa[i];
     }
 #pragma unroll
     for (int i = 0; i < NB; i++) {
         const int ch = tid + THREADS * i;
         const int t = ch >> 5, c = t / SKT, j = t % SKT;
         // codes of rows with e <= 112 (scale 0 on the page) and of tiles past
-        // K are staged as zeros
+        // K are staged as zeros: this lane votes for row ch % 32 of its tile,
+        // then takes the votes of its chunk's 16 rows
         v4i b = s.b[i];
-        const uint32_t k0 = keep_mask(s.eb[i].x), k1 = keep_mask(s.eb[i].y);
-        const uint32_t k2 = keep_mask(s.eb[i].z), k3 = keep_mask(s.eb[i].w);
-        if (kt0 + j >= nkt || (k0 & k1 & k2 & k3) != 0xFFFFFFFFu) {
-            const bool live = kt0 + j < nkt;
-            b.x &= live ? k0 : 0u;
-            b.y &= live ? k1 : 0u;
-            b.z &= live ? k2 : 0u;
-            b.w &= live ? k3 : 0u;
+        const uint32_t e = s.sb[i] & 0xFFu;
+        const uint64_t keep = __builtin_amdgcn_ballot_w64(e > 112u && kt0 + j < nkt);
+        if (keep != ~uint64_t(0)) {
+            const uint32_t k = (uint32_t)(keep >> (32 * ((tid >> 5) & 1) + 16 * (ch & 1)));
+            b.x &= spread4(k & 0xFu);
+            b.y &= spread4((k >> 4) & 0xFu);
+            b.z &= spread4((k >> 8) & 0xFu);
+            b.w &= spread4((k >> 12) & 0xFu);
         }
         *(v4i *)(L.B[buf] + t * 512 + 16 * (ch & 31)) = b;
         // the page's scale: 2^15 for e >= 142 (rows with e <= 112 are zero)
-        const uint32_t e = s.sb[i] & 0xFFu;
-        ((uint8_t *)L.sb[buf])[(32 * c + (ch & 31)) * 8 + scale_byte(j)] = (uint8_t)min(e, 142u);
+        ((uint8_t *)L.sb[buf])[(32 * c + (ch & 31)) * SKT + scale_byte(j)] = (uint8_t)min(e, 142u);
     }
 }
 
@@ -295,15 +310,16 @@ __global__ __launch_bounds__(THREADS) void k_qgemm_mx(const uint8_t *__restrict_
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = (tid >> 6) & 3, grp = tid >> 8;
+    const int wm = w & 1, wn = w >> 1;          // activation fragment, stripe pair
     const int li = lane & 31, lk = lane >> 5;
     const int64_t nct = (N + 31) / 32;
-    const int64_t ct0 = (int64_t)blockIdx.x * (BN / 32);
+    const int64_t ct0 = (int64_t)blockIdx.x * NSTR;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int64_t rows = min<int64_t>(M - m0, BM);
 
     const uint8_t *qw = q + m0 * K, *ew = e + m0 * nkt, *tw = tiles + ct0 * nkt * TB;
     const int64_t qb = rows * K, eb = rows * nkt;
-    const int64_t wb = min<int64_t>(nct - ct0, BN / 32) * nkt * TB;
+    const int64_t wb = min<int64_t>(nct - ct0, NSTR) * nkt * TB;
     const OffsMx o = make_offs_mx(tid, (int)K, (int)nkt);
 
     // B operand: lane 2i + p of 16-lane group G points at column pair 8r + i,
@@ -317,20 +333,25 @@ __global__ __launch_bounds__(THREADS) void k_qgemm_mx(const uint8_t *__restrict_
     // issued first, then the MFMAs.
     auto compute = [&](auto gr, int buf) {
         constexpr int GR = decltype(gr)::value;
-        const uint32_t sav = L.sa[buf][32 * w + li][lk];
-        const uint32_t sbv[2] = {L.sb[buf][li][lk], L.sb[buf][32 + li][lk]};
+        uint32_t sav[SDW / 2], sbv[2][SDW / 2];
+#pragma unroll
+        for (int d = 0; d < SDW / 2; d++) {
+            sav[d] = L.sa[buf][32 * wm + li][lk + 2 * d];
+            sbv[0][d] = L.sb[buf][64 * wn + li][lk + 2 * d];
+            sbv[1][d] = L.sb[buf][64 * wn + 32 + li][lk + 2 * d];
+        }
         v4i a[SPG][2];
         v2i b[SPG][2][2];
 #pragma unroll
         for (int i = 0; i < SPG; i++) {
             constexpr int s0 = GR * SPG;
             const int s = s0 + i;
-            const uint8_t *ar = L.A[buf] + (32 * w + li) * A_ROW + 64 * s + 16 * lk;
+            const uint8_t *ar = L.A[buf] + (32 * wm + li) * A_ROW + 64 * s + 16 * lk;
             a[i][0] = *(const v4i *)ar;
             a[i][1] = *(const v4i *)(ar + 32);
 #pragma unroll
             for (int c = 0; c < 2; c++) {
-                const uint8_t *bt = L.B[buf] + (c * SKT + 2 * s + lk) * 512 + boff;
+                const uint8_t *bt = L.B[buf] + ((2 * wn + c) * SKT + 2 * s + lk) * 512 + boff;
                 b[i][c][0] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                     (__attribute__((address_space(3))) v2i *)(bt));
                 b[i][c][1] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -346,8 +367,8 @@ __global__ __launch_bounds__(THREADS) void k_qgemm_mx(const uint8_t *__restrict_
                 const v2i b0 = b[i][c][0], b1 = b[i][c][1];
                 const v8i bv = {b0.x, b0.y, b1.x, b1.y, 0, 0, 0, 0};
                 // byte select = step: the scale of k-tile 2s + lk
-                acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[c], 0, 4, s,
-                                                                         (int)sav, s, (int)sbv[c]);
+                acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    av, bv, acc[c], 0, 4, s & 3, (int)sav[s >> 2], s & 3, (int)sbv[c][s >> 2]);
             }
         });
     };
@@ -399,14 +420,14 @@ __global__ __launch_bounds__(THREADS) void k_qgemm_mx(const uint8_t *__restrict_
         return;
 #pragma unroll
     for (int c = 0; c < 2; c++) {
-        const int64_t n = 32 * (ct0 + c) + li;
+        const int64_t n = 32 * (ct0 + 2 * wn + c) + li;
 #pragma unroll
         for (int r = 0; r < 16; r++)
             acc[c][r] += red[((w * 2 + c) * 16 + r) * 64 + lane];
         if (n < N) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int64_t m = m0 + 32 * w + 8 * (r >> 2) + 4 * lk + (r & 3);
+                const int64_t m = m0 + 32 * wm + 8 * (r >> 2) + 4 * lk + (r & 3);
                 if (m < M)
                     y[m * ldy + n] = acc[c][r];
             }
@@ -434,7 +455,7 @@ hipError_t launch_qgemm_mx(const void *tiles, int64_t K, int64_t N, const uint8_
                            const uint8_t *e, int64_t M, float *y, int64_t ldy, hipStream_t s)
 {
     const int64_t nkt = K / 32, nct = (N + 31) / 32;
-    dim3 grid((unsigned)((nct + 1) / 2), (unsigned)((M + BM - 1) / BM));
+    dim3 grid((unsigned)((nct + NSTR - 1) / NSTR), (unsigned)((M + BM - 1) / BM));
     k_qgemm_mx<<<grid, THREADS, 0, s>>>((const uint8_t *)tiles, nkt, N, q, e, M, K, y, ldy);
     return hipGetLastError();
 }
