@@ -526,6 +526,20 @@ def cpu_baseline(synth, w, seconds):
                       "1 thread"}
 
 
+def host_info():
+    """The host CPU the oracle baseline ran on: model name and usable threads."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()}
+
+
 def cpu_baseline_threads(synth, w, seconds):
     """The same oracle on every host core: each step's output rows split into
     one contiguous range per thread (the C calls release the GIL)."""
@@ -601,6 +615,7 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(synth, w, args.cpu_seconds)
         line["cpu_baseline_all_cores"] = cpu_baseline_threads(synth, w, args.cpu_seconds / 2)
+        line["host"] = host_info()
     print(json.dumps(line), flush=True)
 
 
