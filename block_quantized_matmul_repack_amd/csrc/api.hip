@@ -140,6 +140,8 @@ int tq_supported(int type, int64_t K, int64_t N, int64_t M, int path)
         return 0;
     if (path == TQ_PATH_GEMV || path == TQ_PATH_GEMV_FLAT)
         return M <= 8;
+    if (path == TQ_PATH_GEMM_MX)
+        return type == TQ_MXFP4;
     return path == TQ_PATH_GEMM || path == TQ_PATH_GEMM_FLAT;
 }
 

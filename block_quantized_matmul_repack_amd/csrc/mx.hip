@@ -167,7 +167,7 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-// Byte of k-tile j in a row's two scale dwords.
+// Byte of k-tile j in a row's scale dwords.
 __device__ __forceinline__ int scale_byte(int j)
 {
     const int s = j >> 1;

@@ -12,7 +12,7 @@ from ._lib import TiledqError, check, lib
 
 Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1, Q4_K = 0, 1, 2, 3, 4, 5
 F32, BF16, F16 = 0, 1, 2
-PATH_GEMV, PATH_GEMM, PATH_GEMV_FLAT, PATH_GEMM_FLAT = 0, 1, 2, 3
+PATH_GEMV, PATH_GEMM, PATH_GEMV_FLAT, PATH_GEMM_FLAT, PATH_GEMM_MX = 0, 1, 2, 3, 4
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 

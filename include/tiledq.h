@@ -106,7 +106,8 @@ typedef enum {
 /* Which kernel family tq_block_dots runs, and whether its weights are tiles
  * or flat GGML blocks. */
 typedef enum {
-    TQ_PATH_GEMV = 0, TQ_PATH_GEMM = 1, TQ_PATH_GEMV_FLAT = 2, TQ_PATH_GEMM_FLAT = 3
+    TQ_PATH_GEMV = 0, TQ_PATH_GEMM = 1, TQ_PATH_GEMV_FLAT = 2, TQ_PATH_GEMM_FLAT = 3,
+    TQ_PATH_GEMM_MX = 4    /* tq_qgemm_mx: MXFP4 tiles only */
 } tq_path;
 
 /* Bytes of one tile ("Block-32 Quantized Formats"): 576, 1088, 576, 544,
@@ -126,7 +127,8 @@ size_t tq_tiled_bytes(int type, int64_t K, int64_t N);
 size_t tq_flat_bytes(int type, int64_t K, int64_t N);
 
 /* 1 if (type, K, N, M) is supported by `path` (TQ_PATH_GEMV and
- * TQ_PATH_GEMV_FLAT need M <= 8; Q4_K needs K % 256 == 0), judged from
+ * TQ_PATH_GEMV_FLAT need M <= 8; Q4_K needs K % 256 == 0; TQ_PATH_GEMM_MX
+ * takes TQ_MXFP4 only), judged from
  * these static properties alone; 0 otherwise. */
 int tq_supported(int type, int64_t K, int64_t N, int64_t M, int path);
 

@@ -67,7 +67,9 @@ def test_supported_static_properties(L):
     assert L.tq_supported(0, 4096, 4096, 8, 2) == 1          # flat GEMV
     assert L.tq_supported(0, 4096, 4096, 9, 2) == 0
     assert L.tq_supported(5, 4096, 4096, 512, 3) == 1        # flat GEMM
-    assert L.tq_supported(0, 4096, 4096, 1, 4) == 0
+    assert L.tq_supported(0, 4096, 4096, 1, 4) == 0          # block-scaled path: MXFP4 only
+    assert L.tq_supported(3, 4096, 4096, 512, 4) == 1
+    assert L.tq_supported(3, 4001, 4096, 512, 4) == 0
     assert L.tq_supported(0, 4001, 4096, 1, 0) == 0
     assert L.tq_supported(0, 4096, 4096, 1, 5) == 0
 
