@@ -48,12 +48,12 @@ WRITE_SCALE = 1.0
 TRAFFIC = {
     "decode": {"fetch_kib": 8779.81, "write_kib": 112.00,
              "src": "55b2e5cfc488b70b6ac82f4971120ec01ad77bdf202d81f3923c58d573de87c7"},
-    "gemm": {"fetch_kib": 13369.53, "write_kib": 8192.00,
+    "gemm": {"fetch_kib": 13369.19, "write_kib": 8192.00,
            "src": "ffaf03ca0cef80b39ffa637f26ec8f0417089ad91034c7db7ac0b60c7b0c975b"},
-    "repack": {"fetch_kib": 16143.86, "write_kib": 32256.00,
+    "repack": {"fetch_kib": 16143.80, "write_kib": 32256.00,
              "src": "b079be5257f056c8da28b20e2af048e64ed280c21bc08e26b4d0bcc56e7546db"},
-    "mx": {"fetch_kib": 12871.01, "write_kib": 8192.00,
-         "src": "b3a202fe6dad40862634398f75f9c071091839e4933f34c28661ddeceab4e348"},
+    "mx": {"fetch_kib": 12871.13, "write_kib": 8192.00,
+         "src": "d4b645c2b57da643ad1ba425d29afc99901fa127d6fab68504982ab16ccefec4"},
 }
 KERNEL_SOURCES = {
     "decode": ("qgemv.hip", "tq_internal.h"),
