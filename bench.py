@@ -46,8 +46,8 @@ ROTATE_BYTES = 1 << 30         # defeat the 256 MB Infinity Cache
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "decode": {"fetch_kib": 8779.81, "write_kib": 112.00,
-             "src": "55b2e5cfc488b70b6ac82f4971120ec01ad77bdf202d81f3923c58d573de87c7"},
+    "decode": {"fetch_kib": 8780.29, "write_kib": 112.00,
+             "src": "d5eff561c61086e67558748f2403c0de00a2e0cee6b7c63c684ad82142b87e6a"},
     "gemm": {"fetch_kib": 13369.19, "write_kib": 8192.00,
            "src": "ffaf03ca0cef80b39ffa637f26ec8f0417089ad91034c7db7ac0b60c7b0c975b"},
     "repack": {"fetch_kib": 16143.80, "write_kib": 32256.00,

@@ -81,6 +81,12 @@ constexpr int ring_depth()
 #ifndef TQ_GEMV_MMA_MIN_M
 #define TQ_GEMV_MMA_MIN_M 2
 #endif
+// Activation batches (one 32-element block per quad of lanes) that the fused
+// kernels load together before quantizing them.
+#ifndef TQ_GEMV_XG
+#define TQ_GEMV_XG 4
+#endif
+
 template <int QT, int MM>
 constexpr bool use_mma()
 {
@@ -537,21 +543,33 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                         ds[b] = f16_bits_to_f32(db);
                 }
             };
-            float v[8];
-            xload(v, bq);
+            // XG batches in flight at once: with several rows the pass has
+            // M batches, and loading them one after another would put a
+            // cache round trip per batch in front of the weight stream
+            constexpr int XG = MM < TQ_GEMV_XG ? MM : TQ_GEMV_XG;
+            float v[XG][8];
+#pragma unroll
+            for (int g = 0; g < XG; g++)
+                xload(v[g], bq + g * QB);
 #pragma unroll
             for (int r = 0; r < D; r++)
                 load_stage(u[r], r);
-            xquant(v, bq);
-            for (int b = bq + QB; b < nblk; b += QB) {
-                xload(v, b);
-                xquant(v, b);
+#pragma unroll
+            for (int g = 0; g < XG; g++)
+                xquant(v[g], bq + g * QB);
+            for (int b = bq + XG * QB; b < nblk; b += XG * QB) {
+#pragma unroll
+                for (int g = 0; g < XG; g++)
+                    xload(v[g], b + g * QB);
+#pragma unroll
+                for (int g = 0; g < XG; g++)
+                    xquant(v[g], b + g * QB);
             }
         }
         __syncthreads();
 
-        auto process = [&](const Unit<QT> &un, int j) {
-            store_unit<QT>(un, my, min(2, pn - 2 * j) * (TS / 16), lane);
+        // the unit is already in this wave's LDS slice (the ring loop below)
+        auto process = [&](int j) {
             if constexpr (MMA) {
                 // the whole wave takes each tile of the unit: lane l holds
                 // output row n = l % 32 for activation rows 4 (l / 32) + r
@@ -632,16 +650,21 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
             }
         };
         // A ring of D unit buffers: buffer r holds the wave's units r, r + D,
-        // ...; after a buffer is used it is refilled with the unit D further
-        // on, so D units stay in flight.  Loads are never under a branch
-        // (past-the-end units are zero-size), which lets the compiler wait
-        // for exactly the oldest buffer.
+        // ...; once a buffer's unit is copied to LDS the buffer is refilled
+        // with the unit D further on, before that unit is computed, so D
+        // units stay in flight during the compute.  Loads are never under a
+        // branch (past-the-end units are zero-size), which lets the compiler
+        // wait for exactly the oldest buffer.
         for (int it = 0; it < count; it += D) {
 #pragma unroll
             for (int r = 0; r < D; r++) {
-                if (it + r < count)
-                    process(u[r], wave + (it + r) * NW);
+                const int j = wave + (it + r) * NW;
+                const bool live = it + r < count;
+                if (live)
+                    store_unit<QT>(u[r], my, min(2, pn - 2 * j) * (TS / 16), lane);
                 load_stage(u[r], it + r + D);
+                if (live)
+                    process(j);
             }
         }
     }
