@@ -105,7 +105,10 @@ def _out(name, q, N, out):
 
 # Zero-filled qgemv workspaces, one per (device, stream): every call leaves
 # its workspace zero-filled, so it is reused by later calls on the same stream
-# without clearing (calls on one stream never overlap).
+# without clearing (calls on one stream never overlap).  A HIP graph captured
+# on a stream keeps that stream's workspace: replaying it on another stream
+# while calls run on the capture stream would share the workspace, so replay
+# it on the capture stream or keep the two apart in time.
 _workspaces = {}
 
 
