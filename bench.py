@@ -48,8 +48,8 @@ WRITE_SCALE = 1.0
 TRAFFIC = {
     "decode": {"fetch_kib": 8780.29, "write_kib": 112.00,
              "src": "d5eff561c61086e67558748f2403c0de00a2e0cee6b7c63c684ad82142b87e6a"},
-    "gemm": {"fetch_kib": 13369.19, "write_kib": 8192.00,
-           "src": "ffaf03ca0cef80b39ffa637f26ec8f0417089ad91034c7db7ac0b60c7b0c975b"},
+    "gemm": {"fetch_kib": 13363.22, "write_kib": 8192.00,
+           "src": "e0e7e4bdde0ddb61a5de1580fb9d244770adc13212512c91ec1b37e3bcff0b74"},
     "repack": {"fetch_kib": 16143.80, "write_kib": 32256.00,
              "src": "b079be5257f056c8da28b20e2af048e64ed280c21bc08e26b4d0bcc56e7546db"},
     "mx": {"fetch_kib": 12871.13, "write_kib": 8192.00,

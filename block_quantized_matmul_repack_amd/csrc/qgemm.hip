@@ -1,11 +1,14 @@
 // Prefill matrix-matrix product over 32x32 tiles with int8 MFMA.
 //
-// A workgroup of 8 waves owns a BM x BN = 128 x 64 output block (128
-// activation rows x two 32-row weight stripes); wave (wm, wn) owns one
-// 32 x 32 sub-block.  The K loop advances KB = 4 k-blocks per step:
-//   - activations: 64 rows x 4 x 32 int8, natural K order, and their fp16
+// A workgroup of 16 waves in two groups of 8 owns a BM x BN = 128 x 64
+// output block (128 activation rows x two 32-row weight stripes); wave
+// (wm, wn) of each group owns one 32 x 32 sub-block, and the two groups
+// split each step's k-blocks (group 0 takes one, group 1 three) and add
+// their sums through LDS at the end.  The K loop advances KB = 4 k-blocks
+// per step, which group 0 stages:
+//   - activations: 128 rows x 4 x 32 int8, natural K order, and their fp16
 //     block scales go to LDS as loaded;
-//   - weights: each of the 8 waves takes one of the step's 8 tiles (2
+//   - weights: each of the group's 8 waves takes one of the step's 8 tiles (2
 //     stripes x 4 blocks) and reads it as dwords of 4 rows / 2 rows of a
 //     column pair ("Block-32 Quantized Formats"), transposes bytes in
 //     registers with v_perm_b32, decodes them to int8 (code - 8, table
@@ -39,15 +42,29 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
-// THREADS = the 8 waves that stage a step's data and own the 8 32 x 32
-// output sub-blocks; KSW groups of them split each step's KB k-blocks.
+// THREADS = a group of 8 waves that owns the 8 32 x 32 output sub-blocks;
+// KSW groups of them split each step's KB k-blocks.
 #ifndef TQ_GEMM_KSPLIT
 #define TQ_GEMM_KSPLIT 2
 #endif
 constexpr int BM = 128, BN = 64, KB = 4, THREADS = 512;
-constexpr int KSW = TQ_GEMM_KSPLIT, KBW = KB / KSW;   // wave groups, k-blocks per group
+constexpr int KSW = TQ_GEMM_KSPLIT;                    // wave groups
 constexpr int WG_THREADS = THREADS * KSW;
-static_assert(KB % KSW == 0 && KBW % 2 == 0, "k-blocks split evenly, in pairs");
+static_assert(KSW == 1 || KSW == 2, "one or two wave groups");
+// k-blocks of each step taken by wave group 0, which also stages the step's
+// data; the other group takes the rest.  Giving the staging group fewer
+// blocks evens out the groups' vector work between two barriers.  Q4_1's
+// min term works on pairs of blocks, so there each group takes two, as in
+// the block-dot output (no rescale to even out).
+#ifndef TQ_GEMM_KB0
+#define TQ_GEMM_KB0 1
+#endif
+template <int QT, bool DOTS>
+constexpr int kb_group0()
+{
+    return KSW == 1 ? KB : ((QT == TQ_Q4_1 || DOTS) ? KB / 2 : TQ_GEMM_KB0);
+}
+static_assert(TQ_GEMM_KB0 >= 0 && TQ_GEMM_KB0 <= KB, "group 0 takes 0 .. KB k-blocks");
 #ifndef TQ_GEMM_MIN_BLOCKS
 #define TQ_GEMM_MIN_BLOCKS 1      // workgroups per CU the register budget is sized for
 #endif
@@ -380,7 +397,7 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = (tid >> 6) & 7;
-    const int grp = tid / THREADS;       // wave group: k-blocks KBW * grp .. of each step
+    const int grp = tid / THREADS;       // wave group (0 stages the data)
     const int wm = wave & 3, wn = wave >> 2;
     const int li = lane & 31, lk = lane >> 5;
     const int64_t nct = (N + 31) / 32;
@@ -447,34 +464,39 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
                 acc[r] = fmaf((float)dot[r], sc[r], acc[r]);
         }
     };
-    // Per step a wave takes its group's KBW k-blocks, each MFMA pair followed
+    // Per step a wave takes its group's k-blocks, each MFMA pair followed
     // by its vector epilogue; the other waves of the SIMD (4 per SIMD) fill
     // the MFMA latency.  (Keeping two blocks' results live, to hide it within
     // the wave, does not fit the 128 registers a wave has at 4 per SIMD.)
-    auto compute = [&](int buf, int64_t step) {
+    auto compute = [&](int buf, int64_t step, auto group0) {
+        // this group's k-blocks J0 .. J1 - 1 of the step
+        constexpr int J0 = decltype(group0)::value ? 0 : kb_group0<QT, DOTS>();
+        constexpr int J1 = decltype(group0)::value ? kb_group0<QT, DOTS>() : KB;
+        if constexpr (J1 == J0)
+            return;
         const v4h ua = __builtin_bit_cast(v4h, L.da[buf][lk][32 * wm + li]);
         const uint64_t wv = L.dw[buf][lk][32 * wn + li];
-        const int kb0 = KBW * grp;
 #pragma unroll
-        for (int j = 0; j < KBW; j++) {
+        for (int j = J0; j < J1; j++) {
             v16i dot;
             v16f sc;
-            mfmas(buf, kb0 + j, ua, wv, dot, sc);
-            epilogue(step * KB + kb0 + j, dot, sc);
+            mfmas(buf, j, ua, wv, dot, sc);
+            epilogue(step * KB + j, dot, sc);
         }
         if constexpr (!DOTS) {
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (QT == TQ_Q4_1) {
                 // min term of the group's k-blocks, two per fp32 MFMA: lane
-                // (li, lk) holds k = lk, i.e. block kb0 + 2j + lk, with A = da
+                // (li, lk) holds k = lk, i.e. block J0 + 2j + lk, with A = da
                 // * asum of activation row li (exact in fp32) and B = the
                 // min of weight row li
                 const int ra = 32 * wm + li;
                 const uint64_t dav = L.da[buf][0][ra];
                 const uint64_t mwv = L.mw[buf][32 * wn + li];
+                static_assert((J1 - J0) % 2 == 0, "min term: pairs of k-blocks");
 #pragma unroll
-                for (int j = 0; j < KBW / 2; j++) {
-                    const int kb = kb0 + 2 * j + lk;
+                for (int j = 0; j < (J1 - J0) / 2; j++) {
+                    const int kb = J0 + 2 * j + lk;
                     const float a = f16_bits_to_f32((uint16_t)(dav >> (16 * kb))) *
                                     L.asum[buf][ra][kb];
                     const float b = f16_bits_to_f32((uint16_t)(mwv >> (16 * kb)));
@@ -505,14 +527,14 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
             // even step: buffer 0 is computed, r1 holds step+1, r0 is free
             if constexpr (ST)
                 load_step<QT, DOTS, FT>(r0, rg, o, (int)nkt, (int)(step + 2) * KB);
-            compute(0, step);
+            compute(0, step, stage);
             if constexpr (ST)
                 store_step<QT, DOTS, FT>(r1, L, 1, lut, tid);
             __syncthreads();
             // odd step: buffer 1 is computed, r0 holds step+2, r1 is free
             if constexpr (ST)
                 load_step<QT, DOTS, FT>(r1, rg, o, (int)nkt, (int)(step + 3) * KB);
-            compute(1, step + 1);
+            compute(1, step + 1, stage);
             if constexpr (ST)
                 store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
             __syncthreads();
