@@ -46,14 +46,14 @@ ROTATE_BYTES = 1 << 30         # defeat the 256 MB Infinity Cache
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "decode": {"fetch_kib": 8780.29, "write_kib": 112.00,
-             "src": "d5eff561c61086e67558748f2403c0de00a2e0cee6b7c63c684ad82142b87e6a"},
-    "gemm": {"fetch_kib": 13363.22, "write_kib": 8192.00,
-           "src": "e0e7e4bdde0ddb61a5de1580fb9d244770adc13212512c91ec1b37e3bcff0b74"},
-    "repack": {"fetch_kib": 16143.80, "write_kib": 32256.00,
-             "src": "b079be5257f056c8da28b20e2af048e64ed280c21bc08e26b4d0bcc56e7546db"},
-    "mx": {"fetch_kib": 12871.13, "write_kib": 8192.00,
-         "src": "d4b645c2b57da643ad1ba425d29afc99901fa127d6fab68504982ab16ccefec4"},
+    "decode": {"fetch_kib": 8780.30, "write_kib": 112.00,
+               "src": "f28b3502bb0bac475ab05dade4c40fafd8e3b87ee2dd2386e48056cda7eba5c1"},
+    "gemm": {"fetch_kib": 13363.18, "write_kib": 8192.00,
+             "src": "cf4e64f80418ffcf75536c463148f42c21f551048dbe477e30a9d190bff3956d"},
+    "repack": {"fetch_kib": 16143.90, "write_kib": 32256.00,
+               "src": "7f60c5b9af92b655461bb894d3e2454e839c4b6ff51fe0636c10b7976b2b5183"},
+    "mx": {"fetch_kib": 12871.09, "write_kib": 8192.00,
+           "src": "e0375ab973c733c2d3825ab444b6d9baf635ebe937af40029474141d9138b660"},
 }
 KERNEL_SOURCES = {
     "decode": ("qgemv.hip", "tq_internal.h"),

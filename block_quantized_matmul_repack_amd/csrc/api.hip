@@ -10,11 +10,15 @@
 
 namespace {
 
+// Shape limits.  With them every grid stays below 2^31 work-items per
+// dimension (a dispatch counts them in 32 bits): the decode and GEMM grids
+// run 16 and 32 work-items per weight row (N <= 2^27), activation
+// quantization 4 per 32-element block (M * K < 2^34).
 constexpr int64_t MAX_K = int64_t(1) << 20;
-constexpr int64_t MAX_N = int64_t(1) << 30;
+constexpr int64_t MAX_N = int64_t(1) << 27;
 constexpr int64_t MAX_M = int64_t(1) << 20;
 constexpr int64_t MAX_PROD = int64_t(1) << 40;
-constexpr int64_t MAX_MK = int64_t(1) << 36;
+constexpr int64_t MAX_MK = int64_t(1) << 34;
 
 bool valid_type(int t)
 {

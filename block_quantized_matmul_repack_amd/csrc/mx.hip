@@ -441,6 +441,8 @@ hipError_t launch_quantize_mx(int dtype, const void *x, int64_t M, int64_t K, in
                               uint8_t *q, uint8_t *e, hipStream_t s)
 {
     const int64_t nb = K / 32;
+    if (!grid_fits((M * nb + QBPW - 1) / QBPW, QTHREADS))
+        return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)((M * nb + QBPW - 1) / QBPW));
     switch (dtype) {
     case TQ_F32: k_quantize_mx<TQ_F32><<<grid, QTHREADS, 0, s>>>(x, M, nb, ldx, q, e); break;
@@ -455,6 +457,8 @@ hipError_t launch_qgemm_mx(const void *tiles, int64_t K, int64_t N, const uint8_
                            const uint8_t *e, int64_t M, float *y, int64_t ldy, hipStream_t s)
 {
     const int64_t nkt = K / 32, nct = (N + 31) / 32;
+    if (!grid_fits((nct + NSTR - 1) / NSTR, THREADS) || !grid_fits((M + BM - 1) / BM, 1))
+        return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)((nct + NSTR - 1) / NSTR), (unsigned)((M + BM - 1) / BM));
     k_qgemm_mx<<<grid, THREADS, 0, s>>>((const uint8_t *)tiles, nkt, N, q, e, M, K, y, ldy);
     return hipGetLastError();

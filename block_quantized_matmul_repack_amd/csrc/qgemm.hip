@@ -588,6 +588,9 @@ hipError_t launch_t(const void *w, int64_t K, int64_t N, const int8_t *q, const 
     // consecutive workgroup ids round-robin to the 8 XCDs, so when the x
     // extent is a multiple of 8 all activation blocks of one weight block run
     // on one XCD and each weight tile is fetched into a single L2.
+    if (!grid_fits((nct + BN / 32 - 1) / (BN / 32), WG_THREADS) ||
+        !grid_fits((M + BM - 1) / BM, 1))
+        return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)((nct + BN / 32 - 1) / (BN / 32)), (unsigned)((M + BM - 1) / BM));
     if (isum)
         k_qgemm<QT, true, FT><<<grid, WG_THREADS, 0, s>>>((const uint8_t *)w, nkt, N, q, d, M, K,

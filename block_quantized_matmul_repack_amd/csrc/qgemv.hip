@@ -741,6 +741,8 @@ hipError_t launch_k(const void *tiles, int64_t K, int64_t N, const Act &act, con
 {
     const int nkt = (int)(K / 32);
     const int64_t nct = (N + 31) / 32;
+    if (!grid_fits(nct * sp.S, NW * 64))
+        return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)(nct * sp.S));
     k_qgemv<QT, MM, NW, XT, DOTS><<<grid, NW * 64, 0, s>>>((const uint8_t *)tiles, nkt, N, act, K,
                                                            lut, y, ldy, isum, sp.chunk, sp.S,

@@ -219,6 +219,8 @@ hipError_t launch_m(const void *flat, int64_t K, int64_t N, const int8_t *q, con
 {
     const int64_t nb = K / 32;
     const int64_t total = N * (K / (QT == TQ_Q4_K ? 256 : 32)) * Fmt<QT>::block;
+    if (!grid_fits((N + ROWS - 1) / ROWS, WAVES * 64))
+        return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)((N + ROWS - 1) / ROWS));
     if (isum)
         k_qgemv_flat<QT, MM, true><<<grid, WAVES * 64, 0, s>>>(

@@ -40,6 +40,8 @@ hipError_t launch_quantize(int dtype, const void *x, int64_t M, int64_t K, int64
 {
     const int64_t nb = K / 32;
     const int64_t blocks = M * nb;
+    if (!grid_fits((blocks + BPW - 1) / BPW, THREADS))
+        return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)((blocks + BPW - 1) / BPW));
     switch (dtype) {
     case TQ_F32: k_quantize<TQ_F32><<<grid, THREADS, 0, s>>>(x, M, nb, ldx, q, d); break;

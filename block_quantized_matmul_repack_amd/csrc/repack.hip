@@ -197,6 +197,8 @@ hipError_t launch_repack(int type, const void *flat, int64_t K, int64_t N, void 
                          hipStream_t s)
 {
     const int64_t nb = K / 32;
+    if (!grid_fits((N + 31) / 32, THREADS))
+        return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)((N + 31) / 32), (unsigned)((nb + KT - 1) / KT));
     const uint8_t *f = (const uint8_t *)flat;
     uint8_t *t = (uint8_t *)tiles;

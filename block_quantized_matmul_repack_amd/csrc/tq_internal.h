@@ -259,6 +259,15 @@ __device__ __forceinline__ void q4k_scale_min(const uint32_t (&s3)[3], int j, ui
     }
 }
 
+// A dispatch counts work-items in 32 bits per grid dimension.  The shape
+// limits of the entry points keep every grid of the library below 2^31
+// work-items; each launcher still checks its grid (`blocks` workgroups of
+// `threads`) before converting it, and refuses an oversized one.
+inline bool grid_fits(int64_t blocks, int threads)
+{
+    return blocks >= 0 && blocks * threads < (int64_t(1) << 32);
+}
+
 // K-split of the decode GEMV: S workgroups per stripe (a power of two),
 // `chunk` k-tiles each; slots points into the caller's workspace when S > 1.
 struct Split {

@@ -75,8 +75,10 @@
  *   - The library is stateless; calls on different streams may run
  *     concurrently.  Outputs of concurrent calls must not overlap.
  *   - Shapes: 32 <= K <= 2^20 with K % 32 == 0 (Q4_K: K % 256 == 0);
- *     0 <= N <= 2^30;
- *     0 <= M <= 2^20; K*N and M*K each below 2^40.
+ *     0 <= N <= 2^27;
+ *     0 <= M <= 2^20; K*N below 2^40 and M*K below 2^34 (so that every
+ *     kernel's grid fits the 32-bit work-item count of a dispatch).
+ *     Shapes outside these limits return TQ_E_SHAPE.
  */
 #ifndef TILEDQ_H
 #define TILEDQ_H

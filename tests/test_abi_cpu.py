@@ -170,9 +170,27 @@ def test_matmul_dispatch_validation(L):
 
 def test_gemv_m_limit(L):
     assert L.tq_qgemv(0, A16, 64, 32, A16, A16, 9, NUL, A16, 32, NUL, 0, NUL) == 3
-    assert L.tq_qgemv(0, A16, 64, 32, A16, A16, 1, NUL, A16, 32, A16 if False else ctypes.c_void_p(0x10010), 4096, NUL) == 4
+    assert L.tq_qgemv(0, A16, 64, 32, A16, A16, 1, NUL, A16, 32, ctypes.c_void_p(0x10010), 4096, NUL) == 4
     assert L.tq_block_dots(0, A16, 64, 32, A16, 9, NUL, A16, 0, NUL) == 3
     assert L.tq_block_dots(0, A16, 64, 32, A16, 9, NUL, A16, 7, NUL) == 2
+
+
+def test_shape_limits(L):
+    """N <= 2^27 and M * K < 2^34 (every grid then fits a dispatch's 32-bit
+    work-item count): one past either limit is TQ_E_SHAPE before any launch."""
+    big_n = 2 ** 27 + 1
+    assert L.tq_supported(0, 32, 2 ** 27, 1, 0) == 1
+    assert L.tq_supported(0, 32, big_n, 1, 0) == 0
+    assert L.tq_supported(1, 32, big_n, 512, 1) == 0
+    assert L.tq_supported(0, 2 ** 20, 2 ** 20 - 32, 2 ** 14 - 1, 1) == 1
+    assert L.tq_supported(0, 2 ** 20, 2 ** 20 - 32, 2 ** 14, 1) == 0      # M * K = 2^34
+    assert L.tq_tiled_bytes(0, 32, big_n) == 0
+    assert L.tq_repack_tiles(0, A16, 32, big_n, A16, NUL) == 3
+    assert L.tq_qgemm(0, A16, 32, big_n, A16, A16, 1, NUL, A16, big_n, NUL) == 3
+    assert L.tq_qgemv(0, A16, 32, big_n, A16, A16, 1, NUL, A16, big_n, NUL, 0, NUL) == 3
+    assert L.tq_quantize_act(0, A16, 2 ** 14, 2 ** 20, 2 ** 20, A16, A16, NUL) == 3
+    assert L.tq_quantize_act_mx(0, A16, 2 ** 14, 2 ** 20, 2 ** 20, A16, A16, NUL) == 3
+    assert L.tq_qgemm_mx(A16, 32, big_n, A16, A16, 1, A16, big_n, NUL) == 3
 
 
 def test_binding_rejects_cpu_tensors():
