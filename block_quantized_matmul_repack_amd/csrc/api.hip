@@ -6,6 +6,8 @@
 // Precomputation via kernel_params").
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "tq_internal.h"
 
 namespace {
@@ -253,6 +255,27 @@ int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
         tq::launch_qgemm(kernel_type(type), tiles, K, N, q, d, M, pack_lut(type, lut), y, ldy, nullptr, stream));
 }
 
+// tq_matmul's choice for 9 <= M <= 16: two decode passes of up to 8 rows
+// (each streams all weight tiles) or the GEMM (one pass, but whole 128-row
+// blocks, and with few of them too little in flight to stream the weights
+// at full rate).  Costs measured on MI355X at K = 4096: a decode pass takes
+// ~4 us plus the tiles at ~5 TB/s (~6.5 TB/s past 128 MB); a GEMM round of
+// up to 256 output blocks (one per CU) takes ~25 us, in proportion to K.
+int tq_matmul_path(int type, int64_t K, int64_t N, int64_t M)
+{
+    if (!valid_type(type) || !valid_tkn(type, K, N) || !valid_mk(M, K))
+        return -1;
+    if (M <= 8)
+        return TQ_PATH_GEMV;
+    if (M > 16)
+        return TQ_PATH_GEMM;
+    const double bytes = (double)tq_tiled_bytes(type, K, N);
+    const double pass_us = 4.0 + bytes / (bytes > 128e6 ? 6.5e6 : 5.0e6);
+    const int64_t blocks = ((N + 63) / 64) * ((M + 127) / 128);
+    const double gemm_us = (double)((blocks + 255) / 256) * 25.0 * (double)K / 4096.0;
+    return 2.0 * pass_us <= gemm_us ? TQ_PATH_GEMV : TQ_PATH_GEMM;
+}
+
 int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
               const uint16_t *d, int64_t M, const int8_t *lut, float *y, int64_t ldy,
               void *workspace, size_t workspace_bytes, hipStream_t stream)
@@ -260,6 +283,23 @@ int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q
     if (M <= 8)
         return tq_qgemv(type, tiles, K, N, q, d, M, lut, y, ldy, workspace, workspace_bytes,
                         stream);
+    if (tq_matmul_path(type, K, N, M) == TQ_PATH_GEMV) {
+        // Two decode passes of up to 8 rows each; everything is validated
+        // before the first launch.
+        int st = check_matmul(type, tiles, K, N, q, d, M, lut, y, ldy, true);
+        if (st != TQ_OK || N == 0)
+            return st;
+        if (workspace && !aligned(workspace, 256))
+            return TQ_E_ALIGN;
+        const int64_t nkt = K / 32;
+        for (int64_t m0 = 0; m0 < M; m0 += 8) {
+            st = tq_qgemv(type, tiles, K, N, q + m0 * K, d + m0 * nkt, std::min<int64_t>(8, M - m0),
+                          lut, y + m0 * ldy, ldy, workspace, workspace_bytes, stream);
+            if (st != TQ_OK)
+                return st;
+        }
+        return TQ_OK;
+    }
     return tq_qgemm(type, tiles, K, N, q, d, M, lut, y, ldy, stream);
 }
 

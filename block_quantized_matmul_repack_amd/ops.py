@@ -163,13 +163,20 @@ def qgemm(qtype, tiles, K, N, q, d, lut=None, out=None):
     return out
 
 
+def matmul_path(qtype, K, N, M):
+    """The path matmul takes: PATH_GEMV or PATH_GEMM."""
+    return lib().tq_matmul_path(qtype, K, N, M)
+
+
 def matmul(qtype, tiles, K, N, q, d, lut=None, out=None):
-    """y [M, N] for any M: the library picks qgemv (M <= 8) or qgemm."""
+    """y [M, N] for any M: the library picks qgemv (M <= 8), two qgemv passes
+    (9 <= M <= 16 when estimated faster: matmul_path) or qgemm."""
     _need_cuda(tiles, q, d, out)
     out = _out("tq_matmul", q, N, out)
     M = q.shape[0]
     st = _stream(q)
-    need = lib().tq_qgemv_workspace_bytes(qtype, K, N, M) if M <= 8 else 0
+    gemv = lib().tq_matmul_path(qtype, K, N, M) == PATH_GEMV
+    need = lib().tq_qgemv_workspace_bytes(qtype, K, N, min(M, 8)) if gemv else 0
     ws = workspace(q.device, st.value, need) if need else None
     check(lib().tq_matmul(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut),
                           _ptr(out), out.stride(0), _ptr(ws), need, st), "tq_matmul")

@@ -166,6 +166,31 @@ def test_matmul_dispatch_validation(L):
     assert f(0, A16, 64, 32, A16, A16, 9, NUL, A16, 31, NUL, 0, NUL) == 3        # ldy < N
     assert f(0, A16, 64, 32, A16, NUL, 9, NUL, A16, 32, NUL, 0, NUL) == 1        # d NULL
     assert f(0, NUL, 64, 0, NUL, NUL, 9, NUL, NUL, 0, NUL, 0, NUL) == 0          # N == 0
+    # 9 <= M <= 16 on the two-pass GEMV path (K = 4096, N = 32): the whole
+    # call is checked before any launch
+    assert L.tq_matmul_path(0, 4096, 32, 12) == 0 and L.tq_matmul_path(2, 4096, 32, 16) == 0
+    assert f(0, A16, 4096, 32, A16, A16, 12, NUL, A16, 32, ctypes.c_void_p(0x10010), 4096,
+             NUL) == 4                                                            # workspace
+    assert f(0, A16, 4096, 32, A2, A16, 16, NUL, A16, 32, NUL, 0, NUL) == 4      # q
+    assert f(2, A16, 4096, 32, A16, A16, 12, NUL, A16, 32, NUL, 0, NUL) == 1     # IQ4_NL table
+    assert f(0, A16, 4096, 32, A16, A16, 16, NUL, A16, 31, NUL, 0, NUL) == 3     # ldy < N
+
+
+def test_matmul_path(L):
+    """tq_matmul's path: GEMV for M <= 8; for 9 <= M <= 16 two GEMV passes
+    where their estimated cost (4 us + tiles at 5 TB/s, 6.5 past 128 MB,
+    per pass) is below the GEMM's (25 us x K / 4096 per round of 256 blocks);
+    GEMM above 16 rows."""
+    G, M_ = 0, 1
+    assert L.tq_matmul_path(1, 4096, 4096, 8) == G
+    assert L.tq_matmul_path(0, 4096, 4096, 12) == G            # 9.4 MB: 2 x 5.9 < 25
+    assert L.tq_matmul_path(2, 4096, 14336, 16) == G           # 33 MB: 2 x 10.6 < 25
+    assert L.tq_matmul_path(1, 4096, 14336, 12) == M_          # Q8_0, 62 MB: 2 x 16.5 > 25
+    assert L.tq_matmul_path(1, 4096, 128001, 16) == G          # 557 MB: 2 x 90 < 8 rounds x 25
+    assert L.tq_matmul_path(0, 512, 100, 12) == M_             # tiny: 2 launches > one GEMM
+    assert L.tq_matmul_path(0, 4096, 4096, 17) == M_
+    assert L.tq_matmul_path(9, 4096, 4096, 12) == -1
+    assert L.tq_matmul_path(0, 4000 + 1, 4096, 12) == -1
 
 
 def test_gemv_m_limit(L):

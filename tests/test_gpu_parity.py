@@ -219,16 +219,30 @@ def test_qgemv_every_row_count(tq, qtype, M, K, N):
 
 
 @pytest.mark.parametrize("qtype", TYPES)
-@pytest.mark.parametrize("M", [1, 8, 9, 40])
-def test_matmul_dispatch(tq, qtype, M):
-    """tq_matmul is bitwise the GEMV for M <= 8 and the GEMM above."""
-    K, N = 512, 100
-    inp = make(qtype, K, N, M, seed=M + 3)
+@pytest.mark.parametrize("M", [1, 8, 9, 13, 16, 17, 40])
+@pytest.mark.parametrize("K,N", [(512, 100), (4096, 300)])
+def test_matmul_dispatch(tq, qtype, M, K, N):
+    """tq_matmul is bitwise the GEMV for M <= 8, two GEMV passes (rows 0..7,
+    8..M-1) where matmul_path picks the GEMV for 9 <= M <= 16 (here at
+    K = 4096, N = 300; the GEMM at K = 512, N = 100) and the GEMM otherwise;
+    each within the tolerance of the oracle."""
+    inp = make(qtype, K, N, M, seed=M + 3 + K)
     tiles, tdev = _dev(inp, qtype, K, N)
+    q, d = oracle.quantize_act(inp.x)
     qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
     y = tq.matmul(qtype, tdev, K, N, qd, dd, lut=LUT)
-    ref = (tq.qgemv if M <= 8 else tq.qgemm)(qtype, tdev, K, N, qd, dd, lut=LUT)
+    path = tq.matmul_path(qtype, K, N, M)
+    assert path == (tq.PATH_GEMV if M <= 8 or (M <= 16 and K == 4096) else tq.PATH_GEMM)
+    if M <= 8:
+        ref = tq.qgemv(qtype, tdev, K, N, qd, dd, lut=LUT)
+    elif path == tq.PATH_GEMV:
+        ref = torch.cat([tq.qgemv(qtype, tdev, K, N, qd[:8], dd[:8], lut=LUT),
+                         tq.qgemv(qtype, tdev, K, N, qd[8:], dd[8:], lut=LUT)])
+    else:
+        ref = tq.qgemm(qtype, tdev, K, N, qd, dd, lut=LUT)
     assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
+    y_ref, acond = oracle.matmul(qtype, tiles, K, N, q, d, LUT)
+    check_y(y.cpu().numpy(), y_ref, acond, (qtype, M, K, N))
 
 
 def test_qgemv_workspace_reused_across_shapes(tq):
