@@ -255,7 +255,7 @@ int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
         tq::launch_qgemm(kernel_type(type), tiles, K, N, q, d, M, pack_lut(type, lut), y, ldy, nullptr, stream));
 }
 
-// tq_matmul's choice for 9 <= M <= 16: two decode passes of up to 8 rows
+// tq_matmul's choice for M > 8: ceil(M / 8) decode passes of up to 8 rows
 // (each streams all weight tiles) or the GEMM (one pass, but whole 128-row
 // blocks, and with few of them too little in flight to stream the weights
 // at full rate).  Costs measured on MI355X at K = 4096: a decode pass takes
@@ -267,13 +267,13 @@ int tq_matmul_path(int type, int64_t K, int64_t N, int64_t M)
         return -1;
     if (M <= 8)
         return TQ_PATH_GEMV;
-    if (M > 16)
+    if (M > 64)
         return TQ_PATH_GEMM;
     const double bytes = (double)tq_tiled_bytes(type, K, N);
     const double pass_us = 4.0 + bytes / (bytes > 128e6 ? 6.5e6 : 5.0e6);
     const int64_t blocks = ((N + 63) / 64) * ((M + 127) / 128);
     const double gemm_us = (double)((blocks + 255) / 256) * 25.0 * (double)K / 4096.0;
-    return 2.0 * pass_us <= gemm_us ? TQ_PATH_GEMV : TQ_PATH_GEMM;
+    return (double)((M + 7) / 8) * pass_us <= gemm_us ? TQ_PATH_GEMV : TQ_PATH_GEMM;
 }
 
 int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
@@ -284,8 +284,8 @@ int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q
         return tq_qgemv(type, tiles, K, N, q, d, M, lut, y, ldy, workspace, workspace_bytes,
                         stream);
     if (tq_matmul_path(type, K, N, M) == TQ_PATH_GEMV) {
-        // Two decode passes of up to 8 rows each; everything is validated
-        // before the first launch.
+        // Decode passes of up to 8 rows each; everything is validated before
+        // the first launch.
         int st = check_matmul(type, tiles, K, N, q, d, M, lut, y, ldy, true);
         if (st != TQ_OK || N == 0)
             return st;

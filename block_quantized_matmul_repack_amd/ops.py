@@ -169,8 +169,8 @@ def matmul_path(qtype, K, N, M):
 
 
 def matmul(qtype, tiles, K, N, q, d, lut=None, out=None):
-    """y [M, N] for any M: the library picks qgemv (M <= 8), two qgemv passes
-    (9 <= M <= 16 when estimated faster: matmul_path) or qgemm."""
+    """y [M, N] for any M: the library picks qgemv (M <= 8), one qgemv pass
+    per 8 rows (up to 64 rows, where estimated faster: matmul_path) or qgemm."""
     _need_cuda(tiles, q, d, out)
     out = _out("tq_matmul", q, N, out)
     M = q.shape[0]

@@ -210,17 +210,17 @@ int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N,
              const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
 
 /* The path tq_matmul takes for (type, K, N, M): TQ_PATH_GEMV for M <= 8
- * and, for 9 <= M <= 16, when two decode passes (rows 0..7, then 8..M-1,
- * each streaming all tiles) are estimated faster than the GEMM, whose
- * whole 128-row blocks are few at such M; else TQ_PATH_GEMM (-1: invalid
- * arguments).  The estimate uses costs measured on MI355X: a decode pass
- * ~4 us plus the tiles at ~5 TB/s (~6.5 TB/s past 128 MB), a GEMM round of
- * up to 256 128x64 output blocks ~25 us x K / 4096.  Static properties
- * only. */
+ * and, for 9 <= M <= 64, when ceil(M / 8) decode passes (rows 0..7, 8..15,
+ * ..., each streaming all tiles) are estimated no slower than the GEMM,
+ * whose whole 128-row blocks are few at such M; else TQ_PATH_GEMM (-1:
+ * invalid arguments).  The estimate uses costs measured on MI355X: a decode
+ * pass ~4 us plus the tiles at ~5 TB/s (~6.5 TB/s past 128 MB), a GEMM
+ * round of up to 256 128x64 output blocks ~25 us x K / 4096.  Static
+ * properties only. */
 int tq_matmul_path(int type, int64_t K, int64_t N, int64_t M);
 
 /* The product for any M, on the path tq_matmul_path() names: tq_qgemv
- * (with the workspace; for 9 <= M <= 16 two passes, the same workspace,
+ * (with the workspace; for M > 8 one pass per 8 rows, the same workspace,
  * sized by tq_qgemv_workspace_bytes(type, K, N, 8)) or tq_qgemm.  Arguments
  * as tq_qgemv, except that M >= 0 is unbounded (TQ_E_SHAPE only for the
  * limits of the calling convention). */

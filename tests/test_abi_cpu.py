@@ -177,10 +177,10 @@ def test_matmul_dispatch_validation(L):
 
 
 def test_matmul_path(L):
-    """tq_matmul's path: GEMV for M <= 8; for 9 <= M <= 16 two GEMV passes
-    where their estimated cost (4 us + tiles at 5 TB/s, 6.5 past 128 MB,
-    per pass) is below the GEMM's (25 us x K / 4096 per round of 256 blocks);
-    GEMM above 16 rows."""
+    """tq_matmul's path: GEMV for M <= 8; for 9 <= M <= 64 one GEMV pass per
+    8 rows where their estimated cost (4 us + tiles at 5 TB/s, 6.5 past
+    128 MB, per pass) is at most the GEMM's (25 us x K / 4096 per round of
+    256 blocks); GEMM above 64 rows."""
     G, M_ = 0, 1
     assert L.tq_matmul_path(1, 4096, 4096, 8) == G
     assert L.tq_matmul_path(0, 4096, 4096, 12) == G            # 9.4 MB: 2 x 5.9 < 25
@@ -188,7 +188,14 @@ def test_matmul_path(L):
     assert L.tq_matmul_path(1, 4096, 14336, 12) == M_          # Q8_0, 62 MB: 2 x 16.5 > 25
     assert L.tq_matmul_path(1, 4096, 128001, 16) == G          # 557 MB: 2 x 90 < 8 rounds x 25
     assert L.tq_matmul_path(0, 512, 100, 12) == M_             # tiny: 2 launches > one GEMM
-    assert L.tq_matmul_path(0, 4096, 4096, 17) == M_
+    assert L.tq_matmul_path(0, 4096, 4096, 24) == G            # 3 x 5.9 < 25
+    assert L.tq_matmul_path(0, 4096, 4096, 32) == G            # 4 x 5.9 < 25
+    assert L.tq_matmul_path(0, 4096, 4096, 33) == M_           # 5 x 5.9 > 25
+    assert L.tq_matmul_path(0, 4096, 14336, 17) == M_          # 3 x 10.6 > 25
+    assert L.tq_matmul_path(0, 4096, 300, 48) == G             # 6 x 4.15 < 25
+    assert L.tq_matmul_path(0, 4096, 300, 49) == M_            # 7 x 4.15 > 25
+    assert L.tq_matmul_path(0, 8192, 32, 64) == G              # 8 x 4.03 < 50 (K = 8192)
+    assert L.tq_matmul_path(0, 8192, 32, 65) == M_             # past 64 rows: always the GEMM
     assert L.tq_matmul_path(9, 4096, 4096, 12) == -1
     assert L.tq_matmul_path(0, 4000 + 1, 4096, 12) == -1
 

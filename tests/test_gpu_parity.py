@@ -219,12 +219,12 @@ def test_qgemv_every_row_count(tq, qtype, M, K, N):
 
 
 @pytest.mark.parametrize("qtype", TYPES)
-@pytest.mark.parametrize("M", [1, 8, 9, 13, 16, 17, 40])
+@pytest.mark.parametrize("M", [1, 8, 9, 13, 16, 17, 40, 49])
 @pytest.mark.parametrize("K,N", [(512, 100), (4096, 300)])
 def test_matmul_dispatch(tq, qtype, M, K, N):
-    """tq_matmul is bitwise the GEMV for M <= 8, two GEMV passes (rows 0..7,
-    8..M-1) where matmul_path picks the GEMV for 9 <= M <= 16 (here at
-    K = 4096, N = 300; the GEMM at K = 512, N = 100) and the GEMM otherwise;
+    """tq_matmul is bitwise the GEMV for M <= 8, one GEMV pass per 8 rows
+    where matmul_path picks the GEMV for larger M (here at K = 4096, N = 300
+    up to 48 rows; the GEMM at K = 512, N = 100) and the GEMM otherwise;
     each within the tolerance of the oracle."""
     inp = make(qtype, K, N, M, seed=M + 3 + K)
     tiles, tdev = _dev(inp, qtype, K, N)
@@ -232,12 +232,10 @@ def test_matmul_dispatch(tq, qtype, M, K, N):
     qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
     y = tq.matmul(qtype, tdev, K, N, qd, dd, lut=LUT)
     path = tq.matmul_path(qtype, K, N, M)
-    assert path == (tq.PATH_GEMV if M <= 8 or (M <= 16 and K == 4096) else tq.PATH_GEMM)
-    if M <= 8:
-        ref = tq.qgemv(qtype, tdev, K, N, qd, dd, lut=LUT)
-    elif path == tq.PATH_GEMV:
-        ref = torch.cat([tq.qgemv(qtype, tdev, K, N, qd[:8], dd[:8], lut=LUT),
-                         tq.qgemv(qtype, tdev, K, N, qd[8:], dd[8:], lut=LUT)])
+    assert path == (tq.PATH_GEMV if M <= 8 or (M <= 48 and K == 4096) else tq.PATH_GEMM)
+    if path == tq.PATH_GEMV:
+        ref = torch.cat([tq.qgemv(qtype, tdev, K, N, qd[i:i + 8], dd[i:i + 8], lut=LUT)
+                         for i in range(0, M, 8)])
     else:
         ref = tq.qgemm(qtype, tdev, K, N, qd, dd, lut=LUT)
     assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
