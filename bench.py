@@ -465,6 +465,31 @@ def measure_others(torch, tq, synth):
             res[f"unpack {name.rsplit('_m', 1)[0]}"] = {
                 "kernel_us": round(uu, 3), "GB_s": round((fb + w.weight_bytes) / uu / 1e3, 1)}
         del flats, tiles
+    # small-M products through tq_matmul (one decode pass per 8 rows where
+    # estimated no slower) beside the GEMM on the same tiles
+    w = synth.WORKLOADS["q8_0_gemv_k4096_n4096_m1"]
+    for qtype in (synth.Q4_0, synth.IQ4_NL):
+        wq = synth.Workload("small_m", qtype, w.K, w.N, 1, "uniform")
+        inp = synth.make_inputs(wq)
+        flat = torch.from_numpy(inp.flat).cuda()
+        R = max(2, -(-ROTATE_BYTES // wq.weight_bytes))
+        tiles = [tq.repack_tiles(qtype, flat, w.K, w.N) for _ in range(R)]
+        del flat
+        for M in (16, 32):
+            rng = np.random.default_rng(M)
+            x = torch.from_numpy(rng.standard_normal((M, w.K), dtype=np.float32)).cuda()
+            q, d = tq.quantize_act(x)
+            y = torch.empty((M, w.N), dtype=torch.float32, device="cuda")
+            fm = lambda i: tq.matmul(qtype, tiles[i % R], w.K, w.N, q, d, lut=inp.lut, out=y)
+            fg = lambda i: tq.qgemm(qtype, tiles[i % R], w.K, w.N, q, d, lut=inp.lut, out=y)
+            for i in range(3):
+                fm(i)
+                fg(i)
+            um, ug = kernel_us(torch, fm, 30), kernel_us(torch, fg, 30)
+            path = "decode passes" if tq.matmul_path(qtype, w.K, w.N, M) == tq.PATH_GEMV else "qgemm"
+            res[f"{synth.TYPE_NAMES[qtype]}_matmul_k4096_n4096_m{M}"] = {
+                "matmul_us": round(um, 3), "path": path, "qgemm_us": round(ug, 3)}
+        del tiles
     return res
 
 
