@@ -194,9 +194,9 @@ int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N,
  *   other arguments as tq_qgemv.
  * Every workgroup reads and quantizes its K range of all M rows, i.e. the
  * activations are read N / 32 times: the fused launch pays off for small
- * products (one launch saved, e.g. M = 1, K = N = 4096), while for large N
- * or M > 2 (a vocabulary head, several rows) tq_quantize_act followed by
- * tq_qgemv is faster. */
+ * products (one launch saved, e.g. M = 1, K = N = 4096; level at M = 4),
+ * while for large N or M >= 8 (a vocabulary head, several rows)
+ * tq_quantize_act followed by tq_qgemv is faster. */
 int tq_qgemv_x(int type, const void *tiles, int64_t K, int64_t N,
                int dtype, const void *x, int64_t ldx, int64_t M,
                const int8_t *lut, float *y, int64_t ldy,
