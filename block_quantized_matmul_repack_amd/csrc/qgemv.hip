@@ -571,24 +571,32 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
         // the unit is already in this wave's LDS slice (the ring loop below)
         auto process = [&](int j) {
             if constexpr (MMA) {
-                // the whole wave takes each tile of the unit: lane l holds
-                // output row n = l % 32 for activation rows 4 (l / 32) + r
+                // the whole wave takes both tiles of the unit: lane l holds
+                // output row n = l % 32 for activation rows 4 (l / 32) + r.
+                // Both tiles' operands are read and both MFMAs issued before
+                // either result is used, so the second tile's reads overlap
+                // the first MFMA.
+                v16i_t dot[2];
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    const int tp = min(2 * j + t, pn - 1);
+                    const v4i_t b = tile_operand<QT>(my + t * TS, tro, lut);
+                    const int8_t *ap = l < MM ? qs + (tp * MM + l) * 32 + 16 * half
+                                              : (const int8_t *)zero16;
+                    const v4i_t a = *(const v4i_t *)ap;
+                    dot[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, v16i_t{}, 0, 0, 0);
+                }
+                // Only dot[t][0..3] are used, but each MFMA writes all 16
+                // registers.  Reading them all here keeps the compiler from
+                // handing the unused ones to other values before the MFMAs
+                // have finished writing them (a variant without this gave
+                // wrong sums at M = 8).
+                asm volatile("" ::"v"(dot[0]), "v"(dot[1]));
 #pragma unroll
                 for (int t = 0; t < 2; t++) {
                     const int tp = min(2 * j + t, pn - 1);
                     const bool valid = 2 * j + t < pn;
                     const uint8_t *tile = my + t * TS;
-                    const v4i_t b = tile_operand<QT>(tile, tro, lut);
-                    const int8_t *ap = l < MM ? qs + (tp * MM + l) * 32 + 16 * half
-                                              : (const int8_t *)zero16;
-                    const v4i_t a = *(const v4i_t *)ap;
-                    const v16i_t dot = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, v16i_t{}, 0, 0, 0);
-                    // Only dot[0..3] are used, but the MFMA writes all 16
-                    // registers.  Reading them all here keeps the compiler
-                    // from handing the unused ones to other values before the
-                    // MFMA has finished writing them (a variant without this
-                    // gave wrong sums at M = 8).
-                    asm volatile("" ::"v"(dot));
                     if constexpr (DOTS) {
                         const int64_t n = 32 * ct + l;
 #pragma unroll
@@ -596,7 +604,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                             const int m = 4 * half + r;
                             if (valid && m < MM && n < N)
                                 isum[((int64_t)m * N + n) * nb + kt0 + pb + tp] =
-                                    (QT == TQ_Q4_0) ? (dot[r] >> 4) : dot[r];
+                                    (QT == TQ_Q4_0) ? (dot[t][r] >> 4) : dot[t][r];
                         }
                     } else {
                         float dw = f16_bits_to_f32(tile_scale_bits<QT>(tile, l)) *
@@ -610,7 +618,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                             const int m = 4 * half + r;
                             const int mi = tp * MM + min(m, MM - 1);
                             const float da = m < MM ? ds[mi] : 0.0f;
-                            acc[r] = fmaf((float)dot[r], dw * da, acc[r]);
+                            acc[r] = fmaf((float)dot[t][r], dw * da, acc[r]);
                             if constexpr (QT == TQ_Q4_1)
                                 acc[r] = fmaf(mw, da * ss[mi], acc[r]);   // the min
                         }
