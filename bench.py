@@ -46,8 +46,8 @@ ROTATE_BYTES = 1 << 30         # defeat the 256 MB Infinity Cache
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "decode": {"fetch_kib": 8780.30, "write_kib": 112.00,
-               "src": "c02c619dcc780a9dfa49419fdb635a61d482afbc826f88fe6e7072905d8c9980"},
+    "decode": {"fetch_kib": 8780.32, "write_kib": 112.00,
+               "src": "2beef0cbad9cd442180bffefa0041c71debc773f13101dc1652c52ec158bfbb4"},
     "gemm": {"fetch_kib": 13363.18, "write_kib": 8192.00,
              "src": "cf4e64f80418ffcf75536c463148f42c21f551048dbe477e30a9d190bff3956d"},
     "repack": {"fetch_kib": 16143.90, "write_kib": 32256.00,

@@ -74,23 +74,28 @@ constexpr int ring_depth()
     return QT == TQ_Q8_0 ? TQ_GEMV_DEPTH_Q8 : TQ_GEMV_DEPTH_Q4;
 }
 
-// 4-bit tiles with at least this many activation rows go through the int8
-// matrix cores (one v_mfma_i32_32x32x32_i8 per tile, rows past M zero)
-// instead of v_dot4; fewer rows stay on v_dot4, where the matrix core would
-// mostly multiply zeros.
-#ifndef TQ_GEMV_MMA_MIN_M
-#define TQ_GEMV_MMA_MIN_M 2
-#endif
 // Activation batches (one 32-element block per quad of lanes) that the fused
 // kernels load together before quantizing them.
 #ifndef TQ_GEMV_XG
 #define TQ_GEMV_XG 4
 #endif
 
+// Tiles with at least this many activation rows go through the int8 matrix
+// cores (one v_mfma_i32_32x32x32_i8 per tile, rows past M zero) instead of
+// v_dot4; fewer rows stay on v_dot4, where the matrix core would mostly
+// multiply zeros.  Q8_0's v_dot4 path needs no nibble decode and stays
+// ahead up to 4 rows (measured level at M = 4, the matrix cores 14-20 %
+// faster at M = 8).
+#ifndef TQ_GEMV_MMA_MIN_M
+#define TQ_GEMV_MMA_MIN_M 2
+#endif
+#ifndef TQ_GEMV_MMA_MIN_M_Q8
+#define TQ_GEMV_MMA_MIN_M_Q8 5
+#endif
 template <int QT, int MM>
 constexpr bool use_mma()
 {
-    return QT != TQ_Q8_0 && MM >= TQ_GEMV_MMA_MIN_M;
+    return MM >= (QT == TQ_Q8_0 ? TQ_GEMV_MMA_MIN_M_Q8 : TQ_GEMV_MMA_MIN_M);
 }
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
@@ -135,6 +140,24 @@ __device__ __forceinline__ v4i_t tile_operand(const uint8_t *tile, int off, cons
         }
     }
     return v4i_t{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
+}
+
+// The same operand for a staged Q8_0 tile, whose byte cp * 64 + 2 r + e is
+// element 2 cp + e of row r: lane l (row r = l % 32, K0 = 16 (l / 32)) reads
+// the dwords holding column pairs 8 (l / 32) .. + 7 of its row pair and keeps
+// its row's halfword of each, K0 + 0 .. 15 in natural order (the staged Q8_0
+// activations are in natural order too).
+__device__ __forceinline__ v4i_t tile_operand_q8(const uint8_t *tile, int lane)
+{
+    const int r = lane & 31, cp0 = 8 * (lane >> 5);
+    const uint32_t *t = (const uint32_t *)tile + (r >> 1);
+    const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        w[i] = t[(cp0 + i) * 16];
+    return v4i_t{(int)__builtin_amdgcn_perm(w[1], w[0], sel), (int)__builtin_amdgcn_perm(w[3], w[2], sel),
+                 (int)__builtin_amdgcn_perm(w[5], w[4], sel), (int)__builtin_amdgcn_perm(w[7], w[6], sel)};
 }
 
 template <int QT>
@@ -580,7 +603,11 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
 #pragma unroll
                 for (int t = 0; t < 2; t++) {
                     const int tp = min(2 * j + t, pn - 1);
-                    const v4i_t b = tile_operand<QT>(my + t * TS, tro, lut);
+                    v4i_t b;
+                    if constexpr (QT == TQ_Q8_0)
+                        b = tile_operand_q8(my + t * TS, lane);
+                    else
+                        b = tile_operand<QT>(my + t * TS, tro, lut);
                     const int8_t *ap = l < MM ? qs + (tp * MM + l) * 32 + 16 * half
                                               : (const int8_t *)zero16;
                     const v4i_t a = *(const v4i_t *)ap;
