@@ -33,6 +33,46 @@ def _need_cuda(*ts):
             raise TiledqError("tiledq expects contiguous tensors")
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _need_bytes(name, what, t, nbytes):
+    if t is not None and _nbytes(t) < nbytes:
+        raise TiledqError(f"{name}: {what} holds {_nbytes(t)} bytes, needs {nbytes}")
+
+
+def _check_weights(name, qtype, w, K, N, flat=False):
+    """The weight buffer covers the tiles (or flat blocks) of (qtype, K, N)."""
+    nbytes = (lib().tq_flat_bytes if flat else lib().tq_tiled_bytes)(qtype, K, N)
+    if nbytes == 0 and N > 0:
+        raise TiledqError(f"{name}: type {qtype} with K={K}, N={N} is not a valid shape")
+    _need_bytes(name, "flat" if flat else "tiles", w, nbytes)
+
+
+def _check_act(name, q, d, K):
+    """q is int8 [M, K] and d fp16 with M * K/32 elements; returns M."""
+    if q.dim() != 2 or q.dtype != torch.int8 or q.shape[1] != K:
+        raise TiledqError(f"{name}: q must be int8 [M, K={K}], got {q.dtype} {tuple(q.shape)}")
+    M = q.shape[0]
+    if d is not None:
+        if d.dtype != torch.float16:
+            raise TiledqError(f"{name}: d must be float16, got {d.dtype}")
+        if d.numel() < M * (K // 32):
+            raise TiledqError(f"{name}: d holds {d.numel()} scales, needs {M * (K // 32)}")
+    return M
+
+
+def _check_out(name, out, M, N):
+    """out is fp32 with unit column stride, at least M rows and N columns."""
+    if out is None:
+        return
+    if out.dim() != 2 or out.dtype != torch.float32 or out.stride(1) != 1 or \
+            out.shape[0] < M or out.shape[1] < N:
+        raise TiledqError(f"{name}: out must be float32 [>={M}, >={N}] with unit column "
+                          f"stride, got {out.dtype} {tuple(out.shape)}")
+
+
 def _lut_arg(lut):
     if lut is None:
         return None
@@ -64,13 +104,12 @@ def supported(qtype, K, N, M, path=PATH_GEMV):
 
 def repack_tiles(qtype, flat, K, N, out=None):
     """Flat GGML blocks (uint8 GPU tensor) -> tiles (uint8 GPU tensor)."""
-    _need_cuda(flat, out)
     nbytes = tiled_bytes(qtype, K, N)
+    _check_weights("repack_tiles", qtype, flat, K, N, flat=True)
+    _need_bytes("repack_tiles", "out", out, nbytes)
+    _need_cuda(flat, out)
     if out is None:
         out = torch.empty(nbytes, dtype=torch.uint8, device=flat.device)
-    if flat.numel() * flat.element_size() < flat_bytes(qtype, K, N) or \
-            out.numel() * out.element_size() < nbytes:
-        raise TiledqError("repack_tiles: buffer too small")
     check(lib().tq_repack_tiles(qtype, _ptr(flat), K, N, _ptr(out), _stream(flat)),
           "tq_repack_tiles")
     return out
@@ -80,14 +119,24 @@ def quantize_act(x, K=None, q=None, d=None):
     """x [M, >=K] fp32 / bf16 / fp16 -> (q int8 [M, K], d fp16 [M, K/32])."""
     if x.dim() != 2 or x.dtype not in _DTYPES:
         raise TiledqError("quantize_act: x must be 2-D fp32, bf16 or fp16")
-    if not x.is_cuda or x.stride(1) != 1:
-        raise TiledqError("quantize_act: x must be a GPU tensor with unit column stride")
+    if x.stride(1) != 1:
+        raise TiledqError("quantize_act: x must have unit column stride")
     M, Kx = x.shape
     K = Kx if K is None else K
+    if K > Kx:
+        raise TiledqError(f"quantize_act: K={K} exceeds the {Kx} columns of x")
+    if q is not None and q.dtype != torch.int8:
+        raise TiledqError("quantize_act: q must be int8")
+    if d is not None and d.dtype != torch.float16:
+        raise TiledqError("quantize_act: d must be float16")
+    _need_bytes("quantize_act", "q", q, M * K)
+    _need_bytes("quantize_act", "d", d, 2 * M * (K // 32))
     if q is None:
         q = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if d is None:
         d = torch.empty((M, K // 32), dtype=torch.float16, device=x.device)
+    if not x.is_cuda:
+        raise TiledqError("tiledq operates on GPU tensors only")
     _need_cuda(q, d)
     check(lib().tq_quantize_act(_DTYPES[x.dtype], _ptr(x), M, K, x.stride(0), _ptr(q), _ptr(d),
                                 _stream(x)), "tq_quantize_act")
@@ -96,10 +145,9 @@ def quantize_act(x, K=None, q=None, d=None):
 
 def _out(name, q, N, out):
     M = q.shape[0]
+    _check_out(name, out, M, N)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=q.device)
-    if out.dim() != 2 or out.shape[0] < M or out.stride(1) != 1 or out.dtype != torch.float32:
-        raise TiledqError(f"{name}: bad output tensor")
     return out
 
 
@@ -124,9 +172,11 @@ def workspace(device, stream_handle, nbytes):
 def qgemv(qtype, tiles, K, N, q, d, lut=None, out=None, split=True):
     """Decode product y [M, N] = W (tiles) x A (q, d), M <= 8.  split=False
     runs one workgroup per stripe (no workspace)."""
+    M = _check_act("tq_qgemv", q, d, K)
+    _check_weights("tq_qgemv", qtype, tiles, K, N)
+    _check_out("tq_qgemv", out, M, N)
     _need_cuda(tiles, q, d, out)
     out = _out("tq_qgemv", q, N, out)
-    M = q.shape[0]
     st = _stream(q)
     need = lib().tq_qgemv_workspace_bytes(qtype, K, N, M) if split else 0
     ws = workspace(q.device, st.value, need) if need else None
@@ -140,6 +190,10 @@ def qgemv_x(qtype, tiles, K, N, x, lut=None, out=None, split=True):
     multiply, y [M, N]; bit-identical to quantize_act followed by qgemv."""
     if x.dim() != 2 or x.dtype not in _DTYPES or x.stride(1) != 1:
         raise TiledqError("qgemv_x: x must be 2-D fp32, bf16 or fp16 with unit column stride")
+    if x.shape[1] < K:
+        raise TiledqError(f"qgemv_x: x has {x.shape[1]} columns, K={K}")
+    _check_weights("tq_qgemv_x", qtype, tiles, K, N)
+    _check_out("tq_qgemv_x", out, x.shape[0], N)
     _need_cuda(tiles, out)
     if not x.is_cuda:
         raise TiledqError("tiledq operates on GPU tensors only")
@@ -156,6 +210,9 @@ def qgemv_x(qtype, tiles, K, N, x, lut=None, out=None, split=True):
 
 def qgemm(qtype, tiles, K, N, q, d, lut=None, out=None):
     """Prefill product y [M, N] on int8 MFMA, any M."""
+    M = _check_act("tq_qgemm", q, d, K)
+    _check_weights("tq_qgemm", qtype, tiles, K, N)
+    _check_out("tq_qgemm", out, M, N)
     _need_cuda(tiles, q, d, out)
     out = _out("tq_qgemm", q, N, out)
     check(lib().tq_qgemm(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), q.shape[0], _lut_arg(lut),
@@ -171,9 +228,11 @@ def matmul_path(qtype, K, N, M):
 def matmul(qtype, tiles, K, N, q, d, lut=None, out=None):
     """y [M, N] for any M: the library picks qgemv (M <= 8), one qgemv pass
     per 8 rows (up to 64 rows, where estimated faster: matmul_path) or qgemm."""
+    M = _check_act("tq_matmul", q, d, K)
+    _check_weights("tq_matmul", qtype, tiles, K, N)
+    _check_out("tq_matmul", out, M, N)
     _need_cuda(tiles, q, d, out)
     out = _out("tq_matmul", q, N, out)
-    M = q.shape[0]
     st = _stream(q)
     gemv = lib().tq_matmul_path(qtype, K, N, M) == PATH_GEMV
     need = lib().tq_qgemv_workspace_bytes(qtype, K, N, min(M, 8)) if gemv else 0
@@ -185,13 +244,12 @@ def matmul(qtype, tiles, K, N, q, d, lut=None, out=None):
 
 def unpack_tiles(qtype, tiles, K, N, out=None):
     """Tiles (uint8 GPU tensor) -> flat GGML blocks (uint8 GPU tensor)."""
-    _need_cuda(tiles, out)
     nbytes = flat_bytes(qtype, K, N)
+    _check_weights("unpack_tiles", qtype, tiles, K, N)
+    _need_bytes("unpack_tiles", "out", out, nbytes)
+    _need_cuda(tiles, out)
     if out is None:
         out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=tiles.device)
-    if tiles.numel() * tiles.element_size() < tiled_bytes(qtype, K, N) or \
-            out.numel() * out.element_size() < nbytes:
-        raise TiledqError("unpack_tiles: buffer too small")
     check(lib().tq_unpack_tiles(qtype, _ptr(tiles), K, N, _ptr(out), _stream(tiles)),
           "tq_unpack_tiles")
     return out[:nbytes]
@@ -202,17 +260,21 @@ def quantize_act_mx(x, K=None, q=None, e=None):
     e uint8 E8M0 scales [M, K/32])."""
     if x.dim() != 2 or x.dtype not in _DTYPES:
         raise TiledqError("quantize_act_mx: x must be 2-D fp32, bf16 or fp16")
-    if not x.is_cuda or x.stride(1) != 1:
-        raise TiledqError("quantize_act_mx: x must be a GPU tensor with unit column stride")
+    if x.stride(1) != 1:
+        raise TiledqError("quantize_act_mx: x must have unit column stride")
     M, Kx = x.shape
     K = Kx if K is None else K
+    if K > Kx:
+        raise TiledqError(f"quantize_act_mx: K={K} exceeds the {Kx} columns of x")
+    _need_bytes("quantize_act_mx", "q", q, M * K)
+    _need_bytes("quantize_act_mx", "e", e, M * (K // 32))
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if e is None:
         e = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    if not x.is_cuda:
+        raise TiledqError("tiledq operates on GPU tensors only")
     _need_cuda(q, e)
-    if q.numel() < M * K or e.numel() < M * (K // 32):
-        raise TiledqError("quantize_act_mx: output too small")
     check(lib().tq_quantize_act_mx(_DTYPES[x.dtype], _ptr(x), M, K, x.stride(0), _ptr(q),
                                    _ptr(e), _stream(x)), "tq_quantize_act_mx")
     return q, e
@@ -221,11 +283,12 @@ def quantize_act_mx(x, K=None, q=None, e=None):
 def qgemm_mx(tiles, K, N, q, e, out=None):
     """MXFP4 tiles x MXFP8 activations on the block-scaled matrix cores:
     y [M, N] fp32, any M."""
-    _need_cuda(tiles, q, e, out)
     M = q.shape[0]
     if tiles.numel() * tiles.element_size() < tiled_bytes(MXFP4, K, N) or \
             q.numel() < M * K or e.numel() < M * (K // 32):
         raise TiledqError("qgemm_mx: buffer too small")
+    _check_out("tq_qgemm_mx", out, M, N)
+    _need_cuda(tiles, q, e, out)
     out = _out("tq_qgemm_mx", q, N, out)
     check(lib().tq_qgemm_mx(_ptr(tiles), K, N, _ptr(q), _ptr(e), M, _ptr(out), out.stride(0),
                             _stream(q)), "tq_qgemm_mx")
@@ -233,6 +296,9 @@ def qgemm_mx(tiles, K, N, q, e, out=None):
 
 
 def _flat_product(name, qtype, flat, K, N, q, d, lut, out):
+    M = _check_act(name, q, d, K)
+    _check_weights(name, qtype, flat, K, N, flat=True)
+    _check_out(name, out, M, N)
     _need_cuda(flat, q, d, out)
     out = _out(name, q, N, out)
     check(getattr(lib(), name)(qtype, _ptr(flat), K, N, _ptr(q), _ptr(d), q.shape[0],
@@ -258,8 +324,13 @@ def matmul_flat(qtype, flat, K, N, q, d, lut=None, out=None):
 def block_dots(qtype, tiles, K, N, q, lut=None, path=PATH_GEMV, out=None):
     """Integer block dots int32 [M, N, K/32] as computed inside qgemv / qgemm
     (paths PATH_GEMV_FLAT / PATH_GEMM_FLAT: `tiles` holds flat blocks)."""
+    M = _check_act("tq_block_dots", q, None, K)
+    _check_weights("tq_block_dots", qtype, tiles, K, N,
+                   flat=path in (PATH_GEMV_FLAT, PATH_GEMM_FLAT))
+    if out is not None and out.dtype != torch.int32:
+        raise TiledqError("tq_block_dots: out must be int32")
+    _need_bytes("tq_block_dots", "out", out, 4 * M * N * (K // 32))
     _need_cuda(tiles, q, out)
-    M = q.shape[0]
     if out is None:
         out = torch.empty((M, N, K // 32), dtype=torch.int32, device=q.device)
     check(lib().tq_block_dots(qtype, _ptr(tiles), K, N, _ptr(q), M, _lut_arg(lut), _ptr(out),

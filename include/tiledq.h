@@ -51,7 +51,11 @@
  *   used as Q8_0 activation tiles by the vector dot of "Q2_0 Format"): per
  *   32-element K block, d = amax/127 (fp32), q = round-half-away(x * (1/d)),
  *   d stored as fp16 (nearest-even).  q is int8 row-major [M][K], d is fp16
- *   [M][K/32].  Domain: finite x, each block all zero or with amax >= 2^-120.
+ *   [M][K/32].  Domain: finite x, each block all zero or with
+ *   2^-120 <= amax <= 65504 * 127: 1/d stays finite and the stored fp16 d
+ *   stays finite (it may be an fp16 subnormal, or round to zero, for
+ *   amax below about 7.75e-3 and 3.8e-6).  Outside it the results are
+ *   unspecified.
  *
  *   Product: y[m*ldy + n] = sum_k W[n][k] * A[m][k] for m < M, n < N, with
  *   W the dequantized weights and A[m][k] = d[m][k/32] * q[m][k] (GGML's
@@ -117,7 +121,13 @@ typedef enum {
 size_t tq_tile_bytes(int type);
 
 /* Bytes of one flat GGML block: 18, 34, 18, 17, 20 (32 elements each), and
- * 144 for a 256-element Q4_K super-block; 0 for an unknown type. */
+ * 144 for a 256-element Q4_K super-block; 0 for an unknown type.  The pages
+ * name the flat source ("Tiled Weight Formats": weights repacked from flat
+ * row-major GGML layouts) but do not print it.  The reading taken is GGML's
+ * own block of 32 elements: the scale field(s) followed by the quants, so
+ * that one tile holds exactly 32 blocks (576 = 32 * 18, 1088 = 32 * 34,
+ * 544 = 32 * 17, 640 = 32 * 20, per the tile sizes of "Block-32 Quantized
+ * Formats"). */
 size_t tq_block_bytes(int type);
 
 /* (K/32) * ((N+31)/32) * tq_tile_bytes(type) ("Tile Dimensions and Grid
@@ -125,16 +135,26 @@ size_t tq_block_bytes(int type);
 size_t tq_tiled_bytes(int type, int64_t K, int64_t N);
 
 /* N * (K/32) * tq_block_bytes(type) (Q4_K: N * (K/256) * 144); 0 if the
- * shape or type is invalid. */
+ * shape or type is invalid.  Row n's blocks are contiguous and rows follow
+ * one another: the flat-block reading stated at tq_block_bytes. */
 size_t tq_flat_bytes(int type, int64_t K, int64_t N);
 
 /* 1 if (type, K, N, M) is supported by `path` (TQ_PATH_GEMV and
  * TQ_PATH_GEMV_FLAT need M <= 8; Q4_K needs K % 256 == 0; TQ_PATH_GEMM_MX
- * takes TQ_MXFP4 only), judged from
- * these static properties alone; 0 otherwise. */
+ * takes TQ_MXFP4 only), judged from these static properties alone; 0
+ * otherwise.  No pointer is needed or read: the page's "supports_op
+ * Independence from Buffer and Repack State" has support decided from
+ * operand types, shapes and operation parameters only, before any buffer
+ * exists, and every type supported tiled is supported flat as well. */
 int tq_supported(int type, int64_t K, int64_t N, int64_t M, int path);
 
-/* Static, NUL-terminated name of a status code. */
+/* Static, NUL-terminated name of a status code.  The codes follow the
+ * status convention of the page's operators: an empty range returns OK
+ * ("Multi-Device Partitioning" > "Row-Partitioned Operators": nrows == 0
+ * returns the OK status) and any status above OK is an error
+ * ("Multi-Device Synchronization" > "Deterministic Monotonic Sequence
+ * Numbers": a peer status greater than OK propagates as an error).  Unknown
+ * codes give "unknown tq_status". */
 const char *tq_status_string(int status);
 
 /* Repack flat GGML blocks into tiles ("Tiled Weight Formats": repacking at
@@ -162,7 +182,12 @@ int tq_quantize_act(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
 size_t tq_qgemv_workspace_bytes(int type, int64_t K, int64_t N, int64_t M);
 
 /* Decode matrix-vector product over tiles (M <= 8 activation rows), reading
- * every weight tile exactly once.
+ * every weight tile exactly once.  Per tile and activation row, the integer
+ * dot of the 32 decoded weights with the 32 int8 activations is formed in
+ * int32 (the int8 multiply-accumulate into 32-bit words against Q8_0
+ * activation tiles of "Q2_0 Format" > "HVX Vector Dot-Product"), then
+ * multiplied by the row scale d ("Block-32 Quantized Formats": each decoded
+ * quant is multiplied by the row scale d) and by the activation scale.
  *   tiles : device, tq_tiled_bytes(type, K, N) bytes, 16-byte aligned.
  *   q, d  : device, from tq_quantize_act with the same M and K; q 16-byte
  *           aligned, d 2-byte aligned.
@@ -178,9 +203,11 @@ size_t tq_qgemv_workspace_bytes(int type, int64_t K, int64_t N, int64_t M);
  *           by later calls of any shape without clearing.  Calls that share
  *           a workspace must not run concurrently.  With NULL or fewer than
  *           tq_qgemv_workspace_bytes() bytes the K dimension is not split
- *           (same result, fewer workgroups).
- * Deterministic: repeated calls give identical bytes, with or without the
- * workspace (partial sums are added in a fixed order). */
+ *           (the same terms summed in another order, fewer workgroups).
+ * Deterministic: each mode (with a large enough workspace, or without) is
+ * bitwise repeatable, its partial sums added in a fixed order; the two
+ * modes add the per-block terms in different orders, so their results may
+ * differ in the last bits (both within the fp32 bound of the sum). */
 int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N,
              const int8_t *q, const uint16_t *d, int64_t M,
              const int8_t *lut, float *y, int64_t ldy,
@@ -204,7 +231,14 @@ int tq_qgemv_x(int type, const void *tiles, int64_t K, int64_t N,
 
 /* Prefill matrix-matrix product over tiles with int8 matrix-core (MFMA)
  * instructions, any M >= 1.  Arguments as tq_qgemv without the workspace.
- * Same integer block dots as tq_qgemv; deterministic. */
+ * The same arithmetic as tq_qgemv: exact int32 block dots of decoded weights
+ * and int8 activations ("Q2_0 Format" > "HVX Vector Dot-Product": int8
+ * multiply-accumulate into 32-bit words against Q8_0 activation tiles),
+ * each multiplied by the row scale d ("Block-32 Quantized Formats") and the
+ * activation scale, summed in fp32.  The pages' prefill converts weights to
+ * FP16 for the matrix unit ("Q2_0 Format" > "HMX Mapping"); here the
+ * matrix unit takes the int8 operands, so that tq_qgemv and tq_qgemm form
+ * identical block dots.  Deterministic. */
 int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N,
              const int8_t *q, const uint16_t *d, int64_t M,
              const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
@@ -296,7 +330,10 @@ int tq_qgemm_mx(const void *tiles, int64_t K, int64_t N, const uint8_t *q,
                 const uint8_t *e, int64_t M, float *y, int64_t ldy,
                 hipStream_t stream);
 
-/* Test instrument: run the tq_qgemv (path TQ_PATH_GEMV, M <= 8) or tq_qgemm
+/* Test instrument for the per-block integer dot ("Q2_0 Format" > "HVX
+ * Vector Dot-Product": int8 products accumulated in 32-bit words, before the
+ * row scale d of "Block-32 Quantized Formats" is applied): run the tq_qgemv
+ * (path TQ_PATH_GEMV, M <= 8) or tq_qgemm
  * (TQ_PATH_GEMM) kernel, or their flat forms (TQ_PATH_GEMV_FLAT,
  * TQ_PATH_GEMM_FLAT; `tiles` then holds flat blocks, aligned as for
  * tq_repack_tiles), with the integer block dots as output instead of y:

@@ -70,7 +70,8 @@ def draw_scales(rng, dist, N, K):
     [N, K/32, 2]: d = fp16 of U[1e-3, 1e-2), m = fp16 of -d * U[6, 10] (a
     block min below zero, codes 0..15 spanning [m, m + 15 d]); 'q4k' -> a
     Q4KScales of d, dmin = fp16 of U[1e-4, 1e-3) per super-block and 6-bit
-    scales and mins uniform 0..63 per sub-block."""
+    scales and mins uniform 0..63 per sub-block; 'edge' -> fp16 scale bits
+    mixing +0, subnormals, the smallest normals, U[1e-3, 1e-2) and 1..8."""
     shape = (N, K // 32)
     if dist == "e8m0":
         return rng.integers(118, 125, size=shape).astype(np.uint16)
@@ -86,6 +87,19 @@ def draw_scales(rng, dist, N, K):
         m = -d * rng.uniform(6.0, 10.0, size=shape)
         pair = np.stack([d, m], axis=-1)
         return pair.astype(np.float32).astype(np.float16).view(np.uint16)
+    if dist == "edge":
+        # fp16 scale bits at the ends of the range: +0, subnormals (bits
+        # 1..1023), the smallest normals (1024..1279), U[1e-3, 1e-2), and
+        # magnitudes 1..8
+        kind = rng.integers(0, 5, size=shape)
+        b = np.where(kind == 0, 0, 0).astype(np.int64)
+        b = np.where(kind == 1, rng.integers(1, 1024, size=shape), b)
+        b = np.where(kind == 2, rng.integers(1024, 1280, size=shape), b)
+        mid = rng.uniform(1e-3, 1e-2, size=shape).astype(np.float32).astype(np.float16)
+        big = rng.uniform(1.0, 8.0, size=shape).astype(np.float32).astype(np.float16)
+        b = np.where(kind == 3, mid.view(np.uint16).astype(np.int64), b)
+        b = np.where(kind == 4, big.view(np.uint16).astype(np.int64), b)
+        return b.astype(np.uint16)
     if dist == "uniform":
         s = rng.uniform(1e-3, 1e-2, size=shape)
     elif dist == "absnormal":
@@ -227,3 +241,96 @@ WORKLOADS = {
                                            "minmax", act_dtype="bf16", path="qgemm"),
     "q4_k_gemv_k4096_n14336_m1": Workload("q4_k_gemv_k4096_n14336_m1", Q4_K, 4096, 14336, 1, "q4k"),
 }
+
+
+# ---------------------------------------------------------------------------
+# Edge-case inputs: the ends of the documented domains.  Like everything in
+# this module they are draws and constants only; no quantization arithmetic.
+
+# Block maxima |x| for the activation edge cases, per input dtype.  f32 and
+# bf16 share fp32's exponent range: the domain's lower end 2^-120 and just
+# above it, the amax whose d = amax/127 is the smallest normal fp32
+# (127 * 2^-126) and one just below (a subnormal fp32 d), maxima whose fp16 d
+# is near the fp16 normal / subnormal boundary (about 7.75e-3), an fp16
+# subnormal d (1e-5) and one that rounds to +0 (3e-6), plain magnitudes, and
+# the domain's upper end 65504 * 127.  fp16 inputs cannot go below 2^-24 or
+# above 65504.
+EDGE_AMAX = {
+    "f32": [2.0 ** -120, 2.0 ** -119, 127 * 2.0 ** -126, 126 * 2.0 ** -126, 7.75e-3, 7e-3,
+            1e-5, 3e-6, 1.0, 3.5, 65504.0 * 127],
+    "bf16": [2.0 ** -120, 2.0 ** -119, 127 * 2.0 ** -126, 126 * 2.0 ** -126, 7.75e-3, 7e-3,
+             1e-5, 3e-6, 1.0, 3.5, 65280.0 * 127],
+    "f16": [2.0 ** -24, 2.0 ** -20, 6.1e-5, 7.75e-3, 7e-3, 1e-5, 3e-6, 1.0, 3.5, 65504.0],
+}
+
+
+def _round_bf16_bits(x):
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def draw_edge_activations(rng, M, K, dtype="f32"):
+    """Activations [M, K] (float32, or bf16 / fp16 bit patterns) built block
+    by block to reach the quantizer's edges.  Each 32-element block is one
+    of: a maximum from EDGE_AMAX[dtype] placed on one element (random sign)
+    with the others uniform in (-amax, amax) -- which puts fp32 / bf16 / fp16
+    subnormal elements into the tiny-maximum blocks; a block with some
+    elements below the fp32 normal range (f32 / bf16: |x| < 2^-126) beside a
+    maximum of 2^-118; an all-zero block (signed zeros); a constant block
+    +c or -c (every code +-127: with weights of -128 the integer dot reaches
+    its extreme 32 * 128 * 127); exact half-way products (x = (k + 1/2) *
+    amax / 127 with amax = 127, where x / d is k + 1/2 exactly); or N(0,1).
+    The kind of block b of row m is (m * 7 + b) mod the number of kinds, so
+    every row and every K range see them all."""
+    amaxes = EDGE_AMAX[dtype]
+    kinds = len(amaxes) + 5
+    nb = K // 32
+    x = np.zeros((M, K), dtype=np.float64)
+    for m in range(M):
+        for b in range(nb):
+            k = (m * 7 + b) % kinds
+            blk = np.zeros(32)
+            if k < len(amaxes):
+                a = amaxes[k]
+                blk = rng.uniform(-a, a, size=32)
+                blk[rng.integers(0, 32)] = a * (1 if rng.integers(0, 2) else -1)
+            elif k == len(amaxes):
+                if dtype == "f16":
+                    blk = rng.integers(-1023, 1024, size=32) * 2.0 ** -24   # fp16 subnormals
+                    blk[rng.integers(0, 32)] = 2.0 ** -14
+                else:
+                    blk = rng.uniform(-1, 1, size=32) * 2.0 ** -130          # fp32 subnormals
+                    blk[rng.integers(0, 32)] = -(2.0 ** -118)
+            elif k == len(amaxes) + 1:
+                blk = np.where(rng.integers(0, 2, size=32) == 1, 0.0, -0.0)
+            elif k == len(amaxes) + 2:
+                c = float(rng.uniform(0.1, 2.0)) * (1 if (m + b) % 2 else -1)
+                blk[:] = c
+            elif k == len(amaxes) + 3:
+                # amax = 127 on one element, so d = 1 and x / d = x exactly;
+                # the others sit on exact halves k + 1/2
+                blk = rng.integers(-126, 126, size=32) + 0.5
+                blk[rng.integers(0, 32)] = 127.0 * (1 if rng.integers(0, 2) else -1)
+            else:
+                blk = rng.standard_normal(32)
+            x[m, 32 * b:32 * b + 32] = blk
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    return _round_bf16_bits(x)
+
+
+def draw_codes_q8_full(rng, N, K):
+    """Q8_0 codes [N, K] over the whole int8 range [-128, 127], with -128
+    planted: every third row is all -128, every other block of the other rows
+    holds -128 in half its elements, and the rest is uniform in [-128, 127]."""
+    c = rng.integers(-128, 128, size=(N, K), dtype=np.int16)
+    for n in range(N):
+        if n % 3 == 0:
+            c[n, :] = -128
+        else:
+            for b in range(0, K // 32, 2):
+                sel = rng.permutation(32)[:16]
+                c[n, 32 * b + sel] = -128
+    return c.astype(np.int8)

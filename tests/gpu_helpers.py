@@ -46,7 +46,44 @@ def check_y(y, y_ref, acond, what="", floor=FLOOR):
     return float(np.linalg.norm(y - y_ref) / nrm) if nrm else 0.0
 
 
+def oracle_matmul_rows(qtype, tiles, K, N, q, d, lut=None, n0=0, n1=None, threads=None):
+    """oracle.matmul over output rows n0..n1, the rows cut into one range per
+    host thread (the oracle's C call releases the GIL): what lets a test
+    check a full-size GEMM output in seconds.  Returns (y_ref, acond) for
+    all N columns, zero outside n0..n1."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    n1 = N if n1 is None else n1
+    T = threads or min(16, len(os.sched_getaffinity(0)))
+    cuts = [n0 + (n1 - n0) * i // T for i in range(T + 1)]
+    with ThreadPoolExecutor(T) as ex:
+        parts = list(ex.map(lambda j: oracle.matmul(qtype, tiles, K, N, q, d, lut,
+                                                    n0=cuts[j], n1=cuts[j + 1]), range(T)))
+    y = sum(p[0] for p in parts)
+    a = sum(p[1] for p in parts)
+    return y, a
+
+
 def tiles_slice(tiles, qtype, K, s0, s1):
     ts = oracle.tile_bytes(qtype)
     nkt = K // 32
     return tiles[s0 * nkt * ts: s1 * nkt * ts]
+
+
+# The block-scaled MXFP4 x MXFP8 path (tq_qgemm_mx): its bound is derived in
+# test_gpu_mx.py's docstring.
+def mx_bound(K, acond):
+    """Elementwise bound of the block-scaled path: 2^-14 * A + (K/64 + 1) *
+    2^-24 * A, A = sum of |terms|."""
+    return (2.0 ** -14 + (-(-K // 64) + 1) * 2.0 ** -24) * acond
+
+
+def check_mx(y, y_ref, acond, what, K):
+    y = np.asarray(y, dtype=np.float64)
+    err = np.abs(y - y_ref)
+    ok = (err <= 1e-3 * np.abs(y_ref)) | (err <= mx_bound(K, acond))
+    bad = np.nonzero(~ok)
+    assert bad[0].size == 0, (what, [(int(i), int(j), float(y[i, j]), float(y_ref[i, j]),
+                                      float(err[i, j] / acond[i, j]))
+                                     for i, j in zip(*bad)][:5])
+    assert np.linalg.norm(y - y_ref) <= 1e-4 * np.linalg.norm(y_ref), what

@@ -293,3 +293,63 @@ def test_mx_validation(L):
     assert g(A16, 64, 32, A16, A16, 1, A2, 32, NUL) == 4
     assert g(NUL, 64, 32, NUL, NUL, 0, NUL, 32, NUL) == 0   # M == 0
     assert g(NUL, 64, 0, NUL, NUL, 4, NUL, 0, NUL) == 0     # N == 0
+
+
+# --- the torch binding checks every buffer against the sizes the call will
+# touch before anything reaches the library: CPU tensors of the wrong size get
+# a size error (a launch would read or write past them); of the right size,
+# the GPU-only error.  Nothing here launches a kernel.
+
+def _raises(fn, words):
+    from block_quantized_matmul_repack_amd import TiledqError
+    with pytest.raises(TiledqError) as e:
+        fn()
+    assert any(w in str(e.value) for w in words), str(e.value)
+
+
+def test_binding_rejects_short_buffers_before_launch():
+    import torch
+    import block_quantized_matmul_repack_amd as tq
+    K, N, M = 256, 70, 3
+    tb = tq.tiled_bytes(tq.Q4_0, K, N)
+    fb = tq.flat_bytes(tq.Q4_0, K, N)
+    tiles = torch.zeros(tb, dtype=torch.uint8)
+    short = torch.zeros(tb - 1, dtype=torch.uint8)
+    q = torch.zeros((M, K), dtype=torch.int8)
+    d = torch.zeros((M, K // 32), dtype=torch.float16)
+    x = torch.zeros((M, K), dtype=torch.float32)
+    size = ("holds", "needs", "must be", "exceeds", "columns", "too small")
+    gpu = ("GPU tensors only",)
+    for fn in (tq.qgemv, tq.qgemm, tq.matmul):
+        _raises(lambda: fn(tq.Q4_0, short, K, N, q, d), size)
+        _raises(lambda: fn(tq.Q4_0, tiles, K + 32, N, q, d), size)            # q width != K
+        _raises(lambda: fn(tq.Q4_0, tiles, K, N, q, d[:2]), size)             # d short
+        _raises(lambda: fn(tq.Q4_0, tiles, K, N, q, d.float()), size)         # d dtype
+        _raises(lambda: fn(tq.Q4_0, tiles, K, N, q.to(torch.uint8), d), size)
+        _raises(lambda: fn(tq.Q4_0, tiles, K, N, q, d,
+                           out=torch.zeros((M - 1, N), dtype=torch.float32)), size)
+        _raises(lambda: fn(tq.Q4_0, tiles, K, N, q, d,
+                           out=torch.zeros((M, N - 1), dtype=torch.float32)), size)
+        _raises(lambda: fn(tq.Q4_0, tiles, K, N, q, d), gpu)
+    _raises(lambda: tq.qgemv_x(tq.Q4_0, short, K, N, x), size)
+    _raises(lambda: tq.qgemv_x(tq.Q4_0, tiles, K + 32, N, x), size)
+    _raises(lambda: tq.qgemv_x(tq.Q4_0, tiles, K, N, x), gpu)
+    flat = torch.zeros(fb, dtype=torch.uint8)
+    for fn in (tq.qgemv_flat, tq.qgemm_flat, tq.matmul_flat):
+        _raises(lambda: fn(tq.Q4_0, flat[:-1], K, N, q, d), size)
+        _raises(lambda: fn(tq.Q4_0, flat, K, N, q, d[:1]), size)
+        _raises(lambda: fn(tq.Q4_0, flat, K, N, q, d), gpu)
+    _raises(lambda: tq.quantize_act(x, q=q[:2]), size)
+    _raises(lambda: tq.quantize_act(x, d=d[:2]), size)
+    _raises(lambda: tq.quantize_act(x, K=K + 32), size)
+    _raises(lambda: tq.quantize_act(x, q=q, d=d), gpu)
+    isum = torch.zeros((M, N, K // 32), dtype=torch.int32)
+    _raises(lambda: tq.block_dots(tq.Q4_0, tiles, K, N, q, out=isum[:, :-1]), size)
+    _raises(lambda: tq.block_dots(tq.Q4_0, short, K, N, q), size)
+    _raises(lambda: tq.block_dots(tq.Q4_0, flat[:-1], K, N, q, path=tq.PATH_GEMV_FLAT), size)
+    _raises(lambda: tq.block_dots(tq.Q4_0, tiles, K, N, q, out=isum), gpu)
+    _raises(lambda: tq.repack_tiles(tq.Q4_0, flat[:-1], K, N), size)
+    _raises(lambda: tq.repack_tiles(tq.Q4_0, flat, K, N, out=short), size)
+    _raises(lambda: tq.unpack_tiles(tq.Q4_0, short, K, N), size)
+    _raises(lambda: tq.unpack_tiles(tq.Q4_0, tiles, K, N, out=flat[:-1]), size)
+    _raises(lambda: tq.repack_tiles(tq.Q4_0, flat, K, N, out=tiles), gpu)
