@@ -26,6 +26,7 @@ SIGNATURES = {
     "tq_quantize_act": (INT, [INT, P, I64, I64, I64, P, P, P]),
     "tq_qgemv_workspace_bytes": (SZ, [INT, I64, I64, I64]),
     "tq_qgemv": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P, SZ, P]),
+    "tq_qgemv_noalloc": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_qgemv_x": (INT, [INT, P, I64, I64, INT, P, I64, I64, P, P, I64, P, SZ, P]),
     "tq_qgemm": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_matmul": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P, SZ, P]),

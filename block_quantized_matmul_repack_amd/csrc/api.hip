@@ -7,10 +7,60 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "tq_internal.h"
 
 namespace {
+
+// Scratch of tq_qgemv_noalloc: the K split's reduction slots live here
+// instead of in a caller's workspace.  Every GPU the library runs on holds
+// its own copy of the array until the process ends.  On the host the name
+// `tq_scratch` is only a stand-in for the symbol: its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is
+// passed to kernels.
+__device__ __align__(256) uint64_t tq_scratch[TQ_NOALLOC_SCRATCH_BYTES / 8];
+
+constexpr int MAX_DEVICES = 64;
+std::once_flag scratch_once[MAX_DEVICES];
+void *scratch_ptr[MAX_DEVICES];
+hipError_t scratch_err[MAX_DEVICES];
+
+__global__ void k_zero_u64(uint64_t *p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// The current device's scratch address, looked up (and the array cleared on
+// `stream`, in stream order before any use) on the first call on that
+// device; nullptr with `err` set if that failed.
+void *device_scratch(hipStream_t stream, hipError_t &err)
+{
+    int dev = -1;
+    err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return nullptr;
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::call_once(scratch_once[dev], [&] {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(tq_scratch));
+        if (e == hipSuccess) {
+            // a fill kernel, not a memset: a first call made under stream
+            // capture records it as an ordinary kernel node
+            k_zero_u64<<<64, 256, 0, stream>>>((uint64_t *)p, TQ_NOALLOC_SCRATCH_BYTES / 8);
+            e = hipGetLastError();
+        }
+        scratch_err[dev] = e;
+        scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
+    });
+    err = scratch_err[dev];
+    return scratch_ptr[dev];
+}
 
 // Shape limits.  With them every grid stays below 2^31 work-items per
 // dimension (a dispatch counts them in 32 bits): the decode and GEMM grids
@@ -218,6 +268,31 @@ int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
     const tq::Act act{q, d, nullptr, -1, 0};
     return launch_status(tq::launch_qgemv(kernel_type(type), tiles, K, N, act, M, pack_lut(type, lut), y, ldy,
                                           nullptr, workspace, workspace_bytes, stream));
+}
+
+int tq_qgemv_noalloc(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
+                     const uint16_t *d, int64_t M, const int8_t *lut, float *y, int64_t ldy,
+                     hipStream_t stream)
+{
+    if (valid_type(type) && M > 8)
+        return TQ_E_SHAPE;
+    int st = check_matmul(type, tiles, K, N, q, d, M, lut, y, ldy, true);
+    if (st != TQ_OK || M == 0 || N == 0)
+        return st;
+    const size_t need = tq::gemv_workspace_bytes(K, N, M);
+    if (need > TQ_NOALLOC_SCRATCH_BYTES)
+        return TQ_E_SHAPE;
+    void *ws = nullptr;
+    if (need > 0) {
+        hipError_t e;
+        ws = device_scratch(stream, e);
+        if (!ws)
+            return TQ_E_LAUNCH;
+    }
+    const tq::Act act{q, d, nullptr, -1, 0};
+    return launch_status(tq::launch_qgemv(kernel_type(type), tiles, K, N, act, M,
+                                          pack_lut(type, lut), y, ldy, nullptr, ws, need,
+                                          stream));
 }
 
 int tq_qgemv_x(int type, const void *tiles, int64_t K, int64_t N, int dtype, const void *x,

@@ -185,6 +185,21 @@ def qgemv(qtype, tiles, K, N, q, d, lut=None, out=None, split=True):
     return out
 
 
+def qgemv_noalloc(qtype, tiles, K, N, q, d, lut=None, out=None):
+    """qgemv through the entry point that allocates nothing (its K-split
+    scratch is a device array inside the library, shared by all calls on a
+    GPU: calls that overlap on one GPU race).  Pass `out` to allocate
+    nothing here either."""
+    M = _check_act("tq_qgemv_noalloc", q, d, K)
+    _check_weights("tq_qgemv_noalloc", qtype, tiles, K, N)
+    _check_out("tq_qgemv_noalloc", out, M, N)
+    _need_cuda(tiles, q, d, out)
+    out = _out("tq_qgemv_noalloc", q, N, out)
+    check(lib().tq_qgemv_noalloc(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut),
+                                 _ptr(out), out.stride(0), _stream(q)), "tq_qgemv_noalloc")
+    return out
+
+
 def qgemv_x(qtype, tiles, K, N, x, lut=None, out=None, split=True):
     """Decode in one launch: quantize x [M, >=K] (fp32 / bf16 / fp16) and
     multiply, y [M, N]; bit-identical to quantize_act followed by qgemv."""

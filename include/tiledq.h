@@ -213,6 +213,29 @@ int tq_qgemv(int type, const void *tiles, int64_t K, int64_t N,
              const int8_t *lut, float *y, int64_t ldy,
              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the device scratch array behind tq_qgemv_noalloc (1 MiB per
+ * GPU).  It covers the K-split workspace of every shape tq_qgemv accepts:
+ * tq_qgemv_workspace_bytes() never exceeds it. */
+#define TQ_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/* tq_qgemv for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments and results as tq_qgemv with a workspace of
+ * tq_qgemv_workspace_bytes() bytes: the K split's reduction slots live in a
+ * device array of TQ_NOALLOC_SCRATCH_BYTES inside the library (one per GPU,
+ * held until the process ends), so y is bit-identical to tq_qgemv given such
+ * a workspace.  The call allocates and frees nothing; the caller passes the
+ * inputs and the output.  The first call on a device looks up the array's
+ * address and clears it with a kernel on `stream`; every call leaves it
+ * zero again.  All calls on one GPU share the array: calls that may overlap
+ * on one GPU (different streams, or concurrent graph replays) race and give
+ * undefined results; serialize them.  A shape whose workspace would exceed
+ * the array returns TQ_E_SHAPE (none of the accepted shapes does); a failed
+ * address lookup or clear returns TQ_E_LAUNCH. */
+int tq_qgemv_noalloc(int type, const void *tiles, int64_t K, int64_t N,
+                     const int8_t *q, const uint16_t *d, int64_t M,
+                     const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
+
 /* Decode in one launch: tq_quantize_act fused into tq_qgemv.  Each
  * workgroup quantizes the activation blocks it needs into on-chip memory
  * with the same arithmetic as tq_quantize_act, so y is bit-identical to

@@ -353,3 +353,19 @@ def test_binding_rejects_short_buffers_before_launch():
     _raises(lambda: tq.unpack_tiles(tq.Q4_0, short, K, N), size)
     _raises(lambda: tq.unpack_tiles(tq.Q4_0, tiles, K, N, out=flat[:-1]), size)
     _raises(lambda: tq.repack_tiles(tq.Q4_0, flat, K, N, out=tiles), gpu)
+
+
+def test_noalloc_scratch_covers_every_split(L):
+    """tq_qgemv_noalloc's device array holds the K-split workspace of every
+    shape tq_qgemv accepts (the entry point rejects larger needs with
+    TQ_E_SHAPE, which no accepted shape reaches)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+TQ_NOALLOC_SCRATCH_BYTES\s+\(1u\s*<<\s*(\d+)\)", text)
+    assert m
+    cap = 1 << int(m.group(1))
+    worst = 0
+    for K in (64, 128, 512, 1024, 4096, 1 << 20):
+        for nct in range(1, 600):
+            for M in (1, 8):
+                worst = max(worst, L.tq_qgemv_workspace_bytes(0, K, 32 * nct, M))
+    assert 0 < worst <= cap
