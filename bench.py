@@ -1,25 +1,29 @@
 #!/usr/bin/env python
 """Benchmark of the tiled block-32 quantized matmul hot path on one MI355X.
 
-Step (the decode hot path, one token): dynamic int8 quantization of the
-activation row and the tiled GEMV over the repacked weights, fused in one
-launch (tq_qgemv_x; the two-launch form is timed as well) -- on the
-Q8_0 K=4096 N=4096 M=1 workload (fp16 scales |N(0,1)|*0.01, int8 codes
-uniform in [-127, 127], fp32 activations N(0,1), seed 0).  The weights are
-repacked on the GPU once, at load (as the pages place repacking), into R
-distinct copies (R * 17.8 MB >= 1 GiB) that the steps rotate through, so
-every step streams its weights from HBM rather than from the 256 MB
-Infinity Cache.  All inputs are resident in HBM before the timed region;
-the K timed steps are replayed from a HIP graph.
+Step (the decode hot path, one token of a vocabulary head): dynamic int8
+quantization of the activation row (tq_quantize_act) and the tiled GEMV over
+the repacked weights (tq_qgemv) -- on the Q8_0 lm-head K=4096 N=128001 M=1
+(4001 row-tiles, the last one with a single valid row; int8 codes uniform in
+[-127, 127], fp16 scales |N(0,1)|*0.01, fp32 activations N(0,1), seed 0).
+This two-launch form is the faster one at this size (the fused tq_qgemv_x is
+timed beside it).  The weights are repacked on the GPU once, at load (as the
+pages place repacking), into R = 2 distinct copies (2 x 557 MB >= 1 GiB)
+that the steps alternate between, so every step streams its weights from HBM
+rather than from the 256 MB Infinity Cache.  All inputs are resident in HBM
+before the timed region; the K timed steps are replayed from a HIP graph and
+timed with HIP events recorded on the stream that replays it.
 
 Printed: one JSON line.  value = weight-tile bytes per step / step time
-(GB/s).  roofline = the fused decode kernel: algorithmic bytes (weight tiles
-+ fp32 activations + fp32 outputs) per launch over
-its average duration: launches replayed back to back from a HIP graph on the
+(GB/s).  roofline = the GEMV kernel of the step: algorithmic bytes (weight
+tiles + int8 activations + fp16 scales + fp32 outputs) per launch over its
+average duration, launches replayed back to back from a HIP graph on the
 current stream, bracketed by HIP events recorded on that stream.
-Also reported: the int8-MFMA GEMM on the IQ4_NL M=512 K=N=4096 workload
-(TOPS and fraction of the int8 peak), the load-time repack, and the CPU
-oracle timed on this host's cores.
+Also reported: the other decode workloads (Q8_0 K=N=4096 M=1; Q4_0 and
+IQ4_NL K=4096 N=14336 M=1/4/8), the int8-MFMA GEMM on IQ4_NL M=512
+K=N=4096 (TOPS and fraction of the int8 peak) and on the lm-head at M=128,
+the block-scaled MXFP4 GEMM, the load-time repack, and the CPU oracle timed
+on this host's cores (the step itself, the GEMM and the repack).
 """
 import argparse
 import json
@@ -34,18 +38,22 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (fp8 x fp4 issues at the fp8 rate)
 ROTATE_BYTES = 1 << 30         # defeat the 256 MB Infinity Cache
+HEADLINE = "q8_0_lmhead_k4096_n128001_m1"
 
 # HBM traffic of the kernels, from rocprofv3 --pmc passes (FETCH_SIZE, then
 # WRITE_SIZE, each in its own run) of `bench.py --launch-only <kernel>`: KiB
-# per dispatch as the counters read them, averaged over the dispatches.  The
-# same counters read for a plain 256 MiB device copy (`--launch-only copy`)
-# give FETCH_SIZE 131083.55 KiB and WRITE_SIZE 262144 KiB for 262144 KiB moved
-# each way, so FETCH_SIZE is scaled by 262144 / 131084.5 and WRITE_SIZE by 1.
-# "src" is the SHA-256 of the kernel's sources when the counters were taken;
-# once they differ, traffic is reported as null.
+# per dispatch of the named kernel as the counters read them, averaged over
+# its dispatches.  The same counters read for a plain 256 MiB device copy
+# (`--launch-only copy`) give FETCH_SIZE 131083.55 KiB and WRITE_SIZE 262144
+# KiB for 262144 KiB moved each way, so FETCH_SIZE is scaled by
+# 262144 / 131083.55 and WRITE_SIZE by 1.  "src" is the SHA-256 of the
+# kernel's sources when the counters were taken; once they differ, traffic
+# is reported as null.
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
+    "lmhead": {"fetch_kib": 272119.54, "write_kib": 500.03,
+               "src": "2beef0cbad9cd442180bffefa0041c71debc773f13101dc1652c52ec158bfbb4"},
     "decode": {"fetch_kib": 8780.32, "write_kib": 112.00,
                "src": "2beef0cbad9cd442180bffefa0041c71debc773f13101dc1652c52ec158bfbb4"},
     "gemm": {"fetch_kib": 13363.18, "write_kib": 8192.00,
@@ -56,12 +64,13 @@ TRAFFIC = {
            "src": "e0375ab973c733c2d3825ab444b6d9baf635ebe937af40029474141d9138b660"},
 }
 KERNEL_SOURCES = {
+    "lmhead": ("qgemv.hip", "tq_internal.h"),
     "decode": ("qgemv.hip", "tq_internal.h"),
     "gemm": ("qgemm.hip", "tq_internal.h"),
     "repack": ("repack.hip", "tq_internal.h"),
     "mx": ("mx.hip", "tq_internal.h"),
 }
-LAUNCH_ONLY = ("decode", "gemm", "repack", "mx", "copy")
+LAUNCH_ONLY = ("lmhead", "decode", "gemm", "repack", "mx", "copy")
 
 
 def source_hash(kernel):
@@ -85,23 +94,17 @@ def traffic_bytes(kernel):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2000)
-    p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="bounded CPU work for the oracle baseline")
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="bounded CPU work per oracle baseline leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true",
-                   help="skip the GEMM and repack measurements")
-    p.add_argument("--eager", action="store_true", help="time eager launches, not a graph")
+                   help="only the headline step (no other workloads)")
     p.add_argument("--launch-only", choices=sorted(LAUNCH_ONLY), default=None,
                    help="no timing: launch one kernel --steps times on the bench's inputs "
                         "(for rocprofv3 --pmc counter passes) and exit")
     return p.parse_args()
-
-
-def gemv_x_bytes(w):
-    """Algorithmic bytes of one fused decode launch: tiles + fp32 x + fp32 y."""
-    return w.weight_bytes + 4 * w.M * w.K + 4 * w.M * w.N
 
 
 def capture(torch, fn, n):
@@ -120,13 +123,12 @@ def capture(torch, fn, n):
     return g
 
 
-def kernel_us(torch, fn, n=200):
-    """Average duration of the kernel that fn(i) launches: n launches replayed
-    back to back from a HIP graph, timed by HIP events recorded on the stream
-    the kernels run on (the current stream, which replays the graph)."""
-    g = capture(torch, fn, n)
+def replay_us(torch, g, n):
+    """Average time per item of a graph of n items: the graph replayed on the
+    current stream between two HIP events recorded on that stream."""
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     a.record()
     g.replay()
     b.record()
@@ -134,130 +136,156 @@ def kernel_us(torch, fn, n=200):
     return a.elapsed_time(b) / n * 1e3
 
 
-def setup_decode(torch, tq, synth):
-    """Decode-step inputs in HBM; returns (workload, copies, step, step2, parts)."""
+def kernel_us(torch, fn, n=200):
+    """Average duration of the kernel(s) fn(i) launches: n launches replayed
+    back to back from a HIP graph, timed by HIP events on the replaying
+    stream."""
+    return replay_us(torch, capture(torch, fn, n), n)
+
+
+def rotating_tiles(torch, tq, w, flat):
+    R = max(2, -(-ROTATE_BYTES // w.weight_bytes))
+    return [tq.repack_tiles(w.qtype, flat, w.K, w.N) for _ in range(R)]
+
+
+def decode_bytes(w, M, fused):
+    """Algorithmic bytes of one decode step: tiles, the activations as the
+    kernel reads them (fp32 x when fused, else int8 q + fp16 d), fp32 y."""
+    act = 4 * M * w.K if fused else M * w.K + 2 * M * (w.K // 32)
+    return w.weight_bytes + act + 4 * M * w.N
+
+
+# ---------------------------------------------------------------------------
+# The headline: the lm-head decode step
+
+def setup_headline(torch, tq, synth):
     import numpy as np
-    w = synth.WORKLOADS["q8_0_gemv_k4096_n4096_m1"]
+    w = synth.WORKLOADS[HEADLINE]
     inp = synth.make_inputs(w)
     flat = torch.from_numpy(inp.flat).cuda()
-    R = max(2, -(-ROTATE_BYTES // w.weight_bytes))
-    tiles = [tq.repack_tiles(w.qtype, flat, w.K, w.N) for _ in range(R)]
+    tiles = rotating_tiles(torch, tq, w, flat)
+    R = len(tiles)
     del flat
     X = 64
     rng = np.random.default_rng(1)
     xs = torch.from_numpy(np.concatenate(
         [inp.x, rng.standard_normal((X - 1, w.K), dtype=np.float32)])).cuda()
-    q = torch.empty((w.M, w.K), dtype=torch.int8, device="cuda")
-    d = torch.empty((w.M, w.K // 32), dtype=torch.float16, device="cuda")
-    y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    q = torch.empty((1, w.K), dtype=torch.int8, device="cuda")
+    d = torch.empty((1, w.K // 32), dtype=torch.float16, device="cuda")
+    y = torch.empty((1, w.N), dtype=torch.float32, device="cuda")
 
-    def step(i):                 # one decode token: quantize + GEMV in one launch
-        tq.qgemv_x(w.qtype, tiles[i % R], w.K, w.N, xs[i % X: i % X + 1], out=y)
-
-    def step2(i):                # the same with the quantization as its own launch
+    def step(i):                 # one decode token: quantize, then the GEMV
         tq.quantize_act(xs[i % X: i % X + 1], q=q, d=d)
         tq.qgemv(w.qtype, tiles[i % R], w.K, w.N, q, d, out=y)
 
-    # the weight copies viewed as fp32 rows of 1024: a plain row-sum reads
-    # exactly the step's tile bytes (one reduction block per row, no
-    # cross-block scratch)
-    rows = [t.view(torch.float32).view(-1, 1024) for t in tiles]
-    rsum = torch.empty(rows[0].shape[0], dtype=torch.float32, device="cuda")
     parts = {
         "qgemv": lambda i: tq.qgemv(w.qtype, tiles[i % R], w.K, w.N, q, d, out=y),
         "quantize_act": lambda i: tq.quantize_act(xs[i % X: i % X + 1], q=q, d=d),
-        # one weight copy: resident in the 256 MB Infinity Cache after the first step
-        "warm": lambda i: tq.qgemv_x(w.qtype, tiles[0], w.K, w.N, xs[i % X: i % X + 1], out=y),
-        "read": lambda i: torch.sum(rows[i % R], dim=1, out=rsum),
+        "fused": lambda i: tq.qgemv_x(w.qtype, tiles[i % R], w.K, w.N, xs[i % X: i % X + 1],
+                                      out=y),
     }
-    return w, R, step, step2, parts
+    return w, R, step, parts, tiles
 
 
-def measure_gemv(torch, tq, synth, args):
-    w, R, step, step2, parts = setup_decode(torch, tq, synth)
+def measure_headline(torch, tq, synth, args):
+    w, R, step, parts, tiles = setup_headline(torch, tq, synth)
     for i in range(args.warmup):
         step(i)
-        step2(i)
     torch.cuda.synchronize()
-
     K = args.steps
-    if args.eager:
-        run = lambda: [step(i) for i in range(K)]
-    else:
-        run = capture(torch, step, K).replay
+    g = capture(torch, step, K)
+    # the timed region: K steps, synchronized on both sides, HIP events on
+    # the replaying stream; the host clock around it is kept as a cross-check
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-
-    two = capture(torch, step2, 500)
-    t1 = time.perf_counter()
-    two.replay()
-    torch.cuda.synchronize()
-    two_us = (time.perf_counter() - t1) / 500 * 1e6
-
+    us_step = replay_us(torch, g, K)
+    host_s = time.perf_counter() - t0
+    del g
     detail = {
-        "qgemv_x_us": kernel_us(torch, step),
-        "qgemv_us": kernel_us(torch, parts["qgemv"]),
-        "quantize_act_us": kernel_us(torch, parts["quantize_act"]),
-        "two_launch_step_us": two_us,
+        "qgemv_us": kernel_us(torch, parts["qgemv"], 100),
+        "quantize_act_us": kernel_us(torch, parts["quantize_act"], 100),
+        "fused_qgemv_x_step_us": kernel_us(torch, parts["fused"], 100),
+        "host_clock_us_per_step": host_s / K * 1e6,
     }
-    # references at this size: an (almost) empty launch, and a plain device
-    # copy of the same number of bytes (read + write), both graph-replayed
-    tiny = torch.zeros(1, device="cuda")
-    detail["empty_launch_us"] = kernel_us(torch, lambda i: tiny.add_(1.0))
-    src = [torch.ones(w.weight_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
-    dst = torch.empty_like(src[0])
-    cu = kernel_us(torch, lambda i: dst.copy_(src[i % R]))
-    del src
-    detail["copy_same_bytes_us"] = cu
-    detail["copy_same_bytes_GB_s"] = 2 * w.weight_bytes / cu / 1e3
+    # a plain read of the same rotating bytes (torch row-sum over fp32 rows)
+    rows = [t.view(torch.float32).view(-1, 1088) for t in tiles]
+    rsum = torch.empty(rows[0].shape[0], dtype=torch.float32, device="cuda")
+    ru = kernel_us(torch, lambda i: torch.sum(rows[i % R], dim=1, out=rsum), 50)
+    ref = {"read_same_bytes": {"us": round(ru, 3), "GB_s": round(w.weight_bytes / ru / 1e3, 1),
+                               "note": "torch row-sum over the same rotating tile copies: "
+                                       "what merely reading these bytes costs"}}
+    del rows, tiles
+    return w, R, us_step, detail, ref
 
-    # per launch: 200 eager launches of the step with a HIP event pair around
-    # each, enqueued while the stream is still busy with in-place passes over a
-    # 256 MiB buffer, so that the launches run back to back on the GPU and each
-    # pair times its kernel rather than the host's launch latency
-    pad = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(200)]
-    ahead = torch.cuda.Event()
-    for passes in (100, 400, 1600):
-        for _ in range(passes):
-            pad.mul_(1.0)
-        ahead.record()
-        for i, (e0, e1) in enumerate(evs):
-            e0.record()
-            step(i)
-            e1.record()
-        queued = not ahead.query()
-        torch.cuda.synchronize()
-        if queued:
-            break
-    del pad
-    t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
-    ref = {"per_launch_us": {"median": round(t[100], 3), "p10": round(t[20], 3),
-                             "p90": round(t[180], 3), "launches": 200,
-                             "queued_behind_busy_stream": queued,
-                             "how": "eager launches, a HIP event pair around each"}}
-    wu = kernel_us(torch, parts["warm"])
-    ref["warm_mall_resident"] = {"us": round(wu, 3), "GB_s": round(w.weight_bytes / wu / 1e3, 1),
-                                 "note": "one weight copy, served from the Infinity Cache; "
-                                         "not an HBM figure"}
-    ru = kernel_us(torch, parts["read"])
-    ref["read_same_bytes"] = {"us": round(ru, 3), "GB_s": round(w.weight_bytes / ru / 1e3, 1),
-                              "note": "torch row-sum over the same rotating tile copies: "
-                                      "what merely reading these bytes costs at this size"}
-    return w, R, dt, detail, ref
 
+# ---------------------------------------------------------------------------
+# Other decode workloads
+
+def measure_decodes(torch, tq, synth):
+    """Decode steps timed fused (qgemv_x) and as quantize_act + qgemv; GB/s
+    counts what the faster form reads and writes.  Config 2 (Q8_0
+    K=N=4096 M=1, fused) also gets a roofline object of its own."""
+    import numpy as np
+    res = {}
+    cases = [("q8_0_gemv_k4096_n4096_m1", synth.Q8_0, 4096, 4096, "absnormal", (1,)),
+             ("q4_0_gemv_k4096_n14336", synth.Q4_0, 4096, 14336, "uniform", (1, 4, 8)),
+             ("iq4_nl_gemv_k4096_n14336", synth.IQ4_NL, 4096, 14336, "uniform", (1, 4, 8))]
+    for name, qtype, K, N, dist, Ms in cases:
+        w = synth.Workload(name, qtype, K, N, 1, dist)
+        inp = synth.make_inputs(w)
+        tiles = rotating_tiles(torch, tq, w, torch.from_numpy(inp.flat).cuda())
+        R = len(tiles)
+        lut = inp.lut if qtype == synth.IQ4_NL else None
+        for M in Ms:
+            rng = np.random.default_rng(M)
+            X = 16
+            xs = torch.from_numpy(rng.standard_normal((X * M, K), dtype=np.float32)).cuda()
+            q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+            d = torch.empty((M, K // 32), dtype=torch.float16, device="cuda")
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            xi = lambda i: xs[(i % X) * M:(i % X + 1) * M]
+            fused = lambda i: tq.qgemv_x(qtype, tiles[i % R], K, N, xi(i), lut=lut, out=y)
+
+            def two(i):
+                tq.quantize_act(xi(i), q=q, d=d)
+                tq.qgemv(qtype, tiles[i % R], K, N, q, d, lut=lut, out=y)
+            for i in range(5):
+                fused(i)
+                two(i)
+            us_f = kernel_us(torch, fused, 100)
+            us_2 = kernel_us(torch, two, 100)
+            f = us_f <= us_2
+            us = min(us_f, us_2)
+            nbytes = decode_bytes(w, M, f)
+            label = name if name.endswith("_m1") else f"{name}_m{M}"
+            res[label] = {"step_us": round(us, 3),
+                          "path": "qgemv_x (fused)" if f else "quantize_act + qgemv",
+                          "qgemv_x_us": round(us_f, 3), "quantize_act_qgemv_us": round(us_2, 3),
+                          "GB_s": round(nbytes / us / 1e3, 1),
+                          "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                          "bytes_per_step": nbytes}
+            if name == "q8_0_gemv_k4096_n4096_m1":
+                ku = kernel_us(torch, fused, 200)
+                nb = decode_bytes(w, M, True)
+                res[label]["roofline"] = {
+                    "bound": "hbm", "achieved": round(nb / ku / 1e3, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(nb / ku / 1e3 / HBM_PEAK_GBS, 4),
+                    "traffic": traffic_bytes("decode"),
+                    "kernel": "k_qgemv (fused quantize, Q8_0, M=1)", "kernel_us": round(ku, 3),
+                    "bytes_per_launch": nb}
+        del tiles
+    return res
+
+
+# ---------------------------------------------------------------------------
+# GEMMs, repack
 
 def setup_gemm(torch, tq, synth):
     import numpy as np
     w = synth.WORKLOADS["iq4_nl_gemm_m512_k4096_n4096"]
     inp = synth.make_inputs(w)
-    flat = torch.from_numpy(inp.flat).cuda()
-    R = max(2, -(-ROTATE_BYTES // w.weight_bytes))
-    tiles = [tq.repack_tiles(w.qtype, flat, w.K, w.N) for _ in range(R)]
+    tiles = rotating_tiles(torch, tq, w, torch.from_numpy(inp.flat).cuda())
+    R = len(tiles)
     x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
     q, d = tq.quantize_act(x)
     y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
@@ -266,9 +294,10 @@ def setup_gemm(torch, tq, synth):
     return w, f, quant
 
 
-def gemm_bytes(w):
+def gemm_bytes(w, M=None):
     """Algorithmic bytes of one GEMM launch: tiles + int8 q + fp16 d + fp32 y."""
-    return w.weight_bytes + w.M * w.K + 2 * w.M * (w.K // 32) + 4 * w.M * w.N
+    M = w.M if M is None else M
+    return w.weight_bytes + M * w.K + 2 * M * (w.K // 32) + 4 * M * w.N
 
 
 def measure_gemm(torch, tq, synth, n=200):
@@ -278,13 +307,36 @@ def measure_gemm(torch, tq, synth, n=200):
     us = kernel_us(torch, f, n)
     quant_us = kernel_us(torch, quant, 50)
     tops = 2.0 * w.M * w.N * w.K / us / 1e6
-    tb = traffic_bytes("gemm")
     return {"workload": w.name, "metric": "qgemm int8 TOPS", "value": round(tops, 2),
             "unit": "TOPS", "kernel_us": round(us, 3), "quantize_act_us": round(quant_us, 3),
             "hbm_GB_s": round(gemm_bytes(w) / us / 1e3, 1),
             "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4),
-                         "traffic": tb, "bytes_per_launch": gemm_bytes(w)}}
+                         "traffic": traffic_bytes("gemm"), "bytes_per_launch": gemm_bytes(w)}}
+
+
+def measure_lmhead_gemm(torch, tq, synth):
+    """The lm-head at M=128 (config 5's prefill side): below the int8 ridge,
+    so both its HBM and its MFMA fractions are reported."""
+    import numpy as np
+    w = synth.WORKLOADS["q8_0_lmhead_k4096_n128001_m128"]
+    inp = synth.make_inputs(w, M=1)
+    tiles = rotating_tiles(torch, tq, w, torch.from_numpy(inp.flat).cuda())
+    R = len(tiles)
+    x = torch.from_numpy(np.random.default_rng(128).standard_normal(
+        (w.M, w.K), dtype=np.float32)).cuda()
+    q, d = tq.quantize_act(x)
+    y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    f = lambda i: tq.qgemm(w.qtype, tiles[i % R], w.K, w.N, q, d, out=y)
+    for i in range(3):
+        f(i)
+    us = kernel_us(torch, f, 30)
+    nb = gemm_bytes(w)
+    tops = 2.0 * w.M * w.N * w.K / us / 1e6
+    del tiles
+    return {"workload": w.name, "kernel_us": round(us, 3), "TOPS": round(tops, 2),
+            "int8_frac": round(tops / INT8_PEAK_TOPS, 4), "GB_s": round(nb / us / 1e3, 1),
+            "hbm_frac": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes_per_launch": nb}
 
 
 def setup_mx(torch, tq, synth):
@@ -293,9 +345,8 @@ def setup_mx(torch, tq, synth):
     import numpy as np
     w = synth.WORKLOADS["mxfp4_gemm_m512_k4096_n4096"]
     inp = synth.make_inputs(w)
-    flat = torch.from_numpy(inp.flat).cuda()
-    R = max(2, -(-ROTATE_BYTES // w.weight_bytes))
-    tiles = [tq.repack_tiles(w.qtype, flat, w.K, w.N) for _ in range(R)]
+    tiles = rotating_tiles(torch, tq, w, torch.from_numpy(inp.flat).cuda())
+    R = len(tiles)
     x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
     q, e = tq.quantize_act_mx(x)
     y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
@@ -351,29 +402,22 @@ def measure_repack(torch, tq, synth, n=50):
 
 
 def measure_others(torch, tq, synth):
-    """The other decode / prefill workloads, timed like the roofline kernel
-    (graph of 50 steps, HIP events); weights rotate over >= 1 GiB.  Decode
-    steps are timed both fused (qgemv_x) and as quantize_act + qgemv; GB/s
-    counts tiles + fp32 x + fp32 y over the faster one."""
+    """The widened formats and paths, timed like the rest (graph of steps,
+    HIP events); weights rotate over >= 1 GiB."""
     import numpy as np
     res = {}
-    cases = [("q4_0_gemv_k4096_n14336_m1", 1), ("q4_0_gemv_k4096_n14336_m1", 4),
-             ("q4_0_gemv_k4096_n14336_m1", 8), ("q8_0_lmhead_k4096_n128001_m1", 1),
-             ("q8_0_lmhead_k4096_n128001_m128", 128), ("mxfp4_gemv_k4096_n14336_m1", 1),
-             ("mxfp4_gemv_k4096_n14336_m1", 4), ("mxfp4_gemm_m512_k4096_n4096", 512),
-             ("q4_1_gemv_k4096_n14336_m1", 1), ("q4_1_gemv_k4096_n14336_m1", 4),
-             ("q4_1_gemm_m512_k4096_n4096", 512), ("q4_k_gemv_k4096_n14336_m1", 1)]
+    cases = [("mxfp4_gemv_k4096_n14336_m1", 1), ("mxfp4_gemv_k4096_n14336_m1", 4),
+             ("mxfp4_gemm_m512_k4096_n4096", 512), ("q4_1_gemv_k4096_n14336_m1", 1),
+             ("q4_1_gemv_k4096_n14336_m1", 4), ("q4_1_gemm_m512_k4096_n4096", 512),
+             ("q4_k_gemv_k4096_n14336_m1", 1)]
     tiles_cache = {}
     for name, M in cases:
         w = synth.WORKLOADS[name]
         key = (w.qtype, w.K, w.N)
         if key not in tiles_cache:
             inp = synth.make_inputs(w, M=1)
-            flat = torch.from_numpy(inp.flat).cuda()
-            R = max(2, -(-ROTATE_BYTES // w.weight_bytes))
             tiles_cache.clear()
-            tiles_cache[key] = [tq.repack_tiles(w.qtype, flat, w.K, w.N) for _ in range(R)]
-            del flat
+            tiles_cache[key] = rotating_tiles(torch, tq, w, torch.from_numpy(inp.flat).cuda())
         tiles = tiles_cache[key]
         R = len(tiles)
         rng = np.random.default_rng(M)
@@ -387,28 +431,27 @@ def measure_others(torch, tq, synth):
             def two(i):
                 tq.quantize_act(x, q=q, d=d)
                 tq.qgemv(w.qtype, tiles[i % R], w.K, w.N, q, d, out=y)
-            label = f"{name.rsplit('_m', 1)[0]}_m{M}"
-            nbytes = w.weight_bytes + 4 * M * w.K + 4 * M * w.N
             for i in range(5):
                 fused(i)
                 two(i)
             us_f = kernel_us(torch, fused, 50)
             us_2 = kernel_us(torch, two, 50)
             us = min(us_f, us_2)
-            res[label] = {"step_us": round(us, 3),
-                          "path": "qgemv_x (fused)" if us_f <= us_2 else "quantize_act + qgemv",
-                          "qgemv_x_us": round(us_f, 3), "quantize_act_qgemv_us": round(us_2, 3),
-                          "GB_s": round(nbytes / us / 1e3, 1),
-                          "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+            nbytes = decode_bytes(w, M, us_f <= us_2)
+            res[f"{name.rsplit('_m', 1)[0]}_m{M}"] = {
+                "step_us": round(us, 3),
+                "path": "qgemv_x (fused)" if us_f <= us_2 else "quantize_act + qgemv",
+                "qgemv_x_us": round(us_f, 3), "quantize_act_qgemv_us": round(us_2, 3),
+                "GB_s": round(nbytes / us / 1e3, 1),
+                "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
         else:
             q, d = tq.quantize_act(x)
             f = lambda i: tq.qgemm(w.qtype, tiles[i % R], w.K, w.N, q, d)
-            nbytes = w.weight_bytes + M * w.K + 2 * M * (w.K // 32) + 4 * M * w.N
             for i in range(5):
                 f(i)
             us = kernel_us(torch, f, 50)
+            nbytes = gemm_bytes(w, M)
             res[f"{name} qgemm"] = {"kernel_us": round(us, 3), "GB_s": round(nbytes / us / 1e3, 1),
-                                    "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                                     "TOPS": round(2.0 * M * w.N * w.K / us / 1e6, 2)}
     tiles_cache.clear()
     # repack of every type at the FFN shape (flat copies rotate over >= 1 GiB)
@@ -418,7 +461,8 @@ def measure_others(torch, tq, synth):
                             synth.Q4_K: "q4k"}.get(qtype, "uniform"))
         inp = synth.make_inputs(w)
         fb = inp.flat.size
-        flats = [torch.from_numpy(inp.flat).cuda() for _ in range(min(32, max(2, -(-ROTATE_BYTES // fb))))]
+        flats = [torch.from_numpy(inp.flat).cuda()
+                 for _ in range(min(32, max(2, -(-ROTATE_BYTES // fb))))]
         out = torch.empty(w.weight_bytes, dtype=torch.uint8, device="cuda")
         f = lambda i: tq.repack_tiles(qtype, flats[i % len(flats)], w.K, w.N, out=out)
         for i in range(3):
@@ -457,7 +501,7 @@ def measure_others(torch, tq, synth):
                       "flat_GB_s_of_weights": round(fb / uf / 1e3, 1)}
         if M > 8:
             res[label]["flat_TOPS"] = round(2.0 * M * w.N * w.K / uf / 1e6, 2)
-        if name.startswith("q4_0"):
+        if name.startswith("q4_0") and M == 1:
             out = torch.empty(fb, dtype=torch.uint8, device="cuda")
             fu = lambda i: tq.unpack_tiles(w.qtype, tiles[i % R], w.K, w.N, out=out)
             fu(0)
@@ -465,38 +509,47 @@ def measure_others(torch, tq, synth):
             res[f"unpack {name.rsplit('_m', 1)[0]}"] = {
                 "kernel_us": round(uu, 3), "GB_s": round((fb + w.weight_bytes) / uu / 1e3, 1)}
         del flats, tiles
-    # small-M products through tq_matmul (one decode pass per 8 rows where
-    # estimated no slower) beside the GEMM on the same tiles
-    w = synth.WORKLOADS["q8_0_gemv_k4096_n4096_m1"]
-    for qtype in (synth.Q4_0, synth.IQ4_NL):
-        wq = synth.Workload("small_m", qtype, w.K, w.N, 1, "uniform")
+    # small-M products through tq_matmul beside the GEMM on the same tiles
+    for qtype in (synth.Q4_0, synth.IQ4_NL, synth.Q8_0):
+        wq = synth.Workload("small_m", qtype, 4096, 4096, 1,
+                            "absnormal" if qtype == synth.Q8_0 else "uniform")
         inp = synth.make_inputs(wq)
-        flat = torch.from_numpy(inp.flat).cuda()
-        R = max(2, -(-ROTATE_BYTES // wq.weight_bytes))
-        tiles = [tq.repack_tiles(qtype, flat, w.K, w.N) for _ in range(R)]
-        del flat
-        for M in (16, 32):
+        tiles = rotating_tiles(torch, tq, wq, torch.from_numpy(inp.flat).cuda())
+        R = len(tiles)
+        lut = inp.lut if qtype == synth.IQ4_NL else None
+        for M in (16, 32, 64, 128):
             rng = np.random.default_rng(M)
-            x = torch.from_numpy(rng.standard_normal((M, w.K), dtype=np.float32)).cuda()
+            x = torch.from_numpy(rng.standard_normal((M, wq.K), dtype=np.float32)).cuda()
             q, d = tq.quantize_act(x)
-            y = torch.empty((M, w.N), dtype=torch.float32, device="cuda")
-            fm = lambda i: tq.matmul(qtype, tiles[i % R], w.K, w.N, q, d, lut=inp.lut, out=y)
-            fg = lambda i: tq.qgemm(qtype, tiles[i % R], w.K, w.N, q, d, lut=inp.lut, out=y)
+            y = torch.empty((M, wq.N), dtype=torch.float32, device="cuda")
+            fm = lambda i: tq.matmul(qtype, tiles[i % R], wq.K, wq.N, q, d, lut=lut, out=y)
+            fg = lambda i: tq.qgemm(qtype, tiles[i % R], wq.K, wq.N, q, d, lut=lut, out=y)
             for i in range(3):
                 fm(i)
                 fg(i)
             um, ug = kernel_us(torch, fm, 30), kernel_us(torch, fg, 30)
-            path = "decode passes" if tq.matmul_path(qtype, w.K, w.N, M) == tq.PATH_GEMV else "qgemm"
+            path = {tq.PATH_GEMV: "decode passes", tq.PATH_GEMM: "qgemm"}.get(
+                tq.matmul_path(qtype, wq.K, wq.N, M), "other")
             res[f"{synth.TYPE_NAMES[qtype]}_matmul_k4096_n4096_m{M}"] = {
-                "matmul_us": round(um, 3), "path": path, "qgemm_us": round(ug, 3)}
+                "matmul_us": round(um, 3), "path": path, "qgemm_us": round(ug, 3),
+                "TOPS": round(2.0 * M * wq.N * wq.K / um / 1e6, 2)}
         del tiles
     return res
 
 
 def launch_only(torch, tq, synth, kernel, n):
     """Launch one kernel n times, eagerly, untimed (counter collection)."""
-    if kernel == "decode":
-        f = setup_decode(torch, tq, synth)[2]
+    if kernel == "lmhead":
+        _, _, _, parts, _ = setup_headline(torch, tq, synth)
+        parts["quantize_act"](0)
+        f = parts["qgemv"]
+    elif kernel == "decode":
+        w = synth.WORKLOADS["q8_0_gemv_k4096_n4096_m1"]
+        inp = synth.make_inputs(w)
+        tiles = rotating_tiles(torch, tq, w, torch.from_numpy(inp.flat).cuda())
+        x = torch.from_numpy(inp.x).cuda()
+        y = torch.empty((1, w.N), dtype=torch.float32, device="cuda")
+        f = lambda i: tq.qgemv_x(w.qtype, tiles[i % len(tiles)], w.K, w.N, x, out=y)
     elif kernel == "gemm":
         f = setup_gemm(torch, tq, synth)[1]
     elif kernel == "repack":
@@ -531,25 +584,8 @@ def device_info(torch):
     return info
 
 
-def cpu_baseline(synth, w, seconds):
-    """The oracle as it stands (single-threaded C), timed on this host."""
-    import oracle
-    inp = synth.make_inputs(w)
-    tiles = oracle.repack(w.qtype, inp.flat, w.K, w.N)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        q, d = oracle.quantize_act(inp.x)
-        oracle.matmul(w.qtype, tiles, w.K, w.N, q, d)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(w.weight_bytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{n} full steps (quantize_act + fp64 matmul) of {w.name} in {dt:.1f} s, "
-                      "1 thread"}
-
+# ---------------------------------------------------------------------------
+# The CPU oracle, timed on this host (bounded samples of the same workloads)
 
 def host_info():
     """The host CPU the oracle baseline ran on: model name and usable threads."""
@@ -565,30 +601,104 @@ def host_info():
     return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()}
 
 
-def cpu_baseline_threads(synth, w, seconds):
-    """The same oracle on every host core: each step's output rows split into
-    one contiguous range per thread (the C calls release the GIL)."""
+def _threads():
+    return len(os.sched_getaffinity(0))
+
+
+def _split_matmul(ex, T, oracle, w, tiles, q, d, lut, n0, n1):
+    cuts = [n0 + (n1 - n0) * i // T for i in range(T + 1)]
+    list(ex.map(lambda j: oracle.matmul(w.qtype, tiles, w.K, w.N, q, d, lut,
+                                        n0=cuts[j], n1=cuts[j + 1]), range(T)))
+
+
+def cpu_baselines(synth, seconds):
+    """The oracle as it stands (plain C, fp64), on the same workloads:
+    - the headline step (quantize_act + matmul of the lm-head, M=1): full
+      steps on 1 thread for about `seconds`, and with the output rows split
+      over every host thread;
+    - the IQ4_NL M=512 GEMM: a stated subset of the 128 row-stripes on 1
+      thread, scaled to the whole product, and the whole product split over
+      every host thread;
+    - the repack of the Q4_0 FFN weights (K=4096 N=14336), 1 thread."""
     from concurrent.futures import ThreadPoolExecutor
     import oracle
-    T = len(os.sched_getaffinity(0))
+    T = _threads()
+    out = {}
+    w = synth.WORKLOADS[HEADLINE]
     inp = synth.make_inputs(w)
     tiles = oracle.repack(w.qtype, inp.flat, w.K, w.N)
-    cuts = [w.N * i // T for i in range(T + 1)]
-    n = 0
+    inp.flat = inp.codes = None
+    n, t0 = 0, time.perf_counter()
+    while True:
+        q, d = oracle.quantize_act(inp.x)
+        oracle.matmul(w.qtype, tiles, w.K, w.N, q, d)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    out["cpu_baseline"] = {
+        "value": round(w.weight_bytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+        "kind": "oracle", "ms_per_step": round(dt / n * 1e3, 1),
+        "sample": f"{n} full steps (quantize_act + fp64 matmul) of {w.name} in {dt:.1f} s, "
+                  "1 thread; GB/s of weight tiles, as value"}
     with ThreadPoolExecutor(T) as ex:
-        t0 = time.perf_counter()
+        n, t0 = 0, time.perf_counter()
         while True:
             q, d = oracle.quantize_act(inp.x)
-            list(ex.map(lambda j: oracle.matmul(w.qtype, tiles, w.K, w.N, q, d,
-                                                n0=cuts[j], n1=cuts[j + 1]), range(T)))
+            _split_matmul(ex, T, oracle, w, tiles, q, d, None, 0, w.N)
             n += 1
-            if time.perf_counter() - t0 >= seconds:
+            if time.perf_counter() - t0 >= seconds / 2:
                 break
         dt = time.perf_counter() - t0
-    return {"value": round(w.weight_bytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": T,
-            "kind": "oracle",
-            "sample": f"{n} full steps of {w.name} in {dt:.1f} s, output rows split over "
-                      f"{T} threads"}
+    out["cpu_baseline_all_cores"] = {
+        "value": round(w.weight_bytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": T,
+        "kind": "oracle", "ms_per_step": round(dt / n * 1e3, 1),
+        "sample": f"{n} full steps of {w.name} in {dt:.1f} s, output rows split over "
+                  f"{T} threads"}
+    del tiles, inp
+
+    # the GEMM (config 4): GOPS = 2 M N K / time, same formula as the GPU's
+    wg = synth.WORKLOADS["iq4_nl_gemm_m512_k4096_n4096"]
+    inp = synth.make_inputs(wg)
+    tiles = oracle.repack(wg.qtype, inp.flat, wg.K, wg.N)
+    q, d = oracle.quantize_act(inp.x, oracle.BF16)
+    stripes = 8
+    t0 = time.perf_counter()
+    oracle.matmul(wg.qtype, tiles, wg.K, wg.N, q, d, inp.lut, n0=0, n1=32 * stripes)
+    dt1 = time.perf_counter() - t0
+    ops_sub = 2.0 * wg.M * 32 * stripes * wg.K
+    with ThreadPoolExecutor(T) as ex:
+        t0 = time.perf_counter()
+        _split_matmul(ex, T, oracle, wg, tiles, q, d, inp.lut, 0, wg.N)
+        dtT = time.perf_counter() - t0
+    ops = 2.0 * wg.M * wg.N * wg.K
+    out["cpu_baseline_qgemm"] = {
+        "value": round(ops_sub / dt1 / 1e9, 3), "unit": "GOPS", "cores": 1, "kind": "oracle",
+        "scaled_full_product_s": round(dt1 * wg.N / (32 * stripes), 1),
+        "sample": f"{wg.name}: {stripes} of {wg.n_col_tiles} row-stripes (all 512 activation "
+                  f"rows) in {dt1:.1f} s on 1 thread, scaled by ops"}
+    out["cpu_baseline_qgemm_all_cores"] = {
+        "value": round(ops / dtT / 1e9, 3), "unit": "GOPS", "cores": T, "kind": "oracle",
+        "sample": f"{wg.name}: the whole product in {dtT:.1f} s, output rows split over "
+                  f"{T} threads"}
+    del tiles, inp
+
+    # the repack of config 3's weights: bytes read + written per second
+    wr = synth.WORKLOADS["q4_0_gemv_k4096_n14336_m1"]
+    inp = synth.make_inputs(wr)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.repack(wr.qtype, inp.flat, wr.K, wr.N)
+        n += 1
+        if time.perf_counter() - t0 >= seconds / 2:
+            break
+    dt = time.perf_counter() - t0
+    out["cpu_baseline_repack"] = {
+        "value": round((inp.flat.size + wr.weight_bytes) * n / dt / 1e9, 4), "unit": "GB/s",
+        "cores": 1, "kind": "oracle",
+        "sample": f"{n} repacks of {wr.name}'s Q4_0 weights in {dt:.1f} s, 1 thread "
+                  "(flat bytes read + tile bytes written)"}
+    return out
 
 
 def main():
@@ -608,38 +718,42 @@ def main():
         launch_only(torch, tq, synth, args.launch_only, args.steps)
         return
 
-    w, R, dt, det, ref = measure_gemv(torch, tq, synth, args)
+    w, R, us_step, det, ref = measure_headline(torch, tq, synth, args)
     K = args.steps
-    ms = dt / K * 1e3
-    value = w.weight_bytes / (dt / K) / 1e9
-    achieved = gemv_x_bytes(w) / det["qgemv_x_us"] / 1e3
+    value = w.weight_bytes / us_step / 1e3
+    kb = decode_bytes(w, 1, False)          # tiles + int8 q + fp16 d + fp32 y
+    achieved = kb / det["qgemv_us"] / 1e3
     line = {
         "metric": "qgemv weight-stream GB/s (% of HBM peak); qgemm int8 TOPS (% MFMA peak)",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(us_step / 1e3, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
-        "config": {"workload": w.name, "qtype": "q8_0", "K": w.K, "N": w.N, "M": w.M,
-                   "step": "quantize_act + qgemv fused (tq_qgemv_x)", "weight_copies": R,
-                   "launch": "eager" if args.eager else "hip graph",
+        "config": {"workload": w.name, "qtype": "q8_0", "K": w.K, "N": w.N, "M": 1,
+                   "step": "quantize_act + qgemv (two launches)", "weight_copies": R,
+                   "launch": "hip graph, HIP events on the replaying stream",
                    "hbm_frac_of_value": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_bytes("decode"),
-                     "kernel": "k_qgemv (fused quantize, Q8_0, M=1)",
-                     "kernel_us": round(det["qgemv_x_us"], 3),
-                     "bytes_per_launch": gemv_x_bytes(w)},
-        "decode_detail_us": {k: round(v, 3) for k, v in det.items()},
-        "decode_reference": ref,
+                     "traffic": traffic_bytes("lmhead"),
+                     "kernel": "k_qgemv (Q8_0, M=1, int8 activations)",
+                     "kernel_us": round(det["qgemv_us"], 3), "bytes_per_launch": kb},
+        "step_detail_us": {k: round(v, 3) for k, v in det.items()},
+        "step_reference": ref,
         "device": device_info(torch),
     }
+    torch.cuda.empty_cache()
     if not args.no_extra:
+        line["decode"] = measure_decodes(torch, tq, synth)
         line["qgemm"] = measure_gemm(torch, tq, synth)
+        line["qgemm_lmhead_m128"] = measure_lmhead_gemm(torch, tq, synth)
+        torch.cuda.empty_cache()
         line["qgemm_mx"] = measure_mx(torch, tq, synth)
         line["repack"] = measure_repack(torch, tq, synth)
         line["other_workloads"] = measure_others(torch, tq, synth)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(synth, w, args.cpu_seconds)
-        line["cpu_baseline_all_cores"] = cpu_baseline_threads(synth, w, args.cpu_seconds / 2)
+        cb = cpu_baselines(synth, args.cpu_seconds)
+        line["cpu_baseline"] = cb.pop("cpu_baseline")
+        line["cpu_baselines_more"] = cb
         line["host"] = host_info()
     print(json.dumps(line), flush=True)
 

@@ -149,13 +149,14 @@ def test_q8_minus128_y(tq, q8_full, fn, M):
 
 
 def _one_block_expect(isum, wsc, asc):
-    """fp32(isum * fp32(dw * da)): dw * da is exact in fp32 (two 11-bit
+    """+0 + fp32(isum * fp32(dw * da)): dw * da is exact in fp32 (two 11-bit
     significands; the smallest product 2^-48 is a normal fp32) and so is
     isum * (dw * da) in fp64 (at most 20 + 22 significant bits); the only
-    rounding is the final one to fp32."""
+    rounding is the final one to fp32.  The sum over blocks starts at +0, so
+    a zero term (a zero scale against a negative dot) gives +0, not -0."""
     sc = (wsc[None, :].astype(np.float64) * asc[:, None].astype(np.float64))
     assert np.array_equal(sc, sc.astype(np.float32).astype(np.float64))
-    return (isum[:, :, 0].astype(np.float64) * sc).astype(np.float32)
+    return (isum[:, :, 0].astype(np.float64) * sc).astype(np.float32) + np.float32(0.0)
 
 
 @pytest.mark.parametrize("qtype", [Q4_0, Q8_0, IQ4_NL, MXFP4])
