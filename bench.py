@@ -528,8 +528,8 @@ def measure_others(torch, tq, synth):
                 fm(i)
                 fg(i)
             um, ug = kernel_us(torch, fm, 30), kernel_us(torch, fg, 30)
-            path = {tq.PATH_GEMV: "decode passes", tq.PATH_GEMM: "qgemm"}.get(
-                tq.matmul_path(qtype, wq.K, wq.N, M), "other")
+            path = {tq.PATH_GEMV: "decode passes", tq.PATH_GEMM: "qgemm",
+                    tq.PATH_GEMM_SPLIT: "qgemm, K split"}[tq.matmul_path(qtype, wq.K, wq.N, M)]
             res[f"{synth.TYPE_NAMES[qtype]}_matmul_k4096_n4096_m{M}"] = {
                 "matmul_us": round(um, 3), "path": path, "qgemm_us": round(ug, 3),
                 "TOPS": round(2.0 * M * wq.N * wq.K / um / 1e6, 2)}

@@ -31,6 +31,9 @@ SIGNATURES = {
     "tq_qgemm": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_matmul": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P, SZ, P]),
     "tq_matmul_path": (INT, [INT, I64, I64, I64]),
+    "tq_matmul_workspace_bytes": (SZ, [INT, I64, I64, I64]),
+    "tq_matmul_x_workspace_bytes": (SZ, [INT, I64, I64, I64]),
+    "tq_matmul_x": (INT, [INT, P, I64, I64, INT, P, I64, I64, P, P, I64, P, SZ, P]),
     "tq_block_dots": (INT, [INT, P, I64, I64, P, I64, P, P, INT, P]),
     "tq_unpack_tiles": (INT, [INT, P, I64, I64, P, P]),
     "tq_quantize_act_mx": (INT, [INT, P, I64, I64, I64, P, P, P]),

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 
 #include "tq_internal.h"
@@ -330,25 +331,119 @@ int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
         tq::launch_qgemm(kernel_type(type), tiles, K, N, q, d, M, pack_lut(type, lut), y, ldy, nullptr, stream));
 }
 
-// tq_matmul's choice for M > 8: ceil(M / 8) decode passes of up to 8 rows
-// (each streams all weight tiles) or the GEMM (one pass, but whole 128-row
-// blocks, and with few of them too little in flight to stream the weights
-// at full rate).  Costs measured on MI355X at K = 4096: a decode pass takes
-// ~4 us plus the tiles at ~5 TB/s (~6.5 TB/s past 128 MB); a GEMM round of
-// up to 256 output blocks (one per CU) takes ~25 us, in proportion to K.
+}  // extern "C"
+
+namespace {
+
+// The cost model behind tq_matmul_path, fitted to times measured on MI355X
+// (K = 1024 .. 8192, N = 1024 .. 14336, M = 9 .. 256, every tile type):
+//   - a decode pass (one qgemv launch of up to 8 rows) takes pass_a + tile
+//     bytes / pass_bw;
+//   - a GEMM launch takes GEMM_A + steps x step_us x (1 + GEMM_LOAD x
+//     w / 256) per round of up to 256 workgroups (128 x 64 outputs each, one
+//     per compute unit), with steps = the launch's k-range / 128 and w the
+//     workgroups of a round: a step costs more when every compute unit is
+//     busy;
+//   - a K split into S ranges adds the sum of the S partial planes, SUM_A +
+//     SUM_US_PER_MB x their MB.
+struct TypeCost {
+    double pass_a, pass_bw, step_us;  // us, bytes per us, us per step of 128 k
+};
+TypeCost type_cost(int type)
+{
+    switch (type) {
+    case TQ_Q4_0: return {4.9, 6.0e6, 0.644};
+    case TQ_Q8_0: return {4.5, 6.1e6, 0.624};
+    case TQ_IQ4_NL: return {4.8, 4.3e6, 0.725};
+    case TQ_MXFP4: return {4.8, 3.7e6, 0.716};
+    default: return {4.7, 5.9e6, 0.89};                  // Q4_1, Q4_K
+    }
+}
+constexpr double GEMM_A = 4.6, GEMM_LOAD = 0.27, SUM_A = 2.2, SUM_US_PER_MB = 0.6;
+
+int64_t gemm_blocks(int64_t N, int64_t M) { return ((N + 63) / 64) * ((M + 127) / 128); }
+
+// Estimated time of the GEMM with its K split into S ranges (S = 1: none).
+double gemm_cost_us(int type, int64_t K, int64_t N, int64_t M, int S)
+{
+    const TypeCost c = type_cost(type);
+    const int64_t wgs = gemm_blocks(N, M) * S;
+    const int64_t rounds = (wgs + 255) / 256;
+    const double per_round = (double)std::min<int64_t>(wgs, 256);
+    const double steps = std::ceil((double)(K / 32) / S / 4.0);
+    double t = (double)rounds * (GEMM_A + steps * c.step_us * (1.0 + GEMM_LOAD * per_round / 256.0));
+    if (S > 1)
+        t += SUM_A + SUM_US_PER_MB * (double)S * (double)M * (double)N * 4.0 / 1e6;
+    return t;
+}
+
+// K split of the GEMM: the S in {1, 2, 4, 8} of least estimated time, each
+// range at least two steps (8 k-tiles) and the split workgroups fitting one
+// round on 256 compute units.
+int gemm_split(int type, int64_t K, int64_t N, int64_t M)
+{
+    const int64_t blocks = gemm_blocks(N, M), nkt = K / 32;
+    int best = 1;
+    double best_t = gemm_cost_us(type, K, N, M, 1);
+    for (int S = 2; S <= 8; S *= 2) {
+        if (blocks * S > 256 || nkt / S < 8)
+            break;
+        const double t = gemm_cost_us(type, K, N, M, S);
+        if (t < best_t)
+            best = S, best_t = t;
+    }
+    return best;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Workspaces of tq_matmul and tq_matmul_x: the decode K split's slots, which
+// every call leaves zero, lie in the first SLOT_REGION bytes for every shape
+// (the largest split workspace is below it); scratch (activation codes,
+// partial planes) starts after it, so that no call writes into another
+// shape's slots when calls of different shapes share one workspace.
+constexpr size_t SLOT_REGION = TQ_NOALLOC_SCRATCH_BYTES;
+
+// Bytes of tq_matmul's workspace for (type, K, N, M) and the K split S of
+// its GEMM (1: none).
+size_t matmul_ws_bytes(int type, int64_t K, int64_t N, int64_t M, int &S)
+{
+    S = 1;
+    const size_t slots = tq_qgemv_workspace_bytes(type, K, N, M < 8 ? M : 8);
+    if (M <= 8 || tq_matmul_path(type, K, N, M) != TQ_PATH_GEMM_SPLIT)
+        return slots;
+    S = gemm_split(kernel_type(type), K, N, M);
+    return SLOT_REGION + (size_t)S * (size_t)M * (size_t)N * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
 int tq_matmul_path(int type, int64_t K, int64_t N, int64_t M)
 {
     if (!valid_type(type) || !valid_tkn(type, K, N) || !valid_mk(M, K))
         return -1;
     if (M <= 8)
         return TQ_PATH_GEMV;
-    if (M > 64)
-        return TQ_PATH_GEMM;
-    const double bytes = (double)tq_tiled_bytes(type, K, N);
-    const double pass_us = 4.0 + bytes / (bytes > 128e6 ? 6.5e6 : 5.0e6);
-    const int64_t blocks = ((N + 63) / 64) * ((M + 127) / 128);
-    const double gemm_us = (double)((blocks + 255) / 256) * 25.0 * (double)K / 4096.0;
-    return (double)((M + 7) / 8) * pass_us <= gemm_us ? TQ_PATH_GEMV : TQ_PATH_GEMM;
+    const int kt = kernel_type(type);
+    const int S = gemm_split(kt, K, N, M);
+    const double gemm = gemm_cost_us(kt, K, N, M, S);
+    if (M <= 64) {
+        const TypeCost c = type_cost(kt);
+        const double pass = c.pass_a + (double)tq_tiled_bytes(type, K, N) / c.pass_bw;
+        if ((double)((M + 7) / 8) * pass <= gemm)
+            return TQ_PATH_GEMV;
+    }
+    return S > 1 ? TQ_PATH_GEMM_SPLIT : TQ_PATH_GEMM;
+}
+
+size_t tq_matmul_workspace_bytes(int type, int64_t K, int64_t N, int64_t M)
+{
+    if (!valid_type(type) || !valid_tkn(type, K, N) || !valid_mk(M, K) || N == 0 || M == 0)
+        return 0;
+    int S;
+    return matmul_ws_bytes(type, K, N, M, S);
 }
 
 int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
@@ -358,14 +453,14 @@ int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q
     if (M <= 8)
         return tq_qgemv(type, tiles, K, N, q, d, M, lut, y, ldy, workspace, workspace_bytes,
                         stream);
-    if (tq_matmul_path(type, K, N, M) == TQ_PATH_GEMV) {
-        // Decode passes of up to 8 rows each; everything is validated before
-        // the first launch.
-        int st = check_matmul(type, tiles, K, N, q, d, M, lut, y, ldy, true);
-        if (st != TQ_OK || N == 0)
-            return st;
-        if (workspace && !aligned(workspace, 256))
-            return TQ_E_ALIGN;
+    int st = check_matmul(type, tiles, K, N, q, d, M, lut, y, ldy, true);
+    if (st != TQ_OK || N == 0)
+        return st;
+    if (workspace && !aligned(workspace, 256))
+        return TQ_E_ALIGN;
+    const int path = tq_matmul_path(type, K, N, M);
+    if (path == TQ_PATH_GEMV) {
+        // decode passes of up to 8 rows each, all validated above
         const int64_t nkt = K / 32;
         for (int64_t m0 = 0; m0 < M; m0 += 8) {
             st = tq_qgemv(type, tiles, K, N, q + m0 * K, d + m0 * nkt, std::min<int64_t>(8, M - m0),
@@ -375,6 +470,99 @@ int tq_matmul(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q
         }
         return TQ_OK;
     }
+    int S = 1;
+    const size_t need = matmul_ws_bytes(type, K, N, M, S);
+    if (path == TQ_PATH_GEMM_SPLIT && workspace && workspace_bytes >= need) {
+        float *part = (float *)((uint8_t *)workspace + SLOT_REGION);
+        return launch_status(tq::launch_qgemm_split(kernel_type(type), tiles, K, N, q, d, M,
+                                                    pack_lut(type, lut), y, ldy, S, part,
+                                                    stream));
+    }
+    return tq_qgemm(type, tiles, K, N, q, d, M, lut, y, ldy, stream);
+}
+
+}  // extern "C"
+
+// tq_matmul_x: the fused decode (tq_qgemv_x) where its activation re-reads
+// stay small, else tq_quantize_act into the workspace and tq_matmul.
+namespace {
+bool matmul_x_fused(int64_t N, int64_t M) { return M <= 8 && M * ((N + 31) / 32) <= 1024; }
+
+// Workspace of tq_matmul_x: the slot region, then q, d and the GEMM's
+// partial planes (S of them, 0 without a split).
+struct XLayout {
+    size_t slots, q, d, rest, total;
+    int S;
+};
+XLayout matmul_x_layout(int type, int64_t K, int64_t N, int64_t M)
+{
+    XLayout L{};
+    L.slots = tq_qgemv_workspace_bytes(type, K, N, M < 8 ? M : 8);
+    if (matmul_x_fused(N, M)) {
+        L.total = L.slots;
+        L.S = 1;
+        return L;
+    }
+    (void)matmul_ws_bytes(type, K, N, M, L.S);
+    L.q = SLOT_REGION;
+    L.d = align256(L.q + (size_t)M * (size_t)K);
+    L.rest = align256(L.d + (size_t)M * (size_t)(K / 32) * 2);
+    L.total = L.rest + (L.S > 1 ? (size_t)L.S * (size_t)M * (size_t)N * 4 : 0);
+    return L;
+}
+}  // namespace
+
+extern "C" {
+
+size_t tq_matmul_x_workspace_bytes(int type, int64_t K, int64_t N, int64_t M)
+{
+    if (!valid_type(type) || !valid_tkn(type, K, N) || !valid_mk(M, K) || N == 0 || M == 0)
+        return 0;
+    return matmul_x_layout(type, K, N, M).total;
+}
+
+int tq_matmul_x(int type, const void *tiles, int64_t K, int64_t N, int dtype, const void *x,
+                int64_t ldx, int64_t M, const int8_t *lut, float *y, int64_t ldy,
+                void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16)
+        return TQ_E_TYPE;
+    if (ldx < K || M * ldx >= MAX_PROD)
+        return TQ_E_SHAPE;
+    // x stands in for q in the common checks; its own alignment is checked below
+    int st = check_matmul(type, tiles, K, N, (const int8_t *)tiles, nullptr, M, lut, y, ldy,
+                          false);
+    if (st != TQ_OK || M == 0 || N == 0)
+        return st;
+    if (!x)
+        return TQ_E_NULL;
+    if (!aligned(x, dtype == TQ_F32 ? 4 : 2) || (workspace && !aligned(workspace, 256)))
+        return TQ_E_ALIGN;
+    const XLayout L = matmul_x_layout(type, K, N, M);
+    if (matmul_x_fused(N, M))
+        return tq_qgemv_x(type, tiles, K, N, dtype, x, ldx, M, lut, y, ldy, workspace,
+                          workspace_bytes, stream);
+    if (!workspace)
+        return TQ_E_NULL;
+    if (workspace_bytes < L.rest)
+        return TQ_E_SHAPE;
+    uint8_t *ws = (uint8_t *)workspace;
+    int8_t *q = (int8_t *)(ws + L.q);
+    uint16_t *d = (uint16_t *)(ws + L.d);
+    st = tq_quantize_act(dtype, x, M, K, ldx, q, d, stream);
+    if (st != TQ_OK)
+        return st;
+    // tq_matmul's workspace: the slots at the front, the planes after q, d:
+    // handed over as one buffer whose slot region is the front of ours
+    if (M <= 8)
+        return tq_qgemv(type, tiles, K, N, q, d, M, lut, y, ldy, workspace, L.slots, stream);
+    const int path = tq_matmul_path(type, K, N, M);
+    if (path == TQ_PATH_GEMV)
+        return tq_matmul(type, tiles, K, N, q, d, M, lut, y, ldy, workspace, L.slots, stream);
+    if (path == TQ_PATH_GEMM_SPLIT && workspace_bytes >= L.total)
+        return launch_status(tq::launch_qgemm_split(kernel_type(type), tiles, K, N, q, d, M,
+                                                    pack_lut(type, lut), y, ldy, L.S,
+                                                    (float *)(ws + L.rest), stream));
     return tq_qgemm(type, tiles, K, N, q, d, M, lut, y, ldy, stream);
 }
 

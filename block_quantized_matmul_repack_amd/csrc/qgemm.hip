@@ -184,13 +184,14 @@ struct StageRegs {
 };
 
 // Every load is a raw buffer load issued by every thread.  Offsets past a
-// range read as zero (rows >= M, stripes past N).  A block kt >= nkt in the
-// last step reads finite bytes of the next row / stripe or zero, and its two
-// scales are forced to zero, so it adds exactly 0; so there are no branches
-// around loads and the compiler can wait for exactly the older stage.
+// range read as zero (rows >= M, stripes past N).  A block kt >= kend (the
+// end of this workgroup's k-range) in the last step reads finite bytes of
+// the next k-range, row or stripe, or zero, and its two scales are forced to
+// zero, so it adds exactly 0; so there are no branches around loads and the
+// compiler can wait for exactly the older stage.
 template <int QT, bool DOTS, int FT>
 __device__ __forceinline__ void load_step(StageRegs<QT, FT> &s, const Ranges &rg,
-                                          const Offs<QT, FT> &o, int nkt, int kt0)
+                                          const Offs<QT, FT> &o, int kend, int kt0)
 {
     constexpr int TS = Fmt<QT>::tile;
 #pragma unroll
@@ -206,8 +207,8 @@ __device__ __forceinline__ void load_step(StageRegs<QT, FT> &s, const Ranges &rg
         // zeroed for blocks past K at store time (a select here would wait
         // for the load)
         s.da = __builtin_amdgcn_raw_buffer_load_b16(rg.d, o.da + kt0 * 2, 0, 0);
-        s.da_ok = kt0 + o.kba < nkt;
-        s.dw_ok = kt0 + o.kbw < nkt;
+        s.da_ok = kt0 + o.kba < kend;
+        s.dw_ok = kt0 + o.kbw < kend;
     }
     if constexpr (FT >= 0) {
         // flat blocks: this thread's quant bytes and the block's scales
@@ -391,7 +392,8 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
                                                    const int8_t *__restrict__ q,
                                                    const uint16_t *__restrict__ d, int64_t M,
                                                    int64_t K, Lut lut, float *__restrict__ y,
-                                                   int64_t ldy, int32_t *__restrict__ isum)
+                                                   int64_t ldy, int32_t *__restrict__ isum,
+                                                   int64_t kchunk, int64_t ysplit)
 {
     __shared__ __attribute__((aligned(16))) Lds<QT> L;
 
@@ -403,7 +405,13 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
     const int64_t nct = (N + 31) / 32;
     const int64_t ct0 = (int64_t)blockIdx.x * (BN / 32);
     const int64_t m0 = (int64_t)blockIdx.y * BM;
-    const int64_t nsteps = (nkt + KB - 1) / KB;
+    // k-range of this workgroup: k-tiles [kbeg, kend) (blockIdx.z-th of the
+    // split; the whole of K without one); a split writes its own partial
+    // plane of y, ysplit elements further per range
+    const int64_t kbeg = (int64_t)blockIdx.z * kchunk;
+    const int64_t kend = min<int64_t>(kbeg + kchunk, nkt);
+    const int64_t nsteps = (kend - kbeg + KB - 1) / KB;
+    y += (int64_t)blockIdx.z * ysplit;
     constexpr int TS = Fmt<QT>::tile;
     Ranges rg;
     rg.q = make_rsrc(q + m0 * K, min<int64_t>(M - m0, BM) * K);
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
     auto epilogue = [&](int64_t kt, const v16i &dot, const v16f &sc) {
         if constexpr (DOTS) {
             const int64_t n = 32 * (ct0 + wn) + li;
-            if (kt >= 0 && kt < nkt && n < N) {
+            if (kt >= kbeg && kt < kend && n < N) {
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int64_t m = m0 + 32 * wm + 8 * (r >> 2) + 4 * lk + (r & 3);
@@ -518,23 +526,23 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
         constexpr bool ST = decltype(stage)::value;
         StageRegs<QT, FT> r0, r1;
         if constexpr (ST) {
-            load_step<QT, DOTS, FT>(r0, rg, o, (int)nkt, 0);
-            load_step<QT, DOTS, FT>(r1, rg, o, (int)nkt, KB);
+            load_step<QT, DOTS, FT>(r0, rg, o, (int)kend, (int)kbeg);
+            load_step<QT, DOTS, FT>(r1, rg, o, (int)kend, (int)kbeg + KB);
             store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
         }
         __syncthreads();
         for (int64_t step = 0; step < nsteps2; step += 2) {
             // even step: buffer 0 is computed, r1 holds step+1, r0 is free
             if constexpr (ST)
-                load_step<QT, DOTS, FT>(r0, rg, o, (int)nkt, (int)(step + 2) * KB);
-            compute(0, step, stage);
+                load_step<QT, DOTS, FT>(r0, rg, o, (int)kend, (int)(kbeg + (step + 2) * KB));
+            compute(0, kbeg / KB + step, stage);
             if constexpr (ST)
                 store_step<QT, DOTS, FT>(r1, L, 1, lut, tid);
             __syncthreads();
             // odd step: buffer 1 is computed, r0 holds step+2, r1 is free
             if constexpr (ST)
-                load_step<QT, DOTS, FT>(r1, rg, o, (int)nkt, (int)(step + 3) * KB);
-            compute(1, step + 1, stage);
+                load_step<QT, DOTS, FT>(r1, rg, o, (int)kend, (int)(kbeg + (step + 3) * KB));
+            compute(1, kbeg / KB + step + 1, stage);
             if constexpr (ST)
                 store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
             __syncthreads();
@@ -577,28 +585,70 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
     }
 }
 
+// S > 1: the K dimension split into S ranges of kchunk k-tiles (a multiple
+// of KB), range z written as partial plane z of y (ysplit elements apart,
+// row stride ldy); S = 1: the whole of K into y.
 template <int QT, int FT>
 hipError_t launch_t(const void *w, int64_t K, int64_t N, const int8_t *q, const uint16_t *d,
                     int64_t M, const Lut &lut, float *y, int64_t ldy, int32_t *isum,
-                    hipStream_t s)
+                    hipStream_t s, int S = 1, int64_t kchunk = 0, int64_t ysplit = 0)
 {
     const int64_t nkt = K / 32;
     const int64_t nct = (N + 31) / 32;
-    // x = weight blocks, y = activation blocks.  The dispatcher deals
-    // consecutive workgroup ids round-robin to the 8 XCDs, so when the x
-    // extent is a multiple of 8 all activation blocks of one weight block run
-    // on one XCD and each weight tile is fetched into a single L2.
+    if (S <= 1)
+        kchunk = nkt;
+    // x = weight blocks, y = activation blocks, z = k-ranges.  The dispatcher
+    // deals consecutive workgroup ids round-robin to the 8 XCDs, so when the
+    // x extent is a multiple of 8 all activation blocks of one weight block
+    // run on one XCD and each weight tile is fetched into a single L2.
     if (!grid_fits((nct + BN / 32 - 1) / (BN / 32), WG_THREADS) ||
-        !grid_fits((M + BM - 1) / BM, 1))
+        !grid_fits((M + BM - 1) / BM, 1) || S < 1 || S > 64)
         return hipErrorInvalidConfiguration;
-    dim3 grid((unsigned)((nct + BN / 32 - 1) / (BN / 32)), (unsigned)((M + BM - 1) / BM));
+    dim3 grid((unsigned)((nct + BN / 32 - 1) / (BN / 32)), (unsigned)((M + BM - 1) / BM),
+              (unsigned)S);
     if (isum)
         k_qgemm<QT, true, FT><<<grid, WG_THREADS, 0, s>>>((const uint8_t *)w, nkt, N, q, d, M, K,
-                                                       lut, y, ldy, isum);
+                                                       lut, y, ldy, isum, kchunk, ysplit);
     else
         k_qgemm<QT, false, FT><<<grid, WG_THREADS, 0, s>>>((const uint8_t *)w, nkt, N, q, d, M, K,
-                                                        lut, y, ldy, isum);
+                                                        lut, y, ldy, isum, kchunk, ysplit);
     return hipGetLastError();
+}
+
+// y[m * ldy + n] = sum over z < S of part[z * M * N + m * N + n], added in
+// the order z = 0, 1, ..., so the result does not depend on scheduling.
+// A thread takes 4 consecutive outputs of a row (N % 4 == 0: 16-byte plane
+// loads; ldy % 4 == 0 and y 16-byte aligned too: 16-byte stores).
+template <bool VEC>
+__global__ void k_sum_planes(const float *__restrict__ part, int64_t M, int64_t N, int S,
+                             float *__restrict__ y, int64_t ldy, bool vec_store)
+{
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    const int64_t plane = M * N;
+    if (i >= plane)
+        return;
+    if constexpr (VEC) {
+        float4 v = *(const float4 *)(part + i);
+        for (int z = 1; z < S; z++) {
+            const float4 w = *(const float4 *)(part + (int64_t)z * plane + i);
+            v.x += w.x, v.y += w.y, v.z += w.z, v.w += w.w;
+        }
+        const int64_t m = i / N, n = i - m * N;
+        float *o = y + m * ldy + n;
+        if (vec_store) {
+            *(float4 *)o = v;
+        } else {
+            o[0] = v.x, o[1] = v.y, o[2] = v.z, o[3] = v.w;
+        }
+    } else {
+        for (int e = 0; e < 4 && i + e < plane; e++) {
+            float v = part[i + e];
+            for (int z = 1; z < S; z++)
+                v += part[(int64_t)z * plane + i + e];
+            const int64_t m = (i + e) / N, n = (i + e) - m * N;
+            y[m * ldy + n] = v;
+        }
+    }
 }
 
 }  // namespace
@@ -615,6 +665,39 @@ hipError_t launch_qgemm(int type, const void *tiles, int64_t K, int64_t N, const
     case TQ_Q4_1: return launch_t<TQ_Q4_1, -1>(tiles, K, N, q, d, M, lut, y, ldy, isum, s);
     }
     return hipErrorInvalidValue;
+}
+
+// The K split of the GEMM for small output grids: S partial planes of M x N
+// fp32 in `part`, then their sum into y.
+hipError_t launch_qgemm_split(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
+                              const uint16_t *d, int64_t M, const Lut &lut, float *y, int64_t ldy,
+                              int S, float *part, hipStream_t s)
+{
+    const int64_t nkt = K / 32;
+    int64_t kchunk = (nkt + S - 1) / S;
+    kchunk = (kchunk + KB - 1) / KB * KB;
+    const int64_t plane = M * N;
+    hipError_t e;
+    switch (type) {
+    case TQ_Q4_0: e = launch_t<TQ_Q4_0, -1>(tiles, K, N, q, d, M, lut, part, N, nullptr, s, S, kchunk, plane); break;
+    case TQ_Q8_0: e = launch_t<TQ_Q8_0, -1>(tiles, K, N, q, d, M, lut, part, N, nullptr, s, S, kchunk, plane); break;
+    case TQ_IQ4_NL: e = launch_t<TQ_IQ4_NL, -1>(tiles, K, N, q, d, M, lut, part, N, nullptr, s, S, kchunk, plane); break;
+    case TQ_MXFP4: e = launch_t<TQ_MXFP4, -1>(tiles, K, N, q, d, M, lut, part, N, nullptr, s, S, kchunk, plane); break;
+    case TQ_Q4_1: e = launch_t<TQ_Q4_1, -1>(tiles, K, N, q, d, M, lut, part, N, nullptr, s, S, kchunk, plane); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess)
+        return e;
+    const int64_t blocks = (plane / 4 + 256) / 256;
+    if (!grid_fits(blocks, 256))
+        return hipErrorInvalidConfiguration;
+    if (N % 4 == 0) {
+        const bool vs = ldy % 4 == 0 && ((uintptr_t)y & 15) == 0;
+        k_sum_planes<true><<<(unsigned)blocks, 256, 0, s>>>(part, M, N, S, y, ldy, vs);
+    } else {
+        k_sum_planes<false><<<(unsigned)blocks, 256, 0, s>>>(part, M, N, S, y, ldy, false);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_qgemm_flat(int type, const void *flat, int64_t K, int64_t N, const int8_t *q,

@@ -297,6 +297,12 @@ hipError_t launch_qgemv(int type, const void *tiles, int64_t K, int64_t N, const
 hipError_t launch_qgemm(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
                         const uint16_t *d, int64_t M, const Lut &lut, float *y, int64_t ldy,
                         int32_t *isum, hipStream_t s);
+// The GEMM with K split into S ranges (S >= 2), for output grids too small
+// to fill the chip: partial planes of M x N fp32 in part (S * M * N floats),
+// then summed in a fixed order into y.
+hipError_t launch_qgemm_split(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
+                              const uint16_t *d, int64_t M, const Lut &lut, float *y, int64_t ldy,
+                              int S, float *part, hipStream_t s);
 // Flat (un-repacked) GGML blocks: unpack of tiles, and the two products.
 hipError_t launch_unpack(int type, const void *tiles, int64_t K, int64_t N, void *flat,
                          hipStream_t s);

@@ -12,7 +12,7 @@ from ._lib import TiledqError, check, lib
 
 Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1, Q4_K = 0, 1, 2, 3, 4, 5
 F32, BF16, F16 = 0, 1, 2
-PATH_GEMV, PATH_GEMM, PATH_GEMV_FLAT, PATH_GEMM_FLAT, PATH_GEMM_MX = 0, 1, 2, 3, 4
+PATH_GEMV, PATH_GEMM, PATH_GEMV_FLAT, PATH_GEMM_FLAT, PATH_GEMM_MX, PATH_GEMM_SPLIT = 0, 1, 2, 3, 4, 5
 
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
@@ -25,12 +25,16 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _need_cuda(*ts):
+def _need_cuda(*ts, out=None):
+    """Inputs must be contiguous GPU tensors; `out` a GPU tensor (its row
+    stride is passed to the library as ldy, checked by _check_out)."""
     for t in ts:
         if t is not None and not t.is_cuda:
             raise TiledqError("tiledq operates on GPU tensors only")
         if t is not None and not t.is_contiguous():
             raise TiledqError("tiledq expects contiguous tensors")
+    if out is not None and not out.is_cuda:
+        raise TiledqError("tiledq operates on GPU tensors only")
 
 
 def _nbytes(t):
@@ -175,7 +179,7 @@ def qgemv(qtype, tiles, K, N, q, d, lut=None, out=None, split=True):
     M = _check_act("tq_qgemv", q, d, K)
     _check_weights("tq_qgemv", qtype, tiles, K, N)
     _check_out("tq_qgemv", out, M, N)
-    _need_cuda(tiles, q, d, out)
+    _need_cuda(tiles, q, d, out=out)
     out = _out("tq_qgemv", q, N, out)
     st = _stream(q)
     need = lib().tq_qgemv_workspace_bytes(qtype, K, N, M) if split else 0
@@ -193,7 +197,7 @@ def qgemv_noalloc(qtype, tiles, K, N, q, d, lut=None, out=None):
     M = _check_act("tq_qgemv_noalloc", q, d, K)
     _check_weights("tq_qgemv_noalloc", qtype, tiles, K, N)
     _check_out("tq_qgemv_noalloc", out, M, N)
-    _need_cuda(tiles, q, d, out)
+    _need_cuda(tiles, q, d, out=out)
     out = _out("tq_qgemv_noalloc", q, N, out)
     check(lib().tq_qgemv_noalloc(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut),
                                  _ptr(out), out.stride(0), _stream(q)), "tq_qgemv_noalloc")
@@ -209,7 +213,7 @@ def qgemv_x(qtype, tiles, K, N, x, lut=None, out=None, split=True):
         raise TiledqError(f"qgemv_x: x has {x.shape[1]} columns, K={K}")
     _check_weights("tq_qgemv_x", qtype, tiles, K, N)
     _check_out("tq_qgemv_x", out, x.shape[0], N)
-    _need_cuda(tiles, out)
+    _need_cuda(tiles, out=out)
     if not x.is_cuda:
         raise TiledqError("tiledq operates on GPU tensors only")
     M = x.shape[0]
@@ -228,7 +232,7 @@ def qgemm(qtype, tiles, K, N, q, d, lut=None, out=None):
     M = _check_act("tq_qgemm", q, d, K)
     _check_weights("tq_qgemm", qtype, tiles, K, N)
     _check_out("tq_qgemm", out, M, N)
-    _need_cuda(tiles, q, d, out)
+    _need_cuda(tiles, q, d, out=out)
     out = _out("tq_qgemm", q, N, out)
     check(lib().tq_qgemm(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), q.shape[0], _lut_arg(lut),
                          _ptr(out), out.stride(0), _stream(q)), "tq_qgemm")
@@ -236,24 +240,48 @@ def qgemm(qtype, tiles, K, N, q, d, lut=None, out=None):
 
 
 def matmul_path(qtype, K, N, M):
-    """The path matmul takes: PATH_GEMV or PATH_GEMM."""
+    """The path matmul takes: PATH_GEMV, PATH_GEMM_SPLIT or PATH_GEMM."""
     return lib().tq_matmul_path(qtype, K, N, M)
 
 
 def matmul(qtype, tiles, K, N, q, d, lut=None, out=None):
     """y [M, N] for any M: the library picks qgemv (M <= 8), one qgemv pass
-    per 8 rows (up to 64 rows, where estimated faster: matmul_path) or qgemm."""
+    per 8 rows (up to 64 rows, where estimated faster), the GEMM with K split
+    over workgroups (small output grids) or qgemm (matmul_path)."""
     M = _check_act("tq_matmul", q, d, K)
     _check_weights("tq_matmul", qtype, tiles, K, N)
     _check_out("tq_matmul", out, M, N)
-    _need_cuda(tiles, q, d, out)
+    _need_cuda(tiles, q, d, out=out)
     out = _out("tq_matmul", q, N, out)
     st = _stream(q)
-    gemv = lib().tq_matmul_path(qtype, K, N, M) == PATH_GEMV
-    need = lib().tq_qgemv_workspace_bytes(qtype, K, N, min(M, 8)) if gemv else 0
+    need = lib().tq_matmul_workspace_bytes(qtype, K, N, M)
     ws = workspace(q.device, st.value, need) if need else None
     check(lib().tq_matmul(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut),
                           _ptr(out), out.stride(0), _ptr(ws), need, st), "tq_matmul")
+    return out
+
+
+def matmul_x(qtype, tiles, K, N, x, lut=None, out=None):
+    """y [M, N] from fp32 / bf16 / fp16 activations x [M, >=K], any M: the
+    fused decode where it is cheaper, else quantize_act into the workspace
+    followed by matmul's path."""
+    if x.dim() != 2 or x.dtype not in _DTYPES or x.stride(1) != 1:
+        raise TiledqError("matmul_x: x must be 2-D fp32, bf16 or fp16 with unit column stride")
+    if x.shape[1] < K:
+        raise TiledqError(f"matmul_x: x has {x.shape[1]} columns, K={K}")
+    M = x.shape[0]
+    _check_weights("tq_matmul_x", qtype, tiles, K, N)
+    _check_out("tq_matmul_x", out, M, N)
+    _need_cuda(tiles, out=out)
+    if not x.is_cuda:
+        raise TiledqError("tiledq operates on GPU tensors only")
+    out = _out("tq_matmul_x", x, N, out)
+    st = _stream(x)
+    need = lib().tq_matmul_x_workspace_bytes(qtype, K, N, M)
+    ws = workspace(x.device, st.value, need) if need else None
+    check(lib().tq_matmul_x(qtype, _ptr(tiles), K, N, _DTYPES[x.dtype], _ptr(x), x.stride(0), M,
+                            _lut_arg(lut), _ptr(out), out.stride(0), _ptr(ws), need, st),
+          "tq_matmul_x")
     return out
 
 
@@ -303,7 +331,7 @@ def qgemm_mx(tiles, K, N, q, e, out=None):
             q.numel() < M * K or e.numel() < M * (K // 32):
         raise TiledqError("qgemm_mx: buffer too small")
     _check_out("tq_qgemm_mx", out, M, N)
-    _need_cuda(tiles, q, e, out)
+    _need_cuda(tiles, q, e, out=out)
     out = _out("tq_qgemm_mx", q, N, out)
     check(lib().tq_qgemm_mx(_ptr(tiles), K, N, _ptr(q), _ptr(e), M, _ptr(out), out.stride(0),
                             _stream(q)), "tq_qgemm_mx")
@@ -314,7 +342,7 @@ def _flat_product(name, qtype, flat, K, N, q, d, lut, out):
     M = _check_act(name, q, d, K)
     _check_weights(name, qtype, flat, K, N, flat=True)
     _check_out(name, out, M, N)
-    _need_cuda(flat, q, d, out)
+    _need_cuda(flat, q, d, out=out)
     out = _out(name, q, N, out)
     check(getattr(lib(), name)(qtype, _ptr(flat), K, N, _ptr(q), _ptr(d), q.shape[0],
                                _lut_arg(lut), _ptr(out), out.stride(0), _stream(q)), name)

@@ -113,7 +113,8 @@ typedef enum {
  * or flat GGML blocks. */
 typedef enum {
     TQ_PATH_GEMV = 0, TQ_PATH_GEMM = 1, TQ_PATH_GEMV_FLAT = 2, TQ_PATH_GEMM_FLAT = 3,
-    TQ_PATH_GEMM_MX = 4    /* tq_qgemm_mx: MXFP4 tiles only */
+    TQ_PATH_GEMM_MX = 4,   /* tq_qgemm_mx: MXFP4 tiles only */
+    TQ_PATH_GEMM_SPLIT = 5 /* tq_matmul: the GEMM with K split over workgroups */
 } tq_path;
 
 /* Bytes of one tile ("Block-32 Quantized Formats"): 576, 1088, 576, 544,
@@ -266,25 +267,69 @@ int tq_qgemm(int type, const void *tiles, int64_t K, int64_t N,
              const int8_t *q, const uint16_t *d, int64_t M,
              const int8_t *lut, float *y, int64_t ldy, hipStream_t stream);
 
-/* The path tq_matmul takes for (type, K, N, M): TQ_PATH_GEMV for M <= 8
- * and, for 9 <= M <= 64, when ceil(M / 8) decode passes (rows 0..7, 8..15,
- * ..., each streaming all tiles) are estimated no slower than the GEMM,
- * whose whole 128-row blocks are few at such M; else TQ_PATH_GEMM (-1:
- * invalid arguments).  The estimate uses costs measured on MI355X: a decode
- * pass ~4 us plus the tiles at ~5 TB/s (~6.5 TB/s past 128 MB), a GEMM
- * round of up to 256 128x64 output blocks ~25 us x K / 4096.  Static
- * properties only. */
+/* The path tq_matmul takes for (type, K, N, M), given a workspace of
+ * tq_matmul_workspace_bytes(type, K, N, M) bytes (-1: invalid arguments):
+ *   TQ_PATH_GEMV       M <= 8: one tq_qgemv launch; 9 <= M <= 64: ceil(M / 8)
+ *                      decode passes (rows 0..7, 8..15, ...), each streaming
+ *                      all tiles, where estimated no slower than the GEMM;
+ *   TQ_PATH_GEMM_SPLIT the GEMM with K split into S ranges (S = 2, 4 or 8) when
+ *                      its 128 x 64 output blocks would leave most of the 256
+ *                      compute units idle ("Op and Kernel Development
+ *                      Guidelines" > "Work Queue and Threading": workers take
+ *                      independent chunks): each range writes a partial fp32
+ *                      plane into the workspace and a second launch adds the S
+ *                      planes in a fixed order;
+ *   TQ_PATH_GEMM       the GEMM (tq_qgemm).
+ * The estimate uses per-type costs measured on MI355X (a decode pass ~5.5 us
+ * plus the tiles at 4.5 (IQ4_NL, MXFP4) to 7.0 (Q8_0) TB/s; a GEMM round of up
+ * to 256 output blocks 29 (Q4_0) to 46 (Q4_1, Q4_K) us x K / 4096; a split
+ * round ~round / S + 2 us, plus the sum of the planes).  Static properties
+ * only. */
 int tq_matmul_path(int type, int64_t K, int64_t N, int64_t M);
 
-/* The product for any M, on the path tq_matmul_path() names: tq_qgemv
- * (with the workspace; for M > 8 one pass per 8 rows, the same workspace,
- * sized by tq_qgemv_workspace_bytes(type, K, N, 8)) or tq_qgemm.  Arguments
- * as tq_qgemv, except that M >= 0 is unbounded (TQ_E_SHAPE only for the
- * limits of the calling convention). */
+/* Bytes of workspace tq_matmul uses for (type, K, N, M) (0: none, or invalid
+ * arguments).  Layout shared by tq_matmul and tq_matmul_x: the decode K
+ * split's slots (tq_qgemv_workspace_bytes for up to 8 rows; for every shape
+ * they lie in the first TQ_NOALLOC_SCRATCH_BYTES) must be zero before the
+ * first use and are left zero by every call; scratch starts at byte
+ * TQ_NOALLOC_SCRATCH_BYTES (on TQ_PATH_GEMM_SPLIT, S * M * N fp32 partial
+ * planes) and its contents do not matter.  So one zero-filled workspace, as
+ * large as the largest call needs, serves calls of any shapes, in turn. */
+size_t tq_matmul_workspace_bytes(int type, int64_t K, int64_t N, int64_t M);
+
+/* The product for any M, on the path tq_matmul_path() names: tq_qgemv (M <= 8,
+ * or one pass per 8 rows), the split GEMM, or tq_qgemm.  Arguments as
+ * tq_qgemv, except that M >= 0 is unbounded (TQ_E_SHAPE only for the limits
+ * of the calling convention) and the workspace (256-byte aligned, layout as
+ * tq_matmul_workspace_bytes states) may be smaller than that size: without
+ * room for the planes the GEMM runs unsplit, without room for the slots the
+ * decode runs unsplit (same results up to the order of the fp32 sums).
+ * Calls sharing a workspace must not run concurrently.  Deterministic for a
+ * given workspace size. */
 int tq_matmul(int type, const void *tiles, int64_t K, int64_t N,
               const int8_t *q, const uint16_t *d, int64_t M,
               const int8_t *lut, float *y, int64_t ldy,
               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The whole product from fp32 / bf16 / fp16 activations, any M: for M <= 8
+ * with M * ceil(N / 32) <= 1024 the fused decode (tq_qgemv_x, which reads
+ * its K range of x once per 32-row stripe, cheap while that is small);
+ * otherwise tq_quantize_act into the workspace followed by tq_matmul on its
+ * path.  y is bit-identical to tq_quantize_act + tq_matmul (or tq_qgemv_x)
+ * with the same workspace regions.
+ *   dtype, x, ldx : as tq_quantize_act;  other arguments as tq_matmul.
+ *   workspace : device, 256-byte aligned, tq_matmul_x_workspace_bytes(type,
+ *     K, N, M) bytes, laid out as tq_matmul's: the decode slots (zero before
+ *     the first use, left zero), then from TQ_NOALLOC_SCRATCH_BYTES on, as
+ *     scratch, q (M * K int8), d (M * K/32 fp16) and the GEMM's planes.  The
+ *     unfused path without room for q and d returns TQ_E_SHAPE (NULL
+ *     workspace: TQ_E_NULL); without room for the planes the GEMM runs
+ *     unsplit. */
+size_t tq_matmul_x_workspace_bytes(int type, int64_t K, int64_t N, int64_t M);
+int tq_matmul_x(int type, const void *tiles, int64_t K, int64_t N,
+                int dtype, const void *x, int64_t ldx, int64_t M,
+                const int8_t *lut, float *y, int64_t ldy,
+                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Flat (un-repacked) weights ("supports_op Independence from Buffer and
  * Repack State": every supported type must work tiled and stored flat).

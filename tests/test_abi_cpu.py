@@ -166,38 +166,81 @@ def test_matmul_dispatch_validation(L):
     assert f(0, A16, 64, 32, A16, A16, 9, NUL, A16, 31, NUL, 0, NUL) == 3        # ldy < N
     assert f(0, A16, 64, 32, A16, NUL, 9, NUL, A16, 32, NUL, 0, NUL) == 1        # d NULL
     assert f(0, NUL, 64, 0, NUL, NUL, 9, NUL, NUL, 0, NUL, 0, NUL) == 0          # N == 0
-    # 9 <= M <= 16 on the two-pass GEMV path (K = 4096, N = 32): the whole
-    # call is checked before any launch
-    assert L.tq_matmul_path(0, 4096, 32, 12) == 0 and L.tq_matmul_path(2, 4096, 32, 16) == 0
-    assert f(0, A16, 4096, 32, A16, A16, 12, NUL, A16, 32, ctypes.c_void_p(0x10010), 4096,
+    # 9 <= M <= 16 on the two-pass GEMV path (K = N = 4096): the whole call
+    # is checked before any launch
+    assert L.tq_matmul_path(0, 4096, 4096, 12) == 0 and L.tq_matmul_path(2, 4096, 4096, 16) == 0
+    assert f(0, A16, 4096, 4096, A16, A16, 12, NUL, A16, 4096, ctypes.c_void_p(0x10010), 4096,
              NUL) == 4                                                            # workspace
-    assert f(0, A16, 4096, 32, A2, A16, 16, NUL, A16, 32, NUL, 0, NUL) == 4      # q
-    assert f(2, A16, 4096, 32, A16, A16, 12, NUL, A16, 32, NUL, 0, NUL) == 1     # IQ4_NL table
-    assert f(0, A16, 4096, 32, A16, A16, 16, NUL, A16, 31, NUL, 0, NUL) == 3     # ldy < N
+    assert f(0, A16, 4096, 4096, A2, A16, 16, NUL, A16, 4096, NUL, 0, NUL) == 4  # q
+    assert f(2, A16, 4096, 4096, A16, A16, 12, NUL, A16, 4096, NUL, 0, NUL) == 1  # IQ4_NL table
+    assert f(0, A16, 4096, 4096, A16, A16, 16, NUL, A16, 4095, NUL, 0, NUL) == 3  # ldy < N
+    # the split GEMM path (M = 128): checked the same way
+    assert L.tq_matmul_path(0, 4096, 4096, 128) == 5
+    assert f(0, A16, 4096, 4096, A16, A16, 128, NUL, A16, 4096, ctypes.c_void_p(0x10010), 1 << 24,
+             NUL) == 4                                                            # workspace
+    assert f(0, A16, 4096, 4096, A16, NUL, 128, NUL, A16, 4096, NUL, 0, NUL) == 1  # d NULL
 
 
 def test_matmul_path(L):
-    """tq_matmul's path: GEMV for M <= 8; for 9 <= M <= 64 one GEMV pass per
-    8 rows where their estimated cost (4 us + tiles at 5 TB/s, 6.5 past
-    128 MB, per pass) is at most the GEMM's (25 us x K / 4096 per round of
-    256 blocks); GEMM above 64 rows."""
-    G, M_ = 0, 1
+    """tq_matmul's path: GEMV for M <= 8; above, the least estimated time of
+    decode passes (9 <= M <= 64), the GEMM, and the GEMM with K split over
+    workgroups.  The expected paths are the fastest measured on MI355X for
+    these shapes (graph-replayed, per call, us): e.g. Q4_0 K=N=4096 M=16:
+    passes 12.5, split GEMM 13.8, GEMM 25.7; M=128: split 18.3, GEMM 26.3;
+    N=14336: no split fits (224 blocks), M=16 passes 21.6 vs GEMM 27.8,
+    M=32 GEMM 28.2 vs passes 43.8; K=1024 M=128: GEMM 10.4 vs split 12.4."""
+    G, GEMM, SPLIT = 0, 1, 5
     assert L.tq_matmul_path(1, 4096, 4096, 8) == G
-    assert L.tq_matmul_path(0, 4096, 4096, 12) == G            # 9.4 MB: 2 x 5.9 < 25
-    assert L.tq_matmul_path(2, 4096, 14336, 16) == G           # 33 MB: 2 x 10.6 < 25
-    assert L.tq_matmul_path(1, 4096, 14336, 12) == M_          # Q8_0, 62 MB: 2 x 16.5 > 25
-    assert L.tq_matmul_path(1, 4096, 128001, 16) == G          # 557 MB: 2 x 90 < 8 rounds x 25
-    assert L.tq_matmul_path(0, 512, 100, 12) == M_             # tiny: 2 launches > one GEMM
-    assert L.tq_matmul_path(0, 4096, 4096, 24) == G            # 3 x 5.9 < 25
-    assert L.tq_matmul_path(0, 4096, 4096, 32) == G            # 4 x 5.9 < 25
-    assert L.tq_matmul_path(0, 4096, 4096, 33) == M_           # 5 x 5.9 > 25
-    assert L.tq_matmul_path(0, 4096, 14336, 17) == M_          # 3 x 10.6 > 25
-    assert L.tq_matmul_path(0, 4096, 300, 48) == G             # 6 x 4.15 < 25
-    assert L.tq_matmul_path(0, 4096, 300, 49) == M_            # 7 x 4.15 > 25
-    assert L.tq_matmul_path(0, 8192, 32, 64) == G              # 8 x 4.03 < 50 (K = 8192)
-    assert L.tq_matmul_path(0, 8192, 32, 65) == M_             # past 64 rows: always the GEMM
+    assert L.tq_matmul_path(0, 4096, 4096, 16) == G
+    assert L.tq_matmul_path(2, 4096, 4096, 9) == G
+    assert L.tq_matmul_path(0, 4096, 4096, 32) == SPLIT
+    assert L.tq_matmul_path(0, 4096, 4096, 128) == SPLIT
+    assert L.tq_matmul_path(2, 4096, 4096, 256) == SPLIT
+    assert L.tq_matmul_path(0, 4096, 1024, 9) == SPLIT
+    assert L.tq_matmul_path(0, 4096, 14336, 16) == G
+    assert L.tq_matmul_path(0, 4096, 14336, 32) == GEMM
+    assert L.tq_matmul_path(1, 4096, 14336, 16) == GEMM
+    assert L.tq_matmul_path(0, 1024, 4096, 128) == GEMM
+    assert L.tq_matmul_path(0, 8192, 4096, 16) == G
+    assert L.tq_matmul_path(2, 8192, 4096, 128) == SPLIT
+    assert L.tq_matmul_path(2, 4096, 4096, 512) == GEMM        # 256 blocks: a full round
+    assert L.tq_matmul_path(1, 4096, 128001, 128) == GEMM      # 2001 blocks
     assert L.tq_matmul_path(9, 4096, 4096, 12) == -1
     assert L.tq_matmul_path(0, 4000 + 1, 4096, 12) == -1
+
+
+def test_matmul_workspace_bytes(L):
+    """Slots for up to 8 rows at the front (the first 1 MiB holds them for
+    every shape); on the split path 1 MiB + S * M * N fp32 planes; for
+    tq_matmul_x the unfused path adds q and d after the first 1 MiB."""
+    MiB = 1 << 20
+    for t, K, N, M in ((0, 4096, 4096, 128), (2, 4096, 1024, 9), (1, 8192, 4096, 128)):
+        assert L.tq_matmul_path(t, K, N, M) == 5
+        ws = L.tq_matmul_workspace_bytes(t, K, N, M)
+        S = (ws - MiB) // (M * N * 4)
+        assert S in (2, 4, 8) and ws == MiB + S * M * N * 4
+        wx = L.tq_matmul_x_workspace_bytes(t, K, N, M)
+        assert wx >= MiB + M * K + M * (K // 32) * 2 + S * M * N * 4
+    for t, K, N, M in ((0, 4096, 4096, 8), (0, 4096, 14336, 32), (2, 4096, 4096, 512)):
+        assert L.tq_matmul_workspace_bytes(t, K, N, M) == L.tq_qgemv_workspace_bytes(t, K, N, min(M, 8))
+    # the fused decode needs only the slots; the unfused path q and d too
+    assert L.tq_matmul_x_workspace_bytes(0, 4096, 4096, 1) == L.tq_qgemv_workspace_bytes(0, 4096, 4096, 1)
+    assert L.tq_matmul_x_workspace_bytes(0, 4096, 14336, 4) >= MiB + 4 * 4096 + 4 * 128 * 2
+    assert L.tq_matmul_workspace_bytes(9, 4096, 4096, 16) == 0
+    assert L.tq_matmul_x_workspace_bytes(0, 4096, 4096, 0) == 0
+
+
+def test_matmul_x_validation(L):
+    f = L.tq_matmul_x
+    assert f(0, A16, 64, 32, 3, A16, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 2        # dtype
+    assert f(0, A16, 64, 32, 0, A16, 63, 1, NUL, A16, 32, NUL, 0, NUL) == 3        # ldx < K
+    assert f(0, NUL, 64, 32, 0, A16, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 1        # tiles
+    assert f(0, A16, 64, 32, 0, NUL, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 1        # x
+    assert f(0, A16, 64, 32, 0, A2, 64, 1, NUL, A16, 32, NUL, 0, NUL) == 4         # fp32 x
+    assert f(0, NUL, 64, 32, 0, NUL, 64, 0, NUL, NUL, 32, NUL, 0, NUL) == 0        # M == 0
+    # the unfused path (M = 40) needs a workspace for q and d
+    assert f(0, A16, 1024, 4096, 0, A16, 1024, 40, NUL, A16, 4096, NUL, 0, NUL) == 1
+    assert f(0, A16, 1024, 4096, 0, A16, 1024, 40, NUL, A16, 4096, A16, 4096, NUL) == 3
 
 
 def test_gemv_m_limit(L):

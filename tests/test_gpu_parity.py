@@ -223,21 +223,25 @@ def test_qgemv_every_row_count(tq, qtype, M, K, N):
 @pytest.mark.parametrize("K,N", [(512, 100), (4096, 300)])
 def test_matmul_dispatch(tq, qtype, M, K, N):
     """tq_matmul is bitwise the GEMV for M <= 8, one GEMV pass per 8 rows
-    where matmul_path picks the GEMV for larger M (here at K = 4096, N = 300
-    up to 48 rows; the GEMM at K = 512, N = 100) and the GEMM otherwise;
-    each within the tolerance of the oracle."""
+    where matmul_path picks the decode passes, bitwise the GEMM where it picks
+    the GEMM, and bitwise repeatable on the split GEMM (whose fp32 sums run in
+    another order than the unsplit GEMM's); each within the tolerance of the
+    oracle."""
     inp = make(qtype, K, N, M, seed=M + 3 + K)
     tiles, tdev = _dev(inp, qtype, K, N)
     q, d = oracle.quantize_act(inp.x)
     qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
     y = tq.matmul(qtype, tdev, K, N, qd, dd, lut=LUT)
     path = tq.matmul_path(qtype, K, N, M)
-    assert path == (tq.PATH_GEMV if M <= 8 or (M <= 48 and K == 4096) else tq.PATH_GEMM)
+    assert path in (tq.PATH_GEMV, tq.PATH_GEMM, tq.PATH_GEMM_SPLIT)
+    assert (path == tq.PATH_GEMV) if M <= 8 else True
     if path == tq.PATH_GEMV:
         ref = torch.cat([tq.qgemv(qtype, tdev, K, N, qd[i:i + 8], dd[i:i + 8], lut=LUT)
                          for i in range(0, M, 8)])
-    else:
+    elif path == tq.PATH_GEMM:
         ref = tq.qgemm(qtype, tdev, K, N, qd, dd, lut=LUT)
+    else:
+        ref = tq.matmul(qtype, tdev, K, N, qd, dd, lut=LUT)
     assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
     y_ref, acond = oracle.matmul(qtype, tiles, K, N, q, d, LUT)
     check_y(y.cpu().numpy(), y_ref, acond, (qtype, M, K, N))
