@@ -101,9 +101,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true",
                    help="only the headline step (no other workloads)")
-    p.add_argument("--launch-only", choices=sorted(LAUNCH_ONLY), default=None,
+    p.add_argument("--launch-only", default=None,
                    help="no timing: launch one kernel --steps times on the bench's inputs "
-                        "(for rocprofv3 --pmc counter passes) and exit")
+                        "(for rocprofv3 --pmc counter passes) and exit: one of "
+                        + ", ".join(LAUNCH_ONLY) + ", or ffn-<type>-m<M> (the decode GEMV, "
+                        "int8 activations, on the K=4096 N=14336 weights of <type>)")
     return p.parse_args()
 
 
@@ -539,7 +541,20 @@ def measure_others(torch, tq, synth):
 
 def launch_only(torch, tq, synth, kernel, n):
     """Launch one kernel n times, eagerly, untimed (counter collection)."""
-    if kernel == "lmhead":
+    if kernel.startswith("ffn-"):
+        import numpy as np
+        _, tname, m = kernel.split("-")
+        qtype = {v: k for k, v in synth.TYPE_NAMES.items()}[tname]
+        M = int(m[1:])
+        w = synth.Workload("ffn", qtype, 4096, 14336, 1, "uniform")
+        inp = synth.make_inputs(w)
+        tiles = rotating_tiles(torch, tq, w, torch.from_numpy(inp.flat).cuda())
+        x = torch.from_numpy(np.random.default_rng(M).standard_normal((M, 4096), dtype=np.float32)).cuda()
+        q, d = tq.quantize_act(x)
+        y = torch.empty((M, w.N), dtype=torch.float32, device="cuda")
+        lut = inp.lut if qtype == synth.IQ4_NL else None
+        f = lambda i: tq.qgemv(qtype, tiles[i % len(tiles)], w.K, w.N, q, d, lut=lut, out=y)
+    elif kernel == "lmhead":
         _, _, _, parts, _ = setup_headline(torch, tq, synth)
         parts["quantize_act"](0)
         f = parts["qgemv"]
@@ -556,10 +571,12 @@ def launch_only(torch, tq, synth, kernel, n):
         f = setup_repack(torch, tq, synth)[1]
     elif kernel == "mx":
         f = setup_mx(torch, tq, synth)[1]
-    else:                                   # calibration: a plain 256 MiB copy
+    elif kernel == "copy":                  # calibration: a plain 256 MiB copy
         a = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         f = lambda i: b.copy_(a)
+    else:
+        raise SystemExit(f"unknown --launch-only kernel {kernel!r}")
     for i in range(n):
         f(i)
     torch.cuda.synchronize()

@@ -183,7 +183,9 @@ struct StageRegs {
     bool da_ok, dw_ok;        // the scales' k-blocks lie inside K
 };
 
-// Every load is a raw buffer load issued by every thread.  Offsets past a
+// Every load is a raw buffer load issued by every thread, the step's k
+// offset (uniform) in the scalar offset and the thread's own offset in the
+// vector one, so that a step adds no vector work.  Offsets past a
 // range read as zero (rows >= M, stripes past N).  A block kt >= kend (the
 // end of this workgroup's k-range) in the last step reads finite bytes of
 // the next k-range, row or stripe, or zero, and its two scales are forced to
@@ -196,7 +198,7 @@ __device__ __forceinline__ void load_step(StageRegs<QT, FT> &s, const Ranges &rg
     constexpr int TS = Fmt<QT>::tile;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rg.q, o.a[i] + kt0 * 32, 0, 0);
+        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rg.q, o.a[i], kt0 * 32, 0);
         s.a[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
     if constexpr (DOTS) {
@@ -206,7 +208,7 @@ __device__ __forceinline__ void load_step(StageRegs<QT, FT> &s, const Ranges &rg
     } else {
         // zeroed for blocks past K at store time (a select here would wait
         // for the load)
-        s.da = __builtin_amdgcn_raw_buffer_load_b16(rg.d, o.da + kt0 * 2, 0, 0);
+        s.da = __builtin_amdgcn_raw_buffer_load_b16(rg.d, o.da, kt0 * 2, 0);
         s.da_ok = kt0 + o.kba < kend;
         s.dw_ok = kt0 + o.kbw < kend;
     }
@@ -252,15 +254,15 @@ __device__ __forceinline__ void load_step(StageRegs<QT, FT> &s, const Ranges &rg
     }
     if constexpr (!DOTS) {
         if constexpr (QT == TQ_MXFP4)
-            s.dw = __builtin_amdgcn_raw_buffer_load_b8(rg.w, o.dw + kt0 * TS, 0, 0);
+            s.dw = __builtin_amdgcn_raw_buffer_load_b8(rg.w, o.dw, kt0 * TS, 0);
         else
-            s.dw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + kt0 * TS, 0, 0);
+            s.dw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw, kt0 * TS, 0);
         if constexpr (QT == TQ_Q4_1)
-            s.mw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + 2 + kt0 * TS, 0, 0);
+            s.mw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + 2, kt0 * TS, 0);
     }
 #pragma unroll
     for (int i = 0; i < Offs<QT, FT>::NWD; i++)
-        s.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rg.w, o.w[i] + kt0 * TS, 0, BUF_NT);
+        s.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rg.w, o.w[i], kt0 * TS, BUF_NT);
 }
 
 // 8 quant bytes of a flat 4-bit block half (elements 8h .. 8h + 7 in the
