@@ -52,16 +52,16 @@ HEADLINE = "q8_0_lmhead_k4096_n128001_m1"
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "lmhead": {"fetch_kib": 272119.54, "write_kib": 500.03,
-               "src": "2beef0cbad9cd442180bffefa0041c71debc773f13101dc1652c52ec158bfbb4"},
-    "decode": {"fetch_kib": 8780.32, "write_kib": 112.00,
-               "src": "2beef0cbad9cd442180bffefa0041c71debc773f13101dc1652c52ec158bfbb4"},
-    "gemm": {"fetch_kib": 13363.18, "write_kib": 8192.00,
-             "src": "cf4e64f80418ffcf75536c463148f42c21f551048dbe477e30a9d190bff3956d"},
-    "repack": {"fetch_kib": 16143.90, "write_kib": 32256.00,
-               "src": "7f60c5b9af92b655461bb894d3e2454e839c4b6ff51fe0636c10b7976b2b5183"},
-    "mx": {"fetch_kib": 12871.09, "write_kib": 8192.00,
-           "src": "e0375ab973c733c2d3825ab444b6d9baf635ebe937af40029474141d9138b660"},
+    "lmhead": {"fetch_kib": 272119.55, "write_kib": 500.03,
+               "src": "917664c5d659068137d92d6ffcba5c676b7860ade0ab890dea6357b96f09f9cb"},
+    "decode": {"fetch_kib": 8780.58, "write_kib": 112.00,
+               "src": "917664c5d659068137d92d6ffcba5c676b7860ade0ab890dea6357b96f09f9cb"},
+    "gemm": {"fetch_kib": 13369.63, "write_kib": 8192.00,
+             "src": "bd398a87427c4c8578e6fb73e778ad9e13e2efaadd94616b779067f9850205b6"},
+    "repack": {"fetch_kib": 16144.36, "write_kib": 32256.00,
+               "src": "aa5c4392af3d2dc4723e0bbb6651ec7963623d0035c70391fa9eaf5424f9433f"},
+    "mx": {"fetch_kib": 12871.42, "write_kib": 8192.00,
+           "src": "5224d553ca62a3f3ef5c6bd77699a0c8db4492954a18d083983f314824849496"},
 }
 KERNEL_SOURCES = {
     "lmhead": ("qgemv.hip", "tq_internal.h"),
