@@ -145,6 +145,30 @@ def kernel_us(torch, fn, n=200):
     return replay_us(torch, capture(torch, fn, n), n)
 
 
+def launch_stats(torch, fn, n=200):
+    """Per-launch durations: n launches enqueued one by one (no graph), a HIP
+    event recorded on the stream between consecutive launches; median, p10
+    and p90 of the n intervals."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        fn(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n))
+    return {"launches": n, "median_us": round(t[n // 2], 3), "p10_us": round(t[n // 10], 3),
+            "p90_us": round(t[(9 * n) // 10], 3),
+            "timing": "HIP event pair around each launch, launches enqueued one by one"}
+
+
+def launch_floor_us(torch):
+    """A one-element fill kernel, graph-replayed: the cost of a launch that
+    does no work."""
+    z = torch.zeros(1, dtype=torch.float32, device="cuda")
+    return round(kernel_us(torch, lambda i: z.fill_(float(i)), 200), 3)
+
+
 def rotating_tiles(torch, tq, w, flat):
     R = max(2, -(-ROTATE_BYTES // w.weight_bytes))
     return [tq.repack_tiles(w.qtype, flat, w.K, w.N) for _ in range(R)]
@@ -203,6 +227,7 @@ def measure_headline(torch, tq, synth, args):
     us_step = replay_us(torch, g, K)
     host_s = time.perf_counter() - t0
     del g
+    stats = launch_stats(torch, parts["qgemv"], 200)
     detail = {
         "qgemv_us": kernel_us(torch, parts["qgemv"], 100),
         "quantize_act_us": kernel_us(torch, parts["quantize_act"], 100),
@@ -216,8 +241,9 @@ def measure_headline(torch, tq, synth, args):
     ref = {"read_same_bytes": {"us": round(ru, 3), "GB_s": round(w.weight_bytes / ru / 1e3, 1),
                                "note": "torch row-sum over the same rotating tile copies: "
                                        "what merely reading these bytes costs"}}
+    ref["empty_launch_floor_us"] = launch_floor_us(torch)
     del rows, tiles
-    return w, R, us_step, detail, ref
+    return w, R, us_step, detail, ref, stats
 
 
 # ---------------------------------------------------------------------------
@@ -267,6 +293,10 @@ def measure_decodes(torch, tq, synth):
                           "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                           "bytes_per_step": nbytes}
             if name == "q8_0_gemv_k4096_n4096_m1":
+                warm = lambda i: tq.qgemv_x(qtype, tiles[0], K, N, xi(i), lut=lut, out=y)
+                res[label]["warm_us"] = round(kernel_us(torch, warm, 200), 3)
+                res[label]["warm_note"] = ("fused, one weight copy only (17.8 MB, resident in "
+                                           "the 256 MB MALL): not an HBM figure")
                 ku = kernel_us(torch, fused, 200)
                 nb = decode_bytes(w, M, True)
                 res[label]["roofline"] = {
@@ -633,6 +663,8 @@ def cpu_baselines(synth, seconds):
     - the headline step (quantize_act + matmul of the lm-head, M=1): full
       steps on 1 thread for about `seconds`, and with the output rows split
       over every host thread;
+    - the lm-head at M=128: 1/32 of its row-stripes on 1 thread, scaled,
+      and the whole product over every host thread;
     - the IQ4_NL M=512 GEMM: a stated subset of the 128 row-stripes on 1
       thread, scaled to the whole product, and the whole product split over
       every host thread;
@@ -672,6 +704,32 @@ def cpu_baselines(synth, seconds):
         "kind": "oracle", "ms_per_step": round(dt / n * 1e3, 1),
         "sample": f"{n} full steps of {w.name} in {dt:.1f} s, output rows split over "
                   f"{T} threads"}
+
+    # the lm-head at M = 128 (the prefill side of config 5), on the same
+    # weights: 1/32 of the stripes on 1 thread, scaled, and the whole
+    # product over every host thread
+    import numpy as np
+    M5 = 128
+    x5 = np.random.default_rng(128).standard_normal((M5, w.K), dtype=np.float32)
+    q5, d5 = oracle.quantize_act(x5)
+    sub = -(-w.n_col_tiles // 32)
+    t0 = time.perf_counter()
+    oracle.matmul(w.qtype, tiles, w.K, w.N, q5, d5, None, n0=0, n1=32 * sub)
+    dt1 = time.perf_counter() - t0
+    with ThreadPoolExecutor(T) as ex:
+        t0 = time.perf_counter()
+        _split_matmul(ex, T, oracle, w, tiles, q5, d5, None, 0, w.N)
+        dtT = time.perf_counter() - t0
+    ops5 = 2.0 * M5 * w.N * w.K
+    out["cpu_baseline_lmhead_m128"] = {
+        "value": round(2.0 * M5 * 32 * sub * w.K / dt1 / 1e9, 3), "unit": "GOPS", "cores": 1,
+        "kind": "oracle", "scaled_full_product_s": round(dt1 * w.N / (32 * sub), 1),
+        "sample": f"{w.name} at M={M5}: {sub} of {w.n_col_tiles} row-stripes in {dt1:.1f} s "
+                  "on 1 thread, scaled by ops"}
+    out["cpu_baseline_lmhead_m128_all_cores"] = {
+        "value": round(ops5 / dtT / 1e9, 3), "unit": "GOPS", "cores": T, "kind": "oracle",
+        "sample": f"{w.name} at M={M5}: the whole product in {dtT:.1f} s, output rows split "
+                  f"over {T} threads"}
     del tiles, inp
 
     # the GEMM (config 4): GOPS = 2 M N K / time, same formula as the GPU's
@@ -735,7 +793,7 @@ def main():
         launch_only(torch, tq, synth, args.launch_only, args.steps)
         return
 
-    w, R, us_step, det, ref = measure_headline(torch, tq, synth, args)
+    w, R, us_step, det, ref, stats = measure_headline(torch, tq, synth, args)
     K = args.steps
     value = w.weight_bytes / us_step / 1e3
     kb = decode_bytes(w, 1, False)          # tiles + int8 q + fp16 d + fp32 y
@@ -755,6 +813,7 @@ def main():
                      "kernel": "k_qgemv (Q8_0, M=1, int8 activations)",
                      "kernel_us": round(det["qgemv_us"], 3), "bytes_per_launch": kb},
         "step_detail_us": {k: round(v, 3) for k, v in det.items()},
+        "qgemv_launch_stats": stats,
         "step_reference": ref,
         "device": device_info(torch),
     }
