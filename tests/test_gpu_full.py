@@ -2,9 +2,10 @@
 (and so the same launch geometry, K split included) that bench.py times.
 
 Repack and quantization are compared in full, bit for bit.  y is compared in
-full where the oracle finishes in seconds (the M = 512 GEMM workloads with
-the oracle's output rows split over the host threads), else on 40 sampled
-32-row stripes (the ragged last one included).  Integer block dots are
+full where the oracle finishes in seconds to tens of seconds with its output
+rows split over the host threads (the M = 512 GEMM workloads, the lm-head
+at M = 128 and M = 1), else on 40 sampled 32-row stripes (the ragged last
+one included).  Integer block dots are
 compared on first, middle and last stripe, running the GEMV / GEMM kernel on
 that stripe's slice of the tile buffer.
 """
@@ -212,6 +213,7 @@ def test_q8_0_lmhead_n128001_m1(tq, lmhead):
 
 
 def test_q8_0_lmhead_n128001_m128(tq, lmhead):
-    """Prefill over the lm-head: sampled stripes, ragged last one included."""
-    _check_case(tq, lmhead, tq.qgemm, full_y=False)
+    """Prefill over the lm-head: every output (128 x 128001, the ragged last
+    stripe included), the oracle's rows split over the host threads."""
+    _check_case(tq, lmhead, tq.qgemm, full_y=True)
     _check_dots(tq, lmhead, tq.PATH_GEMM)
