@@ -60,8 +60,8 @@ TRAFFIC = {
              "src": "bd398a87427c4c8578e6fb73e778ad9e13e2efaadd94616b779067f9850205b6"},
     "repack": {"fetch_kib": 16144.36, "write_kib": 32256.00,
                "src": "aa5c4392af3d2dc4723e0bbb6651ec7963623d0035c70391fa9eaf5424f9433f"},
-    "mx": {"fetch_kib": 12871.42, "write_kib": 8192.00,
-           "src": "5224d553ca62a3f3ef5c6bd77699a0c8db4492954a18d083983f314824849496"},
+    "mx": {"fetch_kib": 12896.51, "write_kib": 8192.00,
+           "src": "f4a718724aa49617bb45f344f4589281ca13aa14a45ea1280f6e2e7b039b382f"},
 }
 KERNEL_SOURCES = {
     "lmhead": ("qgemv.hip", "tq_internal.h"),

@@ -372,38 +372,53 @@ __global__ __launch_bounds__(THREADS) void k_qgemm_mx(const uint8_t *__restrict_
             }
         });
     };
-    auto run_stage = [&](int buf) {
-        if (grp == 0)
-            compute(std::integral_constant<int, 0>(), buf);
-        else
-            compute(std::integral_constant<int, 1>(), buf);
-    };
 
     const int nst = (int)((nkt + SKT - 1) / SKT);
     const int nst2 = (nst + 1) & ~1;
-    StageMx r0, r1;
-    load_stage(r0, stage_ranges(qw, ew, tw, qb, eb, wb, 0), o);
-    load_stage(r1, stage_ranges(qw, ew, tw, qb, eb, wb, SKT), o);
-    store_stage(r0, L, 0, tid, 0, (int)nkt);
-    __syncthreads();
-    // The scheduling barriers keep each phase in place: hoisting a stage's LDS
+    // Each group runs its own copy of the stage loop (the same barriers).
+    // Group 0 computes a stage and then stores the next one into LDS, group
+    // 1 stores first and computes after, so that the two waves sharing a
+    // SIMD are not both waiting for LDS operands or both staging at once.
+    // Storing before computing is safe: the buffer written was last read in
+    // the previous stage, which every wave finished before the barrier.  The
+    // scheduling barriers keep each phase in place: hoisting a stage's LDS
     // stores above its MFMAs would wait for its loads a stage early.
-    for (int st = 0; st < nst2; st += 2) {
-        // even stage: buffer 0 is computed, r1 holds stage st + 1, r0 is free
-        load_stage(r0, stage_ranges(qw, ew, tw, qb, eb, wb, (int64_t)(st + 2) * SKT), o);
-        __builtin_amdgcn_sched_barrier(0);
-        run_stage(0);
-        __builtin_amdgcn_sched_barrier(0);
-        store_stage(r1, L, 1, tid, (st + 1) * SKT, (int)nkt);
+    auto run = [&](auto gr) {
+        constexpr int GR = decltype(gr)::value;
+        StageMx r0, r1;
+        load_stage(r0, stage_ranges(qw, ew, tw, qb, eb, wb, 0), o);
+        load_stage(r1, stage_ranges(qw, ew, tw, qb, eb, wb, SKT), o);
+        store_stage(r0, L, 0, tid, 0, (int)nkt);
         __syncthreads();
-        // odd stage: buffer 1 is computed, r0 holds stage st + 2, r1 is free
-        load_stage(r1, stage_ranges(qw, ew, tw, qb, eb, wb, (int64_t)(st + 3) * SKT), o);
-        __builtin_amdgcn_sched_barrier(0);
-        run_stage(1);
-        __builtin_amdgcn_sched_barrier(0);
-        store_stage(r0, L, 0, tid, (st + 2) * SKT, (int)nkt);
-        __syncthreads();
-    }
+        // compute buffer cb, store staged registers sr (stage kt0) into the other
+        auto stage = [&](int cb, const StageMx &sr, int kt0) {
+            if constexpr (GR == 0) {
+                compute(gr, cb);
+                __builtin_amdgcn_sched_barrier(0);
+                store_stage(sr, L, cb ^ 1, tid, kt0, (int)nkt);
+            } else {
+                store_stage(sr, L, cb ^ 1, tid, kt0, (int)nkt);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(gr, cb);
+            }
+        };
+        for (int st = 0; st < nst2; st += 2) {
+            // even stage: buffer 0 is computed, r1 holds stage st + 1, r0 is free
+            load_stage(r0, stage_ranges(qw, ew, tw, qb, eb, wb, (int64_t)(st + 2) * SKT), o);
+            __builtin_amdgcn_sched_barrier(0);
+            stage(0, r1, (st + 1) * SKT);
+            __syncthreads();
+            // odd stage: buffer 1 is computed, r0 holds stage st + 2, r1 is free
+            load_stage(r1, stage_ranges(qw, ew, tw, qb, eb, wb, (int64_t)(st + 3) * SKT), o);
+            __builtin_amdgcn_sched_barrier(0);
+            stage(1, r0, (st + 2) * SKT);
+            __syncthreads();
+        }
+    };
+    if (grp == 0)
+        run(std::integral_constant<int, 0>());
+    else
+        run(std::integral_constant<int, 1>());
 
     // group 1's sums to group 0 (through the activation buffers, free now)
     float *red = (float *)L.A;
