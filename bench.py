@@ -566,6 +566,30 @@ def measure_others(torch, tq, synth):
                 "matmul_us": round(um, 3), "path": path, "qgemm_us": round(ug, 3),
                 "TOPS": round(2.0 * M * wq.N * wq.K / um / 1e6, 2)}
         del tiles
+    # the block-scaled GEMM at small M: tq_matmul_mx (K split where its cost
+    # model says faster) beside the unsplit tq_qgemm_mx
+    for K, Ms in ((4096, (8, 64, 128)), (8192, (128,))):
+        wm = synth.Workload("mx_small_m", synth.MXFP4, K, 4096, 1, "e8m0")
+        inp = synth.make_inputs(wm)
+        tiles = rotating_tiles(torch, tq, wm, torch.from_numpy(inp.flat).cuda())
+        R = len(tiles)
+        for M in Ms:
+            x = torch.from_numpy(np.random.default_rng(M).standard_normal(
+                (M, K), dtype=np.float32)).cuda()
+            q, e = tq.quantize_act_mx(x)
+            y = torch.empty((M, wm.N), dtype=torch.float32, device="cuda")
+            fm = lambda i: tq.matmul_mx(tiles[i % R], K, wm.N, q, e, out=y)
+            fg = lambda i: tq.qgemm_mx(tiles[i % R], K, wm.N, q, e, out=y)
+            for i in range(3):
+                fm(i)
+                fg(i)
+            um, ug = kernel_us(torch, fm, 30), kernel_us(torch, fg, 30)
+            need = tq.lib().tq_matmul_mx_workspace_bytes(K, wm.N, M)
+            S = (need - (1 << 20)) // (M * wm.N * 4) if need else 1
+            res[f"mxfp4_matmul_mx_k{K}_n4096_m{M}"] = {
+                "matmul_mx_us": round(um, 3), "k_split": int(S), "qgemm_mx_us": round(ug, 3),
+                "TFLOPS": round(2.0 * M * wm.N * K / um / 1e6, 2)}
+        del tiles
     return res
 
 

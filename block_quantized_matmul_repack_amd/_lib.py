@@ -38,6 +38,8 @@ SIGNATURES = {
     "tq_unpack_tiles": (INT, [INT, P, I64, I64, P, P]),
     "tq_quantize_act_mx": (INT, [INT, P, I64, I64, I64, P, P, P]),
     "tq_qgemm_mx": (INT, [P, I64, I64, P, P, I64, P, I64, P]),
+    "tq_matmul_mx_workspace_bytes": (SZ, [I64, I64, I64]),
+    "tq_matmul_mx": (INT, [P, I64, I64, P, P, I64, P, I64, P, SZ, P]),
     "tq_qgemv_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_qgemm_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_matmul_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),

@@ -680,7 +680,79 @@ int tq_qgemm_mx(const void *tiles, int64_t K, int64_t N, const uint8_t *q, const
         return TQ_E_NULL;
     if (!aligned(tiles, 16) || !aligned(q, 16) || !aligned(y, 4))
         return TQ_E_ALIGN;
-    return launch_status(tq::launch_qgemm_mx(tiles, K, N, q, e, M, y, ldy, stream));
+    return launch_status(tq::launch_qgemm_mx(tiles, K, N, q, e, M, y, ldy, 1, nullptr, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// K split of the block-scaled GEMM for output grids too small to fill the
+// chip, from a cost model fitted to times measured on MI355X (K = 4096 and
+// 8192, N = 4096 and 14336, M = 8 .. 512): a launch of one round (its 64 x
+// 128 output blocks times the S ranges, at most one per compute unit) takes
+// MX_A + MX_STAGE per 256-K stage of a range, and a split adds the sum of
+// the S partial planes (SUM_A + SUM_US_PER_MB per MB read and written).
+// S = 1, 2, 4 or 8, each range at least two stages; ties keep the smaller S.
+constexpr double MX_A = 7.0, MX_STAGE = 0.77;
+int mx_split(int64_t K, int64_t N, int64_t M)
+{
+    const int64_t blocks = ((N + 127) / 128) * ((M + 63) / 64);
+    const int64_t nkt = K / 32;
+    int best = 1;
+    double best_us = 0.0;
+    for (int S = 1; S <= 8; S *= 2) {
+        if (S > 1 && (blocks * S > 256 || nkt / S < 16))
+            break;
+        const double stages = (double)((nkt + 8 * S - 1) / (8 * S));
+        double us = MX_A + MX_STAGE * stages;
+        if (S > 1)
+            us += SUM_A + SUM_US_PER_MB * (double)(S + 1) * (double)M * (double)N * 4e-6;
+        if (S == 1 || us < best_us) {
+            best = S;
+            best_us = us;
+        }
+    }
+    return best;
+}
+
+bool mx_args_valid(int64_t K, int64_t N, int64_t M)
+{
+    return valid_kn(K, N) && valid_mk(M, K);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq_matmul_mx_workspace_bytes(int64_t K, int64_t N, int64_t M)
+{
+    if (!mx_args_valid(K, N, M) || N == 0 || M == 0)
+        return 0;
+    const int S = mx_split(K, N, M);
+    return S > 1 ? SLOT_REGION + (size_t)S * (size_t)M * (size_t)N * 4 : 0;
+}
+
+int tq_matmul_mx(const void *tiles, int64_t K, int64_t N, const uint8_t *q, const uint8_t *e,
+                 int64_t M, float *y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream)
+{
+    if (!mx_args_valid(K, N, M) || ldy < N)
+        return TQ_E_SHAPE;
+    if (M == 0 || N == 0)
+        return TQ_OK;
+    if (!tiles || !q || !e || !y)
+        return TQ_E_NULL;
+    if (!aligned(tiles, 16) || !aligned(q, 16) || !aligned(y, 4) ||
+        (workspace && !aligned(workspace, 256)))
+        return TQ_E_ALIGN;
+    const int S = mx_split(K, N, M);
+    const size_t need = tq_matmul_mx_workspace_bytes(K, N, M);
+    if (S > 1 && workspace && workspace_bytes >= need) {
+        float *part = (float *)((uint8_t *)workspace + SLOT_REGION);
+        return launch_status(tq::launch_qgemm_mx(tiles, K, N, q, e, M, y, ldy, S, part, stream));
+    }
+    return launch_status(tq::launch_qgemm_mx(tiles, K, N, q, e, M, y, ldy, 1, nullptr, stream));
 }
 
 }  // extern "C"

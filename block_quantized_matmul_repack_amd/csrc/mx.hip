@@ -261,8 +261,9 @@ __device__ __forceinline__ uint32_t spread4(uint32_t n)
     return ((n * 0x00204081u) & 0x01010101u) * 0xFFu;
 }
 
+// kt0: the stage's first k-tile; tiles at kend and past are staged as zeros.
 __device__ __forceinline__ void store_stage(const StageMx &s, LdsMx &L, int buf, int tid,
-                                            int kt0, int nkt)
+                                            int kt0, int kend)
 {
 #pragma unroll
     for (int i = 0; i < NA; i++) {
@@ -285,7 +286,7 @@ __device__ __forceinline__ void store_stage(const StageMx &s, LdsMx &L, int buf,
         // then takes the votes of its chunk's 16 rows
         v4i b = s.b[i];
         const uint32_t e = s.sb[i] & 0xFFu;
-        const uint64_t keep = __builtin_amdgcn_ballot_w64(e > 112u && kt0 + j < nkt);
+        const uint64_t keep = __builtin_amdgcn_ballot_w64(e > 112u && kt0 + j < kend);
         if (keep != ~uint64_t(0)) {
             const uint32_t k = (uint32_t)(keep >> (32 * ((tid >> 5) & 1) + 16 * (ch & 1)));
             b.x &= spread4(k & 0xFu);
@@ -304,7 +305,8 @@ __global__ __launch_bounds__(THREADS) void k_qgemm_mx(const uint8_t *__restrict_
                                                       const uint8_t *__restrict__ q,
                                                       const uint8_t *__restrict__ e, int64_t M,
                                                       int64_t K, float *__restrict__ y,
-                                                      int64_t ldy)
+                                                      int64_t ldy, int64_t kchunk,
+                                                      int64_t ysplit)
 {
     __shared__ __attribute__((aligned(16))) LdsMx L;
 
@@ -316,6 +318,14 @@ __global__ __launch_bounds__(THREADS) void k_qgemm_mx(const uint8_t *__restrict_
     const int64_t ct0 = (int64_t)blockIdx.x * NSTR;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int64_t rows = min<int64_t>(M - m0, BM);
+    // k-range of this workgroup: k-tiles [kbeg, kend), the blockIdx.z-th of
+    // the split (a multiple of SKT long), the whole of K without one; a
+    // split writes its own partial plane of y, ysplit elements further per
+    // range.  Tiles past kend are staged as zeros, so a range's last stage
+    // adds nothing of the next range.
+    const int64_t kbeg = (int64_t)blockIdx.z * kchunk;
+    const int64_t kend = min<int64_t>(kbeg + kchunk, nkt);
+    y += (int64_t)blockIdx.z * ysplit;
 
     const uint8_t *qw = q + m0 * K, *ew = e + m0 * nkt, *tw = tiles + ct0 * nkt * TB;
     const int64_t qb = rows * K, eb = rows * nkt;
@@ -373,7 +383,7 @@ __global__ __launch_bounds__(THREADS) void k_qgemm_mx(const uint8_t *__restrict_
         });
     };
 
-    const int nst = (int)((nkt + SKT - 1) / SKT);
+    const int nst = (int)((kend - kbeg + SKT - 1) / SKT);
     const int nst2 = (nst + 1) & ~1;
     // Each group runs its own copy of the stage loop (the same barriers).
     // Group 0 computes a stage and then stores the next one into LDS, group
@@ -386,32 +396,32 @@ __global__ __launch_bounds__(THREADS) void k_qgemm_mx(const uint8_t *__restrict_
     auto run = [&](auto gr) {
         constexpr int GR = decltype(gr)::value;
         StageMx r0, r1;
-        load_stage(r0, stage_ranges(qw, ew, tw, qb, eb, wb, 0), o);
-        load_stage(r1, stage_ranges(qw, ew, tw, qb, eb, wb, SKT), o);
-        store_stage(r0, L, 0, tid, 0, (int)nkt);
+        load_stage(r0, stage_ranges(qw, ew, tw, qb, eb, wb, kbeg), o);
+        load_stage(r1, stage_ranges(qw, ew, tw, qb, eb, wb, kbeg + SKT), o);
+        store_stage(r0, L, 0, tid, (int)kbeg, (int)kend);
         __syncthreads();
         // compute buffer cb, store staged registers sr (stage kt0) into the other
         auto stage = [&](int cb, const StageMx &sr, int kt0) {
             if constexpr (GR == 0) {
                 compute(gr, cb);
                 __builtin_amdgcn_sched_barrier(0);
-                store_stage(sr, L, cb ^ 1, tid, kt0, (int)nkt);
+                store_stage(sr, L, cb ^ 1, tid, kt0, (int)kend);
             } else {
-                store_stage(sr, L, cb ^ 1, tid, kt0, (int)nkt);
+                store_stage(sr, L, cb ^ 1, tid, kt0, (int)kend);
                 __builtin_amdgcn_sched_barrier(0);
                 compute(gr, cb);
             }
         };
         for (int st = 0; st < nst2; st += 2) {
             // even stage: buffer 0 is computed, r1 holds stage st + 1, r0 is free
-            load_stage(r0, stage_ranges(qw, ew, tw, qb, eb, wb, (int64_t)(st + 2) * SKT), o);
+            load_stage(r0, stage_ranges(qw, ew, tw, qb, eb, wb, kbeg + (int64_t)(st + 2) * SKT), o);
             __builtin_amdgcn_sched_barrier(0);
-            stage(0, r1, (st + 1) * SKT);
+            stage(0, r1, (int)kbeg + (st + 1) * SKT);
             __syncthreads();
             // odd stage: buffer 1 is computed, r0 holds stage st + 2, r1 is free
-            load_stage(r1, stage_ranges(qw, ew, tw, qb, eb, wb, (int64_t)(st + 3) * SKT), o);
+            load_stage(r1, stage_ranges(qw, ew, tw, qb, eb, wb, kbeg + (int64_t)(st + 3) * SKT), o);
             __builtin_amdgcn_sched_barrier(0);
-            stage(1, r0, (st + 2) * SKT);
+            stage(1, r0, (int)kbeg + (st + 2) * SKT);
             __syncthreads();
         }
     };
@@ -469,14 +479,30 @@ hipError_t launch_quantize_mx(int dtype, const void *x, int64_t M, int64_t K, in
 }
 
 hipError_t launch_qgemm_mx(const void *tiles, int64_t K, int64_t N, const uint8_t *q,
-                           const uint8_t *e, int64_t M, float *y, int64_t ldy, hipStream_t s)
+                           const uint8_t *e, int64_t M, float *y, int64_t ldy, int S, float *part,
+                           hipStream_t s)
 {
     const int64_t nkt = K / 32, nct = (N + 31) / 32;
-    if (!grid_fits((nct + NSTR - 1) / NSTR, THREADS) || !grid_fits((M + BM - 1) / BM, 1))
+    if (!grid_fits((nct + NSTR - 1) / NSTR, THREADS) || !grid_fits((M + BM - 1) / BM, 1) ||
+        S < 1 || S > 64)
         return hipErrorInvalidConfiguration;
-    dim3 grid((unsigned)((nct + NSTR - 1) / NSTR), (unsigned)((M + BM - 1) / BM));
-    k_qgemm_mx<<<grid, THREADS, 0, s>>>((const uint8_t *)tiles, nkt, N, q, e, M, K, y, ldy);
-    return hipGetLastError();
+    int64_t kchunk = nkt, ysplit = 0;
+    float *out = y;
+    int64_t ldo = ldy;
+    if (S > 1) {
+        kchunk = (nkt + S - 1) / S;
+        kchunk = (kchunk + SKT - 1) / SKT * SKT;
+        ysplit = M * N;
+        out = part;
+        ldo = N;
+    }
+    dim3 grid((unsigned)((nct + NSTR - 1) / NSTR), (unsigned)((M + BM - 1) / BM), (unsigned)S);
+    k_qgemm_mx<<<grid, THREADS, 0, s>>>((const uint8_t *)tiles, nkt, N, q, e, M, K, out, ldo,
+                                        kchunk, ysplit);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess || S <= 1)
+        return err;
+    return launch_sum_planes(part, M, N, S, y, ldy, s);
 }
 
 }  // namespace tq

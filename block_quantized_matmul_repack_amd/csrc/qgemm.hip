@@ -68,8 +68,6 @@ static_assert(TQ_GEMM_KB0 >= 0 && TQ_GEMM_KB0 <= KB, "group 0 takes 0 .. KB k-bl
 #ifndef TQ_GEMM_MIN_BLOCKS
 #define TQ_GEMM_MIN_BLOCKS 1      // workgroups per CU the register budget is sized for
 #endif
-// instruction classes of __builtin_amdgcn_sched_group_barrier
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
 // A staged row holds the step's KB * 32 = 128 bytes of one activation or
 // weight row (k-block kb at bytes 32 kb ..), padded to 144 so that the 16
 // lanes of a b128 read of 16 consecutive rows hit 16 different bank groups.
@@ -690,6 +688,13 @@ hipError_t launch_qgemm_split(int type, const void *tiles, int64_t K, int64_t N,
     }
     if (e != hipSuccess)
         return e;
+    return launch_sum_planes(part, M, N, S, y, ldy, s);
+}
+
+hipError_t launch_sum_planes(const float *part, int64_t M, int64_t N, int S, float *y,
+                             int64_t ldy, hipStream_t s)
+{
+    const int64_t plane = M * N;
     const int64_t blocks = (plane / 4 + 256) / 256;
     if (!grid_fits(blocks, 256))
         return hipErrorInvalidConfiguration;

@@ -303,6 +303,10 @@ hipError_t launch_qgemm(int type, const void *tiles, int64_t K, int64_t N, const
 hipError_t launch_qgemm_split(int type, const void *tiles, int64_t K, int64_t N, const int8_t *q,
                               const uint16_t *d, int64_t M, const Lut &lut, float *y, int64_t ldy,
                               int S, float *part, hipStream_t s);
+// y[m * ldy + n] = the sum of S partial planes (M x N fp32 each, contiguous
+// in part) in the order 0, 1, ..., S - 1.
+hipError_t launch_sum_planes(const float *part, int64_t M, int64_t N, int S, float *y,
+                             int64_t ldy, hipStream_t s);
 // Flat (un-repacked) GGML blocks: unpack of tiles, and the two products.
 hipError_t launch_unpack(int type, const void *tiles, int64_t K, int64_t N, void *flat,
                          hipStream_t s);
@@ -315,7 +319,10 @@ hipError_t launch_qgemm_flat(int type, const void *flat, int64_t K, int64_t N, c
 // MXFP4 tiles x MXFP8 activations on the block-scaled matrix cores.
 hipError_t launch_quantize_mx(int dtype, const void *x, int64_t M, int64_t K, int64_t ldx,
                               uint8_t *q, uint8_t *e, hipStream_t s);
+// S >= 2 splits K into S ranges, their partial planes in part (S * M * N
+// floats), summed into y as launch_sum_planes.
 hipError_t launch_qgemm_mx(const void *tiles, int64_t K, int64_t N, const uint8_t *q,
-                           const uint8_t *e, int64_t M, float *y, int64_t ldy, hipStream_t s);
+                           const uint8_t *e, int64_t M, float *y, int64_t ldy, int S, float *part,
+                           hipStream_t s);
 
 }  // namespace tq

@@ -338,6 +338,24 @@ def qgemm_mx(tiles, K, N, q, e, out=None):
     return out
 
 
+def matmul_mx(tiles, K, N, q, e, out=None):
+    """qgemm_mx with K split over workgroups where the output grid is small
+    (tq_matmul_mx; the per-stream workspace holds the partial planes)."""
+    M = q.shape[0]
+    if tiles.numel() * tiles.element_size() < tiled_bytes(MXFP4, K, N) or \
+            q.numel() < M * K or e.numel() < M * (K // 32):
+        raise TiledqError("matmul_mx: buffer too small")
+    _check_out("tq_matmul_mx", out, M, N)
+    _need_cuda(tiles, q, e, out=out)
+    out = _out("tq_matmul_mx", q, N, out)
+    st = _stream(q)
+    need = lib().tq_matmul_mx_workspace_bytes(K, N, M)
+    ws = workspace(q.device, st.value, need) if need else None
+    check(lib().tq_matmul_mx(_ptr(tiles), K, N, _ptr(q), _ptr(e), M, _ptr(out), out.stride(0),
+                             _ptr(ws), need, st), "tq_matmul_mx")
+    return out
+
+
 def _flat_product(name, qtype, flat, K, N, q, d, lut, out):
     M = _check_act(name, q, d, K)
     _check_weights(name, qtype, flat, K, N, flat=True)

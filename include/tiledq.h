@@ -398,6 +398,28 @@ int tq_qgemm_mx(const void *tiles, int64_t K, int64_t N, const uint8_t *q,
                 const uint8_t *e, int64_t M, float *y, int64_t ldy,
                 hipStream_t stream);
 
+/* tq_qgemm_mx with the K dimension split over S = 2, 4 or 8 workgroups per
+ * output block when its 64 x 128 output blocks would leave most of the 256
+ * compute units idle (small M), as tq_matmul splits the int8 GEMM ("Op and
+ * Kernel Development Guidelines" > "Work Queue and Threading": workers take
+ * independent chunks): each range writes a partial fp32 plane into the
+ * workspace and a second launch adds the S planes in a fixed order.  The
+ * split is chosen from (K, N, M) alone, by a cost model fitted to times
+ * measured on MI355X (a split only where it is estimated faster).
+ * tq_matmul_mx_workspace_bytes: the bytes that split needs (0: no split for
+ * this shape, or invalid arguments); the layout is tq_matmul's (planes from
+ * byte TQ_NOALLOC_SCRATCH_BYTES on, the first TQ_NOALLOC_SCRATCH_BYTES
+ * untouched), so one workspace serves both.
+ * tq_matmul_mx: arguments as tq_qgemm_mx plus the workspace (device,
+ * 256-byte aligned, caller-owned); with a smaller workspace (or none) the
+ * product runs unsplit.  Deterministic for a given workspace size; split
+ * and unsplit results differ only in the order of the fp32 sums.  Calls
+ * sharing a workspace must not run concurrently. */
+size_t tq_matmul_mx_workspace_bytes(int64_t K, int64_t N, int64_t M);
+int tq_matmul_mx(const void *tiles, int64_t K, int64_t N, const uint8_t *q,
+                 const uint8_t *e, int64_t M, float *y, int64_t ldy,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Test instrument for the per-block integer dot ("Q2_0 Format" > "HVX
  * Vector Dot-Product": int8 products accumulated in 32-bit words, before the
  * row scale d of "Block-32 Quantized Formats" is applied): run the tq_qgemv

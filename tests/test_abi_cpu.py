@@ -147,6 +147,30 @@ def test_matmul_validation(L, fn):
     assert f(2, NUL, 64, 0, NUL, NUL, 4, LUT, NUL, 0, NUL) == 0
 
 
+def test_matmul_mx_validation_and_workspace(L):
+    """tq_matmul_mx checks its arguments before any launch; its workspace
+    holds S partial planes after the 1 MiB slot region, S = 2, 4 or 8 where
+    the cost model estimates the split faster (few 64 x 128 output blocks;
+    none at M = 256 or 512, N = 4096)."""
+    ws = ctypes.c_void_p(0x20000)
+    f = L.tq_matmul_mx
+    assert f(A16, 48, 32, A16, A16, 1, A16, 32, ws, 0, NUL) == 3           # K % 32
+    assert f(A16, 64, 32, A16, A16, 1, A16, 31, ws, 0, NUL) == 3           # ldy < N
+    assert f(NUL, 64, 32, A16, A16, 1, A16, 32, ws, 0, NUL) == 1
+    assert f(A16, 64, 32, A16, NUL, 1, A16, 32, ws, 0, NUL) == 1
+    assert f(A2, 64, 32, A16, A16, 1, A16, 32, ws, 0, NUL) == 4
+    assert f(A16, 64, 32, A16, A16, 1, A16, 32, ctypes.c_void_p(0x20010), 64, NUL) == 4
+    assert f(NUL, 64, 32, NUL, NUL, 0, NUL, 32, NUL, 0, NUL) == 0          # M == 0
+    W = L.tq_matmul_mx_workspace_bytes
+    assert W(4096, 4096, 512) == 0
+    assert W(4096, 4096, 128) == (1 << 20) + 4 * 128 * 4096 * 4
+    assert W(4096, 4096, 64) == (1 << 20) + 4 * 64 * 4096 * 4
+    assert W(8192, 512, 200) == (1 << 20) + 8 * 200 * 512 * 4
+    assert W(4096, 14336, 8) == (1 << 20) + 2 * 8 * 14336 * 4
+    assert W(1024, 300, 40) == 0 and W(4096, 4096, 256) == 0      # estimated no faster
+    assert W(48, 64, 8) == 0 and W(64, 64, 0) == 0
+
+
 def test_qgemv_x_validation(L):
     f = L.tq_qgemv_x
     # (type, tiles, K, N, dtype, x, ldx, M, lut, y, ldy, ws, ws_bytes, stream)

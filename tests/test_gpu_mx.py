@@ -144,6 +144,49 @@ def test_qgemm_mx_close_to_int8_path(tq):
     assert np.linalg.norm(y_mx - y_i8) / np.linalg.norm(y_i8) < 0.1
 
 
+# (K, N, M) with a small output grid: tq_matmul_mx splits K over 2 .. 8
+# workgroups per output block (partial planes summed in a fixed order)
+SPLIT_SHAPES = [(4096, 4096, 128), (4096, 4096, 64), (1024, 300, 40), (2048, 1000, 130),
+                (8192, 512, 200), (4096, 1000, 8), (512, 4096, 300)]
+
+
+@pytest.mark.parametrize("K,N,M", SPLIT_SHAPES)
+def test_matmul_mx_split(tq, K, N, M):
+    """tq_matmul_mx on its K split: within the bound (the split adds at most
+    2 S fp32 additions of partial sums: S = 8 at most), bitwise repeatable,
+    close to the unsplit tq_qgemm_mx, and the workspace's first 1 MiB (the
+    decode split's zero-kept slots, shared through the per-stream
+    workspace) still zero."""
+    from block_quantized_matmul_repack_amd import ops
+    inp = make(MXFP4, K, N, M, seed=K + N + M)
+    tiles_ref = oracle.repack(MXFP4, inp.flat, K, N)
+    qr, er = oracle.quantize_act_mx(inp.x)
+    y_ref, acond = oracle.matmul_mx(tiles_ref, K, N, qr, er)
+    tiles = torch.from_numpy(tiles_ref).cuda()
+    q, e = tq.quantize_act_mx(torch.from_numpy(inp.x).cuda())
+    need = tq.lib().tq_matmul_mx_workspace_bytes(K, N, M)
+    out = torch.full((M, N + 8), 7.0, dtype=torch.float32, device="cuda")
+    y = tq.matmul_mx(tiles, K, N, q, e, out=out[:, :N])
+    got = out.cpu().numpy()
+    assert (got[:, N:] == 7.0).all()
+    check_mx(got[:, :N], y_ref, acond, ("matmul_mx", K, N, M, need), K, adds=16)
+    y2 = tq.matmul_mx(tiles, K, N, q, e)
+    assert torch.equal(y, y2), "not bitwise repeatable"
+    y1 = tq.qgemm_mx(tiles, K, N, q, e)
+    check_mx(y1.cpu().numpy(), y_ref, acond, ("qgemm_mx", K, N, M), K)
+    torch.cuda.synchronize()
+    assert all(int(torch.count_nonzero(ws[: 1 << 20])) == 0 for ws in ops._workspaces.values())
+
+
+def test_matmul_mx_split_taken(tq):
+    L = tq.lib()
+    assert L.tq_matmul_mx_workspace_bytes(4096, 4096, 128) == (1 << 20) + 4 * 128 * 4096 * 4
+    assert L.tq_matmul_mx_workspace_bytes(4096, 4096, 64) == (1 << 20) + 4 * 64 * 4096 * 4
+    assert L.tq_matmul_mx_workspace_bytes(4096, 1000, 8) == (1 << 20) + 8 * 8 * 1000 * 4
+    assert L.tq_matmul_mx_workspace_bytes(4096, 4096, 256) == 0
+    assert L.tq_matmul_mx_workspace_bytes(4096, 4096, 512) == 0
+
+
 def test_mx_empty_shapes(tq):
     t = torch.zeros(1088, dtype=torch.uint8, device="cuda")
     q = torch.zeros((0, 64), dtype=torch.uint8, device="cuda")
