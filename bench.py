@@ -52,16 +52,16 @@ HEADLINE = "q8_0_lmhead_k4096_n128001_m1"
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "lmhead": {"fetch_kib": 272119.55, "write_kib": 500.03,
-               "src": "917664c5d659068137d92d6ffcba5c676b7860ade0ab890dea6357b96f09f9cb"},
-    "decode": {"fetch_kib": 8780.58, "write_kib": 112.00,
-               "src": "917664c5d659068137d92d6ffcba5c676b7860ade0ab890dea6357b96f09f9cb"},
-    "gemm": {"fetch_kib": 13369.63, "write_kib": 8192.00,
-             "src": "bd398a87427c4c8578e6fb73e778ad9e13e2efaadd94616b779067f9850205b6"},
-    "repack": {"fetch_kib": 16144.36, "write_kib": 32256.00,
-               "src": "aa5c4392af3d2dc4723e0bbb6651ec7963623d0035c70391fa9eaf5424f9433f"},
-    "mx": {"fetch_kib": 12896.51, "write_kib": 8192.00,
-           "src": "f4a718724aa49617bb45f344f4589281ca13aa14a45ea1280f6e2e7b039b382f"},
+    "lmhead": {"fetch_kib": 272119.95, "write_kib": 500.03,
+               "src": "ad53ea866eb34c5515a91e026471379187615e7885881c7fb0c985c43aadf0ed"},
+    "decode": {"fetch_kib": 8780.57, "write_kib": 112.00,
+               "src": "ad53ea866eb34c5515a91e026471379187615e7885881c7fb0c985c43aadf0ed"},
+    "gemm": {"fetch_kib": 13370.04, "write_kib": 8192.00,
+             "src": "025a3f49ca62001f9c0cc8d3a42ecee1e891e7e973e69b9369b6ba040f7e53e8"},
+    "repack": {"fetch_kib": 16144.57, "write_kib": 32256.00,
+               "src": "3f64a21a13e413f9a06bea162e3f0c08fdba044d1c33a65fbee512ddceafb73b"},
+    "mx": {"fetch_kib": 12897.43, "write_kib": 8192.00,
+           "src": "64cc532f3d6f55f515f24abde95a63d62e4da83367b5a3e88177db3770cb3b1b"},
 }
 KERNEL_SOURCES = {
     "lmhead": ("qgemv.hip", "tq_internal.h"),
