@@ -145,9 +145,10 @@ def test_qgemm_mx_close_to_int8_path(tq):
 
 
 # (K, N, M) with a small output grid: tq_matmul_mx splits K over 2 .. 8
-# workgroups per output block (partial planes summed in a fixed order)
+# workgroups per output block (partial planes summed in a fixed order);
+# K = 4160 (130 k-tiles) with S = 8 ranges of 24 leaves two ranges empty
 SPLIT_SHAPES = [(4096, 4096, 128), (4096, 4096, 64), (1024, 300, 40), (2048, 1000, 130),
-                (8192, 512, 200), (4096, 1000, 8), (512, 4096, 300)]
+                (8192, 512, 200), (4096, 1000, 8), (512, 4096, 300), (4160, 4096, 8)]
 
 
 @pytest.mark.parametrize("K,N,M", SPLIT_SHAPES)
