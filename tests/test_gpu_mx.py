@@ -179,6 +179,28 @@ def test_matmul_mx_split(tq, K, N, M):
     assert all(int(torch.count_nonzero(ws[: 1 << 20])) == 0 for ws in ops._workspaces.values())
 
 
+def test_matmul_mx_short_workspace_runs_unsplit(tq):
+    """With less workspace than the split needs (or none), tq_matmul_mx runs
+    the unsplit product: the same bits as tq_qgemm_mx."""
+    import ctypes
+    K, N, M = 4096, 4096, 64
+    inp = make(MXFP4, K, N, M, seed=2)
+    tiles = torch.from_numpy(oracle.repack(MXFP4, inp.flat, K, N)).cuda()
+    q, e = tq.quantize_act_mx(torch.from_numpy(inp.x).cuda())
+    need = tq.lib().tq_matmul_mx_workspace_bytes(K, N, M)
+    assert need > (1 << 20)
+    ref = tq.qgemm_mx(tiles, K, N, q, e)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    for ws_bytes in (need - 256, 0):
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        y = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+        st = tq.lib().tq_matmul_mx(P(tiles), K, N, P(q), P(e), M, P(y), N,
+                                   P(ws) if ws_bytes else None, ws_bytes, None)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), ws_bytes
+
+
 def test_matmul_mx_split_taken(tq):
     L = tq.lib()
     assert L.tq_matmul_mx_workspace_bytes(4096, 4096, 128) == (1 << 20) + 4 * 128 * 4096 * 4
