@@ -306,7 +306,39 @@ def measure_decodes(torch, tq, synth):
                     "kernel": "k_qgemv (fused quantize, Q8_0, M=1)", "kernel_us": round(ku, 3),
                     "bytes_per_launch": nb}
         del tiles
+    res["q4_0_gemv_n_sweep"] = decode_n_sweep(torch, tq, synth)
     return res
+
+
+def decode_n_sweep(torch, tq, synth):
+    """The Q4_0 decode GEMV (M = 1, K = 4096) over N = 4096 .. 32768 (128 to
+    1024 stripes on 256 compute units): the line through 256 and 512
+    stripes separates a fixed cost per launch from the marginal streaming
+    rate, which is what holds a 33 MB decode well below the HBM peak."""
+    import numpy as np
+    K = 4096
+    out = {}
+    for N in (4096, 8192, 14336, 16384, 32768):
+        w = synth.Workload("sweep", synth.Q4_0, K, N, 1, "uniform")
+        inp = synth.make_inputs(w)
+        tiles = rotating_tiles(torch, tq, w, torch.from_numpy(inp.flat).cuda())
+        R = len(tiles)
+        x = torch.from_numpy(np.random.default_rng(1).standard_normal((1, K), dtype=np.float32)).cuda()
+        q, d = tq.quantize_act(x)
+        y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        f = lambda i: tq.qgemv(w.qtype, tiles[i % R], K, N, q, d, out=y)
+        for i in range(3):
+            f(i)
+        us = min(kernel_us(torch, f, 100) for _ in range(2))
+        out[f"n{N}"] = {"stripes": w.n_col_tiles, "kernel_us": round(us, 3),
+                        "GB_s": round(w.weight_bytes / us / 1e3, 1)}
+        del tiles
+    per = (out["n16384"]["kernel_us"] - out["n8192"]["kernel_us"]) / 256     # us per stripe
+    stripe_bytes = (K // 32) * 576
+    out["fit_256_to_512_stripes"] = {
+        "fixed_us": round(out["n8192"]["kernel_us"] - 256 * per, 3),
+        "marginal_GB_s": round(stripe_bytes / per / 1e3, 1) if per > 0 else None}
+    return out
 
 
 # ---------------------------------------------------------------------------
