@@ -169,6 +169,25 @@ def launch_floor_us(torch):
     return round(kernel_us(torch, lambda i: z.fill_(float(i)), 200), 3)
 
 
+def stream_read_ref(torch, tq, tiles, nbytes, decode_us=None, n=100):
+    """The library's streaming-read instrument (tq_stream_read: 16-byte
+    nontemporal loads, one pass, nothing else) over the same rotating tile
+    copies, graph-replayed: what merely reading these bytes costs, and the
+    decode kernel's time as a fraction of it."""
+    R = len(tiles)
+    sink = torch.empty(tq.ops.STREAM_READ_BLOCKS, dtype=torch.int32, device="cuda")
+    f = lambda i: tq.stream_read(tiles[i % R], nbytes, sink=sink)
+    for i in range(3):
+        f(i)
+    us = min(kernel_us(torch, f, n) for _ in range(2))
+    out = {"us": round(us, 3), "GB_s": round(nbytes / us / 1e3, 1),
+           "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    if decode_us:
+        out["decode_rate_over_read_rate"] = round(us / decode_us, 4)
+    out["note"] = "tq_stream_read over the same rotating tile copies"
+    return out
+
+
 def rotating_tiles(torch, tq, w, flat):
     R = max(2, -(-ROTATE_BYTES // w.weight_bytes))
     return [tq.repack_tiles(w.qtype, flat, w.K, w.N) for _ in range(R)]
@@ -234,15 +253,9 @@ def measure_headline(torch, tq, synth, args):
         "fused_qgemv_x_step_us": kernel_us(torch, parts["fused"], 100),
         "host_clock_us_per_step": host_s / K * 1e6,
     }
-    # a plain read of the same rotating bytes (torch row-sum over fp32 rows)
-    rows = [t.view(torch.float32).view(-1, 1088) for t in tiles]
-    rsum = torch.empty(rows[0].shape[0], dtype=torch.float32, device="cuda")
-    ru = kernel_us(torch, lambda i: torch.sum(rows[i % R], dim=1, out=rsum), 50)
-    ref = {"read_same_bytes": {"us": round(ru, 3), "GB_s": round(w.weight_bytes / ru / 1e3, 1),
-                               "note": "torch row-sum over the same rotating tile copies: "
-                                       "what merely reading these bytes costs"}}
+    ref = {"read_same_bytes": stream_read_ref(torch, tq, tiles, w.weight_bytes, detail["qgemv_us"])}
     ref["empty_launch_floor_us"] = launch_floor_us(torch)
-    del rows, tiles
+    del tiles
     return w, R, us_step, detail, ref, stats
 
 
@@ -305,6 +318,10 @@ def measure_decodes(torch, tq, synth):
                     "traffic": traffic_bytes("decode"),
                     "kernel": "k_qgemv (fused quantize, Q8_0, M=1)", "kernel_us": round(ku, 3),
                     "bytes_per_launch": nb}
+        if name != "iq4_nl_gemv_k4096_n14336":
+            label = name if name.endswith("_m1") else f"{name}_m1"
+            res[label]["read_same_bytes"] = stream_read_ref(
+                torch, tq, tiles, w.weight_bytes, res[label]["step_us"])
         del tiles
     res["q4_0_gemv_n_sweep"] = decode_n_sweep(torch, tq, synth)
     return res
@@ -314,7 +331,9 @@ def decode_n_sweep(torch, tq, synth):
     """The Q4_0 decode GEMV (M = 1, K = 4096) over N = 4096 .. 32768 (128 to
     1024 stripes on 256 compute units): the line through 256 and 512
     stripes separates a fixed cost per launch from the marginal streaming
-    rate, which is what holds a 33 MB decode well below the HBM peak."""
+    rate, which is what holds a 33 MB decode well below the HBM peak.  The
+    streaming-read instrument over the same bytes gets the same fit: the
+    fixed cost a plain read of these sizes pays too."""
     import numpy as np
     K = 4096
     out = {}
@@ -330,14 +349,19 @@ def decode_n_sweep(torch, tq, synth):
         for i in range(3):
             f(i)
         us = min(kernel_us(torch, f, 100) for _ in range(2))
+        rd = stream_read_ref(torch, tq, tiles, w.weight_bytes)
         out[f"n{N}"] = {"stripes": w.n_col_tiles, "kernel_us": round(us, 3),
-                        "GB_s": round(w.weight_bytes / us / 1e3, 1)}
+                        "GB_s": round(w.weight_bytes / us / 1e3, 1),
+                        "read_same_bytes_us": rd["us"], "read_GB_s": rd["GB_s"]}
         del tiles
-    per = (out["n16384"]["kernel_us"] - out["n8192"]["kernel_us"]) / 256     # us per stripe
     stripe_bytes = (K // 32) * 576
-    out["fit_256_to_512_stripes"] = {
-        "fixed_us": round(out["n8192"]["kernel_us"] - 256 * per, 3),
-        "marginal_GB_s": round(stripe_bytes / per / 1e3, 1) if per > 0 else None}
+
+    def fit(key):
+        per = (out["n16384"][key] - out["n8192"][key]) / 256     # us per stripe
+        return {"fixed_us": round(out["n8192"][key] - 256 * per, 3),
+                "marginal_GB_s": round(stripe_bytes / per / 1e3, 1) if per > 0 else None}
+    out["fit_256_to_512_stripes"] = fit("kernel_us")
+    out["read_fit_256_to_512_stripes"] = fit("read_same_bytes_us")
     return out
 
 

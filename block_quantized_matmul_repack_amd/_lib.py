@@ -40,6 +40,7 @@ SIGNATURES = {
     "tq_qgemm_mx": (INT, [P, I64, I64, P, P, I64, P, I64, P]),
     "tq_matmul_mx_workspace_bytes": (SZ, [I64, I64, I64]),
     "tq_matmul_mx": (INT, [P, I64, I64, P, P, I64, P, I64, P, SZ, P]),
+    "tq_stream_read": (INT, [P, SZ, P, P]),
     "tq_qgemv_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_qgemm_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),
     "tq_matmul_flat": (INT, [INT, P, I64, I64, P, P, I64, P, P, I64, P]),

@@ -397,3 +397,23 @@ def block_dots(qtype, tiles, K, N, q, lut=None, path=PATH_GEMV, out=None):
     check(lib().tq_block_dots(qtype, _ptr(tiles), K, N, _ptr(q), M, _lut_arg(lut), _ptr(out),
                               path, _stream(q)), "tq_block_dots")
     return out
+
+
+STREAM_READ_BLOCKS = 2048       # TQ_STREAM_READ_BLOCKS: words of the sink
+
+
+def stream_read(buf, nbytes=None, sink=None):
+    """Measurement instrument: read the first `nbytes` bytes of `buf` (all of
+    it by default) once with the library's streaming-read kernel.  Returns
+    the int32 sink [STREAM_READ_BLOCKS]; the XOR of its words is the XOR of
+    every 32-bit word read."""
+    nbytes = _nbytes(buf) if nbytes is None else nbytes
+    _need_bytes("tq_stream_read", "buf", buf, nbytes)
+    if sink is not None and sink.dtype != torch.int32:
+        raise TiledqError("tq_stream_read: sink must be int32")
+    _need_bytes("tq_stream_read", "sink", sink, 4 * STREAM_READ_BLOCKS)
+    _need_cuda(buf, sink)
+    if sink is None:
+        sink = torch.empty(STREAM_READ_BLOCKS, dtype=torch.int32, device=buf.device)
+    check(lib().tq_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf)), "tq_stream_read")
+    return sink

@@ -436,6 +436,22 @@ int tq_block_dots(int type, const void *tiles, int64_t K, int64_t N,
                   const int8_t *q, int64_t M, const int8_t *lut,
                   int32_t *isum, int path, hipStream_t stream);
 
+/* Measurement instrument, outside the product path: the achievable HBM read
+ * rate that the decode's weight stream ("Tiled Weight Formats": a stripe's
+ * tiles are one contiguous byte range, streamed once per call) is compared
+ * with.  Reads `bytes` bytes at `src` once, with 16-byte nontemporal loads
+ * in a grid-stride loop over TQ_STREAM_READ_BLOCKS workgroups of 256
+ * work-items, and writes to sink[b] the XOR of the 32-bit words workgroup b
+ * read, so the XOR of the TQ_STREAM_READ_BLOCKS sink words is the XOR of
+ * every 32-bit word of the buffer.
+ *   src  : device, 16-byte aligned; bytes a multiple of 16 (else TQ_E_ALIGN,
+ *          TQ_E_SHAPE).
+ *   sink : device uint32[TQ_STREAM_READ_BLOCKS], 4-byte aligned, caller-owned;
+ *          every word is written.
+ * bytes == 0: TQ_OK, no launch, sink untouched. */
+#define TQ_STREAM_READ_BLOCKS 2048
+int tq_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

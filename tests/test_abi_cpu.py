@@ -420,6 +420,11 @@ def test_binding_rejects_short_buffers_before_launch():
     _raises(lambda: tq.unpack_tiles(tq.Q4_0, short, K, N), size)
     _raises(lambda: tq.unpack_tiles(tq.Q4_0, tiles, K, N, out=flat[:-1]), size)
     _raises(lambda: tq.repack_tiles(tq.Q4_0, flat, K, N, out=tiles), gpu)
+    sink = torch.zeros(tq.ops.STREAM_READ_BLOCKS, dtype=torch.int32)
+    _raises(lambda: tq.stream_read(tiles, tb + 16), size)
+    _raises(lambda: tq.stream_read(tiles, sink=sink[:-1]), size)
+    _raises(lambda: tq.stream_read(tiles, sink=sink.float()), size)
+    _raises(lambda: tq.stream_read(tiles, sink=sink), gpu)
 
 
 def test_noalloc_scratch_covers_every_split(L):
@@ -436,3 +441,16 @@ def test_noalloc_scratch_covers_every_split(L):
             for M in (1, 8):
                 worst = max(worst, L.tq_qgemv_workspace_bytes(0, K, 32 * nct, M))
     assert 0 < worst <= cap
+
+
+def test_stream_read_validation(L):
+    """The streaming-read instrument rejects bad arguments on the host: the
+    byte count is checked first, an empty read is OK with no launch, then
+    pointers and alignment."""
+    V = ctypes.c_void_p
+    assert L.tq_stream_read(None, 0, None, None) == 0
+    assert L.tq_stream_read(V(4096), 20, V(4096), None) == 3       # not whole 16-byte chunks
+    assert L.tq_stream_read(None, 16, V(4096), None) == 1
+    assert L.tq_stream_read(V(4096), 16, None, None) == 1
+    assert L.tq_stream_read(V(4104), 16, V(4096), None) == 4       # src not 16-byte aligned
+    assert L.tq_stream_read(V(4096), 16, V(4098), None) == 4       # sink not 4-byte aligned
