@@ -45,7 +45,7 @@ __global__ __launch_bounds__(THREADS) void k_stream_read(const v4u *__restrict__
 
 extern "C" int tq_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream)
 {
-    if (bytes % 16 != 0 || bytes / 16 > (size_t)INT64_MAX)
+    if (bytes % 16 != 0)
         return TQ_E_SHAPE;
     if (bytes == 0)
         return TQ_OK;
