@@ -36,15 +36,21 @@ def _k(qtype, K):
 
 @pytest.mark.parametrize("qtype", TYPES[:5])
 @pytest.mark.parametrize("K,N", [(32, 1), (96, 33), (512, 65), (4096, 100)])
-def test_unpack_roundtrip(tq, qtype, K, N):
+@pytest.mark.parametrize("shift", [False, True])
+def test_unpack_roundtrip(tq, qtype, K, N, shift):
+    """Every byte of the flat buffer comes back, and nothing around it is
+    written.  shift: the output starts at the smallest offset the type's
+    alignment allows (2 or 4 bytes), so that each row's run of blocks is
+    written with narrower stores than from an aligned start."""
     inp = make(qtype, K, N, 1, seed=K + N)
     tiles = torch.from_numpy(oracle.repack(qtype, inp.flat, K, N)).cuda()
-    out = torch.full((inp.flat.size + 64,), 0xA5, dtype=torch.uint8, device="cuda")
-    tq.unpack_tiles(qtype, tiles, K, N, out=out[:inp.flat.size])
+    off = (4 if qtype in (synth.MXFP4, synth.Q4_1) else 2) if shift else 0
+    out = torch.full((inp.flat.size + 64 + off,), 0xA5, dtype=torch.uint8, device="cuda")
+    tq.unpack_tiles(qtype, tiles, K, N, out=out[off:off + inp.flat.size])
     got = out.cpu().numpy()
-    bad = np.nonzero(got[:inp.flat.size] != inp.flat)[0]
-    assert bad.size == 0, [(int(b), int(got[b]), int(inp.flat[b])) for b in bad[:8]]
-    assert (got[inp.flat.size:] == 0xA5).all()
+    bad = np.nonzero(got[off:off + inp.flat.size] != inp.flat)[0]
+    assert bad.size == 0, [(int(b), int(got[off + b]), int(inp.flat[b])) for b in bad[:8]]
+    assert (got[:off] == 0xA5).all() and (got[off + inp.flat.size:] == 0xA5).all()
 
 
 @pytest.mark.parametrize("qtype", TYPES)
