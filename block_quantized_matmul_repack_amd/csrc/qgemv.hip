@@ -129,9 +129,8 @@ __device__ __forceinline__ v4i_t tile_operand(const uint8_t *tile, int off, cons
     for (int i = 0; i < 2; i++) {
         const uint32_t x = (uint32_t)w[i];
         if constexpr (QT == TQ_Q4_0) {
-            const uint32_t t = x ^ 0x88888888u;
-            lo[i] = (t << 4) & 0xF0F0F0F0u;
-            hi[i] = t & 0xF0F0F0F0u;
+            lo[i] = ((x << 4) ^ 0x80808080u) & 0xF0F0F0F0u;
+            hi[i] = (x ^ 0x80808080u) & 0xF0F0F0F0u;
         } else if constexpr (QT == TQ_Q4_1) {
             lo[i] = x & 0x0F0F0F0Fu;
             hi[i] = (x >> 4) & 0x0F0F0F0Fu;
@@ -318,9 +317,10 @@ __device__ __forceinline__ void block_dots(int (&s)[MM], const TileRegs<QT> &w,
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             if constexpr (QT == TQ_Q4_0) {
-                const uint32_t t = tr[j] ^ 0x88888888u;       // nibble c -> c - 8 (4-bit two's complement)
-                ev[j] = (t << 4) & 0xF0F0F0F0u;               // 16 * (even-column code - 8)
-                od[j] = t & 0xF0F0F0F0u;                      // 16 * (odd-column code - 8)
+                // nibble c in the high half of a byte, its top bit flipped:
+                // the byte is 16 * (c - 8) (4-bit two's complement)
+                ev[j] = ((tr[j] << 4) ^ 0x80808080u) & 0xF0F0F0F0u;   // even column
+                od[j] = (tr[j] ^ 0x80808080u) & 0xF0F0F0F0u;          // odd column
             } else if constexpr (QT == TQ_Q4_1) {
                 ev[j] = tr[j] & 0x0F0F0F0Fu;                  // the codes themselves
                 od[j] = (tr[j] >> 4) & 0x0F0F0F0Fu;
@@ -355,14 +355,15 @@ struct Unit {
     v4u c[SLOTS];
 };
 
+// Every chunk of the unit is stored: a tile missing from the workgroup's
+// range (the second of a last, odd unit) was loaded as zeros.
 template <int QT>
-__device__ __forceinline__ void store_unit(const Unit<QT> &u, uint8_t *dst, int valid_chunks,
-                                           int lane)
+__device__ __forceinline__ void store_unit(const Unit<QT> &u, uint8_t *dst, int lane)
 {
 #pragma unroll
     for (int i = 0; i < Unit<QT>::SLOTS; i++) {
         const int ch = i * 64 + lane;
-        if (ch < valid_chunks)
+        if (ch < Unit<QT>::CHUNKS)
             *((v4u *)dst + ch) = u.c[i];
     }
 }
@@ -393,7 +394,8 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     __shared__ float red[NSLOT][MM][32];
     __shared__ __attribute__((aligned(16))) uint32_t zero16[4];   // A rows past M
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, l = lane & 31;
     const int hs = 2 * wave + half;                       // half-wave slot in the workgroup
     const int64_t ct = blockIdx.x / S;
@@ -426,10 +428,14 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
 
     uint8_t *my = stage[wave];
     const int tro = tr8_offset(lane);                     // matrix-core path only
-    // Weight loads are raw buffer loads over this workgroup's tiles: a unit
-    // or chunk past the range gets offset BUF_OOB, which returns zeros and
-    // moves no data, so every load is issued unconditionally.
+    // Weight loads are raw buffer loads over this workgroup's tiles: an
+    // offset at or past the range's end returns zeros and moves no data, so
+    // every load is issued unconditionally.
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(cbase, (int64_t)nt * TS);
+    int chunk_off[Unit<QT>::SLOTS];                       // this lane's chunk of a unit
+#pragma unroll
+    for (int s = 0; s < Unit<QT>::SLOTS; s++)
+        chunk_off[s] = s * 64 + lane < Unit<QT>::CHUNKS ? 16 * (s * 64 + lane) : BUF_OOB;
     // The chunk is processed in passes of up to P tiles.  Each pass first
     // stages the pass's int8 activations and scales of all M rows in LDS
     // (layout at lds_act), so the unit loop has only weight loads in flight.
@@ -460,18 +466,18 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
         const int nunits = (pn + 1) >> 1;
         const int count = wave < nunits ? (nunits - 1 - wave) / NW + 1 : 0;   // units of this wave
         // the wave's i-th unit of the pass (i >= count: nothing)
+        // The unit's byte offset is wave-uniform; a lane adds its fixed
+        // chunk offset (lanes past the unit's chunks: BUF_OOB).  A unit past
+        // the wave's count starts at the end of the range, and a last unit
+        // of one tile reads its second tile past the end: zeros either way.
         auto load_stage = [&](Unit<QT> &u, int i) {
             const int j = wave + i * NW;                  // pass-local unit index
-            const bool ok = i < count;
-            const int vc = ok ? min(2, pn - 2 * j) * (TS / 16) : 0;
-            const int base = ok ? (pb + 2 * j) * TS : BUF_OOB;
+            const int base = i < count ? (pb + 2 * j) * TS : nt * TS;
 #pragma unroll
-            for (int s = 0; s < Unit<QT>::SLOTS; s++) {
-                const int ch = s * 64 + lane;
-                const int off = ch < vc ? base + 16 * ch : BUF_OOB;
+            for (int s = 0; s < Unit<QT>::SLOTS; s++)
                 u.c[s] = __builtin_bit_cast(
-                    v4u, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, BUF_NT));
-            }
+                    v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                             wr, (int)((unsigned)chunk_off[s] + (unsigned)base), 0, BUF_NT));
         };
         __syncthreads();                                  // previous pass done with qs / ds
 
@@ -669,14 +675,16 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                                 (QT == TQ_Q4_0) ? (s[m] >> 4) : s[m];
                     }
                 } else {
-                    float dw = f16_bits_to_f32(w.sc) * weight_unscale<QT>();
-                    dw = valid ? dw : 0.0f;                   // a missing second tile adds 0
+                    // a missing second tile was staged as zeros: scale 0, adds 0;
+                    // the weights' power-of-two factor is applied to the sums
+                    // at the end (exact)
+                    const float dw = f16_bits_to_f32(w.sc);
 #pragma unroll
                     for (int m = 0; m < MM; m++)
                         acc[m] = fmaf((float)s[m], dw * x.d[m], acc[m]);
                     if constexpr (QT == TQ_Q4_1) {
                         // the min: m_w * da * sum(q), da * sum exact in fp32
-                        const float mw = valid ? f16_bits_to_f32(w.mn) : 0.0f;
+                        const float mw = f16_bits_to_f32(w.mn);
 #pragma unroll
                         for (int m = 0; m < MM; m++)
                             acc[m] = fmaf(mw, x.d[m] * x.s[m], acc[m]);
@@ -696,7 +704,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                 const int j = wave + (it + r) * NW;
                 const bool live = it + r < count;
                 if (live)
-                    store_unit<QT>(u[r], my, min(2, pn - 2 * j) * (TS / 16), lane);
+                    store_unit<QT>(u[r], my, lane);
                 load_stage(u[r], it + r + D);
                 if (live)
                     process(j);
@@ -715,7 +723,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     } else {
 #pragma unroll
         for (int m = 0; m < MM; m++)
-            red[hs][m][l] = acc[m];
+            red[hs][m][l] = acc[m] * weight_unscale<QT>();
     }
     __syncthreads();
     const int i = threadIdx.x;
