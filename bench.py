@@ -52,10 +52,10 @@ HEADLINE = "q8_0_lmhead_k4096_n128001_m1"
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "lmhead": {"fetch_kib": 272119.95, "write_kib": 500.03,
-               "src": "ad53ea866eb34c5515a91e026471379187615e7885881c7fb0c985c43aadf0ed"},
-    "decode": {"fetch_kib": 8780.57, "write_kib": 112.00,
-               "src": "ad53ea866eb34c5515a91e026471379187615e7885881c7fb0c985c43aadf0ed"},
+    "lmhead": {"fetch_kib": 272115.53, "write_kib": 500.03,
+               "src": "95687413b4de60a8ec04b14c80c0b45aee0d8fc0f5c9a01b610d35b3b7b99dac"},
+    "decode": {"fetch_kib": 8776.06, "write_kib": 112.00,
+               "src": "95687413b4de60a8ec04b14c80c0b45aee0d8fc0f5c9a01b610d35b3b7b99dac"},
     "gemm": {"fetch_kib": 13370.04, "write_kib": 8192.00,
              "src": "025a3f49ca62001f9c0cc8d3a42ecee1e891e7e973e69b9369b6ba040f7e53e8"},
     "repack": {"fetch_kib": 16144.57, "write_kib": 32256.00,

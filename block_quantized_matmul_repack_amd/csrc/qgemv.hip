@@ -640,12 +640,13 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                                     (QT == TQ_Q4_0) ? (dot[t][r] >> 4) : dot[t][r];
                         }
                     } else {
-                        float dw = f16_bits_to_f32(tile_scale_bits<QT>(tile, l)) *
-                                   weight_unscale<QT>();
-                        dw = valid ? dw : 0.0f;               // a missing second tile adds 0
+                        // a missing second tile was staged as zeros: scale
+                        // (and min) 0, adds 0; the weights' power-of-two
+                        // factor is applied to the sums at the end (exact)
+                        const float dw = f16_bits_to_f32(tile_scale_bits<QT>(tile, l));
                         float mw = 0.0f;
                         if constexpr (QT == TQ_Q4_1)
-                            mw = valid ? f16_bits_to_f32(tile_min_bits(tile, l)) : 0.0f;
+                            mw = f16_bits_to_f32(tile_min_bits(tile, l));
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
                             const int m = 4 * half + r;
@@ -718,7 +719,7 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             if (4 * half + r < MM)
-                red[wave][min(4 * half + r, MM - 1)][l] = acc[r];
+                red[wave][min(4 * half + r, MM - 1)][l] = acc[r] * weight_unscale<QT>();
         }
     } else {
 #pragma unroll
