@@ -52,16 +52,16 @@ HEADLINE = "q8_0_lmhead_k4096_n128001_m1"
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "lmhead": {"fetch_kib": 272115.53, "write_kib": 500.03,
-               "src": "95687413b4de60a8ec04b14c80c0b45aee0d8fc0f5c9a01b610d35b3b7b99dac"},
-    "decode": {"fetch_kib": 8776.06, "write_kib": 112.00,
-               "src": "95687413b4de60a8ec04b14c80c0b45aee0d8fc0f5c9a01b610d35b3b7b99dac"},
-    "gemm": {"fetch_kib": 13370.04, "write_kib": 8192.00,
-             "src": "025a3f49ca62001f9c0cc8d3a42ecee1e891e7e973e69b9369b6ba040f7e53e8"},
-    "repack": {"fetch_kib": 16144.57, "write_kib": 32256.00,
-               "src": "3f64a21a13e413f9a06bea162e3f0c08fdba044d1c33a65fbee512ddceafb73b"},
+    "lmhead": {"fetch_kib": 272108.03, "write_kib": 500.03,
+               "src": "3fbf784ffe9dca7d58c268ac056ecbae915f9c8202eca46c50f5bebe9c4ba3c1"},
+    "decode": {"fetch_kib": 8769.58, "write_kib": 112.00,
+               "src": "3fbf784ffe9dca7d58c268ac056ecbae915f9c8202eca46c50f5bebe9c4ba3c1"},
+    "gemm": {"fetch_kib": 13370.08, "write_kib": 8192.00,
+             "src": "20b97be670384a42c4d108761408eb213fb75801df118ce4ee7caf23477a1724"},
+    "repack": {"fetch_kib": 16144.35, "write_kib": 32256.00,
+               "src": "7b0ab8e7dc11b91a8e9e3f2cc3cef412067b8e5dfe6964b11da0d3da7258a4d5"},
     "mx": {"fetch_kib": 12897.43, "write_kib": 8192.00,
-           "src": "64cc532f3d6f55f515f24abde95a63d62e4da83367b5a3e88177db3770cb3b1b"},
+           "src": "bf90f2f38979bf7647fc566c8d3381ffc59d2fb5b92f2e96d8374bc660b4ffe0"},
 }
 KERNEL_SOURCES = {
     "lmhead": ("qgemv.hip", "tq_internal.h"),

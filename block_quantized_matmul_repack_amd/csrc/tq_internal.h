@@ -164,8 +164,16 @@ constexpr float weight_unscale()
 // must be active.  Returns this lane's 8 int8 codes (element 8c + e in byte
 // e) and, in every lane, the fp16 scale bits.  Every kernel that quantizes
 // activations calls this, so they all produce the same bits.
+//
+// Rounding half away from zero is done as a truncating conversion of y +
+// copysign(0.5 - 2^-25, y), the addition in fp32: the two agree for every
+// fp32 |y| < 2^23 (tests/test_host_rounding.py checks every value below 256);
+// here |y| <= 127.  The product y
+// must be rounded on its own, so contraction into a fused multiply-add is
+// off in this function.
 __device__ __forceinline__ void quant_quad(const float (&v)[8], uint2 &q, uint16_t &dbits)
 {
+#pragma clang fp contract(off)
     float amax = fabsf(v[0]);
 #pragma unroll
     for (int e = 1; e < 8; e++)
@@ -175,8 +183,11 @@ __device__ __forceinline__ void quant_quad(const float (&v)[8], uint2 &q, uint16
     const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; e++)
-        w[e >> 2] |= ((uint32_t)(int)roundf(v[e] * id) & 0xFFu) << (8 * (e & 3));
+    for (int e = 0; e < 8; e++) {
+        const float y = v[e] * id;
+        const int c = (int)(y + copysignf(0.49999997f, y));
+        w[e >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (e & 3));
+    }
     q = make_uint2(w[0], w[1]);
     dbits = f32_to_f16_bits(dd);
 }
