@@ -393,6 +393,10 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     __shared__ __attribute__((aligned(16))) uint8_t act_lds[act_lds_bytes<MM>()];
     __shared__ float red[NSLOT][MM][32];
     __shared__ __attribute__((aligned(16))) uint32_t zero16[4];   // A rows past M
+    // stores of staging work-items with nothing to stage land here, so that
+    // their loads are used on every path (a load used only under a branch
+    // gets sunk into it, behind the weight loads)
+    __shared__ __attribute__((aligned(16))) uint8_t sink_lds[48];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -446,8 +450,8 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
     float *ds = (float *)(act_lds + MM * P * 32);
     float *ss = ds + MM * P;                              // Q4_1 only
     // one 16-byte chunk (K 16 h .. 16 h + 15 of a tile) of row m into qs
-    auto put_chunk = [&](int tp, int m, int h, uint4 v) {
-        int8_t *qb = qs + (tp * MM + m) * 32;
+    auto put_chunk = [&](int tp, int m, int h, uint4 v, bool in = true) {
+        int8_t *qb = in ? qs + (tp * MM + m) * 32 : (int8_t *)sink_lds;
         if constexpr (QT == TQ_Q8_0) {
             *(uint4 *)(qb + 16 * h) = v;
         } else {
@@ -517,10 +521,8 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
             };
 #pragma unroll
             for (int m = 0; m < MM; m++) {
-                if (o < 2 * pn)
-                    put_chunk(o >> 1, m, o & 1, qv[m]);
-                if (o < pn)
-                    ds[o * MM + m] = f16_bits_to_f32(dv[m]);
+                put_chunk(o >> 1, m, o & 1, qv[m], o < 2 * pn);
+                *(o < pn ? &ds[o * MM + m] : (float *)(sink_lds + 32)) = f16_bits_to_f32(dv[m]);
                 put_sum(m, o, qv[m]);
             }
             for (int o2 = o + NW * 64; o2 < 2 * pn; o2 += NW * 64) {
