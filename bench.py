@@ -52,10 +52,10 @@ HEADLINE = "q8_0_lmhead_k4096_n128001_m1"
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "lmhead": {"fetch_kib": 272115.04, "write_kib": 500.03,
-               "src": "98c7ebdfa870895cd9033e266a0ce2623eb1eaf67375a238475ea98171b7bdb5"},
-    "decode": {"fetch_kib": 8773.06, "write_kib": 112.00,
-               "src": "98c7ebdfa870895cd9033e266a0ce2623eb1eaf67375a238475ea98171b7bdb5"},
+    "lmhead": {"fetch_kib": 272113.53, "write_kib": 500.03,
+               "src": "2c20358ce7ca5c74a645403ac9326112ea352c70de384604a748ca4eeb62c26b"},
+    "decode": {"fetch_kib": 8765.57, "write_kib": 112.00,
+               "src": "2c20358ce7ca5c74a645403ac9326112ea352c70de384604a748ca4eeb62c26b"},
     "gemm": {"fetch_kib": 13370.08, "write_kib": 8192.00,
              "src": "20b97be670384a42c4d108761408eb213fb75801df118ce4ee7caf23477a1724"},
     "repack": {"fetch_kib": 16144.35, "write_kib": 32256.00,

@@ -432,6 +432,10 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
 
     uint8_t *my = stage[wave];
     const int tro = tr8_offset(lane);                     // matrix-core path only
+    int row_clamped[4];                                   // matrix-core path: this lane's rows
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+        row_clamped[r] = min(4 * half + r, MM - 1);
     // Weight loads are raw buffer loads over this workgroup's tiles: an
     // offset at or past the range's end returns zeros and moves no data, so
     // every load is issued unconditionally.
@@ -649,11 +653,12 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                         float mw = 0.0f;
                         if constexpr (QT == TQ_Q4_1)
                             mw = f16_bits_to_f32(tile_min_bits(tile, l));
+                        // rows past M read row M - 1's scale: their dots are
+                        // 0 (zero A rows) and their sums are never stored
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
-                            const int m = 4 * half + r;
-                            const int mi = tp * MM + min(m, MM - 1);
-                            const float da = m < MM ? ds[mi] : 0.0f;
+                            const int mi = tp * MM + row_clamped[r];
+                            const float da = ds[mi];
                             acc[r] = fmaf((float)dot[t][r], dw * da, acc[r]);
                             if constexpr (QT == TQ_Q4_1)
                                 acc[r] = fmaf(mw, da * ss[mi], acc[r]);   // the min
