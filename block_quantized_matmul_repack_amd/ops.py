@@ -5,6 +5,7 @@ go to libtiledq.so; every step of the computation runs in its HIP kernels.
 Tensors must live on the GPU; outputs are allocated with torch unless given.
 """
 import ctypes
+import functools
 
 import torch
 
@@ -18,11 +19,28 @@ _DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    """Device address as an int (the C-ABI's pointer arguments take ints)."""
+    return t.data_ptr() if t is not None else None
+
+
+# torch's raw handle of a device's current stream (what
+# torch.cuda.current_stream(device).cuda_stream returns, without building a
+# Stream object on every call)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(t):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    """The current HIP stream of tensor t's device, as an int handle."""
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+@functools.lru_cache(maxsize=4096)
+def _size_query(name, *args):
+    """A size / workspace query of the C ABI; they depend on their arguments
+    alone, so results are cached."""
+    return getattr(lib(), name)(*args)
 
 
 def _need_cuda(*ts, out=None):
@@ -48,7 +66,7 @@ def _need_bytes(name, what, t, nbytes):
 
 def _check_weights(name, qtype, w, K, N, flat=False):
     """The weight buffer covers the tiles (or flat blocks) of (qtype, K, N)."""
-    nbytes = (lib().tq_flat_bytes if flat else lib().tq_tiled_bytes)(qtype, K, N)
+    nbytes = _size_query("tq_flat_bytes" if flat else "tq_tiled_bytes", qtype, K, N)
     if nbytes == 0 and N > 0:
         raise TiledqError(f"{name}: type {qtype} with K={K}, N={N} is not a valid shape")
     _need_bytes(name, "flat" if flat else "tiles", w, nbytes)
@@ -182,8 +200,8 @@ def qgemv(qtype, tiles, K, N, q, d, lut=None, out=None, split=True):
     _need_cuda(tiles, q, d, out=out)
     out = _out("tq_qgemv", q, N, out)
     st = _stream(q)
-    need = lib().tq_qgemv_workspace_bytes(qtype, K, N, M) if split else 0
-    ws = workspace(q.device, st.value, need) if need else None
+    need = _size_query("tq_qgemv_workspace_bytes", qtype, K, N, M) if split else 0
+    ws = workspace(q.device, st, need) if need else None
     check(lib().tq_qgemv(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut),
                          _ptr(out), out.stride(0), _ptr(ws), need, st), "tq_qgemv")
     return out
@@ -219,8 +237,8 @@ def qgemv_x(qtype, tiles, K, N, x, lut=None, out=None, split=True):
     M = x.shape[0]
     out = _out("tq_qgemv_x", x, N, out)
     st = _stream(x)
-    need = lib().tq_qgemv_workspace_bytes(qtype, K, N, M) if split else 0
-    ws = workspace(x.device, st.value, need) if need else None
+    need = _size_query("tq_qgemv_workspace_bytes", qtype, K, N, M) if split else 0
+    ws = workspace(x.device, st, need) if need else None
     check(lib().tq_qgemv_x(qtype, _ptr(tiles), K, N, _DTYPES[x.dtype], _ptr(x), x.stride(0), M,
                            _lut_arg(lut), _ptr(out), out.stride(0), _ptr(ws), need, st),
           "tq_qgemv_x")
@@ -254,8 +272,8 @@ def matmul(qtype, tiles, K, N, q, d, lut=None, out=None):
     _need_cuda(tiles, q, d, out=out)
     out = _out("tq_matmul", q, N, out)
     st = _stream(q)
-    need = lib().tq_matmul_workspace_bytes(qtype, K, N, M)
-    ws = workspace(q.device, st.value, need) if need else None
+    need = _size_query("tq_matmul_workspace_bytes", qtype, K, N, M)
+    ws = workspace(q.device, st, need) if need else None
     check(lib().tq_matmul(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut),
                           _ptr(out), out.stride(0), _ptr(ws), need, st), "tq_matmul")
     return out
@@ -277,8 +295,8 @@ def matmul_x(qtype, tiles, K, N, x, lut=None, out=None):
         raise TiledqError("tiledq operates on GPU tensors only")
     out = _out("tq_matmul_x", x, N, out)
     st = _stream(x)
-    need = lib().tq_matmul_x_workspace_bytes(qtype, K, N, M)
-    ws = workspace(x.device, st.value, need) if need else None
+    need = _size_query("tq_matmul_x_workspace_bytes", qtype, K, N, M)
+    ws = workspace(x.device, st, need) if need else None
     check(lib().tq_matmul_x(qtype, _ptr(tiles), K, N, _DTYPES[x.dtype], _ptr(x), x.stride(0), M,
                             _lut_arg(lut), _ptr(out), out.stride(0), _ptr(ws), need, st),
           "tq_matmul_x")
@@ -349,8 +367,8 @@ def matmul_mx(tiles, K, N, q, e, out=None):
     _need_cuda(tiles, q, e, out=out)
     out = _out("tq_matmul_mx", q, N, out)
     st = _stream(q)
-    need = lib().tq_matmul_mx_workspace_bytes(K, N, M)
-    ws = workspace(q.device, st.value, need) if need else None
+    need = _size_query("tq_matmul_mx_workspace_bytes", K, N, M)
+    ws = workspace(q.device, st, need) if need else None
     check(lib().tq_matmul_mx(_ptr(tiles), K, N, _ptr(q), _ptr(e), M, _ptr(out), out.stride(0),
                              _ptr(ws), need, st), "tq_matmul_mx")
     return out
