@@ -165,11 +165,11 @@ def quantize_act(x, K=None, q=None, d=None):
     return q, d
 
 
-def _out(name, q, N, out):
-    M = q.shape[0]
-    _check_out(name, out, M, N)
+def _out(q, N, out):
+    """`out` as given (the caller has checked it with _check_out), else a new
+    fp32 [M, N] tensor on q's device."""
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=q.device)
+        out = torch.empty((q.shape[0], N), dtype=torch.float32, device=q.device)
     return out
 
 
@@ -198,7 +198,7 @@ def qgemv(qtype, tiles, K, N, q, d, lut=None, out=None, split=True):
     _check_weights("tq_qgemv", qtype, tiles, K, N)
     _check_out("tq_qgemv", out, M, N)
     _need_cuda(tiles, q, d, out=out)
-    out = _out("tq_qgemv", q, N, out)
+    out = _out(q, N, out)
     st = _stream(q)
     need = _size_query("tq_qgemv_workspace_bytes", qtype, K, N, M) if split else 0
     ws = workspace(q.device, st, need) if need else None
@@ -216,7 +216,7 @@ def qgemv_noalloc(qtype, tiles, K, N, q, d, lut=None, out=None):
     _check_weights("tq_qgemv_noalloc", qtype, tiles, K, N)
     _check_out("tq_qgemv_noalloc", out, M, N)
     _need_cuda(tiles, q, d, out=out)
-    out = _out("tq_qgemv_noalloc", q, N, out)
+    out = _out(q, N, out)
     check(lib().tq_qgemv_noalloc(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), M, _lut_arg(lut),
                                  _ptr(out), out.stride(0), _stream(q)), "tq_qgemv_noalloc")
     return out
@@ -235,7 +235,7 @@ def qgemv_x(qtype, tiles, K, N, x, lut=None, out=None, split=True):
     if not x.is_cuda:
         raise TiledqError("tiledq operates on GPU tensors only")
     M = x.shape[0]
-    out = _out("tq_qgemv_x", x, N, out)
+    out = _out(x, N, out)
     st = _stream(x)
     need = _size_query("tq_qgemv_workspace_bytes", qtype, K, N, M) if split else 0
     ws = workspace(x.device, st, need) if need else None
@@ -251,7 +251,7 @@ def qgemm(qtype, tiles, K, N, q, d, lut=None, out=None):
     _check_weights("tq_qgemm", qtype, tiles, K, N)
     _check_out("tq_qgemm", out, M, N)
     _need_cuda(tiles, q, d, out=out)
-    out = _out("tq_qgemm", q, N, out)
+    out = _out(q, N, out)
     check(lib().tq_qgemm(qtype, _ptr(tiles), K, N, _ptr(q), _ptr(d), q.shape[0], _lut_arg(lut),
                          _ptr(out), out.stride(0), _stream(q)), "tq_qgemm")
     return out
@@ -270,7 +270,7 @@ def matmul(qtype, tiles, K, N, q, d, lut=None, out=None):
     _check_weights("tq_matmul", qtype, tiles, K, N)
     _check_out("tq_matmul", out, M, N)
     _need_cuda(tiles, q, d, out=out)
-    out = _out("tq_matmul", q, N, out)
+    out = _out(q, N, out)
     st = _stream(q)
     need = _size_query("tq_matmul_workspace_bytes", qtype, K, N, M)
     ws = workspace(q.device, st, need) if need else None
@@ -293,7 +293,7 @@ def matmul_x(qtype, tiles, K, N, x, lut=None, out=None):
     _need_cuda(tiles, out=out)
     if not x.is_cuda:
         raise TiledqError("tiledq operates on GPU tensors only")
-    out = _out("tq_matmul_x", x, N, out)
+    out = _out(x, N, out)
     st = _stream(x)
     need = _size_query("tq_matmul_x_workspace_bytes", qtype, K, N, M)
     ws = workspace(x.device, st, need) if need else None
@@ -350,7 +350,7 @@ def qgemm_mx(tiles, K, N, q, e, out=None):
         raise TiledqError("qgemm_mx: buffer too small")
     _check_out("tq_qgemm_mx", out, M, N)
     _need_cuda(tiles, q, e, out=out)
-    out = _out("tq_qgemm_mx", q, N, out)
+    out = _out(q, N, out)
     check(lib().tq_qgemm_mx(_ptr(tiles), K, N, _ptr(q), _ptr(e), M, _ptr(out), out.stride(0),
                             _stream(q)), "tq_qgemm_mx")
     return out
@@ -365,7 +365,7 @@ def matmul_mx(tiles, K, N, q, e, out=None):
         raise TiledqError("matmul_mx: buffer too small")
     _check_out("tq_matmul_mx", out, M, N)
     _need_cuda(tiles, q, e, out=out)
-    out = _out("tq_matmul_mx", q, N, out)
+    out = _out(q, N, out)
     st = _stream(q)
     need = _size_query("tq_matmul_mx_workspace_bytes", K, N, M)
     ws = workspace(q.device, st, need) if need else None
@@ -379,7 +379,7 @@ def _flat_product(name, qtype, flat, K, N, q, d, lut, out):
     _check_weights(name, qtype, flat, K, N, flat=True)
     _check_out(name, out, M, N)
     _need_cuda(flat, q, d, out=out)
-    out = _out(name, q, N, out)
+    out = _out(q, N, out)
     check(getattr(lib(), name)(qtype, _ptr(flat), K, N, _ptr(q), _ptr(d), q.shape[0],
                                _lut_arg(lut), _ptr(out), out.stride(0), _stream(q)), name)
     return out
