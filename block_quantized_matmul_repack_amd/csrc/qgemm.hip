@@ -9,11 +9,13 @@
 //   - activations: 128 rows x 4 x 32 int8, natural K order, and their fp16
 //     block scales go to LDS as loaded;
 //   - weights: each of the group's 8 waves takes one of the step's 8 tiles (2
-//     stripes x 4 blocks) and reads it as dwords of 4 rows / 2 rows of a
-//     column pair ("Block-32 Quantized Formats"), transposes bytes in
-//     registers with v_perm_b32, decodes them to int8 (code - 8, table
-//     lookup, or the int8 itself) and writes them to LDS in [row][K] order,
-//     with the fp16 row scales.
+//     stripes x 4 blocks) and gets it as dwords of 4 rows / 2 rows of a
+//     column pair ("Block-32 Quantized Formats") -- read from the tile
+//     directly, or (Q8_0, IQ4_NL) loaded as contiguous chunks and read back
+//     from a per-wave LDS slice -- transposes bytes in registers with
+//     v_perm_b32, decodes them to int8 (code - 8, table lookup, or the int8
+//     itself) and writes them to LDS in [row][K] order, with the fp16 row
+//     scales.
 // LDS is double-buffered and the global loads run two steps ahead of the
 // MFMAs (two register stages), with one barrier per step.  Q4_0 weights are
 // staged as 16 * (code - 8) (two bit operations per 4 weights); the 16 is
@@ -73,6 +75,18 @@ static_assert(TQ_GEMM_KB0 >= 0 && TQ_GEMM_KB0 <= KB, "group 0 takes 0 .. KB k-bl
 // lanes of a b128 read of 16 consecutive rows hit 16 different bank groups.
 constexpr int LDS_ROW = 144;
 
+// Q8_0 and IQ4_NL tiles are loaded as contiguous chunks in lane order (16
+// or 8 bytes per lane, every request whole cache lines), put through a
+// per-wave LDS slice and read back in the transposing order; the other
+// types load the lane's dwords straight from the tile (4 per 64-byte column
+// pair row, half of each line per request), which measured as fast or
+// faster for them.
+template <int QT>
+constexpr bool raw_tiles()
+{
+    return QT == TQ_Q8_0 || QT == TQ_IQ4_NL;
+}
+
 struct LdsMain {
     uint8_t A[2][BM * LDS_ROW];
     uint8_t B[2][BN * LDS_ROW];
@@ -88,10 +102,19 @@ struct LdsMin {
     float asum[2][BM][KB];
     uint64_t mw[2][BN];
 };
+// Each staging wave's tile quants as loaded (raw_tiles types).
+template <int QT>
+struct LdsRaw {
+    uint32_t raw[BN / 32 * KB][Fmt<QT>::scale_off / 4];
+};
 template <int QT>
 struct Lds : LdsMain {};
 template <>
 struct Lds<TQ_Q4_1> : LdsMain, LdsMin {};
+template <>
+struct Lds<TQ_Q8_0> : LdsMain, LdsRaw<TQ_Q8_0> {};
+template <>
+struct Lds<TQ_IQ4_NL> : LdsMain, LdsRaw<TQ_IQ4_NL> {};
 
 // Buffer ranges of one workgroup: its activation rows, their scales, and its
 // two weight stripes.  Loads past them return zero.
@@ -114,7 +137,7 @@ struct Ranges {
 template <int QT, int FT>
 struct Offs {
     static constexpr int NWD = (QT == TQ_Q8_0 || FT == TQ_Q4_K) ? 4 : 2;
-    int a[2], da, w[NWD], dw;
+    int a[2], da, w[NWD], dw, wt;
     int kba, kbw;                 // k-block of this thread's activation / weight scale
     int hw, rowsb;                // flat: half, and (Q4_K) the row's first super-block
 };
@@ -152,16 +175,18 @@ __device__ __forceinline__ Offs<QT, FT> make_offs(int64_t nkt, int64_t K, int ti
     const int tt = wave >> 2, l = lane & 31, hh = lane >> 5;
     o.kbw = wave & 3;
     const int tile = (int)(tt * nkt + o.kbw) * TS;
+    // o.w: the lane's quant dwords, relative to the tile
+    o.wt = tile;
     if constexpr (QT == TQ_Q8_0) {
         const int p = l >> 1, h = l & 1;
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            o.w[i] = tile + ((8 * h + 4 * hh + i) * 16 + p) * 4;
+            o.w[i] = ((8 * h + 4 * hh + i) * 16 + p) * 4;
     } else {
         const int g = l >> 2, c = l & 3;
 #pragma unroll
         for (int i = 0; i < 2; i++)
-            o.w[i] = tile + ((4 * c + 2 * hh + i) * 8 + g) * 4;
+            o.w[i] = ((4 * c + 2 * hh + i) * 8 + g) * 4;
     }
     o.dw = tile + Fmt<QT>::scale_off + (QT == TQ_MXFP4 ? l : (QT == TQ_Q4_1 ? 4 * l : 2 * l));
     return o;
@@ -258,9 +283,23 @@ __device__ __forceinline__ void load_step(StageRegs<QT, FT> &s, const Ranges &rg
         if constexpr (QT == TQ_Q4_1)
             s.mw = __builtin_amdgcn_raw_buffer_load_b16(rg.w, o.dw + 2, kt0 * TS, 0);
     }
+    if constexpr (raw_tiles<QT>()) {
+        // the tile's quant bytes as contiguous chunks in lane order
+        const int lane = threadIdx.x & 63;
+        if constexpr (QT == TQ_Q8_0) {
+            const v4i v =
+                __builtin_amdgcn_raw_buffer_load_b128(rg.w, o.wt + 16 * lane, kt0 * TS, BUF_NT);
+            s.w[0] = v.x, s.w[1] = v.y, s.w[2] = v.z, s.w[3] = v.w;
+        } else {
+            const auto v =
+                __builtin_amdgcn_raw_buffer_load_b64(rg.w, o.wt + 8 * lane, kt0 * TS, BUF_NT);
+            s.w[0] = (uint32_t)v[0], s.w[1] = (uint32_t)v[1];
+        }
+    } else {
 #pragma unroll
-    for (int i = 0; i < Offs<QT, FT>::NWD; i++)
-        s.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rg.w, o.w[i], kt0 * TS, BUF_NT);
+        for (int i = 0; i < Offs<QT, FT>::NWD; i++)
+            s.w[i] = __builtin_amdgcn_raw_buffer_load_b32(rg.w, o.wt + o.w[i], kt0 * TS, BUF_NT);
+    }
 }
 
 // 8 quant bytes of a flat 4-bit block half (elements 8h .. 8h + 7 in the
@@ -283,9 +322,25 @@ __device__ __forceinline__ void decode_flat4(uint32_t v, const Lut &lut, uint32_
 }
 
 template <int QT, bool DOTS, int FT>
-__device__ __forceinline__ void store_step(const StageRegs<QT, FT> &s, Lds<QT> &L, int buf,
-                                           const Lut &lut, int tid)
+__device__ __forceinline__ void store_step(const StageRegs<QT, FT> &s0, Lds<QT> &L, int buf,
+                                           const Lut &lut, int tid, const Offs<QT, FT> &o)
 {
+    // raw_tiles types: the loaded chunks go to the wave's LDS slice, and the
+    // lane's dwords are read back from it in the transposing order (a wave's
+    // LDS operations take effect in program order)
+    StageRegs<QT, FT> s = s0;
+    if constexpr (FT < 0 && raw_tiles<QT>()) {
+        const int lane = tid & 63;
+        uint32_t *raw = L.raw[tid >> 6];
+        if constexpr (QT == TQ_Q8_0)
+            *(v4i *)(raw + 4 * lane) = v4i{(int)s0.w[0], (int)s0.w[1], (int)s0.w[2], (int)s0.w[3]};
+        else
+            *(uint2 *)(raw + 2 * lane) = make_uint2(s0.w[0], s0.w[1]);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < Offs<QT, FT>::NWD; i++)
+            s.w[i] = raw[o.w[i] / 4];
+    }
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int ch = tid + THREADS * i;
@@ -528,7 +583,7 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
         if constexpr (ST) {
             load_step<QT, DOTS, FT>(r0, rg, o, (int)kend, (int)kbeg);
             load_step<QT, DOTS, FT>(r1, rg, o, (int)kend, (int)kbeg + KB);
-            store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
+            store_step<QT, DOTS, FT>(r0, L, 0, lut, tid, o);
         }
         __syncthreads();
         for (int64_t step = 0; step < nsteps2; step += 2) {
@@ -537,14 +592,14 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
                 load_step<QT, DOTS, FT>(r0, rg, o, (int)kend, (int)(kbeg + (step + 2) * KB));
             compute(0, kbeg / KB + step, stage);
             if constexpr (ST)
-                store_step<QT, DOTS, FT>(r1, L, 1, lut, tid);
+                store_step<QT, DOTS, FT>(r1, L, 1, lut, tid, o);
             __syncthreads();
             // odd step: buffer 1 is computed, r0 holds step+2, r1 is free
             if constexpr (ST)
                 load_step<QT, DOTS, FT>(r1, rg, o, (int)kend, (int)(kbeg + (step + 3) * KB));
             compute(1, kbeg / KB + step + 1, stage);
             if constexpr (ST)
-                store_step<QT, DOTS, FT>(r0, L, 0, lut, tid);
+                store_step<QT, DOTS, FT>(r0, L, 0, lut, tid, o);
             __syncthreads();
         }
     };
