@@ -131,6 +131,30 @@ def test_qgemm_y(tq, qtype, M, K, N):
     _y_case(tq, tq.qgemm, qtype, M, K, N, seed=M * 5 + K + N)
 
 
+# K whose k-blocks do not fill the GEMM's 4-block steps (5, 12 and 13
+# blocks: an odd step count, a padded last step, a last step of one block),
+# with row counts that end inside a 32-row sub-block and inside a 128-row
+# block; y and the block dots of the GEMM.
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M", [7, 129])
+@pytest.mark.parametrize("K,N", [(160, 40), (384, 96), (416, 65)])
+def test_qgemm_y_partial_steps(tq, qtype, M, K, N):
+    _y_case(tq, tq.qgemm, qtype, M, K, N, seed=M * 11 + K + N)
+
+
+@pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M", [7, 129])
+@pytest.mark.parametrize("K,N", [(160, 40), (416, 65)])
+def test_block_dots_gemm_partial_steps(tq, qtype, M, K, N):
+    inp = make(qtype, K, N, M, seed=M * 13 + K + N)
+    tiles, tdev = _dev(inp, qtype, K, N)
+    q, _ = oracle.quantize_act(inp.x)
+    ref = oracle.block_dots(qtype, tiles, K, N, q, LUT)
+    got = tq.block_dots(qtype, tdev, K, N, torch.from_numpy(q).cuda(), lut=LUT,
+                        path=tq.PATH_GEMM).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
 @pytest.mark.parametrize("qtype", TYPES)
 def test_gemv_gemm_agree(tq, qtype):
     K, N, M = 1024, 130, 8
