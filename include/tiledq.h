@@ -2,8 +2,8 @@
  * tiledq -- matrix-vector and matrix-matrix multiply over block-32 quantized
  * weights repacked into 32x32 tiles, on AMD Instinct MI355X (gfx950).
  *
- * Formats follow the page "Hexagon backend developer details" (llama.cpp
- * docs/backend/snapdragon/developer.md), section "Tiled Weight Formats":
+ * Formats follow the page "Hexagon backend developer details", section
+ * "Tiled Weight Formats":
  *
  *   Grid ("Tile Dimensions and Grid Layout").  A weight matrix of logical
  *   shape [ne0, ne1] = [K, N] (N output rows of K elements each) is cut into

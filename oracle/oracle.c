@@ -6,9 +6,8 @@
  * HIP library and its Python binding) never calls it and shares no code,
  * header, table or constant with it.
  *
- * Source of every definition: the page "Hexagon backend developer details"
- * (llama.cpp docs/backend/snapdragon/developer.md), section "Tiled Weight
- * Formats" with its subsections "Tile Dimensions and Grid Layout" and
+ * Source of every definition: the page "Hexagon backend developer details",
+ * section "Tiled Weight Formats" with its subsections "Tile Dimensions and Grid Layout" and
  * "Block-32 Quantized Formats" (Q4_0, Q8_0, IQ4_NL, MXFP4, Q4_1), and section "Memory
  * buffers" (dynamically quantized activations).  Where the page is silent the
  * reading taken is stated at the function.  The MXFP8 activation side of the
