@@ -56,8 +56,8 @@ TRAFFIC = {
                "src": "2c20358ce7ca5c74a645403ac9326112ea352c70de384604a748ca4eeb62c26b"},
     "decode": {"fetch_kib": 8765.57, "write_kib": 112.00,
                "src": "2c20358ce7ca5c74a645403ac9326112ea352c70de384604a748ca4eeb62c26b"},
-    "gemm": {"fetch_kib": 13370.56, "write_kib": 8192.00,
-             "src": "7821bb389538a565ab68bcb17151d0c0ea66791e98159c760870f1c9a277bfc0"},
+    "gemm": {"fetch_kib": 13370.22, "write_kib": 8192.00,
+             "src": "60c94a51a98aaf7081516f7acd81c43e05f9dff37a86452764a4966e399a397e"},
     "repack": {"fetch_kib": 16144.35, "write_kib": 32256.00,
                "src": "7b0ab8e7dc11b91a8e9e3f2cc3cef412067b8e5dfe6964b11da0d3da7258a4d5"},
     "mx": {"fetch_kib": 12897.43, "write_kib": 8192.00,

@@ -9,13 +9,14 @@
 //   - activations: 128 rows x 4 x 32 int8, natural K order, and their fp16
 //     block scales go to LDS as loaded;
 //   - weights: each of the group's 8 waves takes one of the step's 8 tiles (2
-//     stripes x 4 blocks) and gets it as dwords of 4 rows / 2 rows of a
-//     column pair ("Block-32 Quantized Formats") -- read from the tile
-//     directly, or (Q8_0, IQ4_NL) loaded as contiguous chunks and read back
+//     stripes x 4 blocks).  4-bit tiles: the wave gets it as dwords of 4
+//     rows of a column pair ("Block-32 Quantized Formats") -- read from the
+//     tile directly, or (IQ4_NL) loaded as contiguous chunks and read back
 //     from a per-wave LDS slice -- transposes bytes in registers with
-//     v_perm_b32, decodes them to int8 (code - 8, table lookup, or the int8
-//     itself) and writes them to LDS in [row][K] order, with the fp16 row
-//     scales.
+//     v_perm_b32, decodes them to int8 (code - 8 or a table lookup) and
+//     writes them to LDS in [row][K] order.  Q8_0 tiles go to LDS as loaded
+//     and the MFMA operand is gathered from them with 16-bit transposing
+//     reads.  The fp16 row scales go to LDS beside them.
 // LDS is double-buffered and the global loads run two steps ahead of the
 // MFMAs (two register stages), with one barrier per step.  Q4_0 weights are
 // staged as 16 * (code - 8) (two bit operations per 4 weights); the 16 is
@@ -39,6 +40,7 @@
 namespace tq {
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -76,15 +78,26 @@ static_assert(TQ_GEMM_KB0 >= 0 && TQ_GEMM_KB0 <= KB, "group 0 takes 0 .. KB k-bl
 constexpr int LDS_ROW = 144;
 
 // Q8_0 and IQ4_NL tiles are loaded as contiguous chunks in lane order (16
-// or 8 bytes per lane, every request whole cache lines), put through a
-// per-wave LDS slice and read back in the transposing order; the other
-// types load the lane's dwords straight from the tile (4 per 64-byte column
-// pair row, half of each line per request), which measured as fast or
-// faster for them.
+// or 8 bytes per lane, every request whole cache lines).  IQ4_NL chunks go
+// through a per-wave LDS slice and are read back in the transposing order
+// the decode takes; Q8_0 tiles stay in the B buffer as loaded (see q8_tr).
+// The other types load the lane's dwords straight from the tile (4 per
+// 64-byte column pair row, half of each line per request), which measured
+// as fast or faster for them.
 template <int QT>
 constexpr bool raw_tiles()
 {
     return QT == TQ_Q8_0 || QT == TQ_IQ4_NL;
+}
+// Q8_0 tiles in the B buffer as loaded (the tile's byte layout, one 1 KB
+// tile per stripe and k-block), the MFMA operand read with two
+// ds_read_b64_tr_b16: the tile's halfwords are (column pair, row) pairs of
+// int8, so a 16-bit transposing read gathers one row's column pairs, in K
+// order, with no byte permutes in the staging wave.
+template <int QT, int FT>
+constexpr bool q8_tr()
+{
+    return QT == TQ_Q8_0 && FT < 0;
 }
 
 struct LdsMain {
@@ -102,19 +115,17 @@ struct LdsMin {
     float asum[2][BM][KB];
     uint64_t mw[2][BN];
 };
-// Each staging wave's tile quants as loaded (raw_tiles types).
-template <int QT>
+// Each staging wave's IQ4_NL tile quants as loaded.
 struct LdsRaw {
-    uint32_t raw[BN / 32 * KB][Fmt<QT>::scale_off / 4];
+    uint32_t raw[BN / 32 * KB][Fmt<TQ_IQ4_NL>::scale_off / 4];
 };
 template <int QT>
 struct Lds : LdsMain {};
 template <>
 struct Lds<TQ_Q4_1> : LdsMain, LdsMin {};
 template <>
-struct Lds<TQ_Q8_0> : LdsMain, LdsRaw<TQ_Q8_0> {};
-template <>
-struct Lds<TQ_IQ4_NL> : LdsMain, LdsRaw<TQ_IQ4_NL> {};
+struct Lds<TQ_IQ4_NL> : LdsMain, LdsRaw {};
+static_assert(BN / 32 * KB * 1024 <= BN * LDS_ROW, "Q8_0 tiles of a step fit a B buffer");
 
 // Buffer ranges of one workgroup: its activation rows, their scales, and its
 // two weight stripes.  Loads past them return zero.
@@ -175,13 +186,13 @@ __device__ __forceinline__ Offs<QT, FT> make_offs(int64_t nkt, int64_t K, int ti
     const int tt = wave >> 2, l = lane & 31, hh = lane >> 5;
     o.kbw = wave & 3;
     const int tile = (int)(tt * nkt + o.kbw) * TS;
-    // o.w: the lane's quant dwords, relative to the tile
+    // o.w: the lane's quant dwords, relative to the tile (Q8_0 tiles are
+    // loaded and staged whole)
     o.wt = tile;
     if constexpr (QT == TQ_Q8_0) {
-        const int p = l >> 1, h = l & 1;
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            o.w[i] = ((8 * h + 4 * hh + i) * 16 + p) * 4;
+            o.w[i] = 0;
     } else {
         const int g = l >> 2, c = l & 3;
 #pragma unroll
@@ -197,8 +208,8 @@ struct StageRegs {
     uint4 a[2];               // activations: 2 x 16 bytes
     uint16_t da;              // one activation block scale
     uint32_t w[Offs<QT, FT>::NWD]; // weight dwords (tiles, 4-bit: rows 4g..4g+3 at column
-                              // pairs 4c+2hh, 4c+2hh+1; Q8_0: rows 2p, 2p+1 at 8h+4hh ..
-                              // +3; flat: the thread's quant bytes in order)
+                              // pairs 4c+2hh, 4c+2hh+1; Q8_0: the lane's 16 bytes of
+                              // the tile in order; flat: the thread's quant bytes in order)
     uint16_t dw;              // weight row scale (MXFP4: its E8M0 byte)
     uint16_t mw;              // Q4_1: weight row min
     uint4 hdr;                // flat Q4_K: the super-block's d, dmin and scale bytes
@@ -325,17 +336,14 @@ template <int QT, bool DOTS, int FT>
 __device__ __forceinline__ void store_step(const StageRegs<QT, FT> &s0, Lds<QT> &L, int buf,
                                            const Lut &lut, int tid, const Offs<QT, FT> &o)
 {
-    // raw_tiles types: the loaded chunks go to the wave's LDS slice, and the
+    // IQ4_NL tiles: the loaded chunks go to the wave's LDS slice, and the
     // lane's dwords are read back from it in the transposing order (a wave's
     // LDS operations take effect in program order)
     StageRegs<QT, FT> s = s0;
-    if constexpr (FT < 0 && raw_tiles<QT>()) {
+    if constexpr (FT < 0 && QT == TQ_IQ4_NL) {
         const int lane = tid & 63;
         uint32_t *raw = L.raw[tid >> 6];
-        if constexpr (QT == TQ_Q8_0)
-            *(v4i *)(raw + 4 * lane) = v4i{(int)s0.w[0], (int)s0.w[1], (int)s0.w[2], (int)s0.w[3]};
-        else
-            *(uint2 *)(raw + 2 * lane) = make_uint2(s0.w[0], s0.w[1]);
+        *(uint2 *)(raw + 2 * lane) = make_uint2(s0.w[0], s0.w[1]);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int i = 0; i < Offs<QT, FT>::NWD; i++)
@@ -397,15 +405,10 @@ __device__ __forceinline__ void store_step(const StageRegs<QT, FT> &s0, Lds<QT> 
     const int wave = tid >> 6, lane = tid & 63;
     const int tt = wave >> 2, kb = wave & 3, l = lane & 31, hh = lane >> 5;
     uint8_t *B = L.B[buf] + (32 * tt) * LDS_ROW + 32 * kb;
-    if constexpr (QT == TQ_Q8_0) {
-        // rows 2p (low halfwords) and 2p+1 (high halfwords), K 16h+8hh .. +7
-        const int p = l >> 1, h = l & 1;
-        const uint32_t a0 = __builtin_amdgcn_perm(s.w[1], s.w[0], 0x05040100u);
-        const uint32_t a1 = __builtin_amdgcn_perm(s.w[3], s.w[2], 0x05040100u);
-        const uint32_t b0 = __builtin_amdgcn_perm(s.w[1], s.w[0], 0x07060302u);
-        const uint32_t b1 = __builtin_amdgcn_perm(s.w[3], s.w[2], 0x07060302u);
-        *(uint2 *)(B + (2 * p) * LDS_ROW + 16 * h + 8 * hh) = make_uint2(a0, a1);
-        *(uint2 *)(B + (2 * p + 1) * LDS_ROW + 16 * h + 8 * hh) = make_uint2(b0, b1);
+    if constexpr (q8_tr<QT, FT>()) {
+        // the tile as loaded: tile (stripe tt, k-block kb) at 1 KB (tt KB + kb)
+        *(v4i *)(L.B[buf] + (tt * KB + kb) * 1024 + 16 * lane) =
+            v4i{(int)s.w[0], (int)s.w[1], (int)s.w[2], (int)s.w[3]};
     } else {
         // rows 4g+j: byte j of the two column-pair dwords holds K = 2cp (low
         // nibble) and 2cp+1 (high nibble) for cp = 4c+2hh, 4c+2hh+1, i.e. the
@@ -497,9 +500,29 @@ __global__ __launch_bounds__(WG_THREADS, TQ_GEMM_MIN_BLOCKS) void k_qgemm(const 
     // operand holds the step's KB activation scales of row m (k = 0..3) and
     // serves every k-block of the step; its B operand keeps only k-block kb's
     // weight scale (k = kb), so the k-sum is the one product.
+    // Q8_0 operand through ds_read_b64_tr_b16: lane j of each 16-lane group
+    // G gets halfword j % 4 of the 8-byte runs that lanes 4 i + j / 4 of the
+    // group point at (i = 0..3).  Lane 4 i + a points at column pair c0 + i,
+    // rows 4 s .. 4 s + 3 (s = 4 (G % 2) + a), so lane j holds column pairs
+    // c0 .. c0 + 3 of row 16 (G % 2) + j = li: K 2 c0 .. 2 c0 + 7, in order;
+    // c0 = 16 lk / 2 for the first read, 4 more for the second.
+    const int trq = lane & 15, trg = (lane >> 4) & 1;
+    const int tr_off = ((8 * lk + (trq >> 2)) * 32 + 4 * (4 * trg + (trq & 3))) * 2;
     auto mfmas = [&](int buf, int kb, const v4h &ua, uint64_t wv, v16i &dot, v16f &sc) {
         const v4i a = *(const v4i *)(L.A[buf] + (32 * wm + li) * LDS_ROW + 32 * kb + 16 * lk);
-        const v4i b = *(const v4i *)(L.B[buf] + (32 * wn + li) * LDS_ROW + 32 * kb + 16 * lk);
+        v4i b;
+        if constexpr (q8_tr<QT, FT>()) {
+            typedef short v4s __attribute__((ext_vector_type(4)));
+            const uint8_t *t = L.B[buf] + (wn * KB + kb) * 1024 + tr_off;
+            const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s *)(t));
+            const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s *)(t + 256));
+            const v2i x0 = __builtin_bit_cast(v2i, r0), x1 = __builtin_bit_cast(v2i, r1);
+            b = v4i{x0.x, x0.y, x1.x, x1.y};
+        } else {
+            b = *(const v4i *)(L.B[buf] + (32 * wn + li) * LDS_ROW + 32 * kb + 16 * lk);
+        }
         const v16i z = {};
         dot = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
         if constexpr (!DOTS) {
