@@ -53,15 +53,15 @@ FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
     "lmhead": {"fetch_kib": 272113.53, "write_kib": 500.03,
-               "src": "2c20358ce7ca5c74a645403ac9326112ea352c70de384604a748ca4eeb62c26b"},
+               "src": "996cede1de25dd7278eebba978226b59e07278c63834404b568d998c0d27cf8d"},
     "decode": {"fetch_kib": 8765.57, "write_kib": 112.00,
-               "src": "2c20358ce7ca5c74a645403ac9326112ea352c70de384604a748ca4eeb62c26b"},
+               "src": "996cede1de25dd7278eebba978226b59e07278c63834404b568d998c0d27cf8d"},
     "gemm": {"fetch_kib": 13370.22, "write_kib": 8192.00,
-             "src": "60c94a51a98aaf7081516f7acd81c43e05f9dff37a86452764a4966e399a397e"},
+             "src": "85eea73c90c07c699538e430d7765b8606d76769b19020a9682e93b45cb58ec0"},
     "repack": {"fetch_kib": 16144.35, "write_kib": 32256.00,
-               "src": "7b0ab8e7dc11b91a8e9e3f2cc3cef412067b8e5dfe6964b11da0d3da7258a4d5"},
+               "src": "13ee865d5b5d1480aafc1f034eaad5446734deecedae01956acf64171bf07d6e"},
     "mx": {"fetch_kib": 12897.43, "write_kib": 8192.00,
-           "src": "bf90f2f38979bf7647fc566c8d3381ffc59d2fb5b92f2e96d8374bc660b4ffe0"},
+           "src": "4413a56d8387d2cf011c0fb2982931b0ad3d4c460d439b67a01c5f4de04f9923"},
 }
 KERNEL_SOURCES = {
     "lmhead": ("qgemv.hip", "tq_internal.h"),

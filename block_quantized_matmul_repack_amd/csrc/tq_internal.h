@@ -35,8 +35,12 @@ template <> struct Fmt<TQ_Q4_K> {
 
 // Raw buffer loads (CDNA buffer resource descriptor, stride 0): a load whose
 // byte offset lies outside [0, bytes) returns zero, so out-of-range operands
-// are zeroed without branches and every path issues the same loads.  Ranges
-// stay below 2^31 bytes; BUF_OOB is an offset past all of them.
+// are zeroed without branches and every path issues the same loads.  The
+// offset checked is the whole one, vector plus scalar operand, and a load of
+// several dwords is checked dword by dword: a dword with any byte at or past
+// `bytes` reads zero, the dwords wholly inside are returned (checked on
+// gfx950).  Ranges stay below 2^31 bytes; BUF_OOB is an offset past all of
+// them.
 constexpr int64_t BUF_MAX_BYTES = 0x7E000000;
 constexpr int BUF_OOB = 0x7F000000;  // + any in-tile offset stays positive
 constexpr int BUF_NT = 2;                 // aux bits: nontemporal (stream past the caches)
