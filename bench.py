@@ -53,9 +53,9 @@ FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
     "lmhead": {"fetch_kib": 272113.53, "write_kib": 500.03,
-               "src": "996cede1de25dd7278eebba978226b59e07278c63834404b568d998c0d27cf8d"},
+               "src": "a023ec3067616ae97e19ad8584e4de2345103f85d509d2e6820554b092c1d9f4"},
     "decode": {"fetch_kib": 8765.57, "write_kib": 112.00,
-               "src": "996cede1de25dd7278eebba978226b59e07278c63834404b568d998c0d27cf8d"},
+               "src": "a023ec3067616ae97e19ad8584e4de2345103f85d509d2e6820554b092c1d9f4"},
     "gemm": {"fetch_kib": 13370.22, "write_kib": 8192.00,
              "src": "85eea73c90c07c699538e430d7765b8606d76769b19020a9682e93b45cb58ec0"},
     "repack": {"fetch_kib": 16144.35, "write_kib": 32256.00,

@@ -654,14 +654,33 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
                         if constexpr (QT == TQ_Q4_1)
                             mw = f16_bits_to_f32(tile_min_bits(tile, l));
                         // rows past M read row M - 1's scale: their dots are
-                        // 0 (zero A rows) and their sums are never stored
+                        // 0 (zero A rows) and their sums are never stored.
+                        // M = 4 / 8: the half's 4 rows are contiguous (16-byte
+                        // aligned), one read; at M = 4 half 1 holds no row and
+                        // takes half 0's scales
+                        float da[4], sa[4];
+                        if constexpr (MM == 4 || MM == 8) {
+                            const int mi0 = tp * MM + (MM == 8 ? 4 * half : 0);
+                            const float4 v = *(const float4 *)(ds + mi0);
+                            da[0] = v.x, da[1] = v.y, da[2] = v.z, da[3] = v.w;
+                            if constexpr (QT == TQ_Q4_1) {
+                                const float4 w4 = *(const float4 *)(ss + mi0);
+                                sa[0] = w4.x, sa[1] = w4.y, sa[2] = w4.z, sa[3] = w4.w;
+                            }
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; r++) {
+                                const int mi = tp * MM + row_clamped[r];
+                                da[r] = ds[mi];
+                                if constexpr (QT == TQ_Q4_1)
+                                    sa[r] = ss[mi];
+                            }
+                        }
 #pragma unroll
                         for (int r = 0; r < 4; r++) {
-                            const int mi = tp * MM + row_clamped[r];
-                            const float da = ds[mi];
-                            acc[r] = fmaf((float)dot[t][r], dw * da, acc[r]);
+                            acc[r] = fmaf((float)dot[t][r], dw * da[r], acc[r]);
                             if constexpr (QT == TQ_Q4_1)
-                                acc[r] = fmaf(mw, da * ss[mi], acc[r]);   // the min
+                                acc[r] = fmaf(mw, da[r] * sa[r], acc[r]);   // the min
                         }
                     }
                 }
