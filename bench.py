@@ -55,7 +55,7 @@ TRAFFIC = {
     "lmhead": {"fetch_kib": 272113.53, "write_kib": 500.03,
                "src": "a023ec3067616ae97e19ad8584e4de2345103f85d509d2e6820554b092c1d9f4"},
     "decode": {"fetch_kib": 8765.57, "write_kib": 112.00,
-               "src": "a023ec3067616ae97e19ad8584e4de2345103f85d509d2e6820554b092c1d9f4"},
+               "src": "7fae92fe729906a405c91cb156f6c5d2120677d4e4b852edd949caa09e718952"},
     "gemm": {"fetch_kib": 13370.22, "write_kib": 8192.00,
              "src": "85eea73c90c07c699538e430d7765b8606d76769b19020a9682e93b45cb58ec0"},
     "repack": {"fetch_kib": 16144.35, "write_kib": 32256.00,

@@ -494,51 +494,73 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
         // wave are then all in flight while the activations are staged.
         Unit<QT> u[D];
         if constexpr (XT < 0) {
-            // per row m: 16-byte chunks o < 2 pn of q, scales o < pn
+            // The pass's 2 MM pn 16-byte chunks of q in staged order: chunk c
+            // is half c % 2 of row (c / 2) % MM of tile c / (2 MM), and scale
+            // s is row s % MM of tile s / MM (ds[s]).  Consecutive threads
+            // take consecutive chunks: every load is a distinct 16 bytes
+            // (each row's 32 bytes of 2 NT / (2 MM) tiles per instruction,
+            // whole lines) and the LDS stores are contiguous.  The first
+            // batch, loaded before the weight units, holds QB1 chunks and
+            // SB1 scales per thread: a whole pass of up to NT / 2 tiles.
             const int64_t q0 = (int64_t)(kt0 + pb) * 32;
-            auto qload = [&](int m, int o) {
-                return *(const uint4 *)(act.q + m * K + q0 + 16 * min(o, 2 * pn - 1));
+            const int nch = 2 * MM * pn, nsc = MM * pn;
+            constexpr int NT = NW * 64;
+            constexpr int QB1 = (MM + 1) / 2, SB1 = (MM + 3) / 4;
+            auto qload = [&](int c) {
+                c = min(c, nch - 1);
+                const int tm = c >> 1, tp = tm / MM, m = tm - tp * MM;
+                return *(const uint4 *)(act.q + m * K + q0 + 32 * tp + 16 * (c & 1));
             };
-            auto dload = [&](int m, int o) -> uint16_t {
-                return DOTS ? (uint16_t)0 : act.d[m * nb + kt0 + pb + min(o, pn - 1)];
+            auto dload = [&](int s) -> uint16_t {
+                s = min(s, nsc - 1);
+                const int tp = s / MM, m = s - tp * MM;
+                return DOTS ? (uint16_t)0 : act.d[m * nb + kt0 + pb + tp];
             };
             const int o = threadIdx.x;
-            uint4 qv[MM];
-            uint16_t dv[MM];
+            uint4 qv[QB1];
+            uint16_t dv[SB1];
 #pragma unroll
-            for (int m = 0; m < MM; m++) {
-                qv[m] = qload(m, o);
-                dv[m] = dload(m, o);
-            }
+            for (int i = 0; i < QB1; i++)
+                qv[i] = qload(o + i * NT);
+#pragma unroll
+            for (int i = 0; i < SB1; i++)
+                dv[i] = dload(o + i * NT);
 #pragma unroll
             for (int r = 0; r < D; r++)
                 load_stage(u[r], r);
-            // Q4_1: the sum of a tile's 32 int8 from its two chunks, held by
-            // neighbouring threads (o, o ^ 1; pairs are in range together)
-            auto put_sum = [&](int m, int oo, const uint4 &v) {
+            // Q4_1: the sum of a tile row's 32 int8 from its two chunks, held
+            // by neighbouring threads (c, c ^ 1; NT is even, so pairs are in
+            // range together)
+            auto put_sum = [&](int c, const uint4 &v) {
                 if constexpr (QT == TQ_Q4_1 && !DOTS) {
                     int p = byte_sum(v.x, byte_sum(v.y, byte_sum(v.z, byte_sum(v.w, 0))));
                     p += dpp_xor1(p);
-                    if (oo < 2 * pn && (oo & 1) == 0)
-                        ss[(oo >> 1) * MM + m] = (float)p;
+                    if (c < nch && (c & 1) == 0)
+                        ss[c >> 1] = (float)p;
                 }
             };
+            auto put = [&](int c, const uint4 &v, bool in) {
+                const int tm = c >> 1, tp = tm / MM;
+                put_chunk(tp, tm - tp * MM, c & 1, v, in);
+            };
 #pragma unroll
-            for (int m = 0; m < MM; m++) {
-                put_chunk(o >> 1, m, o & 1, qv[m], o < 2 * pn);
-                *(o < pn ? &ds[o * MM + m] : (float *)(sink_lds + 32)) = f16_bits_to_f32(dv[m]);
-                put_sum(m, o, qv[m]);
+            for (int i = 0; i < QB1; i++) {
+                const int c = o + i * NT;
+                put(c, qv[i], c < nch);
+                put_sum(c, qv[i]);
             }
-            for (int o2 = o + NW * 64; o2 < 2 * pn; o2 += NW * 64) {
 #pragma unroll
-                for (int m = 0; m < MM; m++) {
-                    const uint4 v2 = qload(m, o2);
-                    put_chunk(o2 >> 1, m, o2 & 1, v2);
-                    if (o2 < pn)
-                        ds[o2 * MM + m] = f16_bits_to_f32(dload(m, o2));
-                    put_sum(m, o2, v2);
-                }
+            for (int i = 0; i < SB1; i++) {
+                const int sc = o + i * NT;
+                *(sc < nsc ? &ds[sc] : (float *)(sink_lds + 32)) = f16_bits_to_f32(dv[i]);
             }
+            for (int c = o + QB1 * NT; c < nch; c += NT) {
+                const uint4 v2 = qload(c);
+                put(c, v2, true);
+                put_sum(c, v2);
+            }
+            for (int sc = o + SB1 * NT; sc < nsc; sc += NT)
+                ds[sc] = f16_bits_to_f32(dload(sc));
         } else {
             // one 32-element block per quad of lanes, 8 elements per lane
             // (quant_quad); block b = tp * MM + m, QB blocks per batch
