@@ -52,8 +52,8 @@ HEADLINE = "q8_0_lmhead_k4096_n128001_m1"
 FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "lmhead": {"fetch_kib": 272113.53, "write_kib": 500.03,
-               "src": "a023ec3067616ae97e19ad8584e4de2345103f85d509d2e6820554b092c1d9f4"},
+    "lmhead": {"fetch_kib": 272114.03, "write_kib": 500.03,
+               "src": "7fae92fe729906a405c91cb156f6c5d2120677d4e4b852edd949caa09e718952"},
     "decode": {"fetch_kib": 8765.57, "write_kib": 112.00,
                "src": "7fae92fe729906a405c91cb156f6c5d2120677d4e4b852edd949caa09e718952"},
     "gemm": {"fetch_kib": 13370.22, "write_kib": 8192.00,
