@@ -243,6 +243,32 @@ def test_qgemv_every_row_count(tq, qtype, M, K, N):
 
 
 @pytest.mark.parametrize("qtype", TYPES)
+@pytest.mark.parametrize("M,K", [(1, 20480), (2, 9216), (4, 9216), (5, 9216), (8, 9216),
+                                 (8, 4544)])
+def test_qgemv_long_passes(tq, qtype, M, K):
+    """One workgroup per stripe over 142 to 640 k-tiles: a staging pass of
+    the int8 activations then holds more chunks and scales than the loads
+    issued ahead of the weight stream cover (128 tiles at M = 4 and 8, 256
+    at M = 1 and 512 for M = 1's scales), so the trailing staging loops run,
+    and at M >= 2 several passes follow each other.  Block dots bit for bit;
+    y unsplit, split and fused within tolerance."""
+    N = 40
+    inp = make(qtype, K, N, M, seed=M * 13 + K)
+    tiles, tdev = _dev(inp, qtype, K, N)
+    q, d = oracle.quantize_act(inp.x)
+    y_ref, acond = oracle.matmul(qtype, tiles, K, N, q, d, LUT)
+    qd, dd = tq.quantize_act(torch.from_numpy(inp.x).cuda())
+    for split in (False, True):
+        y = tq.qgemv(qtype, tdev, K, N, qd, dd, lut=LUT, split=split)
+        check_y(y.cpu().numpy(), y_ref, acond, (qtype, M, K, N, split))
+    yx = tq.qgemv_x(qtype, tdev, K, N, torch.from_numpy(inp.x).cuda(), lut=LUT, split=False)
+    check_y(yx.cpu().numpy(), y_ref, acond, (qtype, M, K, N, "fused"))
+    ref = oracle.block_dots(qtype, tiles, K, N, q, LUT)
+    got = tq.block_dots(qtype, tdev, K, N, qd, lut=LUT, path=tq.PATH_GEMV).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("qtype", TYPES)
 @pytest.mark.parametrize("M", [1, 8, 9, 13, 16, 17, 40, 49])
 @pytest.mark.parametrize("K,N", [(512, 100), (4096, 300)])
 def test_matmul_dispatch(tq, qtype, M, K, N):
