@@ -53,9 +53,9 @@ FETCH_SCALE = 262144.0 / 131083.55
 WRITE_SCALE = 1.0
 TRAFFIC = {
     "lmhead": {"fetch_kib": 272114.03, "write_kib": 500.03,
-               "src": "7fae92fe729906a405c91cb156f6c5d2120677d4e4b852edd949caa09e718952"},
+               "src": "3a423a43e4d871f6bb6356bd6ea67de6b15fe92051fa5175fcce1628c83275ea"},
     "decode": {"fetch_kib": 8765.57, "write_kib": 112.00,
-               "src": "7fae92fe729906a405c91cb156f6c5d2120677d4e4b852edd949caa09e718952"},
+               "src": "3a423a43e4d871f6bb6356bd6ea67de6b15fe92051fa5175fcce1628c83275ea"},
     "gemm": {"fetch_kib": 13370.22, "write_kib": 8192.00,
              "src": "85eea73c90c07c699538e430d7765b8606d76769b19020a9682e93b45cb58ec0"},
     "repack": {"fetch_kib": 16144.35, "write_kib": 32256.00,

@@ -497,11 +497,13 @@ __global__ __launch_bounds__(NW * 64) void k_qgemv(const uint8_t *__restrict__ t
             // The pass's 2 MM pn 16-byte chunks of q in staged order: chunk c
             // is half c % 2 of row (c / 2) % MM of tile c / (2 MM), and scale
             // s is row s % MM of tile s / MM (ds[s]).  Consecutive threads
-            // take consecutive chunks: every load is a distinct 16 bytes
-            // (each row's 32 bytes of 2 NT / (2 MM) tiles per instruction,
-            // whole lines) and the LDS stores are contiguous.  The first
-            // batch, loaded before the weight units, holds QB1 chunks and
-            // SB1 scales per thread: a whole pass of up to NT / 2 tiles.
+            // take consecutive chunks: every load is a distinct 16 bytes (a
+            // wave's load reads 32 / MM consecutive tiles of each row, runs
+            // of 1024 / MM bytes, whole 128-byte lines) and the LDS stores
+            // are contiguous.  The first batch, loaded before the weight
+            // units, holds QB1 chunks and SB1 scales per thread: all of a
+            // pass of up to NT / 4 tiles (NT / 2 at MM = 1); the rest of a
+            // longer pass is loaded after it.
             const int64_t q0 = (int64_t)(kt0 + pb) * 32;
             const int nch = 2 * MM * pn, nsc = MM * pn;
             constexpr int NT = NW * 64;
